@@ -1,0 +1,347 @@
+"""Pins of the CPU oracle to facts fixed outside itself (CPU only).
+
+Each test checks the oracle against hand-encoded bytes, closed forms, brute force
+on tiny inputs, identities of the mathematics, or an independent library routine,
+so that a dropped term, a wrong sign, index or nibble position, or a transposed
+operand in the oracle fails at least one of them.
+"""
+
+import itertools
+import math
+import os
+from collections import OrderedDict
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                yield [p.strip() for p in line.split(";")]
+
+
+# ----------------------------------------------------------------------------- dequant
+
+def test_dequant_hand_encoded_blocks():
+    n = 0
+    for name, bhex, shex, sval, codes in _rows("dequant_blocks.txt"):
+        code_bytes = np.array([int(b, 16) for b in bhex.split()], dtype=np.uint8)
+        scale_bits = int(shex, 16)
+        scale = Fraction(sval)
+        u = [int(c) for c in codes.split()]
+        assert len(code_bytes) == 16 and len(u) == 32
+        # fp16 decoding of the scale is exact, subnormals included
+        assert O.fp16_codes_to_f64(np.array([scale_bits], np.uint16))[0] == float(scale), name
+        scale_bytes = np.array([scale_bits & 0xFF, scale_bits >> 8], dtype=np.uint8)
+        assert list(O.decode_codes(code_bytes, 1, 32)[0]) == u, name
+        w = O.dequant(code_bytes, scale_bytes, 1, 32)[0]
+        want = [float((ui - 8) * scale) for ui in u]
+        assert list(w) == want, name
+        n += 1
+    assert n >= 12
+
+
+def test_dequant_rows_and_blocks_are_independent():
+    # two rows, two blocks each: each block takes its own scale, rows do not mix
+    ramp = [0x20, 0x64, 0x31, 0x75, 0xA8, 0xEC, 0xB9, 0xFD] * 2
+    zero = [0x88] * 16
+    code_bytes = np.array(ramp + zero + zero + ramp, dtype=np.uint8)
+    scales = np.array([0x3C00, 0x4000, 0x3800, 0x4400], dtype=np.uint16)  # 1, 2, 0.5, 4
+    w = O.dequant(code_bytes, scales.view(np.uint8), 2, 64)
+    q = np.array([(i % 16) - 8 for i in range(32)], dtype=np.float64)
+    assert np.array_equal(w[0, :32], q * 1.0)
+    assert np.array_equal(w[0, 32:], np.zeros(32))
+    assert np.array_equal(w[1, :32], np.zeros(32))
+    assert np.array_equal(w[1, 32:], q * 4.0)
+
+
+def test_blob_layout_sizes():
+    # model shape: 3 matrices x (786,432 code bytes + 98,304 scale bytes) = 2,654,208 = 648 x 4 KiB
+    lay = O.blob_layout(2048, 768)
+    assert lay["total"][1] == 2_654_208 == 648 * 4096
+    assert lay["gate_scales"][0] == 3 * 786_432
+    assert O.blob_layout(256, 128)["total"][1] == 55_296
+
+
+# ----------------------------------------------------------------------------- router
+
+def test_router_one_hot_and_zero():
+    rng = np.random.default_rng(3)
+    E, H = 16, 64
+    Wr = rng.standard_normal((E, H)).astype(np.float32).astype(np.float64)
+    bias = rng.standard_normal(E).astype(np.float32)
+    for h in (0, 17, 63):
+        x = np.zeros((1, H))
+        x[0, h] = 1.0
+        assert np.array_equal(O.router_logits(x, Wr)[0], Wr[:, h])
+    assert np.array_equal(O.router_logits(np.zeros((2, H)), Wr, bias), np.tile(bias.astype(np.float64), (2, 1)))
+
+
+def test_select_closed_form_k10_of_512():
+    rows = list(_rows("topk_closed_form.txt"))
+    k = int([r for r in rows if r[0] == "k"][0][1])
+    E = int([r for r in rows if r[0] == "E"][0][1])
+    logits = -np.arange(E, dtype=np.float32)[None, :]
+    ids = O.select_topk(logits, k)
+    assert list(ids[0]) == list(range(k))
+    w = O.route_weights(logits, ids)[0]
+    for _, j, val in [r for r in rows if r[0] == "w"]:
+        assert w[int(j)] == pytest.approx(float(val), rel=1e-14)
+    assert abs(w.sum() - 1.0) < 1e-15
+
+
+def test_select_all_equal_takes_lowest_ids():
+    logits = np.zeros((3, 512), dtype=np.float32)
+    ids = O.select_topk(logits, 10)
+    assert (ids == np.arange(10)).all()
+    w = O.route_weights(logits, ids)
+    assert np.allclose(w, 0.1, rtol=0, atol=1e-16)
+
+
+def _brute_topk(l, k):
+    """The unique k-subset S with l_i > l_j, or l_i == l_j and i < j, for i in S, j not in S."""
+    E = len(l)
+    found = []
+    for S in itertools.combinations(range(E), k):
+        rest = [j for j in range(E) if j not in S]
+        if all(l[i] > l[j] or (l[i] == l[j] and i < j) for i in S for j in rest):
+            found.append(S)
+    assert len(found) == 1
+    return sorted(found[0], key=lambda i: (-l[i], i))
+
+
+def test_select_matches_brute_force_with_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(60):
+        E = int(rng.integers(3, 9))
+        k = int(rng.integers(1, E + 1))
+        l = rng.integers(-3, 4, size=E).astype(np.float32)  # many ties
+        ids = O.select_topk(l[None, :], k)[0]
+        assert list(ids) == _brute_topk(list(l), k), (l, k)
+
+
+def test_weights_equal_full_softmax_renormalised():
+    rng = np.random.default_rng(7)
+    l = (rng.standard_normal((8, 64)) * 2).astype(np.float32)
+    ids = O.select_topk(l, 6)
+    w = O.route_weights(l, ids)
+    full = np.exp(l.astype(np.float64) - l.max(axis=1, keepdims=True))
+    full /= full.sum(axis=1, keepdims=True)
+    sel = np.take_along_axis(full, ids.astype(np.int64), axis=1)
+    assert np.allclose(w, sel / sel.sum(axis=1, keepdims=True), rtol=1e-13, atol=0)
+    # selected logits dominate the rest
+    for t in range(8):
+        rest = np.setdiff1d(np.arange(64), ids[t])
+        assert l[t, ids[t]].min() >= l[t, rest].max()
+        assert np.all(np.diff(w[t]) <= 0)
+
+
+# ----------------------------------------------------------------------------- FFN
+
+def _hand_blob():
+    H, F = 64, 32
+    lay = O.blob_layout(H, F)
+    blob = np.zeros(lay["total"][1], dtype=np.uint8)
+    for name in ("gate_codes", "up_codes", "down_codes"):
+        off, sz = lay[name]
+        blob[off:off + sz] = 0x88
+    for name in ("gate_scales", "up_scales", "down_scales"):
+        off, sz = lay[name]
+        blob[off:off + sz].view(np.uint16)[:] = 0x3C00
+    row_bytes = {"gate": H // 2, "up": H // 2, "down": F // 2}
+    row_blocks = {"gate": H // 32, "up": H // 32, "down": F // 32}
+    # element -> (byte within the row, nibble shift), hand-derived for the elements used
+    pos = {0: (0, 0), 1: (2, 0), 5: (3, 0)}
+    expect = {}
+    for r in _rows("hand_expert.txt"):
+        if r[0] == "expect":
+            expect[int(r[1])] = float(r[2])
+            continue
+        mat, row, el, u, sbits = r[0], int(r[1]), int(r[2]), int(r[3]), int(r[4], 16)
+        coff = lay[mat + "_codes"][0] + row * row_bytes[mat]
+        b, sh = pos[el]
+        blob[coff + b] = (blob[coff + b] & (0xF0 if sh == 0 else 0x0F)) | (u << sh)
+        soff = lay[mat + "_scales"][0] + row * row_blocks[mat] * 2
+        blob[soff:soff + 2].view(np.uint16)[0] = sbits
+    return blob, H, F, expect
+
+
+def test_ffn_hand_built_expert_closed_form():
+    blob, H, F, expect = _hand_blob()
+    Wg, Wu, Wd = O.expert_weights(blob, H, F)
+    x = np.zeros((1, H))
+    x[0, 0] = 2.0
+    y = O.swiglu_ffn(Wg, Wu, Wd, x)[0]
+    want = np.zeros(H)
+    for o, v in expect.items():
+        want[o] = v
+    assert np.allclose(y, want, rtol=1e-15, atol=0), (np.nonzero(y), y[list(expect)])
+    # the same expert through the whole layer (k = 1, no shared expert): weight exactly 1
+    Wr = np.zeros((4, H))
+    Wr[2, 0] = 1.0
+    out = O.moe_layer(x, Wr, None, 1, lambda e: blob, None, H, F)
+    assert list(out["ids"][0]) == [2] and out["w"][0, 0] == 1.0
+    assert np.allclose(out["y"][0], want, rtol=1e-15, atol=0)
+
+
+def test_silu_spot_values():
+    assert O.silu(np.array([1.0]))[0] == pytest.approx(0.7310585786300049, rel=1e-15)
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    assert O.silu(np.array([-40.0]))[0] == pytest.approx(-40.0 * math.exp(-40.0), rel=1e-12)
+
+
+def _tiny_layer(seed, T=4, E=8, H=256, F=128, k=2, shared=True):
+    rng = np.random.default_rng(seed)
+    blobs = [rng.integers(0, 256, size=O.blob_layout(H, F)["total"][1], dtype=np.uint8) for _ in range(E + 1)]
+    for b in blobs:  # sane scales: fp16 |N(0, 0.02)|
+        lay = O.blob_layout(H, F)
+        off = lay["gate_scales"][0]
+        n = (len(b) - off) // 2
+        b[off:] = np.abs(rng.standard_normal(n) * 0.02).astype(np.float16).view(np.uint8)
+    Wr = (rng.standard_normal((E, H)) * 0.1).astype(np.float32).astype(np.float64)
+    x = rng.standard_normal((T, H)).astype(np.float32).astype(np.float64)
+    return x, Wr, blobs, (blobs[E] if shared else None)
+
+
+def test_layer_matches_fp64_dense_brute_force():
+    """Every expert computed densely, weighted by a dense gate vector zero off the top-k."""
+    H, F, E, k = 256, 128, 8, 2
+    x, Wr, blobs, sh = _tiny_layer(11)
+    out = O.moe_layer(x, Wr, None, k, lambda e: blobs[e], sh, H, F)
+    T = x.shape[0]
+    y = np.zeros((T, H))
+    l = x @ Wr.T
+    for t in range(T):
+        # brute-force selection on fp32 logits, weights by the plain softmax formula
+        l32 = l[t].astype(np.float32)
+        S = _brute_topk(list(l32), k)
+        dense = np.zeros(E)
+        z = sum(math.exp(float(l32[i]) - float(l32[S[0]])) for i in S)
+        for i in S:
+            dense[i] = math.exp(float(l32[i]) - float(l32[S[0]])) / z
+        for e in range(E + 1):
+            Wg, Wu, Wd = O.expert_weights(blobs[e], H, F)
+            ge = sum(Wg[:, c] * x[t, c] for c in range(H))  # column-sum formulation
+            ue = sum(Wu[:, c] * x[t, c] for c in range(H))
+            he = ge / (1 + np.exp(-ge)) * ue
+            ye = sum(Wd[:, r] * he[r] for r in range(F))
+            y[t] += (dense[e] if e < E else 1.0) * ye
+    assert np.allclose(out["y"], y, rtol=1e-10, atol=1e-10)
+
+
+def test_layer_zero_input_gives_zero():
+    x, Wr, blobs, sh = _tiny_layer(13)
+    out = O.moe_layer(np.zeros_like(x), Wr, None, 2, lambda e: blobs[e], sh, 256, 128)
+    assert np.array_equal(out["y"], np.zeros_like(out["y"]))
+
+
+def test_layer_top1_without_shared_is_one_expert():
+    H, F = 256, 128
+    x, Wr, blobs, _ = _tiny_layer(17, shared=False)
+    out = O.moe_layer(x, Wr, None, 1, lambda e: blobs[e], None, H, F)
+    assert np.all(out["w"] == 1.0)
+    for t in range(x.shape[0]):
+        e = int(np.argmax((x[t] @ Wr.T).astype(np.float32)))
+        Wg, Wu, Wd = O.expert_weights(blobs[e], H, F)
+        # equal up to the BLAS's own rounding order (one row vs a batch of rows)
+        assert np.allclose(out["y"][t], O.swiglu_ffn(Wg, Wu, Wd, x[t:t + 1])[0], rtol=1e-13, atol=1e-13)
+
+
+def test_all_resident_equals_slot_pool_bitwise():
+    H, F, E = 256, 128, 8
+    x, Wr, blobs, sh = _tiny_layer(19)
+    direct = O.moe_layer(x, Wr, None, 2, lambda e: blobs[e], sh, H, F)
+    # the same experts scattered over a larger arena through a slot table
+    rng = np.random.default_rng(1)
+    n_slots = 13
+    slots = rng.permutation(n_slots)[:E]
+    arena = [None] * n_slots
+    for e in range(E):
+        arena[slots[e]] = blobs[e].copy()
+    table = np.full(E, -1)
+    table[np.arange(E)] = slots
+    pooled = O.moe_layer(x, Wr, None, 2, lambda e: arena[table[e]], sh, H, F)
+    assert np.array_equal(direct["y"], pooled["y"])
+
+
+# ----------------------------------------------------------------------------- residency
+
+def test_slot_lookup_identity_and_set_difference():
+    ids = np.array([[3, 1, 7], [7, 0, 2]])
+    slots, miss = O.slot_lookup(np.arange(8), ids)
+    assert np.array_equal(slots, ids) and miss.size == 0
+    rng = np.random.default_rng(2)
+    for _ in range(50):
+        E = 64
+        table = np.where(rng.random(E) < 0.6, rng.permutation(E), -1)
+        ids = np.stack([rng.choice(E, 10, replace=False) for _ in range(int(rng.integers(1, 9)))])
+        slots, miss = O.slot_lookup(table, ids)
+        assert np.array_equal(slots, table[ids])
+        assert list(miss) == sorted(set(ids.ravel().tolist()) - set(np.nonzero(table >= 0)[0].tolist()))
+
+
+def _lru_recency_list(n_experts, initial, steps):
+    """LRU as a recency-ordered list of slots (an independent formulation)."""
+    S = len(initial)
+    where = {e: s for s, e in enumerate(initial)}
+    holder = list(initial)
+    order = OrderedDict((s, None) for s in reversed(range(S)))  # least recent first
+    log = []
+    for ids in steps:
+        selected = set(int(e) for e in np.ravel(ids))
+        misses = sorted(e for e in selected if e not in where)
+        fills = []
+        for e in misses:
+            victim = next(s for s in order if holder[s] not in selected)
+            old = holder[victim]
+            del where[old]
+            where[e] = victim
+            holder[victim] = e
+            fills.append((e, victim, old))
+        for e in np.ravel(ids):
+            s = where[int(e)]
+            order.move_to_end(s)
+        log.append((misses, fills))
+    return log
+
+
+def test_slot_pool_lru_matches_recency_list():
+    rng = np.random.default_rng(23)
+    for trial in range(30):
+        E = int(rng.integers(12, 40))
+        S = int(rng.integers(4, 10))
+        k = int(rng.integers(1, min(S, 4) + 1))
+        T = int(rng.integers(1, 3))
+        if T * k > S:
+            T = 1
+        initial = list(rng.permutation(E)[:S])
+        steps = [np.stack([rng.choice(E, k, replace=False) for _ in range(T)]) for _ in range(40)]
+        pool = O.SlotPoolLRU(E, initial)
+        got = [pool.step(s) for s in steps]
+        want = _lru_recency_list(E, initial, steps)
+        assert got == want
+        # exclusive tiers: every expert is in exactly one place
+        resident = set(np.nonzero(pool.table >= 0)[0].tolist())
+        assert len(resident) == S and sorted(pool.table[list(resident)]) == list(range(S))
+
+
+# ----------------------------------------------------------------------------- grouping
+
+def test_group_pairs_matches_stable_argsort():
+    rng = np.random.default_rng(29)
+    for n, E in ((1, 1), (40, 8), (4096, 513), (3000, 5)):
+        ids = rng.integers(0, E, size=n)
+        counts, offsets, perm = O.group_pairs(ids, E)
+        assert np.array_equal(perm, np.argsort(ids, kind="stable"))
+        assert np.array_equal(counts, np.bincount(ids, minlength=E))
+        assert offsets[0] == 0 and offsets[-1] == n
+    counts, offsets, perm = O.group_pairs(np.zeros(0, dtype=np.int64), 4)
+    assert counts.sum() == 0 and perm.size == 0 and list(offsets) == [0] * 5

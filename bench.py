@@ -1,0 +1,235 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode1|decode8x48|prefill4k|prefill32k]
+
+A step is one pass of the whole layer (router -> top-k -> residency check -> expert FFNs ->
+combine) through ``moe_layer_forward`` over one batch of seeded synthetic input that is
+already resident in HBM.  The default workload is single-token decode through one
+model-shaped layer (512 routed experts top-10 + 1 shared, hidden 2048, expert FFN 768,
+4-bit block-32 weights with fp16 scales), with a fresh bf16 token each step.
+
+One JSON line is printed, with the live roofline of the dominant kernel (timed per launch
+with HIP events recorded around that kernel alone) and the CPU oracle timed on a bounded
+sample on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s at decode (HBM GB/s %) and 4K prefill (MFMA %), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+
+H, F, E, K_TOP = 2048, 768, 512, 10
+X_STREAM = 1_000_000  # stream index of the benchmark's activations
+
+
+def _hip():
+    import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+    lib = ctypes.CDLL("libamdhip64.so.7")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+class KernelTimer:
+    """One (start, stop) hipEvent pair per timed step around the named kernel."""
+
+    def __init__(self, n: int):
+        self.hip = _hip()
+        self.pairs = []
+        for _ in range(n):
+            a, b = ctypes.c_void_p(), ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(a)) == 0 and self.hip.hipEventCreate(ctypes.byref(b)) == 0
+            self.pairs.append((a, b))
+
+    def durations_ms(self):
+        out = []
+        for a, b in self.pairs:
+            ms = ctypes.c_float()
+            assert self.hip.hipEventSynchronize(b) == 0
+            assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+            out.append(ms.value)
+        return out
+
+    def close(self):
+        for a, b in self.pairs:
+            self.hip.hipEventDestroy(a)
+            self.hip.hipEventDestroy(b)
+
+
+def build_model_layer(device, seed=0, cfg=2, layer=0, bias_c=None, table_perm=True):
+    """Arena of the 512 routed experts, the shared expert, bf16 router: all in HBM."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_route_amd import synth as S
+
+    stride = (S.blob_bytes(H, F) + 4095) // 4096 * 4096
+    arena = torch.empty((E, stride), dtype=torch.uint8, device=device)
+    keys = [S.stream_key(seed, cfg, "blob", layer, e) for e in range(E)]
+    rng = np.random.default_rng(seed + 1000 * layer)
+    slot_of = rng.permutation(E) if table_perm else np.arange(E)
+    tmp = torch.empty((64, stride), dtype=torch.uint8, device=device)
+    for i in range(0, E, 64):
+        S.expert_blobs_torch(keys[i:i + 64], H, F, tmp)
+        idx = torch.as_tensor(slot_of[i:i + 64], device=device, dtype=torch.long)
+        arena[idx] = tmp[:len(keys[i:i + 64])]
+    shared = torch.empty((stride,), dtype=torch.uint8, device=device)
+    S.expert_blobs_torch([S.stream_key(seed, cfg, "shared", layer, 0)], H, F, shared.view(1, -1))
+    router = S.bf16_normal_torch(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02, device)
+    bias = None
+    if bias_c is not None:
+        bias = torch.from_numpy(S.zipf_bias(S.rank_permutation(seed, cfg, layer, 0, E), bias_c)).to(device)
+    table = torch.from_numpy(slot_of.astype(np.int32)).to(device)
+    return dict(arena=arena, shared=shared, router=router, bias=bias, table=table, stride=stride, keys=keys,
+                slot_of=slot_of, seed=seed, cfg=cfg, layer=layer)
+
+
+def cpu_baseline_decode(n_tokens: int, seed=0, cfg=2, layer=0):
+    """The oracle (as it stands) timed on host cores for `n_tokens` single-token steps."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from mixture_experts_route_amd import synth as S
+    from oracle import moe_oracle as O
+
+    Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02)).astype(np.float64)
+    shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
+    # the first n_tokens steps' tokens of the GPU run (same stream, same rows)
+    xall = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), (n_tokens, H), 1.0))
+    xs = [xall[s:s + 1].astype(np.float64) for s in range(n_tokens)]
+    # the expert bytes are generated before the clock starts (data generation is not timed)
+    need = set()
+    for x in xs:
+        _, _, ids, _ = O.route(x, Wr, None, K_TOP)
+        need.update(int(e) for e in ids.ravel())
+    blobs = {e: S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, e), H, F) for e in need}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for x in xs:
+            O.moe_layer(x, Wr, None, K_TOP, lambda e: blobs[e], shared, H, F)
+        dt = time.perf_counter() - t0
+    return n_tokens / dt, dt
+
+
+def bench_decode1(args):
+    import numpy as np
+    import torch
+
+    from mixture_experts_route_amd import native as N
+    from mixture_experts_route_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    L = build_model_layer(dev)
+    d = N.dims(H, F, E, K_TOP, 1)
+    w = N.layer_weights(L["router"], L["arena"], L["stride"], E, L["shared"], L["bias"])
+    n_steps = args.warmup + args.steps
+    # fresh bf16 token per step, all resident before timing
+    xs = S.bf16_normal_torch(S.stream_key(0, 2, "x", 0, X_STREAM), (n_steps, H), 1.0, dev)
+    y = torch.empty((1, H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(N.moe_workspace_bytes(d, 1) // 4 + 64, dtype=torch.int32, device=dev)
+    N.moe_workspace_init(ws)
+    ids = torch.empty((1, K_TOP), dtype=torch.int32, device=dev)
+    tw = torch.empty((1, K_TOP), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    for s in range(args.warmup):
+        N.moe_layer_forward(d, w, L["table"], xs[s:s + 1], 1, y, ws, topk_ids=ids, topk_w=tw)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) == 0
+
+    timer = KernelTimer(args.steps)
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = args.warmup + i
+        N.moe_debug_kernel_events(N.TIME_DECODE_GATE_UP, timer.pairs[i][0], timer.pairs[i][1])
+        N.moe_layer_forward(d, w, L["table"], xs[s:s + 1], 1, y, ws, topk_ids=ids, topk_w=tw, stream=st)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    N.moe_debug_kernel_events(0, None, None)
+    assert N.moe_check_device_error(ws) == 0
+    k_ms = timer.durations_ms()
+    timer.close()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    # algorithmic bytes of one gate/up launch: 11 experts (10 routed, distinct, + shared), each
+    # reading its gate and up codes and scales once, plus x in and h out
+    per_expert = 2 * (F * H // 2 + F * (H // 32) * 2)
+    gu_bytes = 11 * per_expert + H * 2 + 11 * F * 4
+    gu_avg_s = float(np.mean(k_ms)) * 1e-3
+    achieved = gu_bytes / gu_avg_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x int4 -> f32",
+        "data": "synthetic",
+        "config": {
+            "workload": "single-token decode through one layer: 512 routed experts top-10 + 1 shared, hidden 2048, "
+                        "expert FFN 768, SwiGLU, 4-bit block-32 weights with fp16 scales, bf16 activations N(0,1), "
+                        "bf16 router N(0,0.02), all experts resident behind a permuted slot table; fresh token per step",
+            "tokens_per_step": 1,
+            "layer_bytes_per_step": 11 * 2_654_208 + E * H * 2 + H * 2 + H * 4,
+        },
+        "roofline": {
+            "kernel": "k_decode_gate_up (4-bit GEMV gate+up, SwiGLU fused)",
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": gu_bytes,
+            "avg_launch_us": gu_avg_s * 1e6,
+        },
+    }
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample
+        v, dt = cpu_baseline_decode(n)
+        result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                                  "sample": f"first {n} single-token steps of the same layer (seed 0), "
+                                            f"{dt:.1f} s of float64 numpy on 1 thread"}
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="decode1", choices=["decode1"])
+    ap.add_argument("--cpu-sample", type=int, default=40)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the layer's data-parallel scale-out has no exchange on the path, "
+              "so only --gpus 1 is run here", file=sys.stderr)
+        sys.exit(2)
+    res = bench_decode1(args)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

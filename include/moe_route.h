@@ -1,0 +1,236 @@
+/*
+ * moe_route.h -- C interface of the MI355X (gfx950) routed mixture-of-experts layer.
+ *
+ * The layer, as the pages describe it:
+ *   - Betelgeuse news article (fanjiajia.top, "Betelgeuse: RTX 3060 12GB + 16GB ..."),
+ *     section "mechanism: VRAM expert-slot pool, in-stream doorbell and victim cache":
+ *     48 layers x 512 routed experts; each token takes 10 routed experts + 1 shared one;
+ *     router and shared expert always resident; routed experts sit in a per-layer pool
+ *     of HBM slots; a GPU-side check finds the misses and rings the host only on a miss;
+ *     HBM and host copies of an expert are exclusive.  Section "what bit-exact means":
+ *     the top-10 selection is exact and never altered; a failed expert read is an error,
+ *     never a silent zero weight.
+ *   - halogen-flash-server README, section "Bring your own GGUF": expert weights are a
+ *     small set of values times a per-block scale (the Q4_0 family), repacked losslessly
+ *     into the kernels' own layout; unsupported formats are refused by name.
+ *   - Basalt README, section "The .basalt model file": quantized bytes used as stored.
+ *
+ * Readings where the pages are silent: router weights = softmax over the k selected
+ * logits (they sum to 1 over the chosen experts); equal logits -> lower expert id first;
+ * the optional per-expert bias is added to the logits before selection; the shared expert
+ * has weight 1; the expert FFN is SwiGLU, y_e = Wd (silu(Wg x) * (Wu x)); the layer output
+ * is y = sum_j w_j y_{e_j} (j = 0..k-1, selection order) + y_shared, with no residual.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are device pointers owned by the caller (allocated by any means);
+ *     the library never allocates or frees device memory and keeps no global state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
+ *     enqueued asynchronously on it; the call returns once it is enqueued.
+ *   - Every call validates its arguments on the host first and enqueues nothing when
+ *     it returns an error.  Return value: MOE_OK (0) or a negative MOE_E* code.
+ *   - `ws` is a caller-owned device workspace of `ws_bytes` bytes (256-byte aligned),
+ *     at least moe_workspace_bytes(dims, n_tokens).  It must be cleared once with
+ *     moe_workspace_init before its first use; calls leave it reusable.  Calls that
+ *     share one workspace must be ordered on one stream.
+ *   - Faults the device detects (an expert id out of range, a slot index out of range,
+ *     a selected expert that is not resident when its weights are needed, a NaN logit)
+ *     set bits of an error word in `ws`; the outputs of that call are then invalid.
+ *     moe_check_device_error reads and clears the word.
+ *
+ * Expert blob (one routed or shared expert; H = hidden, F = ffn):
+ *   [gate codes F x H/2][up codes F x H/2][down codes H x F/2]
+ *   [gate scales F x H/32][up scales F x H/32][down scales H x F/32]     (bytes)
+ *   Matrices are row-major: gate/up rows are the F outputs over the H inputs, down rows
+ *   the H outputs over the F inputs.  Blocks of 32 consecutive elements of a row share
+ *   one fp16 scale (little-endian).  A row's codes are 32-bit little-endian words; word d
+ *   holds elements 8d..8d+7: element 8d+2j in bits 4j..4j+3 and element 8d+2j+1 in bits
+ *   16+4j..16+4j+3 (j = 0..3).  A code u (0..15) stands for q = u - 8, and the weight is
+ *   q * scale.  Model shape (H 2048, F 768): 2,654,208 bytes = 648 x 4 KiB.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_EINVAL = -1,        /* a NULL pointer, a size out of range, inconsistent dimensions */
+  MOE_EUNSUPPORTED = -2,  /* valid request this library does not implement (dtype, block, shape) */
+  MOE_EWORKSPACE = -3,    /* ws NULL, misaligned or smaller than moe_workspace_bytes */
+  MOE_EHIP = -4,          /* a HIP runtime call failed (launch, copy, stream wait) */
+  MOE_EDEVICE = -5,       /* the device error word was set (moe_check_device_error) */
+  MOE_EFILL = -6          /* a slot-pool fill (host -> HBM expert copy) failed */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* Device error word bits (moe_check_device_error). */
+enum moe_device_error {
+  MOE_DERR_EXPERT_ID = 1,     /* a selected / given expert id outside [0, n_experts) */
+  MOE_DERR_SLOT = 2,          /* a slot-table entry >= n_slots */
+  MOE_DERR_NOT_RESIDENT = 4,  /* an expert needed by an FFN call has no slot (-1) */
+  MOE_DERR_NAN = 8,           /* a NaN logit reached the selection */
+  MOE_DERR_FILL = 16          /* the slot-pool service reported a failed fill */
+};
+
+/* Largest token count the decode entry points take (the pages' concurrent streams: Basalt
+ * README "Concurrent requests: --parallel N", N = 1..8). */
+#define MOE_DECODE_MAX_TOKENS 8
+
+/* Layer dimensions.  hidden = H, ffn = F (expert FFN width, shared expert too),
+ * n_experts = E routed experts, top_k = k, n_shared = 0 or 1, block = 32 (the only
+ * supported quantization block; anything else is MOE_EUNSUPPORTED).
+ * Supported: H and F multiples of 32 with H/32 and F/32 <= 128; 1 <= k <= 16; k <= E;
+ * E <= 1024.  The prefill path further needs H % 128 == 0 and F % 64 == 0. */
+typedef struct moe_dims {
+  int32_t hidden;
+  int32_t ffn;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t n_shared;
+  int32_t block;
+} moe_dims;
+
+/* One layer's weights (all device pointers).
+ *   router       [E][H], dtype router_dtype (MOE_F32 or MOE_BF16); row e scores expert e.
+ *   router_bias  [E] fp32 added to the logits, or NULL.
+ *   arena        expert blobs; the blob in slot s starts at arena + s * slot_stride.
+ *   slot_stride  bytes; >= moe_expert_blob_bytes and a multiple of 4096 (the Betelgeuse
+ *                article stores each expert as one 4 KB-aligned blob).
+ *   n_slots      number of slots in the arena.
+ *   shared_blob  the shared expert's blob when n_shared == 1 (always resident), else NULL. */
+typedef struct moe_layer_weights {
+  const void* router;
+  int32_t router_dtype;
+  const float* router_bias;
+  const uint8_t* arena;
+  int64_t slot_stride;
+  int32_t n_slots;
+  const uint8_t* shared_blob;
+} moe_layer_weights;
+
+/* Miss notification for a slot pool served by the host (Betelgeuse article, "mechanism":
+ * the in-stream check rings a host doorbell only on a miss).
+ *   host_miss_ids    host-mapped pinned int32[E]: the step's miss list (ascending ids).
+ *   host_miss_count  host-mapped pinned int32[2]: [0] = number of misses, [1] = epoch,
+ *                    written after the list (the host polls [1] == epoch).
+ *   ready            device-visible uint32 the stream waits on: work after the check
+ *                    runs once *ready >= epoch.  With no miss the check kernel writes
+ *                    *ready = epoch itself; otherwise the host writes it after the fills.
+ *   epoch            this call's epoch (strictly increasing over calls). */
+typedef struct moe_doorbell {
+  int32_t* host_miss_ids;
+  int32_t* host_miss_count;
+  uint32_t* ready;
+  uint32_t epoch;
+} moe_doorbell;
+
+/* Bytes of one expert blob (layout above) for `dims`; 0 if dims are invalid. */
+MOE_API size_t moe_expert_blob_bytes(const moe_dims* dims);
+
+/* Workspace bytes that every entry point below needs for up to `max_tokens` tokens;
+ * 0 if dims are invalid or max_tokens < 1. */
+MOE_API size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_tokens);
+
+/* Static message for a status code (never NULL). */
+MOE_API const char* moe_strerror(int code);
+
+/* Clears the control area at the start of `ws` (its first 4 KiB: error word, counters, miss
+ * flags) with a fill kernel on `stream`.  Call once before the workspace's first use. */
+MOE_API int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronizes `stream`, reads the device error word of `ws` into *bits_out (may be NULL)
+ * and clears it.  Returns MOE_OK when the word was 0, MOE_EDEVICE otherwise. */
+MOE_API int moe_check_device_error(void* ws, void* stream, int32_t* bits_out);
+
+/* Profiling aid.  Until the next call, every launch of kernel `which` (1 = decode gate/up
+ * GEMV, 2 = decode down GEMV, 3 = prefill gate/up grouped GEMM, 4 = prefill down grouped GEMM;
+ * 0 = off) records the hipEvent_t `start_event` / `stop_event` (created by the caller with
+ * timing enabled) around that kernel alone, via hipExtLaunchKernel.  Process-wide setting,
+ * not for concurrent use from several threads. */
+MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop_event);
+
+/* Test entry point: dequantizes matrix `matrix` (0 = gate [F][H], 1 = up [F][H],
+ * 2 = down [H][F]) of the expert blob at `blob` into fp32 `out` (row-major), exactly
+ * (q * scale is exact in fp32).  Follows halogen README "Bring your own GGUF" (a small
+ * set of values times a per-block scale). */
+MOE_API int moe_debug_dequant(const moe_dims* dims, const uint8_t* blob, int32_t matrix,
+                              float* out, void* stream);
+
+/* Router and top-k selection (Betelgeuse article, "mechanism": 10 routed experts of 512
+ * per token; "what bit-exact means": the selection is exact).
+ *   x        [n_tokens][H], dtype x_dtype (MOE_F32 or MOE_BF16).
+ *   router   [E][H], dtype router_dtype; bias [E] fp32 or NULL.
+ *   topk_ids [n_tokens][k] int32 out: ids ranked by (logit desc, id asc).
+ *   topk_w   [n_tokens][k] fp32 out: softmax over the k selected logits.
+ *   logits   [n_tokens][E] fp32 out (x . router_e + bias_e), or NULL.
+ * Logits accumulate in fp32 (bf16 x bf16 products are exact).  With more than
+ * MOE_DECODE_MAX_TOKENS tokens both x and router must be bf16. */
+MOE_API int moe_route(const moe_dims* dims, const void* x, int32_t x_dtype, int32_t n_tokens,
+                      const void* router, int32_t router_dtype, const float* bias,
+                      int32_t* topk_ids, float* topk_w, float* logits_or_null,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* In-stream residency check (Betelgeuse article, "mechanism", scheduling row: expert id ->
+ * slot on the GPU, host notified only on a miss).
+ *   layer_table [E] int32: slot of each expert, -1 = not resident (cached in LDS).
+ *   topk_ids    [n_tokens][k].
+ *   slots       [n_tokens][k] int32 out: layer_table[id] (-1 for a miss).
+ *   miss_ids    [E] int32 out: the distinct missing ids, ascending; miss_count [1] out.
+ *   bell        optional doorbell (see moe_doorbell), or NULL.
+ * Entries >= n_slots set MOE_DERR_SLOT; ids outside [0, E) set MOE_DERR_EXPERT_ID. */
+MOE_API int moe_slot_lookup(const moe_dims* dims, const int32_t* layer_table, int32_t n_slots,
+                            const int32_t* topk_ids, int32_t n_tokens, int32_t* slots,
+                            int32_t* miss_ids, int32_t* miss_count, const moe_doorbell* bell_or_null,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* Grouping of the (token, choice) pairs p = t*k + j by expert: a stable counting sort.
+ *   counts [E] out, offsets [E+1] out (exclusive prefix sums), perm [n_tokens*k] out:
+ *   pair indices in (expert, p) order.  (halogen README, "Measured": the ordering step
+ *   of the tokens moves prefill speed.) */
+MOE_API int moe_group_tokens(const moe_dims* dims, const int32_t* topk_ids, int32_t n_tokens,
+                             int32_t* counts, int32_t* offsets, int32_t* perm,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs + combine for a small batch (1..MOE_DECODE_MAX_TOKENS tokens): 4-bit GEMV,
+ * dequantized in registers, fp32 accumulation, bandwidth-bound.
+ *   layer_table [E] or NULL (NULL: expert e sits in slot e, all resident).
+ *   x [n_tokens][H] (MOE_F32 or MOE_BF16); topk_ids / topk_w [n_tokens][k] (as moe_route
+ *   writes them); y [n_tokens][H] fp32 out.
+ * Every expert a token selected must be resident (else MOE_DERR_NOT_RESIDENT). */
+MOE_API int moe_expert_ffn_decode(const moe_dims* dims, const moe_layer_weights* w,
+                                  const int32_t* layer_table_or_null, const void* x, int32_t x_dtype,
+                                  int32_t n_tokens, const int32_t* topk_ids, const float* topk_w,
+                                  float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* Expert FFNs + combine for a long batch (prefill): tokens grouped by expert, grouped GEMM
+ * on MFMA with dequantized fp16 tiles and fp32 accumulation, SwiGLU fused into the gate/up
+ * epilogue.  x must be MOE_BF16.  Arguments as moe_expert_ffn_decode, any n_tokens >= 1. */
+MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights* w,
+                                   const int32_t* layer_table_or_null, const void* x, int32_t x_dtype,
+                                   int32_t n_tokens, const int32_t* topk_ids, const float* topk_w,
+                                   float* y, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer: route -> residency check -> (wait for fills) -> expert FFNs -> combine.
+ * Uses the decode kernels for n_tokens <= MOE_DECODE_MAX_TOKENS and the prefill kernels
+ * above.  With a layer_table and a doorbell, misses are reported to the host and the FFNs
+ * run after *bell->ready >= bell->epoch (the host fills the slots and updates the table
+ * meanwhile).  topk_ids_out / topk_w_out [n_tokens][k] receive the routing if not NULL. */
+MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w,
+                              const int32_t* layer_table_or_null, const moe_doorbell* bell_or_null,
+                              const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
+                              int32_t* topk_ids_out_or_null, float* topk_w_out_or_null,
+                              void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

@@ -1,0 +1,301 @@
+// The C interface (include/moe_route.h): host-side validation, workspace carving and launches.
+// Nothing here allocates device memory; every error is reported before anything is enqueued.
+#include "kernels.hpp"
+
+namespace moe {
+
+KernelEvents g_kernel_events = {kTimeNone, nullptr, nullptr};
+
+// Workspace carve-up for up to `T` tokens.  The first kCtrlBytes hold the control words
+// (error word, counters) and, at byte 1024, the residency miss flags (one byte per expert).
+struct WsLayout {
+  size_t tasks, h, y_pairs, logits, ids, w, slots, miss_ids, miss_flag;
+  size_t prefill;  // start of the prefill region
+  size_t total;
+};
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static WsLayout ws_layout(const moe_dims* d, int T) {
+  WsLayout L{};
+  const int Td = T < kMaxDecodeTok ? T : kMaxDecodeTok;
+  const int pairs_d = Td * (d->top_k + d->n_shared);
+  size_t off = kCtrlBytes;
+  L.miss_flag = 1024;
+  L.tasks = off;
+  off = align256(off + sizeof(DecodeTask) * (size_t)decode_max_tasks(Td, d->top_k, d->n_shared));
+  L.h = off;
+  off = align256(off + sizeof(float) * (size_t)pairs_d * d->ffn);
+  L.y_pairs = off;
+  off = align256(off + sizeof(float) * (size_t)pairs_d * d->hidden);
+  L.logits = off;
+  off = align256(off + sizeof(float) * (size_t)T * d->n_experts);
+  L.ids = off;
+  off = align256(off + sizeof(int32_t) * (size_t)T * d->top_k);
+  L.w = off;
+  off = align256(off + sizeof(float) * (size_t)T * d->top_k);
+  L.slots = off;
+  off = align256(off + sizeof(int32_t) * (size_t)T * d->top_k);
+  L.miss_ids = off;
+  off = align256(off + sizeof(int32_t) * (size_t)d->n_experts);
+  L.prefill = off;
+  L.total = off;
+  return L;
+}
+
+static int check_dims(const moe_dims* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->hidden <= 0 || d->ffn <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
+  if (d->n_shared != 0 && d->n_shared != 1) return MOE_EINVAL;
+  if (d->top_k > d->n_experts) return MOE_EINVAL;
+  if (d->block != kBlock) return MOE_EUNSUPPORTED;
+  if (d->hidden % kBlock || d->ffn % kBlock) return MOE_EINVAL;
+  if (d->hidden / kBlock > 128 || d->ffn / kBlock > 128) return MOE_EUNSUPPORTED;
+  if (d->hidden / kBlock > 64 && d->hidden / kBlock != 128) return MOE_EUNSUPPORTED;
+  if (d->ffn / kBlock > 64 && d->ffn / kBlock != 128) return MOE_EUNSUPPORTED;
+  if (d->top_k > kMaxK || d->n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+static int check_ws(const moe_dims* d, int T, const void* ws, size_t ws_bytes) {
+  if (!ws || ((uintptr_t)ws & 255)) return MOE_EWORKSPACE;
+  if (ws_bytes < ws_layout(d, T).total) return MOE_EWORKSPACE;
+  return MOE_OK;
+}
+
+static int check_weights(const moe_dims* d, const moe_layer_weights* w, const int32_t* table) {
+  if (!w || !w->arena) return MOE_EINVAL;
+  if (w->n_slots <= 0) return MOE_EINVAL;
+  if (w->slot_stride < blob_layout(d->hidden, d->ffn).total || (w->slot_stride % 4096)) return MOE_EINVAL;
+  if (((uintptr_t)w->arena & 255)) return MOE_EINVAL;
+  if (d->n_shared == 1 && (!w->shared_blob || ((uintptr_t)w->shared_blob & 15))) return MOE_EINVAL;
+  if (d->n_shared == 0 && w->shared_blob) return MOE_EINVAL;
+  if (!table && w->n_slots < d->n_experts) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+static int check_dtype(int dt) { return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_EUNSUPPORTED; }
+
+static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+static int32_t* ctrl_of(void* ws) { return (int32_t*)ws; }
+
+template <typename T>
+static T* at(void* ws, size_t off) {
+  return (T*)((uint8_t*)ws + off);
+}
+
+static DoorbellArgs bell_args(const moe_doorbell* b) {
+  DoorbellArgs a{};
+  if (b) {
+    a.active = 1;
+    a.host_miss_ids = b->host_miss_ids;
+    a.host_miss_count = b->host_miss_count;
+    a.ready = b->ready;
+    a.epoch = b->epoch;
+  }
+  return a;
+}
+
+static int check_bell(const moe_doorbell* b) {
+  if (!b) return MOE_OK;
+  if (!b->host_miss_ids || !b->host_miss_count || !b->ready) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+// route: logits + top-k.  Inputs validated by the caller.
+static int do_route(const moe_dims* d, const void* x, int x_dtype, int T, const void* router, int r_dtype,
+                    const float* bias, int32_t* ids, float* w, float* logits, void* ws, hipStream_t st) {
+  const WsLayout L = ws_layout(d, T);
+  float* lg = logits ? logits : at<float>(ws, L.logits);
+  if (T > kMaxDecodeTok) return MOE_EUNSUPPORTED;  // prefill router: separate kernel
+  int rc = hip_status(launch_router_gemv(x, x_dtype, router, r_dtype, bias, T, d->n_experts, d->hidden, lg, st));
+  if (rc) return rc;
+  return hip_status(launch_topk(lg, T, d->n_experts, d->top_k, ids, w, ctrl_of(ws), st));
+}
+
+static ExpertSource source_of(const moe_layer_weights* w, const int32_t* table) {
+  ExpertSource s;
+  s.arena = w->arena;
+  s.slot_stride = w->slot_stride;
+  s.n_slots = w->n_slots;
+  s.table = table;
+  s.shared_blob = w->shared_blob;
+  return s;
+}
+
+// decode FFN after routing; `bell` (may be null) is rung by the plan kernel.
+static int do_decode_ffn(const moe_dims* d, const moe_layer_weights* w, const int32_t* table,
+                         const moe_doorbell* bell, const void* x, int x_dtype, int T, const int32_t* ids,
+                         const float* topk_w, float* y, void* ws, hipStream_t st) {
+  const WsLayout L = ws_layout(d, T);
+  int32_t* ctrl = ctrl_of(ws);
+  DecodeTask* tasks = at<DecodeTask>(ws, L.tasks);
+  int rc = hip_status(launch_decode_plan(ids, T, d->top_k, d->n_experts, d->n_shared, table, w->n_slots, nullptr,
+                                         at<int32_t>(ws, L.miss_ids), nullptr, tasks, ctrl, bell_args(bell), st));
+  if (rc) return rc;
+  if (bell) {
+    if (hipStreamWaitValue32(st, bell->ready, bell->epoch, hipStreamWaitValueGte, 0xFFFFFFFFu) != hipSuccess)
+      return MOE_EHIP;
+  }
+  return hip_status(launch_decode_ffn(d->hidden, d->ffn, d->top_k, d->n_shared, T,
+                                      decode_max_tasks(T, d->top_k, d->n_shared), source_of(w, table), x, x_dtype,
+                                      tasks, topk_w, at<float>(ws, L.h), at<float>(ws, L.y_pairs), y, ctrl, st));
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+MOE_API size_t moe_expert_blob_bytes(const moe_dims* dims) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return (size_t)blob_layout(dims->hidden, dims->ffn).total;
+}
+
+MOE_API size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_tokens) {
+  if (check_dims(dims) != MOE_OK || max_tokens < 1) return 0;
+  return ws_layout(dims, max_tokens).total;
+}
+
+MOE_API const char* moe_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported dtype, block size or shape";
+    case MOE_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case MOE_EHIP: return "HIP runtime call failed";
+    case MOE_EDEVICE: return "the device reported an error (see moe_check_device_error bits)";
+    case MOE_EFILL: return "slot-pool fill failed";
+    default: return "unknown status code";
+  }
+}
+
+MOE_API int moe_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ((uintptr_t)ws & 255) || ws_bytes < (size_t)kCtrlBytes) return MOE_EWORKSPACE;
+  return hip_status(launch_fill_zero(ws, kCtrlBytes, (hipStream_t)stream));
+}
+
+MOE_API int moe_check_device_error(void* ws, void* stream, int32_t* bits_out) {
+  if (!ws || ((uintptr_t)ws & 255)) return MOE_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  int32_t bits = 0;
+  if (hipMemcpyAsync(&bits, ws, sizeof(int32_t), hipMemcpyDeviceToHost, st) != hipSuccess) return MOE_EHIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return MOE_EHIP;
+  if (bits_out) *bits_out = bits;
+  if (bits) {
+    if (launch_fill_zero(ws, sizeof(int32_t), st) != hipSuccess) return MOE_EHIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return MOE_EHIP;
+    return MOE_EDEVICE;
+  }
+  return MOE_OK;
+}
+
+MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop_event) {
+  if (which < kTimeNone || which > kTimePrefillDown) return MOE_EINVAL;
+  if (which != kTimeNone && (!start_event || !stop_event)) return MOE_EINVAL;
+  g_kernel_events.which = which;
+  g_kernel_events.start = (hipEvent_t)start_event;
+  g_kernel_events.stop = (hipEvent_t)stop_event;
+  return MOE_OK;
+}
+
+MOE_API int moe_debug_dequant(const moe_dims* dims, const uint8_t* blob, int32_t matrix, float* out,
+                              void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!blob || !out || matrix < 0 || matrix > 2 || ((uintptr_t)blob & 3)) return MOE_EINVAL;
+  return hip_status(launch_debug_dequant(dims->hidden, dims->ffn, blob, matrix, out, (hipStream_t)stream));
+}
+
+MOE_API int moe_route(const moe_dims* dims, const void* x, int32_t x_dtype, int32_t n_tokens, const void* router,
+                      int32_t router_dtype, const float* bias, int32_t* topk_ids, float* topk_w,
+                      float* logits_or_null, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!x || !router || !topk_ids || !topk_w || n_tokens < 1) return MOE_EINVAL;
+  if ((rc = check_dtype(x_dtype)) || (rc = check_dtype(router_dtype))) return rc;
+  if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
+  return do_route(dims, x, x_dtype, n_tokens, router, router_dtype, bias, topk_ids, topk_w, logits_or_null, ws,
+                  (hipStream_t)stream);
+}
+
+MOE_API int moe_slot_lookup(const moe_dims* dims, const int32_t* layer_table, int32_t n_slots,
+                            const int32_t* topk_ids, int32_t n_tokens, int32_t* slots, int32_t* miss_ids,
+                            int32_t* miss_count, const moe_doorbell* bell_or_null, void* ws, size_t ws_bytes,
+                            void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!layer_table || !topk_ids || !slots || !miss_ids || !miss_count || n_tokens < 1 || n_slots < 1)
+    return MOE_EINVAL;
+  if ((rc = check_bell(bell_or_null))) return rc;
+  if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
+  const WsLayout L = ws_layout(dims, n_tokens);
+  return hip_status(launch_lookup(topk_ids, n_tokens * dims->top_k, dims->n_experts, layer_table, n_slots, slots,
+                                  at<uint8_t>(ws, L.miss_flag), miss_ids, miss_count, ctrl_of(ws),
+                                  bell_args(bell_or_null), (hipStream_t)stream));
+}
+
+MOE_API int moe_group_tokens(const moe_dims* dims, const int32_t* topk_ids, int32_t n_tokens, int32_t* counts,
+                             int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!topk_ids || !counts || !offsets || !perm || n_tokens < 1) return MOE_EINVAL;
+  if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
+  (void)stream;
+  return MOE_EUNSUPPORTED;
+}
+
+MOE_API int moe_expert_ffn_decode(const moe_dims* dims, const moe_layer_weights* w, const int32_t* layer_table_or_null,
+                                  const void* x, int32_t x_dtype, int32_t n_tokens, const int32_t* topk_ids,
+                                  const float* topk_w, float* y, void* ws, size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!x || !topk_ids || !topk_w || !y) return MOE_EINVAL;
+  if (n_tokens < 1 || n_tokens > kMaxDecodeTok) return MOE_EINVAL;
+  if ((rc = check_dtype(x_dtype))) return rc;
+  if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
+  if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
+  return do_decode_ffn(dims, w, layer_table_or_null, nullptr, x, x_dtype, n_tokens, topk_ids, topk_w, y, ws,
+                       (hipStream_t)stream);
+}
+
+MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights* w,
+                                   const int32_t* layer_table_or_null, const void* x, int32_t x_dtype,
+                                   int32_t n_tokens, const int32_t* topk_ids, const float* topk_w, float* y, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!x || !topk_ids || !topk_w || !y || n_tokens < 1) return MOE_EINVAL;
+  if (x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+  if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
+  if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
+  (void)stream;
+  return MOE_EUNSUPPORTED;
+}
+
+MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, const int32_t* layer_table_or_null,
+                              const moe_doorbell* bell_or_null, const void* x, int32_t x_dtype, int32_t n_tokens,
+                              float* y, int32_t* topk_ids_out_or_null, float* topk_w_out_or_null, void* ws,
+                              size_t ws_bytes, void* stream) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!x || !y || n_tokens < 1) return MOE_EINVAL;
+  if ((rc = check_dtype(x_dtype))) return rc;
+  if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
+  if (!w->router || (rc = check_dtype(w->router_dtype))) return rc ? rc : MOE_EINVAL;
+  if ((rc = check_bell(bell_or_null))) return rc;
+  if (bell_or_null && !layer_table_or_null) return MOE_EINVAL;
+  if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
+  if (n_tokens > kMaxDecodeTok) return MOE_EUNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  const WsLayout L = ws_layout(dims, n_tokens);
+  int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);
+  float* tw = topk_w_out_or_null ? topk_w_out_or_null : at<float>(ws, L.w);
+  rc = do_route(dims, x, x_dtype, n_tokens, w->router, w->router_dtype, w->router_bias, ids, tw, nullptr, ws, st);
+  if (rc) return rc;
+  return do_decode_ffn(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, ids, tw, y, ws, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,401 @@
+// Expert FFNs for a small batch of tokens (decode): 4-bit GEMV, bandwidth-bound.
+//
+// Weights: halogen-flash-server README, "Bring your own GGUF" (small set of values x one scale
+// per block, used as stored).  The layer: Betelgeuse news article, "mechanism" (10 routed + 1
+// shared expert per token).  Decode pays per byte of weights read (halogen README, "Bring your
+// own GGUF": an 8-bit trunk costs 2 GB more per token at 240 GB/s), so these kernels aim at
+// streaming each selected expert's blob once from HBM per step.
+//
+// Design (gfx950): one lane per quantization block of a row.  A row of K inputs has L = K/32
+// blocks; the L lanes of a row group (L rounded up to a power of two Lp, so P = 64/Lp rows per
+// wave pass) each load the block's 16 code bytes with one 128-bit load and its fp16 scale.  The
+// activations of the lane's block live in registers as bf16 pairs for the whole kernel, so the
+// inner loop is: one mask per code pair (the pair becomes two bf16 values q + 136, exact), one
+// v_dot2c_f32_bf16 per pair and token, and one scale FMA per block and token.  The -136 offset is
+// removed by starting each block's chain at -136 * sum(x over the block).  fp32 inputs (the FFN
+// intermediate h, fp32 activations) are split into two bf16 parts hi + lo (16 significant bits),
+// each run through the same chain.  Partial sums are reduced across the Lp lanes of a row.
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kDecodeWaves = 4;    // waves per workgroup
+constexpr int kRowsPerWave = 4;    // wave passes per wave (each pass covers P rows)
+
+MOE_DEV const uint8_t* expert_blob(const ExpertSource& s, int expert) {
+  if (expert < 0) return s.shared_blob;
+  const int slot = s.table ? s.table[expert] : expert;
+  if (slot < 0 || slot >= s.n_slots) return nullptr;
+  return s.arena + (int64_t)slot * s.slot_stride;
+}
+
+// The 32 activations of block `blk` of row `src` as bf16 pair words (pair i = elements 2i,
+// 2i+1) in NPART parts, and each part's chain start -136 * sum(part over the block).
+template <int NPART, bool SRC_BF16>
+MOE_DEV void load_x_block(const void* src, int blk, uint32_t (&q)[NPART][16], float (&init)[NPART]) {
+  if constexpr (SRC_BF16) {
+    static_assert(NPART == 1, "bf16 activations are one part");
+    const uint4* p = (const uint4*)((const uint16_t*)src + (size_t)blk * kBlock);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = p[i];
+      q[0][4 * i + 0] = v.x;
+      q[0][4 * i + 1] = v.y;
+      q[0][4 * i + 2] = v.z;
+      q[0][4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s += bf16_lo(q[0][i]) + bf16_hi(q[0][i]);
+    init[0] = -136.f * s;
+  } else {
+    const float4* p = (const float4*)((const float*)src + (size_t)blk * kBlock);
+    float s[NPART];
+#pragma unroll
+    for (int pp = 0; pp < NPART; ++pp) s[pp] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float4 v = p[i];
+      const float f[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t hi[2], lo[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float xv = f[2 * h + e];
+          hi[e] = f32_to_bf16_rne(xv);
+          const float hv = __uint_as_float(hi[e] << 16);
+          lo[e] = f32_to_bf16_rne(xv - hv);
+          s[0] += hv;
+          if constexpr (NPART == 2) s[1] += __uint_as_float(lo[e] << 16);
+        }
+        q[0][2 * i + h] = hi[0] | (hi[1] << 16);
+        if constexpr (NPART == 2) q[1][2 * i + h] = lo[0] | (lo[1] << 16);
+      }
+    }
+#pragma unroll
+    for (int pp = 0; pp < NPART; ++pp) init[pp] = -136.f * s[pp];
+  }
+}
+
+// sum over the block of x * q, for one part: starts at init = -136 * sum(x).
+MOE_DEV float block_dot(const uint4 c, const uint32_t (&xq)[16], float init) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float acc = init;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = dot2_bf16(xq[4 * d + j], code_pair_bf16_q136(w[d], j), acc);
+  }
+  return acc;
+}
+
+struct DecodeArgs {
+  ExpertSource src;
+  const DecodeTask* tasks;
+  int32_t* ctrl;
+  const void* x;   // gate/up: activations [T][H]; down: h [pairs][F] fp32
+  float* out;      // gate/up: h [pairs][F]; down: y_pairs [pairs][H]
+  int H, F;
+  int tiles;       // workgroups per task
+};
+
+// Row geometry of a matrix with K inputs per row.
+MOE_DEV int lanes_per_row(int L) {
+  int Lp = 1;
+  while (Lp < L && Lp < 64) Lp <<= 1;
+  return Lp;
+}
+
+// gate/up (+ SwiGLU): h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for r < F.
+template <int MAXTOK, int NPART, int BPL, bool X_BF16>
+__global__ __launch_bounds__(256) void k_decode_gate_up(DecodeArgs a) {
+  const int task_id = blockIdx.x / a.tiles;
+  if (task_id >= a.ctrl[kCtrlNTasks]) return;
+  const int tile = blockIdx.x - task_id * a.tiles;
+  const DecodeTask* tk = a.tasks + task_id;
+  const int ntok = tk->n_tok;
+  const uint8_t* blob = expert_blob(a.src, tk->expert);
+  if (!blob) {
+    if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+    return;
+  }
+  const int H = a.H, F = a.F, L = H / kBlock;
+  const BlobLayout lay = blob_layout(H, F);
+  const int Lp = lanes_per_row(L), P = 64 / Lp;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / Lp, b0 = lane - sub * Lp;
+  const bool active = b0 < L;
+
+  uint32_t xq[MAXTOK][BPL][NPART][16];
+  float xi[MAXTOK][BPL][NPART];
+#pragma unroll
+  for (int n = 0; n < MAXTOK; ++n) {
+#pragma unroll
+    for (int bb = 0; bb < BPL; ++bb) {
+      if (n < ntok && active && b0 + 64 * bb < L) {
+        const int t = tk->tok[n];
+        const void* xrow = X_BF16 ? (const void*)((const uint16_t*)a.x + (size_t)t * H)
+                                  : (const void*)((const float*)a.x + (size_t)t * H);
+        load_x_block<NPART, X_BF16>(xrow, b0 + 64 * bb, xq[n][bb], xi[n][bb]);
+      } else {
+#pragma unroll
+        for (int p = 0; p < NPART; ++p) {
+          xi[n][bb][p] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xq[n][bb][p][i] = 0u;
+        }
+      }
+    }
+  }
+
+  const int row0 = (tile * kDecodeWaves + wave) * kRowsPerWave * P;
+  uint4 gc[kRowsPerWave][BPL], uc[kRowsPerWave][BPL];
+  float gs[kRowsPerWave][BPL], us[kRowsPerWave][BPL];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = row0 + i * P + sub;
+#pragma unroll
+    for (int bb = 0; bb < BPL; ++bb) {
+      const int blk = b0 + 64 * bb;
+      if (active && blk < L && r < F) {
+        gc[i][bb] = *(const uint4*)(blob + lay.gate_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
+        uc[i][bb] = *(const uint4*)(blob + lay.up_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
+        gs[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.gate_scales + ((size_t)r * L + blk) * 2));
+        us[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.up_scales + ((size_t)r * L + blk) * 2));
+      } else {
+        gc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+        uc[i][bb] = gc[i][bb];
+        gs[i][bb] = 0.f;
+        us[i][bb] = 0.f;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    float g[MAXTOK], u[MAXTOK];
+#pragma unroll
+    for (int n = 0; n < MAXTOK; ++n) {
+      g[n] = 0.f;
+      u[n] = 0.f;
+      if (n < ntok) {
+#pragma unroll
+        for (int bb = 0; bb < BPL; ++bb) {
+          float sg = 0.f, su = 0.f;
+#pragma unroll
+          for (int p = 0; p < NPART; ++p) {
+            sg += block_dot(gc[i][bb], xq[n][bb][p], xi[n][bb][p]);
+            su += block_dot(uc[i][bb], xq[n][bb][p], xi[n][bb][p]);
+          }
+          g[n] = fmaf(sg, gs[i][bb], g[n]);
+          u[n] = fmaf(su, us[i][bb], u[n]);
+        }
+      }
+    }
+    const int r = row0 + i * P + sub;
+#pragma unroll
+    for (int n = 0; n < MAXTOK; ++n) {
+      if (n < ntok) {
+        const float gt = group_sum(g[n], Lp);
+        const float ut = group_sum(u[n], Lp);
+        if (b0 == 0 && r < F) a.out[(size_t)tk->pair[n] * F + r] = silu(gt) * ut;
+      }
+    }
+  }
+}
+
+// down: y_pairs[pair][o] = Wd[o] . h[pair] for o < H.
+template <int MAXTOK, int BPL>
+__global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
+  const int task_id = blockIdx.x / a.tiles;
+  if (task_id >= a.ctrl[kCtrlNTasks]) return;
+  const int tile = blockIdx.x - task_id * a.tiles;
+  const DecodeTask* tk = a.tasks + task_id;
+  const int ntok = tk->n_tok;
+  const uint8_t* blob = expert_blob(a.src, tk->expert);
+  if (!blob) {
+    if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+    return;
+  }
+  const int H = a.H, F = a.F, L = F / kBlock;
+  const BlobLayout lay = blob_layout(H, F);
+  const int Lp = lanes_per_row(L), P = 64 / Lp;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane / Lp, b0 = lane - sub * Lp;
+  const bool active = b0 < L;
+  constexpr int NPART = 2;
+
+  uint32_t xq[MAXTOK][BPL][NPART][16];
+  float xi[MAXTOK][BPL][NPART];
+#pragma unroll
+  for (int n = 0; n < MAXTOK; ++n) {
+#pragma unroll
+    for (int bb = 0; bb < BPL; ++bb) {
+      if (n < ntok && active && b0 + 64 * bb < L) {
+        const float* hrow = (const float*)a.x + (size_t)tk->pair[n] * F;
+        load_x_block<NPART, false>(hrow, b0 + 64 * bb, xq[n][bb], xi[n][bb]);
+      } else {
+#pragma unroll
+        for (int p = 0; p < NPART; ++p) {
+          xi[n][bb][p] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xq[n][bb][p][i] = 0u;
+        }
+      }
+    }
+  }
+
+  const int row0 = (tile * kDecodeWaves + wave) * kRowsPerWave * P;
+  uint4 dc[kRowsPerWave][BPL];
+  float ds[kRowsPerWave][BPL];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = row0 + i * P + sub;
+#pragma unroll
+    for (int bb = 0; bb < BPL; ++bb) {
+      const int blk = b0 + 64 * bb;
+      if (active && blk < L && r < H) {
+        dc[i][bb] = *(const uint4*)(blob + lay.down_codes + (size_t)r * (F / 2) + (size_t)blk * 16);
+        ds[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.down_scales + ((size_t)r * L + blk) * 2));
+      } else {
+        dc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+        ds[i][bb] = 0.f;
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    float yv[MAXTOK];
+#pragma unroll
+    for (int n = 0; n < MAXTOK; ++n) {
+      yv[n] = 0.f;
+      if (n < ntok) {
+#pragma unroll
+        for (int bb = 0; bb < BPL; ++bb) {
+          float sd = 0.f;
+#pragma unroll
+          for (int p = 0; p < NPART; ++p) sd += block_dot(dc[i][bb], xq[n][bb][p], xi[n][bb][p]);
+          yv[n] = fmaf(sd, ds[i][bb], yv[n]);
+        }
+      }
+    }
+    const int r = row0 + i * P + sub;
+#pragma unroll
+    for (int n = 0; n < MAXTOK; ++n) {
+      if (n < ntok) {
+        const float yt = group_sum(yv[n], Lp);
+        if (b0 == 0 && r < H) a.out[(size_t)tk->pair[n] * H + r] = yt;
+      }
+    }
+  }
+}
+
+// y[t][o] = sum_{j<k} w[t][j] * y_pairs[t*k+j][o] + y_pairs[T*k+t][o] (shared), fixed order.
+__global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict__ y_pairs,
+                                                         const float* __restrict__ topk_w, int T, int k,
+                                                         int n_shared, int H, float* __restrict__ y) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * H) return;
+  const int t = idx / H, o = idx - t * H;
+  float acc = 0.f;
+  for (int j = 0; j < k; ++j) acc = fmaf(topk_w[t * k + j], y_pairs[(size_t)(t * k + j) * H + o], acc);
+  if (n_shared) acc += y_pairs[(size_t)(T * k + t) * H + o];
+  y[idx] = acc;
+}
+
+// ------------------------------------------------------------------------------------------
+// Test entry: dequantize one matrix of a blob to fp32 (exact).
+// ------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_debug_dequant(int H, int F, const uint8_t* __restrict__ blob,
+                                                        int matrix, float* __restrict__ out) {
+  const BlobLayout lay = blob_layout(H, F);
+  const int rows = matrix == 2 ? H : F, cols = matrix == 2 ? F : H;
+  const int64_t codes = matrix == 0 ? lay.gate_codes : matrix == 1 ? lay.up_codes : lay.down_codes;
+  const int64_t scales = matrix == 0 ? lay.gate_scales : matrix == 1 ? lay.up_scales : lay.down_scales;
+  const int n_words = rows * cols / 8;
+  for (int wi = blockIdx.x * blockDim.x + threadIdx.x; wi < n_words; wi += gridDim.x * blockDim.x) {
+    const int r = wi / (cols / 8), d = wi - r * (cols / 8);
+    const uint32_t w = *(const uint32_t*)(blob + codes + (size_t)wi * 4);
+    const int c0 = d * 8;
+    const float s = fp16_bits_to_f32(*(const uint16_t*)(blob + scales + ((size_t)r * (cols / kBlock) + c0 / kBlock) * 2));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t pr = code_pair_bf16_q136(w, j);
+      out[(size_t)r * cols + c0 + 2 * j] = (bf16_lo(pr) - 136.f) * s;
+      out[(size_t)r * cols + c0 + 2 * j + 1] = (bf16_hi(pr) - 136.f) * s;
+    }
+  }
+}
+
+__global__ void k_fill_zero(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers
+// ------------------------------------------------------------------------------------------
+template <int MAXTOK>
+static hipError_t launch_decode_ffn_t(const DecodeArgs& gu, const DecodeArgs& dn, int grid_gu, int grid_dn,
+                                      int bpl_gu, int bpl_dn, bool x_bf16, hipStream_t st) {
+  hipError_t err;
+  if (x_bf16) {
+    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 1, true>, grid_gu, 256, 0, st, gu);
+    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 2, true>, grid_gu, 256, 0, st, gu);
+  } else {
+    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 1, false>, grid_gu, 256, 0, st, gu);
+    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 2, false>, grid_gu, 256, 0, st, gu);
+  }
+  if (err != hipSuccess) return err;
+  if (bpl_dn == 1) return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 1>, grid_dn, 256, 0, st, dn);
+  return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 2>, grid_dn, 256, 0, st, dn);
+}
+
+static int rows_per_wg(int K) {
+  const int L = K / kBlock;
+  int Lp = 1;
+  while (Lp < L && Lp < 64) Lp <<= 1;
+  return kDecodeWaves * kRowsPerWave * (64 / Lp);
+}
+
+hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
+                             const void* x, int x_dtype, const DecodeTask* tasks, const float* topk_w,
+                             float* h, float* y_pairs, float* y, int32_t* ctrl, hipStream_t st) {
+  DecodeArgs gu{src, tasks, ctrl, x, h, H, F, 0};
+  gu.tiles = (F + rows_per_wg(H) - 1) / rows_per_wg(H);
+  DecodeArgs dn{src, tasks, ctrl, h, y_pairs, H, F, 0};
+  dn.tiles = (H + rows_per_wg(F) - 1) / rows_per_wg(F);
+  const int bpl_gu = (H / kBlock) > 64 ? 2 : 1;
+  const int bpl_dn = (F / kBlock) > 64 ? 2 : 1;
+  const int grid_gu = max_tasks * gu.tiles, grid_dn = max_tasks * dn.tiles;
+  const bool xb = x_dtype == MOE_BF16;
+  hipError_t err;
+  static_assert(kTaskTok == 4, "instantiations below cover tasks of up to 4 tokens");
+  if (T <= 1) err = launch_decode_ffn_t<1>(gu, dn, grid_gu, grid_dn, bpl_gu, bpl_dn, xb, st);
+  else if (T <= 2) err = launch_decode_ffn_t<2>(gu, dn, grid_gu, grid_dn, bpl_gu, bpl_dn, xb, st);
+  else err = launch_decode_ffn_t<4>(gu, dn, grid_gu, grid_dn, bpl_gu, bpl_dn, xb, st);
+  if (err != hipSuccess) return err;
+  const int n = T * H;
+  k_decode_combine<<<(n + 255) / 256, 256, 0, st>>>(y_pairs, topk_w, T, k, n_shared, H, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st) {
+  const int n_words = H * F / 8;
+  int grid = (n_words + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  k_debug_dequant<<<grid, 256, 0, st>>>(H, F, blob, matrix, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st) {
+  const size_t n = bytes / 4;
+  int grid = (int)((n + 255) / 256);
+  if (grid > 1024) grid = 1024;
+  if (grid < 1) grid = 1;
+  k_fill_zero<<<grid, 256, 0, st>>>((uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

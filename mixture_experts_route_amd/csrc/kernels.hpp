@@ -1,0 +1,82 @@
+// Declarations shared between the kernel sources and the C-ABI host layer.
+#pragma once
+
+#include <hip/hip_ext.h>
+
+#include "common.hpp"
+
+namespace moe {
+
+// Profiling aid (moe_debug_kernel_events): launches of kernel `which` record `start` / `stop`
+// around the kernel itself through hipExtLaunchKernelGGL.
+enum TimedKernel { kTimeNone = 0, kTimeDecodeGateUp = 1, kTimeDecodeDown = 2, kTimePrefillGateUp = 3,
+                   kTimePrefillDown = 4 };
+struct KernelEvents {
+  int which;
+  hipEvent_t start, stop;
+};
+extern KernelEvents g_kernel_events;
+
+template <typename K, typename... Args>
+hipError_t launch_timed(int which, K kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, Args... args) {
+  if (which != kTimeNone && g_kernel_events.which == which)
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, g_kernel_events.start, g_kernel_events.stop, 0u, args...);
+  else
+    kernel<<<grid, block, lds, st>>>(args...);
+  return hipGetLastError();
+}
+
+// One expert's work in a decode step: the tokens that chose it and, for each, the pair
+// index whose FFN output row it owns (routed pair t*k + j, shared pair T*k + t).
+constexpr int kTaskTok = 4;  // tokens per decode task (an expert chosen by more is split)
+
+struct DecodeTask {
+  int32_t expert;  // routed expert id, or -1 for the shared expert
+  int32_t n_tok;
+  int32_t tok[kTaskTok];
+  int32_t pair[kTaskTok];
+};
+
+// Upper bound on decode tasks for T tokens: every routed task holds >= 1 pair, and the
+// shared expert's T tokens make ceil(T / kTaskTok) tasks.
+inline int decode_max_tasks(int T, int k, int n_shared) {
+  return T * k + (n_shared ? (T + kTaskTok - 1) / kTaskTok : 0);
+}
+
+struct DoorbellArgs {
+  int active;
+  int32_t* host_miss_ids;
+  int32_t* host_miss_count;
+  uint32_t* ready;
+  uint32_t epoch;
+};
+
+// Where each expert blob lives: routed expert e in slot table[e] (identity without a table).
+struct ExpertSource {
+  const uint8_t* arena;
+  int64_t slot_stride;
+  int32_t n_slots;
+  const int32_t* table;  // may be null
+  const uint8_t* shared_blob;
+};
+
+// route.hip
+hipError_t launch_router_gemv(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias,
+                              int T, int E, int H, float* logits, hipStream_t st);
+hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* ctrl,
+                       hipStream_t st);
+hipError_t launch_lookup(const int32_t* ids, int n_pairs, int E, const int32_t* table, int n_slots,
+                         int32_t* slots, uint8_t* miss_flag, int32_t* miss_ids, int32_t* miss_count,
+                         int32_t* ctrl, const DoorbellArgs& bell, hipStream_t st);
+hipError_t launch_decode_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table,
+                              int n_slots, int32_t* slots_out, int32_t* miss_ids, int32_t* miss_count_out,
+                              DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell, hipStream_t st);
+
+// ffn_decode.hip
+hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
+                             const void* x, int x_dtype, const DecodeTask* tasks, const float* topk_w,
+                             float* h, float* y_pairs, float* y, int32_t* ctrl, hipStream_t st);
+hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,211 @@
+"""Thin ctypes binding of libmoe_route.so (include/moe_route.h), argument marshalling only.
+
+Every function has the C entry point's name and takes torch tensors (device memory) or
+plain integers; it passes their addresses, sizes and the current HIP stream to the
+library and raises :class:`MoeError` on a non-zero status.  Importing this module loads
+the native library and raises ImportError when it is missing: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_route.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing; build it with `python -m mixture_experts_route_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EDEVICE, MOE_EFILL = 0, -1, -2, -3, -4, -5, -6
+MOE_F32, MOE_BF16 = 0, 1
+MOE_DECODE_MAX_TOKENS = 8
+DERR_EXPERT_ID, DERR_SLOT, DERR_NOT_RESIDENT, DERR_NAN, DERR_FILL = 1, 2, 4, 8, 16
+
+EXPORTS = [
+    "moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_workspace_init",
+    "moe_check_device_error", "moe_debug_kernel_events", "moe_debug_dequant", "moe_route", "moe_slot_lookup", "moe_group_tokens",
+    "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "moe_layer_forward",
+]
+
+
+class moe_dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("block", ctypes.c_int32)]
+
+
+class moe_layer_weights(ctypes.Structure):
+    _fields_ = [("router", ctypes.c_void_p), ("router_dtype", ctypes.c_int32), ("router_bias", ctypes.c_void_p),
+                ("arena", ctypes.c_void_p), ("slot_stride", ctypes.c_int64), ("n_slots", ctypes.c_int32),
+                ("shared_blob", ctypes.c_void_p)]
+
+
+class moe_doorbell(ctypes.Structure):
+    _fields_ = [("host_miss_ids", ctypes.c_void_p), ("host_miss_count", ctypes.c_void_p),
+                ("ready", ctypes.c_void_p), ("epoch", ctypes.c_uint32)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} ({code})")
+        self.code = code
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_D = ctypes.POINTER(moe_dims)
+_W = ctypes.POINTER(moe_layer_weights)
+_B = ctypes.POINTER(moe_doorbell)
+
+_sig = {
+    "moe_expert_blob_bytes": (_SZ, [_D]),
+    "moe_workspace_bytes": (_SZ, [_D, _I]),
+    "moe_strerror": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
+    "moe_check_device_error": (ctypes.c_int, [_P, _P, ctypes.POINTER(ctypes.c_int32)]),
+    "moe_debug_dequant": (ctypes.c_int, [_D, _P, _I, _P, _P]),
+    "moe_debug_kernel_events": (ctypes.c_int, [_I, _P, _P]),
+    "moe_route": (ctypes.c_int, [_D, _P, _I, _I, _P, _I, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_slot_lookup": (ctypes.c_int, [_D, _P, _I, _P, _I, _P, _P, _P, _B, _P, _SZ, _P]),
+    "moe_group_tokens": (ctypes.c_int, [_D, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_ffn_decode": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_expert_ffn_prefill": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward": (ctypes.c_int, [_D, _W, _P, _B, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+
+def strerror(code: int) -> str:
+    return _lib.moe_strerror(code).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != MOE_OK:
+        raise MoeError(rc, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def dims(hidden: int, ffn: int, n_experts: int, top_k: int, n_shared: int = 1, block: int = 32) -> moe_dims:
+    return moe_dims(hidden, ffn, n_experts, top_k, n_shared, block)
+
+
+def dtype_code(t) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype in (torch.bfloat16, torch.int16, torch.uint16):
+        return MOE_BF16
+    raise TypeError(f"unsupported activation dtype {t.dtype}")
+
+
+def layer_weights(router, arena, slot_stride: int, n_slots: int, shared_blob=None, router_bias=None,
+                  router_dtype=None) -> moe_layer_weights:
+    rd = dtype_code(router) if router_dtype is None else router_dtype
+    return moe_layer_weights(_ptr(router), rd, _ptr(router_bias), _ptr(arena), int(slot_stride), int(n_slots),
+                             _ptr(shared_blob))
+
+
+def doorbell(host_miss_ids: int, host_miss_count: int, ready: int, epoch: int) -> moe_doorbell:
+    return moe_doorbell(host_miss_ids, host_miss_count, ready, epoch)
+
+
+def moe_expert_blob_bytes(d: moe_dims) -> int:
+    return _lib.moe_expert_blob_bytes(ctypes.byref(d))
+
+
+def moe_workspace_bytes(d: moe_dims, max_tokens: int) -> int:
+    return _lib.moe_workspace_bytes(ctypes.byref(d), max_tokens)
+
+
+def moe_workspace_init(ws, stream=None):
+    _check(_lib.moe_workspace_init(_ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_workspace_init")
+
+
+def moe_check_device_error(ws, stream=None) -> int:
+    bits = ctypes.c_int32(0)
+    rc = _lib.moe_check_device_error(_ptr(ws), _stream(stream), ctypes.byref(bits))
+    if rc not in (MOE_OK, MOE_EDEVICE):
+        _check(rc, "moe_check_device_error")
+    return bits.value
+
+
+TIME_DECODE_GATE_UP, TIME_DECODE_DOWN, TIME_PREFILL_GATE_UP, TIME_PREFILL_DOWN = 1, 2, 3, 4
+
+
+def moe_debug_kernel_events(which: int, start_event, stop_event):
+    _check(_lib.moe_debug_kernel_events(which, start_event, stop_event), "moe_debug_kernel_events")
+
+
+def moe_debug_dequant(d: moe_dims, blob, matrix: int, out, stream=None):
+    _check(_lib.moe_debug_dequant(ctypes.byref(d), _ptr(blob), matrix, _ptr(out), _stream(stream)),
+           "moe_debug_dequant")
+
+
+def moe_route(d: moe_dims, x, n_tokens: int, router, bias, topk_ids, topk_w, logits, ws, stream=None,
+              x_dtype=None, router_dtype=None):
+    xd = dtype_code(x) if x_dtype is None else x_dtype
+    rd = dtype_code(router) if router_dtype is None else router_dtype
+    _check(_lib.moe_route(ctypes.byref(d), _ptr(x), xd, n_tokens, _ptr(router), rd, _ptr(bias), _ptr(topk_ids),
+                          _ptr(topk_w), _ptr(logits), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_route")
+
+
+def moe_slot_lookup(d: moe_dims, table, n_slots: int, topk_ids, n_tokens: int, slots, miss_ids, miss_count, ws,
+                    bell: moe_doorbell | None = None, stream=None):
+    _check(_lib.moe_slot_lookup(ctypes.byref(d), _ptr(table), n_slots, _ptr(topk_ids), n_tokens, _ptr(slots),
+                                _ptr(miss_ids), _ptr(miss_count), ctypes.byref(bell) if bell else None, _ptr(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)), "moe_slot_lookup")
+
+
+def moe_group_tokens(d: moe_dims, topk_ids, n_tokens: int, counts, offsets, perm, ws, stream=None):
+    _check(_lib.moe_group_tokens(ctypes.byref(d), _ptr(topk_ids), n_tokens, _ptr(counts), _ptr(offsets), _ptr(perm),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "moe_group_tokens")
+
+
+def moe_expert_ffn_decode(d: moe_dims, w: moe_layer_weights, table, x, n_tokens: int, topk_ids, topk_w, y, ws,
+                          stream=None, x_dtype=None):
+    xd = dtype_code(x) if x_dtype is None else x_dtype
+    _check(_lib.moe_expert_ffn_decode(ctypes.byref(d), ctypes.byref(w), _ptr(table), _ptr(x), xd, n_tokens,
+                                      _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream(stream)), "moe_expert_ffn_decode")
+
+
+def moe_expert_ffn_prefill(d: moe_dims, w: moe_layer_weights, table, x, n_tokens: int, topk_ids, topk_w, y, ws,
+                           stream=None, x_dtype=None):
+    xd = dtype_code(x) if x_dtype is None else x_dtype
+    _check(_lib.moe_expert_ffn_prefill(ctypes.byref(d), ctypes.byref(w), _ptr(table), _ptr(x), xd, n_tokens,
+                                       _ptr(topk_ids), _ptr(topk_w), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
+                                       _stream(stream)), "moe_expert_ffn_prefill")
+
+
+def moe_layer_forward(d: moe_dims, w: moe_layer_weights, table, x, n_tokens: int, y, ws, topk_ids=None,
+                      topk_w=None, bell: moe_doorbell | None = None, stream=None, x_dtype=None):
+    xd = dtype_code(x) if x_dtype is None else x_dtype
+    _check(_lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), _ptr(table), ctypes.byref(bell) if bell else None,
+                                  _ptr(x), xd, n_tokens, _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+def raw(name: str):
+    """The raw ctypes function (for tests of the C-level validation)."""
+    return getattr(_lib, name)

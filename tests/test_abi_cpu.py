@@ -1,0 +1,103 @@
+"""The C interface on the CPU: the library loads, exports every declared symbol, and
+rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def N():
+    from mixture_experts_route_amd import native
+
+    return native
+
+
+def test_header_declares_the_layer_entry_points():
+    names = _declared()
+    for n in ("moe_route", "moe_slot_lookup", "moe_expert_ffn_decode", "moe_expert_ffn_prefill",
+              "moe_layer_forward", "moe_group_tokens"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(N):
+    lib = ctypes.CDLL(N.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert sorted(N.EXPORTS) == _declared()
+
+
+def test_blob_and_workspace_sizes(N):
+    d = N.dims(2048, 768, 512, 10, 1)
+    assert N.moe_expert_blob_bytes(d) == 2_654_208
+    assert N.moe_expert_blob_bytes(N.dims(256, 128, 8, 2, 1)) == 55_296
+    assert N.moe_workspace_bytes(d, 1) > 0
+    assert N.moe_workspace_bytes(d, 8) >= N.moe_workspace_bytes(d, 1)
+    assert N.moe_workspace_bytes(d, 0) == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(block=16), -2),             # unsupported block size, refused by name
+    (dict(hidden=100), -1),           # not a multiple of 32
+    (dict(top_k=0), -1),
+    (dict(top_k=600), -1),            # k > E
+    (dict(n_shared=2), -1),
+    (dict(n_experts=2048), -2),       # beyond the selection kernel's 1024
+    (dict(top_k=17, n_experts=64), -2),
+    (dict(hidden=32 * 96), -2),       # 96 blocks per row: not a layout the GEMV maps
+])
+def test_invalid_dims_rejected_on_host(N, bad, code):
+    args = dict(hidden=2048, ffn=768, n_experts=512, top_k=10, n_shared=1, block=32)
+    args.update(bad)
+    d = N.dims(**args)
+    assert N.moe_expert_blob_bytes(d) == 0
+    f = N.raw("moe_route")
+    rc = f(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, 1 << 20, 1 << 30, None)
+    assert rc == code
+
+
+def test_invalid_arguments_rejected_on_host(N):
+    d = N.dims(2048, 768, 512, 10, 1)
+    route = N.raw("moe_route")
+    # NULL x
+    assert route(ctypes.byref(d), None, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, 1 << 20, 1 << 30, None) == -1
+    # bad dtype
+    assert route(ctypes.byref(d), 1 << 20, 7, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, 1 << 20, 1 << 30, None) == -2
+    # workspace missing / misaligned / too small
+    assert route(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, None, 1 << 30, None) == -3
+    assert route(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, (1 << 20) + 8, 1 << 30,
+                 None) == -3
+    assert route(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, 1 << 20, 64, None) == -3
+    # decode refuses more than MOE_DECODE_MAX_TOKENS tokens
+    dec = N.raw("moe_expert_ffn_decode")
+    w = N.moe_layer_weights(1 << 20, 1, None, 1 << 20, 2_654_208, 512, 1 << 24)
+    assert dec(ctypes.byref(d), ctypes.byref(w), None, 1 << 20, 1, 9, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 30,
+               None) == -1
+    # slot stride must hold a blob and be 4 KiB aligned
+    w_bad = N.moe_layer_weights(1 << 20, 1, None, 1 << 20, 2_654_208 + 512, 512, 1 << 24)
+    assert dec(ctypes.byref(d), ctypes.byref(w_bad), None, 1 << 20, 1, 1, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+               1 << 30, None) == -1
+    # without a table the arena must hold every expert
+    w_few = N.moe_layer_weights(1 << 20, 1, None, 1 << 20, 2_654_208, 100, 1 << 24)
+    assert dec(ctypes.byref(d), ctypes.byref(w_few), None, 1 << 20, 1, 1, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+               1 << 30, None) == -1
+    # prefill takes bf16 activations only
+    pre = N.raw("moe_expert_ffn_prefill")
+    assert pre(ctypes.byref(d), ctypes.byref(w), None, 1 << 20, 0, 64, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 30,
+               None) == -2
+
+
+def test_strerror(N):
+    for c in range(-6, 1):
+        assert isinstance(N.strerror(c), str) and N.strerror(c)
+    assert N.strerror(42) == "unknown status code"

@@ -88,7 +88,8 @@ enum moe_device_error {
  * n_experts = E routed experts, top_k = k, n_shared = 0 or 1, block = 32 (the only
  * supported quantization block; anything else is MOE_EUNSUPPORTED).
  * Supported: H and F multiples of 32 with H/32 and F/32 <= 128; 1 <= k <= 16; k <= E;
- * E <= 1024.  The prefill path further needs H % 128 == 0 and F % 64 == 0. */
+ * E <= 1024.  The prefill path (more than MOE_DECODE_MAX_TOKENS tokens) further needs
+ * H % 256 == 0, F % 128 == 0 and bf16 activations and router. */
 typedef struct moe_dims {
   int32_t hidden;
   int32_t ffn;

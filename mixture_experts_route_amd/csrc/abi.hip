@@ -10,7 +10,8 @@ KernelEvents g_kernel_events = {kTimeNone, nullptr, nullptr};
 // (error word, counters) and, at byte 1024, the residency miss flags (one byte per expert).
 struct WsLayout {
   size_t tasks, h, y_pairs, logits, ids, w, slots, miss_ids, miss_flag;
-  size_t prefill;  // start of the prefill region
+  // prefill region
+  size_t x16, bits, prefix, count, offsets, items, perm, row_tok, row_w, inv, h16, y_rows;
   size_t total;
 };
 
@@ -38,7 +39,33 @@ static WsLayout ws_layout(const moe_dims* d, int T) {
   off = align256(off + sizeof(int32_t) * (size_t)T * d->top_k);
   L.miss_ids = off;
   off = align256(off + sizeof(int32_t) * (size_t)d->n_experts);
-  L.prefill = off;
+  // prefill: grouping and grouped-GEMM buffers for T tokens
+  const size_t W = ((size_t)T + 31) / 32;
+  const size_t P = (size_t)T * (d->top_k + d->n_shared);
+  L.x16 = off;
+  off = align256(off + 2 * (size_t)T * d->hidden);
+  L.bits = off;
+  off = align256(off + 4 * (size_t)d->n_experts * W);
+  L.prefix = off;
+  off = align256(off + 4 * (size_t)d->n_experts * W);
+  L.count = off;
+  off = align256(off + 4 * (size_t)d->n_experts);
+  L.offsets = off;
+  off = align256(off + 4 * ((size_t)d->n_experts + 2));
+  L.items = off;
+  off = align256(off + sizeof(TileItem) * (size_t)prefill_max_items(T, d->top_k, d->n_experts, d->n_shared));
+  L.perm = off;
+  off = align256(off + 4 * P);
+  L.row_tok = off;
+  off = align256(off + 4 * P);
+  L.row_w = off;
+  off = align256(off + 4 * P);
+  L.inv = off;
+  off = align256(off + 4 * P);
+  L.h16 = off;
+  off = align256(off + 2 * P * d->ffn);
+  L.y_rows = off;
+  off = align256(off + 4 * P * d->hidden);
   L.total = off;
   return L;
 }
@@ -108,8 +135,14 @@ static int do_route(const moe_dims* d, const void* x, int x_dtype, int T, const 
                     const float* bias, int32_t* ids, float* w, float* logits, void* ws, hipStream_t st) {
   const WsLayout L = ws_layout(d, T);
   float* lg = logits ? logits : at<float>(ws, L.logits);
-  if (T > kMaxDecodeTok) return MOE_EUNSUPPORTED;  // prefill router: separate kernel
-  int rc = hip_status(launch_router_gemv(x, x_dtype, router, r_dtype, bias, T, d->n_experts, d->hidden, lg, st));
+  int rc;
+  if (T > kMaxDecodeTok) {
+    // long batches: router GEMM on MFMA (bf16 x bf16, fp32 accumulation)
+    if (x_dtype != MOE_BF16 || r_dtype != MOE_BF16 || d->hidden % 128) return MOE_EUNSUPPORTED;
+    rc = hip_status(launch_router_gemm(x, router, bias, T, d->n_experts, d->hidden, lg, st));
+  } else {
+    rc = hip_status(launch_router_gemv(x, x_dtype, router, r_dtype, bias, T, d->n_experts, d->hidden, lg, st));
+  }
   if (rc) return rc;
   return hip_status(launch_topk(lg, T, d->n_experts, d->top_k, ids, w, ctrl_of(ws), st));
 }
@@ -141,6 +174,40 @@ static int do_decode_ffn(const moe_dims* d, const moe_layer_weights* w, const in
   return hip_status(launch_decode_ffn(d->hidden, d->ffn, d->top_k, d->n_shared, T,
                                       decode_max_tasks(T, d->top_k, d->n_shared), source_of(w, table), x, x_dtype,
                                       tasks, topk_w, at<float>(ws, L.h), at<float>(ws, L.y_pairs), y, ctrl, st));
+}
+
+static GroupBuffers group_buffers(const WsLayout& L, void* ws) {
+  GroupBuffers g;
+  g.bits = at<uint32_t>(ws, L.bits);
+  g.prefix = at<int32_t>(ws, L.prefix);
+  g.count = at<int32_t>(ws, L.count);
+  g.offsets = at<int32_t>(ws, L.offsets);
+  g.items = at<TileItem>(ws, L.items);
+  g.perm = at<int32_t>(ws, L.perm);
+  g.row_tok = at<int32_t>(ws, L.row_tok);
+  g.row_w = at<float>(ws, L.row_w);
+  g.inv = at<int32_t>(ws, L.inv);
+  return g;
+}
+
+static int prefill_shape_ok(const moe_dims* d) {
+  return (d->hidden % 256 == 0 && d->ffn % 128 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
+}
+
+// prefill FFN after routing (and after any residency wait).
+static int do_prefill_ffn(const moe_dims* d, const moe_layer_weights* w, const int32_t* table, const void* x, int T,
+                          const int32_t* ids, const float* topk_w, float* y, void* ws, hipStream_t st) {
+  const WsLayout L = ws_layout(d, T);
+  int32_t* ctrl = ctrl_of(ws);
+  const GroupBuffers g = group_buffers(L, ws);
+  int rc = hip_status(launch_group(ids, topk_w, T, d->top_k, d->n_experts, d->n_shared, g, ctrl, nullptr, nullptr, st));
+  if (rc) return rc;
+  PrefillBuffers b;
+  b.x16 = at<_Float16>(ws, L.x16);
+  b.h16 = at<_Float16>(ws, L.h16);
+  b.y_rows = at<float>(ws, L.y_rows);
+  return hip_status(launch_prefill_ffn(d->hidden, d->ffn, d->top_k, d->n_experts, d->n_shared, T, source_of(w, table),
+                                       x, g, b, y, ctrl, st));
 }
 
 }  // namespace moe
@@ -243,8 +310,11 @@ MOE_API int moe_group_tokens(const moe_dims* dims, const int32_t* topk_ids, int3
   if (rc) return rc;
   if (!topk_ids || !counts || !offsets || !perm || n_tokens < 1) return MOE_EINVAL;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
-  (void)stream;
-  return MOE_EUNSUPPORTED;
+  const WsLayout L = ws_layout(dims, n_tokens);
+  GroupBuffers g = group_buffers(L, ws);
+  g.perm = perm;  // routed pairs only (no shared bucket): perm[0 .. T*k) is the public output
+  return hip_status(launch_group(topk_ids, nullptr, n_tokens, dims->top_k, dims->n_experts, 0, g, ctrl_of(ws), counts,
+                                 offsets, (hipStream_t)stream));
 }
 
 MOE_API int moe_expert_ffn_decode(const moe_dims* dims, const moe_layer_weights* w, const int32_t* layer_table_or_null,
@@ -270,9 +340,9 @@ MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights
   if (!x || !topk_ids || !topk_w || !y || n_tokens < 1) return MOE_EINVAL;
   if (x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
+  if ((rc = prefill_shape_ok(dims))) return rc;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
-  (void)stream;
-  return MOE_EUNSUPPORTED;
+  return do_prefill_ffn(dims, w, layer_table_or_null, x, n_tokens, topk_ids, topk_w, y, ws, (hipStream_t)stream);
 }
 
 MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, const int32_t* layer_table_or_null,
@@ -288,14 +358,31 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   if ((rc = check_bell(bell_or_null))) return rc;
   if (bell_or_null && !layer_table_or_null) return MOE_EINVAL;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
-  if (n_tokens > kMaxDecodeTok) return MOE_EUNSUPPORTED;
+  const bool prefill = n_tokens > kMaxDecodeTok;
+  if (prefill) {
+    if (x_dtype != MOE_BF16 || w->router_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if ((rc = prefill_shape_ok(dims))) return rc;
+  }
   hipStream_t st = (hipStream_t)stream;
   const WsLayout L = ws_layout(dims, n_tokens);
   int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);
   float* tw = topk_w_out_or_null ? topk_w_out_or_null : at<float>(ws, L.w);
   rc = do_route(dims, x, x_dtype, n_tokens, w->router, w->router_dtype, w->router_bias, ids, tw, nullptr, ws, st);
   if (rc) return rc;
-  return do_decode_ffn(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, ids, tw, y, ws, st);
+  if (!prefill)
+    return do_decode_ffn(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, ids, tw, y, ws, st);
+  if (layer_table_or_null) {
+    // residency check over all pairs; the doorbell is rung from the compaction kernel
+    rc = hip_status(launch_lookup(ids, n_tokens * dims->top_k, dims->n_experts, layer_table_or_null, w->n_slots,
+                                  at<int32_t>(ws, L.slots), at<uint8_t>(ws, L.miss_flag), at<int32_t>(ws, L.miss_ids),
+                                  ctrl_of(ws) + kCtrlMissCount, ctrl_of(ws), bell_args(bell_or_null), st));
+    if (rc) return rc;
+    if (bell_or_null &&
+        hipStreamWaitValue32(st, bell_or_null->ready, bell_or_null->epoch, hipStreamWaitValueGte, 0xFFFFFFFFu) !=
+            hipSuccess)
+      return MOE_EHIP;
+  }
+  return do_prefill_ffn(dims, w, layer_table_or_null, x, n_tokens, ids, tw, y, ws, st);
 }
 
 }  // extern "C"

@@ -1,0 +1,401 @@
+// Prefill: expert FFNs as grouped GEMMs on MFMA, plus the prefill router GEMM.
+//
+// The work is a dense contraction per expert once tokens are grouped by expert (halogen README,
+// "Measured": prefill is compute-bound; Basalt README, "Prompt chunks": per-token cost keeps
+// falling up to a few thousand tokens per call).  Weights: halogen README, "Bring your own GGUF"
+// (small set of values x one scale per block, used as stored).
+//
+// Tile of one workgroup (4 waves): up to 128 rows of one expert (a TileItem, bucket-sorted rows)
+// x 256 weight rows; each wave owns 64 weight rows (4 MFMA subtiles of 16) for all rows of the
+// item.  Per 128-wide K chunk:
+//   A (activations, fp16): staged global -> LDS (double-buffered, 16-byte padded rows), read
+//     back as 16x16x32 MFMA fragments (one 16-byte LDS read per lane per MFMA, reused by the
+//     wave's 4 subtiles);
+//   B (weights): each lane loads the 16 code bytes + fp16 scale of one quantization block of its
+//     weight row straight into registers (lane group g takes block 4c+g) and dequantizes to fp16
+//     in registers, q * scale rounded once: two bit operations build (1024 + u) in fp16, one
+//     packed subtract gives q exactly, one packed multiply applies the scale.
+//   MFMA v_mfma_f32_16x16x32_f16, fp32 accumulation.  MFMA d (0..3) of a chunk pairs word d of
+//   every lane's block with the matching 8 activations of that block, so each B register is
+//   used as loaded.
+// Rows of an item are processed in 16-row subtiles up to the item's row count (no work on
+// padding beyond the last 16-row subtile).  fp16 (11 significant bits) instead of bf16 (8) for
+// the dequantized weights and the SwiGLU intermediate keeps the layer within a 2e-3 relative
+// error; the MFMA rate is the same.
+// Work items are mapped XCD-aware: consecutive work indices (the n-tiles of one item, then the
+// next item of the same expert) land on the same XCD and share its L2.
+#include "kernels.hpp"
+
+namespace moe {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+constexpr int kKC = 128;                  // K per pipeline stage (4 quantization blocks)
+constexpr int kAStride = kKC + 8;         // LDS row stride in 16-bit elements (16-byte pad)
+constexpr int kMSub = kTileRows / 16;     // 16-row subtiles per item
+constexpr int kNTileW = 256;              // weight rows per workgroup (4 waves x 64)
+
+enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
+
+struct GemmArgs {
+  ExpertSource src;
+  const TileItem* items;
+  const int32_t* n_items;  // device count (ctrl word); null for the router (dense m-tiles)
+  int32_t* ctrl;
+  int n_ntiles;
+  int n_works;             // items_max * n_ntiles
+  int E;                   // bucket E = the shared expert
+  int H, F;
+  int T;                   // router: tokens
+  const uint16_t* a16;     // gate/up: x16 [T][H]; down: h16 [P][F]; router: x bf16 [T][H]
+  const int32_t* row_tok;  // gate/up: token of each sorted row
+  const float* row_w;      // down: router weight of each sorted row
+  const uint16_t* wr;      // router: Wr bf16 [E][H]
+  const float* bias;       // router: bias [E] or null
+  _Float16* h_out;         // gate/up: h16 [P][F]
+  float* y_out;            // down: y_rows [P][H]; router: logits [T][E]
+};
+
+MOE_DEV const uint8_t* bucket_blob(const ExpertSource& s, int bucket, int E) {
+  if (bucket == E) return s.shared_blob;
+  const int slot = s.table ? s.table[bucket] : bucket;
+  if (slot < 0 || slot >= s.n_slots) return nullptr;
+  return s.arena + (int64_t)slot * s.slot_stride;
+}
+
+// Word d of a block's codes -> the 8 fp16 weights (elements 8d..8d+7) of MFMA d.
+MOE_DEV half8 dequant_word(uint32_t w, half2v s2) {
+  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  half8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;  // fp16 (1024 + u) pair
+    const half2v q = __builtin_bit_cast(half2v, t) - off;              // q = u - 8, exact
+    const half2v v = q * s2;                                           // fp16(q * scale)
+    r[2 * j] = v.x;
+    r[2 * j + 1] = v.y;
+  }
+  return r;
+}
+
+MOE_DEV uint32_t word_of(const uint4& c, int d) { return d == 0 ? c.x : d == 1 ? c.y : d == 2 ? c.z : c.w; }
+
+// Asynchronous global -> LDS copy of 16 bytes per lane: lane l's bytes land at lds_base + 16 l.
+MOE_DEV void lds_dma16(const void* gsrc, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+MOE_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int MODE>
+__global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
+  // A tile: 128 rows x 128 16-bit elements per stage, two stages.  16-byte chunk c of row r is
+  // stored at chunk c ^ (r & 15) of the row, so the 16 lanes of a fragment read (16 rows, one
+  // chunk) hit 16 different chunk slots.
+  __shared__ __attribute__((aligned(1024))) uint16_t As0[kTileRows * kKC];
+  __shared__ __attribute__((aligned(1024))) uint16_t As1[kTileRows * kKC];
+
+  // XCD-aware work index: blockIdx i runs on XCD i % 8; give each XCD a contiguous range.
+  const int per_xcd = gridDim.x >> 3;
+  const int work = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (work >= a.n_works) return;
+  const int item_id = work / a.n_ntiles;
+  const int ntile = work - item_id * a.n_ntiles;
+
+  TileItem it;
+  const uint8_t* blob = nullptr;
+  if constexpr (MODE == kRouter) {
+    it.bucket = 0;
+    it.row0 = item_id * kTileRows;
+    it.rows = min(kTileRows, a.T - it.row0);
+    if (it.rows <= 0) return;
+  } else {
+    if (item_id >= *a.n_items) return;
+    it = a.items[item_id];
+    blob = bucket_blob(a.src, it.bucket, a.E);
+    if (!blob) {
+      if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+      return;
+    }
+  }
+
+  const int H = a.H, F = a.F;
+  const int K = MODE == kDown ? F : H;
+  const int nk = K / kKC;
+  const int L = K / kBlock;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int ms = (it.rows + 15) >> 4;
+
+  // ---- this lane's 4 weight rows (one per subtile): byte offsets from one base --------------
+  const uint8_t* bbase;
+  uint32_t coff[4], soff[4];
+  bool bvalid[4];
+  if constexpr (MODE == kRouter) {
+    bbase = (const uint8_t*)a.wr;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int e = ntile * kNTileW + wave * 64 + 16 * s + n;
+      bvalid[s] = e < a.E;
+      coff[s] = (uint32_t)(bvalid[s] ? e : 0) * (uint32_t)H * 2u;
+      soff[s] = 0;
+    }
+  } else {
+    const BlobLayout lay = blob_layout(H, F);
+    bbase = blob;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      int row;
+      int64_t cb, sb;
+      if constexpr (MODE == kGateUp) {
+        const bool up = s >= 2;
+        row = ntile * (kNTileW / 2) + wave * 32 + 16 * (s & 1) + n;
+        cb = up ? lay.up_codes : lay.gate_codes;
+        sb = up ? lay.up_scales : lay.gate_scales;
+      } else {
+        row = ntile * kNTileW + wave * 64 + 16 * s + n;
+        cb = lay.down_codes;
+        sb = lay.down_scales;
+      }
+      bvalid[s] = true;
+      coff[s] = (uint32_t)(cb + (int64_t)row * (K / 2));
+      soff[s] = (uint32_t)(sb + (int64_t)row * L * 2);
+    }
+  }
+
+  // ---- A staging by DMA: instruction i of wave w fills rows 16i + 4w + (lane >> 4) ---------
+  const int a_ld = MODE == kDown ? F : H;
+  const int a_pc = lane & 15;  // physical chunk written by this lane
+  int32_t a_src[kMSub];        // source row (token or sorted row) of this lane's row per instruction
+#pragma unroll
+  for (int i = 0; i < kMSub; ++i) {
+    const int r = 16 * i + 4 * wave + (lane >> 4);
+    const int rr = r < it.rows ? r : 0;  // padding rows copy row 0 (their outputs are dropped)
+    if constexpr (MODE == kGateUp) a_src[i] = a.row_tok[it.row0 + rr];
+    else a_src[i] = it.row0 + rr;
+  }
+  const int a_lc = a_pc ^ ((4 * wave + (lane >> 4)) & 15);  // logical chunk: row & 15 = (4w + l/16) & 15
+  auto issue_a = [&](int kc, uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < kMSub; ++i) {
+      if (i < ms)
+        lds_dma16(a.a16 + (size_t)a_src[i] * a_ld + kc * kKC + a_lc * 8, buf + (16 * i + 4 * wave) * kKC);
+    }
+  };
+
+  // ---- B registers --------------------------------------------------------------------------
+  constexpr int kBW = MODE == kRouter ? 4 : 1;  // 16-byte loads per subtile per chunk
+  uint4 braw[4][kBW];
+  uint32_t bsc[4];
+  auto load_b = [&](int kc) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if constexpr (MODE == kRouter) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          braw[s][d] = bvalid[s] ? *(const uint4*)(bbase + coff[s] + ((size_t)kc * kKC + g * 32 + 8 * d) * 2)
+                                 : make_uint4(0u, 0u, 0u, 0u);
+        bsc[s] = 0;
+      } else {
+        braw[s][0] = *(const uint4*)(bbase + coff[s] + (size_t)(kc * 4 + g) * 16);
+        bsc[s] = *(const uint16_t*)(bbase + soff[s] + (size_t)(kc * 4 + g) * 2);
+      }
+    }
+  };
+
+  float4v acc[kMSub][4];
+#pragma unroll
+  for (int i = 0; i < kMSub; ++i)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[i][s] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  issue_a(0, As0);
+  load_b(0);
+  wait_vm();
+  __syncthreads();
+
+  for (int kc = 0; kc < nk; ++kc) {
+    uint16_t* Ab = (kc & 1) ? As1 : As0;
+    uint4 bcur[4][kBW];
+    half2v s2[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int d = 0; d < kBW; ++d) bcur[s][d] = braw[s][d];
+      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)bsc[s]);
+      s2[s] = (half2v){sv, sv};
+    }
+    if (kc + 1 < nk) {
+      issue_a(kc + 1, (kc & 1) ? As0 : As1);
+      if constexpr (MODE != kRouter) load_b(kc + 1);
+    }
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // fragment read: row 16i + n, logical chunk 4g + d -> physical (4g + d) ^ n
+      const int pcol = (((4 * g + d) ^ n) * 8);
+      if constexpr (MODE == kRouter) {
+#pragma unroll
+        for (int i = 0; i < kMSub; ++i) {
+          if (i < ms) {
+            const bf16x8 af = *(const bf16x8*)(Ab + (16 * i + n) * kKC + pcol);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, bcur[s][d]),
+                                                                  acc[i][s], 0, 0, 0);
+          }
+        }
+      } else {
+        half8 bf[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) bf[s] = dequant_word(word_of(bcur[s][0], d), s2[s]);
+#pragma unroll
+        for (int i = 0; i < kMSub; ++i) {
+          if (i < ms) {
+            const half8 af = *(const half8*)(Ab + (16 * i + n) * kKC + pcol);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[s], acc[i][s], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if constexpr (MODE == kRouter) {
+      if (kc + 1 < nk) load_b(kc + 1);
+    }
+    wait_vm();
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds D[16i + 4g + r][16s + n] -----------------------------------------
+#pragma unroll
+  for (int i = 0; i < kMSub; ++i) {
+    if (i >= ms) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * i + 4 * g + r;
+      if (row >= it.rows) continue;
+      if constexpr (MODE == kGateUp) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float gv = acc[i][s][r], uv = acc[i][s + 2][r];
+          const int col = ntile * (kNTileW / 2) + wave * 32 + 16 * s + n;
+          a.h_out[(size_t)(it.row0 + row) * F + col] = (_Float16)(silu(gv) * uv);
+        }
+      } else if constexpr (MODE == kDown) {
+        const float wv = a.row_w[it.row0 + row];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int col = ntile * kNTileW + wave * 64 + 16 * s + n;
+          a.y_out[(size_t)(it.row0 + row) * H + col] = acc[i][s][r] * wv;
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int e = ntile * kNTileW + wave * 64 + 16 * s + n;
+          if (e < a.E)
+            a.y_out[(size_t)(it.row0 + row) * a.E + e] = acc[i][s][r] + (a.bias ? a.bias[e] : 0.f);
+        }
+      }
+    }
+  }
+}
+
+// x (bf16) -> fp16, exact for values inside the fp16 normal range.
+__global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* __restrict__ x, _Float16* __restrict__ y,
+                                                     size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    y[i] = (_Float16)__uint_as_float((uint32_t)x[i] << 16);
+}
+
+// y[t] = sum_{j<k} y_rows[inv[t*k+j]] + y_rows[inv[T*k+t]] (rows already weighted), fixed order.
+__global__ __launch_bounds__(256) void k_prefill_combine(const float* __restrict__ y_rows,
+                                                          const int32_t* __restrict__ inv, int T, int k,
+                                                          int n_shared, int H, float* __restrict__ y) {
+  const int H4 = H / 4;
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)T * H4;
+       idx += (size_t)gridDim.x * blockDim.x) {
+    const int t = (int)(idx / H4), o4 = (int)(idx - (size_t)t * H4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int pos = inv[t * k + j];
+      if (pos < 0) continue;
+      const float4 v = ((const float4*)(y_rows + (size_t)pos * H))[o4];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if (n_shared) {
+      const int pos = inv[T * k + t];
+      const float4 v = ((const float4*)(y_rows + (size_t)pos * H))[o4];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    ((float4*)(y + (size_t)t * H))[o4] = acc;
+  }
+}
+
+static int round8(int v) { return (v + 7) & ~7; }
+
+hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, const ExpertSource& src,
+                              const void* x_bf16, const GroupBuffers& g, const PrefillBuffers& b, float* y,
+                              int32_t* ctrl, hipStream_t st) {
+  hipError_t err;
+  const size_t nx = (size_t)T * H;
+  int grid = (int)((nx + 255) / 256);
+  if (grid > 4096) grid = 4096;
+  k_bf16_to_f16<<<grid, 256, 0, st>>>((const uint16_t*)x_bf16, b.x16, nx);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  const int max_items = prefill_max_items(T, k, E, n_shared);
+  GemmArgs a{};
+  a.src = src;
+  a.items = g.items;
+  a.n_items = ctrl + kCtrlNTiles;
+  a.ctrl = ctrl;
+  a.E = E;
+  a.H = H;
+  a.F = F;
+  a.T = T;
+
+  // gate/up + SwiGLU: h16[row][F]
+  a.n_ntiles = F / (kNTileW / 2);
+  a.n_works = max_items * a.n_ntiles;
+  a.a16 = (const uint16_t*)b.x16;
+  a.row_tok = g.row_tok;
+  a.h_out = b.h16;
+  err = launch_timed(kTimePrefillGateUp, k_expert_gemm<kGateUp>, round8(a.n_works), 256, 0, st, a);
+  if (err != hipSuccess) return err;
+
+  // down: y_rows[row][H] = w_row * (Wd h)
+  a.n_ntiles = H / kNTileW;
+  a.n_works = max_items * a.n_ntiles;
+  a.a16 = (const uint16_t*)b.h16;
+  a.row_w = g.row_w;
+  a.y_out = b.y_rows;
+  err = launch_timed(kTimePrefillDown, k_expert_gemm<kDown>, round8(a.n_works), 256, 0, st, a);
+  if (err != hipSuccess) return err;
+
+  const size_t nc = (size_t)T * (H / 4);
+  grid = (int)((nc + 255) / 256);
+  if (grid > 8192) grid = 8192;
+  k_prefill_combine<<<grid, 256, 0, st>>>(b.y_rows, g.inv, T, k, n_shared, H, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const float* bias, int T, int E, int H,
+                              float* logits, hipStream_t st) {
+  GemmArgs a{};
+  a.E = E;
+  a.H = H;
+  a.T = T;
+  a.a16 = (const uint16_t*)x_bf16;
+  a.wr = (const uint16_t*)Wr_bf16;
+  a.bias = bias;
+  a.y_out = logits;
+  a.n_ntiles = (E + kNTileW - 1) / kNTileW;
+  a.n_works = ((T + kTileRows - 1) / kTileRows) * a.n_ntiles;
+  k_expert_gemm<kRouter><<<round8(a.n_works), 256, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -60,6 +60,35 @@ struct ExpertSource {
   const uint8_t* shared_blob;
 };
 
+// Prefill: one grouped-GEMM work item = up to kTileRows consecutive rows of one bucket
+// (bucket E = the shared expert) in bucket-sorted order.
+constexpr int kTileRows = 128;
+
+struct TileItem {
+  int32_t bucket;
+  int32_t row0;  // first sorted row
+  int32_t rows;  // 1..kTileRows
+  int32_t pad;
+};
+
+// Upper bound on work items: sum over non-empty buckets of ceil(c / kTileRows).
+inline int prefill_max_items(int T, int k, int E, int n_shared) {
+  const long long rows = (long long)T * (k + n_shared);
+  return (int)((rows + kTileRows - 1) / kTileRows) + E + 1;
+}
+
+struct GroupBuffers {
+  uint32_t* bits;    // [E][W] token bitmaps, W = ceil(T / 32)
+  int32_t* prefix;   // [E][W] exclusive popcount prefix per bucket
+  int32_t* count;    // [E]
+  int32_t* offsets;  // [E + 2]
+  TileItem* items;   // [prefill_max_items]
+  int32_t* perm;     // [P] pair index of each sorted row
+  int32_t* row_tok;  // [P] token of each sorted row
+  float* row_w;      // [P] router weight of each sorted row (1 for the shared expert)
+  int32_t* inv;      // [P] sorted row of each pair (-1 = invalid id)
+};
+
 // route.hip
 hipError_t launch_router_gemv(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias,
                               int T, int E, int H, float* logits, hipStream_t st);
@@ -76,6 +105,23 @@ hipError_t launch_decode_plan(const int32_t* ids, int T, int k, int E, int n_sha
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
                              const void* x, int x_dtype, const DecodeTask* tasks, const float* topk_w,
                              float* h, float* y_pairs, float* y, int32_t* ctrl, hipStream_t st);
+// group.hip
+hipError_t launch_group(const int32_t* ids, const float* topk_w, int T, int k, int E, int n_shared,
+                        const GroupBuffers& g, int32_t* ctrl, int32_t* counts_out, int32_t* offsets_out,
+                        hipStream_t st);
+
+// ffn_prefill.hip
+struct PrefillBuffers {
+  _Float16* x16;   // [T][H]
+  _Float16* h16;   // [P][F]
+  float* y_rows;   // [P][H]
+};
+hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, const ExpertSource& src,
+                              const void* x_bf16, const GroupBuffers& g, const PrefillBuffers& b, float* y,
+                              int32_t* ctrl, hipStream_t st);
+hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const float* bias, int T, int E, int H,
+                              float* logits, hipStream_t st);
+
 hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 

@@ -1,0 +1,183 @@
+"""GPU parity of the prefill path (router GEMM, grouping, grouped-GEMM FFNs, combine) against the
+CPU oracle, through the C interface.
+
+Bars: grouping (counts, offsets, permutation) bit-exact; top-k ids bit-exact outside oracle
+near-ties (k-th / (k+1)-th logit gap < 1e-4, counted); layer outputs within a per-token
+normwise relative error of 2e-3.  The prefill GEMMs run fp16 MFMA on fp16-rounded weights
+(q * scale) and an fp16 SwiGLU intermediate, so outputs are not bit-equal to the decode path.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from layer_fixtures import MODEL, TINY, Layer, near_tie_tokens  # noqa: E402
+from mixture_experts_route_amd import synth as S  # noqa: E402
+from oracle import moe_oracle as O  # noqa: E402
+
+Y_TOL = 2e-3
+TINY_BF16 = dict(TINY, x_f32=False, r_f32=False, cfg=11)
+
+
+@pytest.fixture(scope="module")
+def N():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mixture_experts_route_amd import native
+
+    return native
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def model_layer(N, dev):
+    return Layer(MODEL, dev, seed=0)
+
+
+def _ws(N, d, T, dev):
+    ws = torch.zeros(N.moe_workspace_bytes(d, T) // 4 + 64, dtype=torch.int32, device=dev)
+    N.moe_workspace_init(ws)
+    return ws
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (9, 512, 10), (300, 512, 10), (4096, 512, 10), (37, 64, 16)])
+def test_group_tokens_bit_exact(N, dev, T, E, k):
+    rng = np.random.default_rng(T * 7 + E)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    d = N.dims(2048, 768, E, k, 1)
+    ws = _ws(N, d, T, dev)
+    counts = torch.full((E,), -1, dtype=torch.int32, device=dev)
+    offsets = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    perm = torch.full((T * k,), -1, dtype=torch.int32, device=dev)
+    N.moe_group_tokens(d, torch.from_numpy(ids).to(dev), T, counts, offsets, perm, ws)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) == 0
+    c_ref, o_ref, p_ref = O.group_pairs(ids.ravel(), E)
+    assert np.array_equal(counts.cpu().numpy(), c_ref)
+    assert np.array_equal(offsets.cpu().numpy(), o_ref)
+    assert np.array_equal(perm.cpu().numpy(), p_ref)
+
+
+def test_group_tokens_skewed(N, dev):
+    """Every token picks the same experts: one 600-row group per chosen expert."""
+    T, E, k = 600, 512, 10
+    ids = np.tile(np.array([5, 9, 100, 3, 7, 200, 511, 0, 42, 77], np.int32), (T, 1))
+    d = N.dims(2048, 768, E, k, 1)
+    ws = _ws(N, d, T, dev)
+    counts = torch.zeros((E,), dtype=torch.int32, device=dev)
+    offsets = torch.zeros((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.zeros((T * k,), dtype=torch.int32, device=dev)
+    N.moe_group_tokens(d, torch.from_numpy(ids).to(dev), T, counts, offsets, perm, ws)
+    torch.cuda.synchronize()
+    c_ref, o_ref, p_ref = O.group_pairs(ids.ravel(), E)
+    assert np.array_equal(perm.cpu().numpy(), p_ref) and np.array_equal(counts.cpu().numpy(), c_ref)
+
+
+def _prefill_check(N, dev, layer, T, step, sample=None, via_layer=True, table=None):
+    d = layer.dims()
+    x, x64 = layer.x(T, step, dev)
+    ws = _ws(N, d, T, dev)
+    y = torch.full((T, layer.H), float("nan"), dtype=torch.float32, device=dev)
+    ids = torch.zeros((T, layer.k), dtype=torch.int32, device=dev)
+    w = torch.zeros((T, layer.k), dtype=torch.float32, device=dev)
+    wts = layer.native_weights()
+    if via_layer:
+        N.moe_layer_forward(d, wts, table, x, T, y, ws, topk_ids=ids, topk_w=w)
+    else:
+        logits = torch.zeros((T, layer.E), dtype=torch.float32, device=dev)
+        N.moe_route(d, x, T, layer.router, layer.bias, ids, w, logits, ws)
+        N.moe_expert_ffn_prefill(d, wts, table, x, T, ids, w, y, ws)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) == 0
+    rows = np.arange(T) if sample is None else np.asarray(sample)
+    ref = layer.oracle(x64[rows])
+    ok = ~near_tie_tokens(ref["logits64"], layer.k)
+    ids_np = ids.cpu().numpy()[rows]
+    assert np.array_equal(ids_np[ok], ref["ids"][ok])
+    err = O.per_token_rel_err(y.cpu().numpy()[rows], ref["y"])
+    assert np.all(err[ok] <= Y_TOL), (err.max(), np.argmax(err))
+    return y, err
+
+
+@pytest.mark.parametrize("T", [9, 40, 200])
+def test_prefill_tiny(N, dev, T):
+    layer = Layer(TINY_BF16, dev, seed=0)
+    _, err = _prefill_check(N, dev, layer, T, step=T)
+    assert err.max() < 1e-3
+
+
+@pytest.mark.parametrize("T", [9, 300])
+def test_prefill_model_shape(N, dev, model_layer, T):
+    _prefill_check(N, dev, model_layer, T, step=100 + T)
+
+
+def test_prefill_ffn_entry_point(N, dev, model_layer):
+    _prefill_check(N, dev, model_layer, 130, step=7, via_layer=False)
+
+
+def test_prefill_4k_sampled(N, dev, model_layer):
+    """The benchmark's shape (4096 tokens) on sampled tokens, including both ends."""
+    rng = np.random.default_rng(0)
+    sample = np.unique(np.concatenate([[0, 1, 4095], rng.choice(4096, 13, replace=False)]))
+    _prefill_check(N, dev, model_layer, 4096, step=4096, sample=sample)
+
+
+def test_prefill_skewed_zipf_routing(N, dev):
+    """Zipf(1.1)-skewed routing (uneven groups, several 128-row items per hot expert)."""
+    layer = Layer(MODEL, dev, seed=3, bias_c=S.ZIPF_C)
+    _prefill_check(N, dev, layer, 700, step=1)
+
+
+def test_prefill_slot_table_bitwise(N, dev):
+    rng = np.random.default_rng(9)
+    E = MODEL["E"]
+    n_slots = E + 16
+    perm = rng.permutation(n_slots)[:E]
+    pooled = Layer(MODEL, dev, seed=0, n_slots=n_slots, slot_of=perm)
+    direct = Layer(MODEL, dev, seed=0)
+    d = direct.dims()
+    T = 257
+    x, _ = direct.x(T, 3, dev)
+    ws = _ws(N, d, T, dev)
+    ya = torch.zeros((T, direct.H), dtype=torch.float32, device=dev)
+    yb = torch.zeros_like(ya)
+    N.moe_layer_forward(d, direct.native_weights(), None, x, T, ya, ws)
+    N.moe_layer_forward(d, pooled.native_weights(), pooled.table_tensor(dev), x, T, yb, ws)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) == 0
+    assert torch.equal(ya, yb)
+
+
+def test_prefill_deterministic_and_batch_invariant_rows(N, dev, model_layer):
+    layer = model_layer
+    d = layer.dims()
+    T = 520
+    x, _ = layer.x(T, 77, dev)
+    ws = _ws(N, d, T, dev)
+    y1 = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
+    y2 = torch.zeros_like(y1)
+    N.moe_layer_forward(d, layer.native_weights(), None, x, T, y1, ws)
+    N.moe_layer_forward(d, layer.native_weights(), None, x, T, y2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+def test_prefill_not_resident_is_an_error(N, dev, model_layer):
+    layer = model_layer
+    d = layer.dims()
+    T = 64
+    x, _ = layer.x(T, 5, dev)
+    ws = _ws(N, d, T, dev)
+    ids = torch.from_numpy(np.tile(np.arange(10, dtype=np.int32), (T, 1))).to(dev)
+    w = torch.full((T, 10), 0.1, dtype=torch.float32, device=dev)
+    table = torch.arange(layer.E, dtype=torch.int32, device=dev)
+    table[4] = -1
+    y = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
+    N.moe_expert_ffn_prefill(d, layer.native_weights(), table, x, T, ids, w, y, ws)
+    assert N.moe_check_device_error(ws) & N.DERR_NOT_RESIDENT

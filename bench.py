@@ -214,6 +214,102 @@ def bench_decode1(args):
     return result
 
 
+def cpu_baseline_prefill(T: int, n_tokens: int, seed=0, cfg=4, layer=0):
+    """The oracle timed on a sample of `n_tokens` tokens of the T-token prefill batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from mixture_experts_route_amd import synth as S
+    from oracle import moe_oracle as O
+
+    Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02)).astype(np.float64)
+    bias = S.zipf_bias(S.rank_permutation(seed, cfg, layer, 0, E), S.ZIPF_C)
+    shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
+    x = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), (n_tokens, H), 1.0))
+    x = x.astype(np.float64)
+    _, _, ids, _ = O.route(x, Wr, bias, K_TOP)
+    blobs = {int(e): S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, int(e)), H, F) for e in np.unique(ids)}
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        O.moe_layer(x, Wr, bias, K_TOP, lambda e: blobs[e], shared, H, F)
+        dt = time.perf_counter() - t0
+    return n_tokens / dt, dt
+
+
+def bench_prefill(T: int, steps: int, warmup: int, cpu_sample: int | None):
+    """T-token prefill through one model-shaped layer with Zipf(1.1)-skewed routing."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_route_amd import native as N
+    from mixture_experts_route_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    L = build_model_layer(dev, cfg=4, bias_c=S.ZIPF_C)
+    d = N.dims(H, F, E, K_TOP, 1)
+    w = N.layer_weights(L["router"], L["arena"], L["stride"], E, L["shared"], L["bias"])
+    n_batches = 2
+    xs = [S.bf16_normal_torch(S.stream_key(0, 4, "x", 0, X_STREAM + b), (T, H), 1.0, dev) for b in range(n_batches)]
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(N.moe_workspace_bytes(d, T) // 4 + 64, dtype=torch.int32, device=dev)
+    N.moe_workspace_init(ws)
+    ids = torch.empty((T, K_TOP), dtype=torch.int32, device=dev)
+    for s in range(warmup):
+        N.moe_layer_forward(d, w, L["table"], xs[s % n_batches], T, y, ws, topk_ids=ids)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) == 0
+    timer = KernelTimer(steps)
+    st = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        which = N.TIME_PREFILL_GATE_UP if i % 2 == 0 else N.TIME_PREFILL_DOWN
+        N.moe_debug_kernel_events(which, timer.pairs[i][0], timer.pairs[i][1])
+        N.moe_layer_forward(d, w, L["table"], xs[i % n_batches], T, y, ws, topk_ids=ids, stream=st)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    N.moe_debug_kernel_events(0, None, None)
+    assert N.moe_check_device_error(ws) == 0
+    k_ms = timer.durations_ms()
+    timer.close()
+    gu_s = float(np.mean(k_ms[0::2])) * 1e-3
+    dn_s = float(np.mean(k_ms[1::2])) * 1e-3 if steps > 1 else float("nan")
+    rows = T * (K_TOP + 1)
+    gu_flop = rows * 2.0 * (2 * F) * H
+    dn_flop = rows * 2.0 * H * F
+    cnt = np.bincount(ids.cpu().numpy().ravel(), minlength=E)
+    elapsed = t1 - t0
+    out = {
+        "workload": f"{T}-token prefill through one layer: 512 routed experts top-10 + 1 shared, hidden 2048, "
+                    f"expert FFN 768, 4-bit block-32 weights dequantized to fp16 in registers, fp16 MFMA with fp32 "
+                    f"accumulation, bf16 activations N(0,1), Zipf(1.1)-skewed routing",
+        "tokens_per_s": T * steps / elapsed,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "groups": {"max": int(cnt.max()), "median": float(np.median(cnt)), "under_16": int((cnt < 16).sum())},
+        "expert_gflop_per_step": (gu_flop + dn_flop) / 1e9,
+        "roofline": {
+            "kernel": "k_expert_gemm<gate/up> (grouped GEMM, SwiGLU epilogue)",
+            "bound": "mfma",
+            "achieved": gu_flop / gu_s / 1e12,
+            "peak": FP16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": gu_flop / gu_s / 1e12 / FP16_MFMA_PEAK_TFLOPS,
+            "traffic": None,
+            "flop_per_launch": gu_flop,
+            "avg_launch_us": gu_s * 1e6,
+        },
+        "down_gemm": {"achieved_tflops": dn_flop / dn_s / 1e12, "avg_launch_us": dn_s * 1e6,
+                      "frac": dn_flop / dn_s / 1e12 / FP16_MFMA_PEAK_TFLOPS},
+        "both_gemms_mfma_frac": (gu_flop + dn_flop) / (gu_s + dn_s) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
+    }
+    if cpu_sample:
+        v, dt = cpu_baseline_prefill(T, cpu_sample)
+        out["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {cpu_sample} tokens of the batch in one oracle call, "
+                                         f"{dt:.1f} s of float64 numpy on 1 thread"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,12 +318,18 @@ def main():
     ap.add_argument("--workload", default="decode1", choices=["decode1"])
     ap.add_argument("--cpu-sample", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill", default="4096", help="comma-separated prefill token counts to add ('' = none)")
+    ap.add_argument("--prefill-steps", type=int, default=20)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's data-parallel scale-out has no exchange on the path, "
               "so only --gpus 1 is run here", file=sys.stderr)
         sys.exit(2)
     res = bench_decode1(args)
+    for T in [int(v) for v in args.prefill.split(",") if v.strip()]:
+        steps = args.prefill_steps if T <= 8192 else max(4, args.prefill_steps // 4)
+        sample = None if args.no_cpu_baseline else (48 if T == 4096 else None)
+        res[f"prefill_{T}"] = bench_prefill(T, steps, max(2, steps // 5), sample)
     print(json.dumps(res), flush=True)
 
 

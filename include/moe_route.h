@@ -87,7 +87,8 @@ enum moe_device_error {
 /* Layer dimensions.  hidden = H, ffn = F (expert FFN width, shared expert too),
  * n_experts = E routed experts, top_k = k, n_shared = 0 or 1, block = 32 (the only
  * supported quantization block; anything else is MOE_EUNSUPPORTED).
- * Supported: H and F multiples of 32 with H/32 and F/32 <= 128; 1 <= k <= 16; k <= E;
+ * Supported: H and F multiples of 32 in [128, 4096] (H/32 and F/32 either <= 64 or exactly
+ * 128); 1 <= k <= 16; k <= E;
  * E <= 1024.  The prefill path (more than MOE_DECODE_MAX_TOKENS tokens) further needs
  * H % 256 == 0, F % 128 == 0 and bf16 activations and router. */
 typedef struct moe_dims {
@@ -151,9 +152,9 @@ MOE_API int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
  * and clears it.  Returns MOE_OK when the word was 0, MOE_EDEVICE otherwise. */
 MOE_API int moe_check_device_error(void* ws, void* stream, int32_t* bits_out);
 
-/* Profiling aid.  Until the next call, every launch of kernel `which` (1 = decode gate/up
- * GEMV, 2 = decode down GEMV, 3 = prefill gate/up grouped GEMM, 4 = prefill down grouped GEMM;
- * 0 = off) records the hipEvent_t `start_event` / `stop_event` (created by the caller with
+/* Profiling aid.  Until the next call, every launch of kernel `which` (1 = decode gate/up GEMV,
+ * 2 = decode down GEMV (+ combine), 3 = prefill gate/up grouped GEMM, 4 = prefill down grouped
+ * GEMM, 5 = decode route (router GEMV, top-k, residency check and plan); 0 = off) records the hipEvent_t `start_event` / `stop_event` (created by the caller with
  * timing enabled) around that kernel alone, via hipExtLaunchKernel.  Process-wide setting,
  * not for concurrent use from several threads. */
 MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop_event);

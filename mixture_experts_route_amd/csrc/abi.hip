@@ -7,7 +7,7 @@ namespace moe {
 KernelEvents g_kernel_events = {kTimeNone, nullptr, nullptr};
 
 // Workspace carve-up for up to `T` tokens.  The first kCtrlBytes hold the control words
-// (error word, counters) and, at byte 1024, the residency miss flags (one byte per expert).
+// (error word, counters) and, at byte 3072, the residency miss flags (one byte per expert).
 struct WsLayout {
   size_t tasks, h, y_pairs, logits, ids, w, slots, miss_ids, miss_flag;
   // prefill region
@@ -22,7 +22,7 @@ static WsLayout ws_layout(const moe_dims* d, int T) {
   const int Td = T < kMaxDecodeTok ? T : kMaxDecodeTok;
   const int pairs_d = Td * (d->top_k + d->n_shared);
   size_t off = kCtrlBytes;
-  L.miss_flag = 1024;
+  L.miss_flag = 3072;
   L.tasks = off;
   off = align256(off + sizeof(DecodeTask) * (size_t)decode_max_tasks(Td, d->top_k, d->n_shared));
   L.h = off;
@@ -77,6 +77,7 @@ static int check_dims(const moe_dims* d) {
   if (d->top_k > d->n_experts) return MOE_EINVAL;
   if (d->block != kBlock) return MOE_EUNSUPPORTED;
   if (d->hidden % kBlock || d->ffn % kBlock) return MOE_EINVAL;
+  if (d->hidden < 128 || d->ffn < 128) return MOE_EUNSUPPORTED;  // GEMV row groups need >= 4 blocks
   if (d->hidden / kBlock > 128 || d->ffn / kBlock > 128) return MOE_EUNSUPPORTED;
   if (d->hidden / kBlock > 64 && d->hidden / kBlock != 128) return MOE_EUNSUPPORTED;
   if (d->ffn / kBlock > 64 && d->ffn / kBlock != 128) return MOE_EUNSUPPORTED;
@@ -140,11 +141,13 @@ static int do_route(const moe_dims* d, const void* x, int x_dtype, int T, const 
     // long batches: router GEMM on MFMA (bf16 x bf16, fp32 accumulation)
     if (x_dtype != MOE_BF16 || r_dtype != MOE_BF16 || d->hidden % 128) return MOE_EUNSUPPORTED;
     rc = hip_status(launch_router_gemm(x, router, bias, T, d->n_experts, d->hidden, lg, st));
-  } else {
-    rc = hip_status(launch_router_gemv(x, x_dtype, router, r_dtype, bias, T, d->n_experts, d->hidden, lg, st));
+    if (rc) return rc;
+    return hip_status(launch_topk(lg, T, d->n_experts, d->top_k, ids, w, ctrl_of(ws), st));
   }
-  if (rc) return rc;
-  return hip_status(launch_topk(lg, T, d->n_experts, d->top_k, ids, w, ctrl_of(ws), st));
+  // short batches: router GEMV whose last workgroup selects the top-k
+  return hip_status(launch_decode_route(x, x_dtype, router, r_dtype, bias, T, d->n_experts, d->hidden, d->top_k,
+                                        d->n_shared, lg, ids, w, ctrl_of(ws), false, nullptr, 0, nullptr, nullptr,
+                                        DoorbellArgs{}, st));
 }
 
 static ExpertSource source_of(const moe_layer_weights* w, const int32_t* table) {
@@ -157,16 +160,20 @@ static ExpertSource source_of(const moe_layer_weights* w, const int32_t* table) 
   return s;
 }
 
-// decode FFN after routing; `bell` (may be null) is rung by the plan kernel.
+// decode FFN; with `plan_done` the plan is already in the workspace (fused route), otherwise it
+// is built from `ids` here.  `bell` (may be null) was or is rung by the planning kernel.
 static int do_decode_ffn(const moe_dims* d, const moe_layer_weights* w, const int32_t* table,
                          const moe_doorbell* bell, const void* x, int x_dtype, int T, const int32_t* ids,
-                         const float* topk_w, float* y, void* ws, hipStream_t st) {
+                         const float* topk_w, float* y, void* ws, hipStream_t st, bool plan_done) {
   const WsLayout L = ws_layout(d, T);
   int32_t* ctrl = ctrl_of(ws);
   DecodeTask* tasks = at<DecodeTask>(ws, L.tasks);
-  int rc = hip_status(launch_decode_plan(ids, T, d->top_k, d->n_experts, d->n_shared, table, w->n_slots, nullptr,
-                                         at<int32_t>(ws, L.miss_ids), nullptr, tasks, ctrl, bell_args(bell), st));
-  if (rc) return rc;
+  int rc;
+  if (!plan_done) {
+    rc = hip_status(launch_decode_plan(ids, T, d->top_k, d->n_experts, d->n_shared, table, w->n_slots,
+                                       at<int32_t>(ws, L.miss_ids), tasks, ctrl, bell_args(bell), st));
+    if (rc) return rc;
+  }
   if (bell) {
     if (hipStreamWaitValue32(st, bell->ready, bell->epoch, hipStreamWaitValueGte, 0xFFFFFFFFu) != hipSuccess)
       return MOE_EHIP;
@@ -260,7 +267,7 @@ MOE_API int moe_check_device_error(void* ws, void* stream, int32_t* bits_out) {
 }
 
 MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop_event) {
-  if (which < kTimeNone || which > kTimePrefillDown) return MOE_EINVAL;
+  if (which < kTimeNone || which > kTimeDecodeRoute) return MOE_EINVAL;
   if (which != kTimeNone && (!start_event || !stop_event)) return MOE_EINVAL;
   g_kernel_events.which = which;
   g_kernel_events.start = (hipEvent_t)start_event;
@@ -328,7 +335,7 @@ MOE_API int moe_expert_ffn_decode(const moe_dims* dims, const moe_layer_weights*
   if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
   return do_decode_ffn(dims, w, layer_table_or_null, nullptr, x, x_dtype, n_tokens, topk_ids, topk_w, y, ws,
-                       (hipStream_t)stream);
+                       (hipStream_t)stream, false);
 }
 
 MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights* w,
@@ -367,10 +374,18 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   const WsLayout L = ws_layout(dims, n_tokens);
   int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);
   float* tw = topk_w_out_or_null ? topk_w_out_or_null : at<float>(ws, L.w);
+  if (!prefill) {
+    // fused route: router GEMV, top-k, residency check, plan and doorbell in one kernel
+    rc = hip_status(launch_decode_route(x, x_dtype, w->router, w->router_dtype, w->router_bias, n_tokens,
+                                        dims->n_experts, dims->hidden, dims->top_k, dims->n_shared,
+                                        at<float>(ws, L.logits), ids, tw, ctrl_of(ws), true, layer_table_or_null,
+                                        w->n_slots, at<int32_t>(ws, L.miss_ids), at<DecodeTask>(ws, L.tasks),
+                                        bell_args(bell_or_null), st));
+    if (rc) return rc;
+    return do_decode_ffn(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, ids, tw, y, ws, st, true);
+  }
   rc = do_route(dims, x, x_dtype, n_tokens, w->router, w->router_dtype, w->router_bias, ids, tw, nullptr, ws, st);
   if (rc) return rc;
-  if (!prefill)
-    return do_decode_ffn(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, ids, tw, y, ws, st);
   if (layer_table_or_null) {
     // residency check over all pairs; the doorbell is rung from the compaction kernel
     rc = hip_status(launch_lookup(ids, n_tokens * dims->top_k, dims->n_experts, layer_table_or_null, w->n_slots,

@@ -26,6 +26,7 @@ enum CtrlWord {
   kCtrlNTiles = 3,     // prefill: number of m-tiles in the work list
 };
 
+
 // ---------------------------------------------------------------------------------------
 // Expert blob layout (see moe_route.h)
 // ---------------------------------------------------------------------------------------
@@ -99,5 +100,61 @@ MOE_DEV void set_error(int32_t* ctrl, int bits) {
 }
 
 MOE_DEV float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// ---------------------------------------------------------------------------------------
+// DPP reductions (VALU lane moves instead of LDS-crossbar shuffles)
+// ---------------------------------------------------------------------------------------
+enum DppCtrl {
+  kDppQuadXor1 = 0xB1,  // quad_perm [1,0,3,2]
+  kDppQuadXor2 = 0x4E,  // quad_perm [2,3,0,1]
+  kDppRowRor4 = 0x124,
+  kDppRowRor8 = 0x128,
+  kDppRowBcast15 = 0x142,
+  kDppRowBcast31 = 0x143,
+};
+
+template <int CTRL, int ROW_MASK>
+MOE_DEV float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+template <int CTRL, int ROW_MASK>
+MOE_DEV int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(v, v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Sum over aligned groups of `width` lanes (16, 32 or 64); the total is valid in the last lane of
+// each group (lane 15 of each row for 16; lanes 31 and 63 for 32; lane 63 for 64).
+MOE_DEV float group_sum_dpp(float v, int width) {
+  v += dpp_f<kDppQuadXor1, 0xF>(v);
+  v += dpp_f<kDppQuadXor2, 0xF>(v);
+  v += dpp_f<kDppRowRor4, 0xF>(v);
+  v += dpp_f<kDppRowRor8, 0xF>(v);
+  if (width >= 32) v += dpp_f<kDppRowBcast15, 0xA>(v);
+  if (width >= 64) v += dpp_f<kDppRowBcast31, 0xC>(v);
+  return v;
+}
+
+MOE_DEV bool group_last_lane(int lane, int width) { return (lane & (width - 1)) == width - 1; }
+
+// Wave-wide arg-max on (value desc, index asc); the result is returned to every lane.
+MOE_DEV void wave_argmax(float& v, int& i) {
+#define MOE_ARGMAX_STEP(C, M)                                        \
+  {                                                                  \
+    const float ov = dpp_f<C, M>(v);                                 \
+    const int oi = dpp_i<C, M>(i);                                   \
+    const bool take = ov > v || (ov == v && oi < i);                 \
+    v = take ? ov : v;                                               \
+    i = take ? oi : i;                                               \
+  }
+  MOE_ARGMAX_STEP(kDppQuadXor1, 0xF)
+  MOE_ARGMAX_STEP(kDppQuadXor2, 0xF)
+  MOE_ARGMAX_STEP(kDppRowRor4, 0xF)
+  MOE_ARGMAX_STEP(kDppRowRor8, 0xF)
+  MOE_ARGMAX_STEP(kDppRowBcast15, 0xA)
+  MOE_ARGMAX_STEP(kDppRowBcast31, 0xC)
+#undef MOE_ARGMAX_STEP
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  i = __builtin_amdgcn_readlane(i, 63);
+}
 
 }  // namespace moe

@@ -3,28 +3,39 @@
 // Weights: halogen-flash-server README, "Bring your own GGUF" (small set of values x one scale
 // per block, used as stored).  The layer: Betelgeuse news article, "mechanism" (10 routed + 1
 // shared expert per token).  Decode pays per byte of weights read (halogen README, "Bring your
-// own GGUF": an 8-bit trunk costs 2 GB more per token at 240 GB/s), so these kernels aim at
-// streaming each selected expert's blob once from HBM per step.
+// own GGUF": an 8-bit trunk costs 2 GB more per token at 240 GB/s), so each selected expert's blob
+// is streamed once from HBM per step.
 //
-// Design (gfx950): one lane per quantization block of a row.  A row of K inputs has L = K/32
+// GEMV design (gfx950): one lane per quantization block of a row.  A row of K inputs has L = K/32
 // blocks; the L lanes of a row group (L rounded up to a power of two Lp, so P = 64/Lp rows per
 // wave pass) each load the block's 16 code bytes with one 128-bit load and its fp16 scale.  The
-// activations of the lane's block live in registers as bf16 pairs for the whole kernel, so the
-// inner loop is: one mask per code pair (the pair becomes two bf16 values q + 136, exact), one
-// v_dot2c_f32_bf16 per pair and token, and one scale FMA per block and token.  The -136 offset is
-// removed by starting each block's chain at -136 * sum(x over the block).  fp32 inputs (the FFN
-// intermediate h, fp32 activations) are split into two bf16 parts hi + lo (16 significant bits),
-// each run through the same chain.  Partial sums are reduced across the Lp lanes of a row.
+// activations of the lane's block live in registers as bf16 pairs, so the inner loop is: one mask
+// per code pair (the pair becomes two bf16 values q + 136, exact), one v_dot2c_f32_bf16 per pair
+// and token, and one scale FMA per block and token.  The +136 offset is removed by starting each
+// block's chain at -136 * sum(x over the block).  fp32 inputs (the FFN intermediate h, fp32
+// activations) are split into two bf16 parts hi + lo (16 significant bits), each run through the
+// same chain.  Row sums are reduced across the Lp lanes with DPP.
+//
+// Two kernels run the FFN of a step and no workgroup depends on another: the gate/up kernel (one
+// workgroup per (task, 16-row tile)) writes h; in the down kernel one workgroup owns a tile of
+// output rows for every task of the step (its waves take the tasks in turn), keeps each pair's
+// partial rows in LDS and combines them for every token in the fixed order j = 0..k-1, then the
+// shared expert.
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kDecodeWaves = 4;    // waves per workgroup
-constexpr int kRowsPerWave = 4;    // wave passes per wave (each pass covers P rows)
+constexpr int kDecodeWaves = 4;  // waves per workgroup
+constexpr int kRowsPerWave = 4;  // wave passes per unit (each pass covers P rows)
+constexpr int kDnPasses = 4;     // down: wave passes per task (each pass covers P rows)
+constexpr int kMaxPairs = kMaxDecodeTok * (kMaxK + 1);
 
-MOE_DEV const uint8_t* expert_blob(const ExpertSource& s, int expert) {
-  if (expert < 0) return s.shared_blob;
-  const int slot = s.table ? s.table[expert] : expert;
+// A task's blob: the shared expert, the slot the plan resolved, or (for an expert that missed when
+// the plan ran and was filled since) the table entry read now.
+MOE_DEV const uint8_t* task_blob(const ExpertSource& s, const DecodeTask& tk) {
+  if (tk.expert < 0) return s.shared_blob;
+  int slot = tk.slot;
+  if (slot < 0) slot = s.table ? s.table[tk.expert] : tk.expert;
   if (slot < 0 || slot >= s.n_slots) return nullptr;
   return s.arena + (int64_t)slot * s.slot_stride;
 }
@@ -94,38 +105,69 @@ struct DecodeArgs {
   ExpertSource src;
   const DecodeTask* tasks;
   int32_t* ctrl;
-  const void* x;   // gate/up: activations [T][H]; down: h [pairs][F] fp32
-  float* out;      // gate/up: h [pairs][F]; down: y_pairs [pairs][H]
-  int H, F;
-  int tiles;       // workgroups per task
+  const void* x;         // activations [T][H], bf16 or fp32
+  float* h;              // [pairs][F]
+  float* y_pairs;        // [pairs][H]
+  const float* topk_w;   // [T][k]
+  float* y;              // [T][H]
+  int H, F, T, k, n_shared;
+  int tiles_gu, tiles_dn, max_tasks;
 };
 
-// Row geometry of a matrix with K inputs per row.
 MOE_DEV int lanes_per_row(int L) {
   int Lp = 1;
   while (Lp < L && Lp < 64) Lp <<= 1;
   return Lp;
 }
 
-// gate/up (+ SwiGLU): h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for r < F.
+// Sum over the Lp lanes of a row group; valid in the group's last lane.
+MOE_DEV float row_sum(float v, int Lp) {
+  if (Lp >= 16) return group_sum_dpp(v, Lp);
+  return group_sum(v, Lp);  // narrow rows (small hidden sizes): shuffles, valid in every lane
+}
+
+MOE_DEV bool row_writer(int lane, int Lp) { return Lp >= 16 ? group_last_lane(lane, Lp) : (lane % Lp) == 0; }
+
+// ---- gate/up unit: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for the unit's rows ------------
 template <int MAXTOK, int NPART, int BPL, bool X_BF16>
-__global__ __launch_bounds__(256) void k_decode_gate_up(DecodeArgs a) {
-  const int task_id = blockIdx.x / a.tiles;
-  if (task_id >= a.ctrl[kCtrlNTasks]) return;
-  const int tile = blockIdx.x - task_id * a.tiles;
+MOE_DEV void gate_up_unit(const DecodeArgs& a, int task_id, int tile) {
   const DecodeTask* tk = a.tasks + task_id;
-  const int ntok = tk->n_tok;
-  const uint8_t* blob = expert_blob(a.src, tk->expert);
+  const uint8_t* blob = task_blob(a.src, *tk);
   if (!blob) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
     return;
   }
+  const int ntok = tk->n_tok;
   const int H = a.H, F = a.F, L = H / kBlock;
   const BlobLayout lay = blob_layout(H, F);
   const int Lp = lanes_per_row(L), P = 64 / Lp;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / Lp, b0 = lane - sub * Lp;
   const bool active = b0 < L;
+  const int row0 = (tile * kDecodeWaves + wave) * kRowsPerWave * P;
+
+  // weights first: they do not depend on the activations
+  uint4 gc[kRowsPerWave][BPL], uc[kRowsPerWave][BPL];
+  float gs[kRowsPerWave][BPL], us[kRowsPerWave][BPL];
+#pragma unroll
+  for (int i = 0; i < kRowsPerWave; ++i) {
+    const int r = row0 + i * P + sub;
+#pragma unroll
+    for (int bb = 0; bb < BPL; ++bb) {
+      const int blk = b0 + 64 * bb;
+      if (active && blk < L && r < F) {
+        gc[i][bb] = *(const uint4*)(blob + lay.gate_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
+        uc[i][bb] = *(const uint4*)(blob + lay.up_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
+        gs[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.gate_scales + ((size_t)r * L + blk) * 2));
+        us[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.up_scales + ((size_t)r * L + blk) * 2));
+      } else {
+        gc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+        uc[i][bb] = gc[i][bb];
+        gs[i][bb] = 0.f;
+        us[i][bb] = 0.f;
+      }
+    }
+  }
 
   uint32_t xq[MAXTOK][BPL][NPART][16];
   float xi[MAXTOK][BPL][NPART];
@@ -149,37 +191,13 @@ __global__ __launch_bounds__(256) void k_decode_gate_up(DecodeArgs a) {
     }
   }
 
-  const int row0 = (tile * kDecodeWaves + wave) * kRowsPerWave * P;
-  uint4 gc[kRowsPerWave][BPL], uc[kRowsPerWave][BPL];
-  float gs[kRowsPerWave][BPL], us[kRowsPerWave][BPL];
 #pragma unroll
   for (int i = 0; i < kRowsPerWave; ++i) {
     const int r = row0 + i * P + sub;
 #pragma unroll
-    for (int bb = 0; bb < BPL; ++bb) {
-      const int blk = b0 + 64 * bb;
-      if (active && blk < L && r < F) {
-        gc[i][bb] = *(const uint4*)(blob + lay.gate_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
-        uc[i][bb] = *(const uint4*)(blob + lay.up_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
-        gs[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.gate_scales + ((size_t)r * L + blk) * 2));
-        us[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.up_scales + ((size_t)r * L + blk) * 2));
-      } else {
-        gc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        uc[i][bb] = gc[i][bb];
-        gs[i][bb] = 0.f;
-        us[i][bb] = 0.f;
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    float g[MAXTOK], u[MAXTOK];
-#pragma unroll
     for (int n = 0; n < MAXTOK; ++n) {
-      g[n] = 0.f;
-      u[n] = 0.f;
       if (n < ntok) {
+        float g = 0.f, u = 0.f;
 #pragma unroll
         for (int bb = 0; bb < BPL; ++bb) {
           float sg = 0.f, su = 0.f;
@@ -188,121 +206,111 @@ __global__ __launch_bounds__(256) void k_decode_gate_up(DecodeArgs a) {
             sg += block_dot(gc[i][bb], xq[n][bb][p], xi[n][bb][p]);
             su += block_dot(uc[i][bb], xq[n][bb][p], xi[n][bb][p]);
           }
-          g[n] = fmaf(sg, gs[i][bb], g[n]);
-          u[n] = fmaf(su, us[i][bb], u[n]);
+          g = fmaf(sg, gs[i][bb], g);
+          u = fmaf(su, us[i][bb], u);
         }
-      }
-    }
-    const int r = row0 + i * P + sub;
-#pragma unroll
-    for (int n = 0; n < MAXTOK; ++n) {
-      if (n < ntok) {
-        const float gt = group_sum(g[n], Lp);
-        const float ut = group_sum(u[n], Lp);
-        if (b0 == 0 && r < F) a.out[(size_t)tk->pair[n] * F + r] = silu(gt) * ut;
+        const float gt = row_sum(g, Lp);
+        const float ut = row_sum(u, Lp);
+        if (row_writer(lane, Lp) && r < F) a.h[(size_t)tk->pair[n] * F + r] = silu(gt) * ut;
       }
     }
   }
 }
 
-// down: y_pairs[pair][o] = Wd[o] . h[pair] for o < H.
+template <int MAXTOK, int NPART_X, int BPL, bool X_BF16>
+__global__ __launch_bounds__(256) void k_decode_gate_up(DecodeArgs a) {
+  const int task = blockIdx.x / a.tiles_gu;
+  if (task >= a.ctrl[kCtrlNTasks]) return;
+  gate_up_unit<MAXTOK, NPART_X, BPL, X_BF16>(a, task, blockIdx.x - task * a.tiles_gu);
+}
+
+// ---- down + combine: rows [tile*RW, tile*RW + RW) of y for every token ----------------------
+// RW = kDnPasses * P rows; wave w computes tasks w, w+4, ... for all RW rows.
 template <int MAXTOK, int BPL>
 __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
-  const int task_id = blockIdx.x / a.tiles;
-  if (task_id >= a.ctrl[kCtrlNTasks]) return;
-  const int tile = blockIdx.x - task_id * a.tiles;
-  const DecodeTask* tk = a.tasks + task_id;
-  const int ntok = tk->n_tok;
-  const uint8_t* blob = expert_blob(a.src, tk->expert);
-  if (!blob) {
-    if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
-    return;
-  }
+  __shared__ float ys[kMaxPairs][kDnPasses * 16];
+  const int n_tasks = a.ctrl[kCtrlNTasks];
   const int H = a.H, F = a.F, L = F / kBlock;
   const BlobLayout lay = blob_layout(H, F);
   const int Lp = lanes_per_row(L), P = 64 / Lp;
+  const int RW = kDnPasses * P;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane / Lp, b0 = lane - sub * Lp;
   const bool active = b0 < L;
   constexpr int NPART = 2;
-
-  uint32_t xq[MAXTOK][BPL][NPART][16];
-  float xi[MAXTOK][BPL][NPART];
+  const int row0 = blockIdx.x * RW;
+  for (int task = wave; task < n_tasks; task += kDecodeWaves) {
+    const DecodeTask* tk = a.tasks + task;
+    const uint8_t* blob = task_blob(a.src, *tk);
+    if (!blob) {
+      if (lane == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+      continue;
+    }
+    const int ntok = tk->n_tok;
+    uint4 dc[kDnPasses][BPL];
+    float ds[kDnPasses][BPL];
 #pragma unroll
-  for (int n = 0; n < MAXTOK; ++n) {
+    for (int i = 0; i < kDnPasses; ++i) {
+      const int r = row0 + i * P + sub;
 #pragma unroll
-    for (int bb = 0; bb < BPL; ++bb) {
-      if (n < ntok && active && b0 + 64 * bb < L) {
-        const float* hrow = (const float*)a.x + (size_t)tk->pair[n] * F;
-        load_x_block<NPART, false>(hrow, b0 + 64 * bb, xq[n][bb], xi[n][bb]);
-      } else {
+      for (int bb = 0; bb < BPL; ++bb) {
+        const int blk = b0 + 64 * bb;
+        if (active && blk < L && r < H) {
+          dc[i][bb] = *(const uint4*)(blob + lay.down_codes + (size_t)r * (F / 2) + (size_t)blk * 16);
+          ds[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.down_scales + ((size_t)r * L + blk) * 2));
+        } else {
+          dc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+          ds[i][bb] = 0.f;
+        }
+      }
+    }
+    uint32_t xq[MAXTOK][BPL][NPART][16];
+    float xi[MAXTOK][BPL][NPART];
 #pragma unroll
-        for (int p = 0; p < NPART; ++p) {
-          xi[n][bb][p] = 0.f;
+    for (int n = 0; n < MAXTOK; ++n) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) xq[n][bb][p][i] = 0u;
+      for (int bb = 0; bb < BPL; ++bb) {
+        if (n < ntok && active && b0 + 64 * bb < L) {
+          const float* hrow = a.h + (size_t)tk->pair[n] * F;
+          load_x_block<NPART, false>(hrow, b0 + 64 * bb, xq[n][bb], xi[n][bb]);
+        } else {
+#pragma unroll
+          for (int p = 0; p < NPART; ++p) {
+            xi[n][bb][p] = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) xq[n][bb][p][i] = 0u;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kDnPasses; ++i) {
+#pragma unroll
+      for (int n = 0; n < MAXTOK; ++n) {
+        if (n < ntok) {
+          float yv = 0.f;
+#pragma unroll
+          for (int bb = 0; bb < BPL; ++bb) {
+            float sd = 0.f;
+#pragma unroll
+            for (int p = 0; p < NPART; ++p) sd += block_dot(dc[i][bb], xq[n][bb][p], xi[n][bb][p]);
+            yv = fmaf(sd, ds[i][bb], yv);
+          }
+          const float yt = row_sum(yv, Lp);
+          if (row_writer(lane, Lp)) ys[tk->pair[n]][i * P + sub] = yt;
         }
       }
     }
   }
-
-  const int row0 = (tile * kDecodeWaves + wave) * kRowsPerWave * P;
-  uint4 dc[kRowsPerWave][BPL];
-  float ds[kRowsPerWave][BPL];
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int r = row0 + i * P + sub;
-#pragma unroll
-    for (int bb = 0; bb < BPL; ++bb) {
-      const int blk = b0 + 64 * bb;
-      if (active && blk < L && r < H) {
-        dc[i][bb] = *(const uint4*)(blob + lay.down_codes + (size_t)r * (F / 2) + (size_t)blk * 16);
-        ds[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.down_scales + ((size_t)r * L + blk) * 2));
-      } else {
-        dc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        ds[i][bb] = 0.f;
-      }
-    }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < a.T * RW; idx += blockDim.x) {
+    const int t = idx / RW, rr = idx - t * RW, o = row0 + rr;
+    if (o >= H) continue;
+    float acc = 0.f;
+    for (int j = 0; j < a.k; ++j) acc = fmaf(a.topk_w[t * a.k + j], ys[t * a.k + j][rr], acc);
+    if (a.n_shared) acc += ys[a.T * a.k + t][rr];
+    a.y[(size_t)t * H + o] = acc;
   }
-
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    float yv[MAXTOK];
-#pragma unroll
-    for (int n = 0; n < MAXTOK; ++n) {
-      yv[n] = 0.f;
-      if (n < ntok) {
-#pragma unroll
-        for (int bb = 0; bb < BPL; ++bb) {
-          float sd = 0.f;
-#pragma unroll
-          for (int p = 0; p < NPART; ++p) sd += block_dot(dc[i][bb], xq[n][bb][p], xi[n][bb][p]);
-          yv[n] = fmaf(sd, ds[i][bb], yv[n]);
-        }
-      }
-    }
-    const int r = row0 + i * P + sub;
-#pragma unroll
-    for (int n = 0; n < MAXTOK; ++n) {
-      if (n < ntok) {
-        const float yt = group_sum(yv[n], Lp);
-        if (b0 == 0 && r < H) a.out[(size_t)tk->pair[n] * H + r] = yt;
-      }
-    }
-  }
-}
-
-// y[t][o] = sum_{j<k} w[t][j] * y_pairs[t*k+j][o] + y_pairs[T*k+t][o] (shared), fixed order.
-__global__ __launch_bounds__(256) void k_decode_combine(const float* __restrict__ y_pairs,
-                                                         const float* __restrict__ topk_w, int T, int k,
-                                                         int n_shared, int H, float* __restrict__ y) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= T * H) return;
-  const int t = idx / H, o = idx - t * H;
-  float acc = 0.f;
-  for (int j = 0; j < k; ++j) acc = fmaf(topk_w[t * k + j], y_pairs[(size_t)(t * k + j) * H + o], acc);
-  if (n_shared) acc += y_pairs[(size_t)(T * k + t) * H + o];
-  y[idx] = acc;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -336,49 +344,62 @@ __global__ void k_fill_zero(uint32_t* p, size_t n) {
 // ------------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------------
-template <int MAXTOK>
-static hipError_t launch_decode_ffn_t(const DecodeArgs& gu, const DecodeArgs& dn, int grid_gu, int grid_dn,
-                                      int bpl_gu, int bpl_dn, bool x_bf16, hipStream_t st) {
-  hipError_t err;
-  if (x_bf16) {
-    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 1, true>, grid_gu, 256, 0, st, gu);
-    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 2, true>, grid_gu, 256, 0, st, gu);
-  } else {
-    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 1, false>, grid_gu, 256, 0, st, gu);
-    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 2, false>, grid_gu, 256, 0, st, gu);
-  }
-  if (err != hipSuccess) return err;
-  if (bpl_dn == 1) return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 1>, grid_dn, 256, 0, st, dn);
-  return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 2>, grid_dn, 256, 0, st, dn);
-}
-
-static int rows_per_wg(int K) {
+static int lanes_per_row_host(int K) {
   const int L = K / kBlock;
   int Lp = 1;
   while (Lp < L && Lp < 64) Lp <<= 1;
-  return kDecodeWaves * kRowsPerWave * (64 / Lp);
+  return Lp;
+}
+
+// gate/up: rows per workgroup; down: rows per workgroup (one tile of y for all tasks)
+static int rows_per_unit(int K) { return kDecodeWaves * kRowsPerWave * (64 / lanes_per_row_host(K)); }
+static int rows_per_down_tile(int F) { return kDnPasses * (64 / lanes_per_row_host(F)); }
+
+int decode_tiles_dn(int H, int F) { return (H + rows_per_down_tile(F) - 1) / rows_per_down_tile(F); }
+
+template <int MAXTOK>
+static hipError_t launch_decode_ffn_t(const DecodeArgs& a, int bpl_gu, int bpl_dn, bool xb, hipStream_t st) {
+  const int grid_gu = a.max_tasks * a.tiles_gu, grid_dn = a.tiles_dn;
+  hipError_t err;
+  if (xb) {
+    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 1, true>, grid_gu, 256, 0, st, a);
+    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 2, true>, grid_gu, 256, 0, st, a);
+  } else {
+    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 1, false>, grid_gu, 256, 0, st, a);
+    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 2, false>, grid_gu, 256, 0, st, a);
+  }
+  if (err != hipSuccess) return err;
+  if (bpl_dn == 1) return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 1>, grid_dn, 256, 0, st, a);
+  return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 2>, grid_dn, 256, 0, st, a);
 }
 
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
                              const void* x, int x_dtype, const DecodeTask* tasks, const float* topk_w,
                              float* h, float* y_pairs, float* y, int32_t* ctrl, hipStream_t st) {
-  DecodeArgs gu{src, tasks, ctrl, x, h, H, F, 0};
-  gu.tiles = (F + rows_per_wg(H) - 1) / rows_per_wg(H);
-  DecodeArgs dn{src, tasks, ctrl, h, y_pairs, H, F, 0};
-  dn.tiles = (H + rows_per_wg(F) - 1) / rows_per_wg(F);
+  DecodeArgs a{};
+  a.src = src;
+  a.tasks = tasks;
+  a.ctrl = ctrl;
+  a.x = x;
+  a.h = h;
+  a.y_pairs = y_pairs;
+  a.topk_w = topk_w;
+  a.y = y;
+  a.H = H;
+  a.F = F;
+  a.T = T;
+  a.k = k;
+  a.n_shared = n_shared;
+  a.tiles_gu = (F + rows_per_unit(H) - 1) / rows_per_unit(H);
+  a.tiles_dn = decode_tiles_dn(H, F);
+  a.max_tasks = max_tasks;
   const int bpl_gu = (H / kBlock) > 64 ? 2 : 1;
   const int bpl_dn = (F / kBlock) > 64 ? 2 : 1;
-  const int grid_gu = max_tasks * gu.tiles, grid_dn = max_tasks * dn.tiles;
   const bool xb = x_dtype == MOE_BF16;
-  hipError_t err;
   static_assert(kTaskTok == 4, "instantiations below cover tasks of up to 4 tokens");
-  if (T <= 1) err = launch_decode_ffn_t<1>(gu, dn, grid_gu, grid_dn, bpl_gu, bpl_dn, xb, st);
-  else if (T <= 2) err = launch_decode_ffn_t<2>(gu, dn, grid_gu, grid_dn, bpl_gu, bpl_dn, xb, st);
-  else err = launch_decode_ffn_t<4>(gu, dn, grid_gu, grid_dn, bpl_gu, bpl_dn, xb, st);
-  if (err != hipSuccess) return err;
-  const int n = T * H;
-  k_decode_combine<<<(n + 255) / 256, 256, 0, st>>>(y_pairs, topk_w, T, k, n_shared, H, y);
-  return hipGetLastError();
+  if (T <= 1) return launch_decode_ffn_t<1>(a, bpl_gu, bpl_dn, xb, st);
+  if (T <= 2) return launch_decode_ffn_t<2>(a, bpl_gu, bpl_dn, xb, st);
+  return launch_decode_ffn_t<4>(a, bpl_gu, bpl_dn, xb, st);
 }
 
 hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st) {

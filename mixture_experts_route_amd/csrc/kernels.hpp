@@ -10,7 +10,7 @@ namespace moe {
 // Profiling aid (moe_debug_kernel_events): launches of kernel `which` record `start` / `stop`
 // around the kernel itself through hipExtLaunchKernelGGL.
 enum TimedKernel { kTimeNone = 0, kTimeDecodeGateUp = 1, kTimeDecodeDown = 2, kTimePrefillGateUp = 3,
-                   kTimePrefillDown = 4 };
+                   kTimePrefillDown = 4, kTimeDecodeRoute = 5 };
 struct KernelEvents {
   int which;
   hipEvent_t start, stop;
@@ -32,6 +32,7 @@ constexpr int kTaskTok = 4;  // tokens per decode task (an expert chosen by more
 
 struct DecodeTask {
   int32_t expert;  // routed expert id, or -1 for the shared expert
+  int32_t slot;    // slot resolved by the plan, or -1: look the table up when the FFN runs (a miss)
   int32_t n_tok;
   int32_t tok[kTaskTok];
   int32_t pair[kTaskTok];
@@ -90,16 +91,18 @@ struct GroupBuffers {
 };
 
 // route.hip
-hipError_t launch_router_gemv(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias,
-                              int T, int E, int H, float* logits, hipStream_t st);
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* ctrl,
                        hipStream_t st);
 hipError_t launch_lookup(const int32_t* ids, int n_pairs, int E, const int32_t* table, int n_slots,
                          int32_t* slots, uint8_t* miss_flag, int32_t* miss_ids, int32_t* miss_count,
                          int32_t* ctrl, const DoorbellArgs& bell, hipStream_t st);
 hipError_t launch_decode_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table,
-                              int n_slots, int32_t* slots_out, int32_t* miss_ids, int32_t* miss_count_out,
-                              DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell, hipStream_t st);
+                              int n_slots, int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl,
+                              const DoorbellArgs& bell, hipStream_t st);
+hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias, int T,
+                               int E, int H, int k, int n_shared, float* logits, int32_t* ids, float* w,
+                               int32_t* ctrl, bool plan, const int32_t* table, int n_slots, int32_t* miss_ids,
+                               DecodeTask* tasks, const DoorbellArgs& bell, hipStream_t st);
 
 // ffn_decode.hip
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,

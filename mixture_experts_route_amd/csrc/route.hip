@@ -9,66 +9,6 @@
 namespace moe {
 
 // ------------------------------------------------------------------------------------------
-// Router GEMV for <= 8 tokens: logits[t][e] = sum_h x[t][h] * Wr[e][h] + bias[e].
-// x is staged once per workgroup in LDS as fp32 (exact widening of bf16/fp32); each wave
-// streams router rows with 16-byte loads (8 bf16 or 4 fp32 per lane per load), accumulates
-// in fp32 and reduces across the wave.  Bandwidth-bound on the router rows.
-// ------------------------------------------------------------------------------------------
-template <bool X_BF16, bool R_BF16>
-__global__ __launch_bounds__(256) void k_router_gemv(const void* __restrict__ x, const void* __restrict__ Wr,
-                                                      const float* __restrict__ bias, int T, int E, int H,
-                                                      float* __restrict__ logits) {
-  extern __shared__ float xs[];  // [T][H]
-  for (int i = threadIdx.x; i < T * H; i += blockDim.x) {
-    float v;
-    if (X_BF16) v = __uint_as_float(((uint32_t)((const uint16_t*)x)[i]) << 16);
-    else v = ((const float*)x)[i];
-    xs[i] = v;
-  }
-  __syncthreads();
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int waves_total = gridDim.x * (blockDim.x >> 6);
-  constexpr int kPer = R_BF16 ? 8 : 4;  // elements per 16-byte load
-  const int n_chunks = H / kPer;
-  for (int e = blockIdx.x * (blockDim.x >> 6) + wave; e < E; e += waves_total) {
-    float acc[kMaxDecodeTok];
-#pragma unroll
-    for (int t = 0; t < kMaxDecodeTok; ++t) acc[t] = 0.f;
-    for (int c = lane; c < n_chunks; c += 64) {
-      float wv[kPer];
-      if (R_BF16) {
-        uint4 q = *((const uint4*)((const uint16_t*)Wr + (size_t)e * H) + c);
-        uint32_t p[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          wv[2 * i] = bf16_lo(p[i]);
-          wv[2 * i + 1] = bf16_hi(p[i]);
-        }
-      } else {
-        float4 q = *((const float4*)((const float*)Wr + (size_t)e * H) + c);
-        wv[0] = q.x; wv[1] = q.y; wv[2] = q.z; wv[3] = q.w;
-      }
-#pragma unroll
-      for (int t = 0; t < kMaxDecodeTok; ++t) {
-        if (t < T) {
-          const float* xr = xs + t * H + c * kPer;
-#pragma unroll
-          for (int i = 0; i < kPer; ++i) acc[t] = fmaf(xr[i], wv[i], acc[t]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < kMaxDecodeTok; ++t) {
-      if (t < T) {
-        float s = wave_sum(acc[t]);
-        if (lane == 0) logits[(size_t)t * E + e] = s + (bias ? bias[e] : 0.f);
-      }
-    }
-  }
-}
-
-// ------------------------------------------------------------------------------------------
 // Top-k of E logits per token, one wave per token.  Each lane holds E/64 logits; k rounds of
 // (local best, wave arg-max on (value desc, id asc)) pick the experts in rank order.  The
 // weights are a softmax over the selected logits, summed in selection order.
@@ -111,15 +51,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
         bi = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    wave_argmax(bv, bi);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
     if (lane == r) {
       my_v = bv;
@@ -235,82 +167,94 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode plan (one workgroup, <= 8 tokens): residency check + the list of distinct experts
-// (ascending id) with the tokens that chose each, then the shared expert over all tokens.
-// The FFN kernels resolve each task's slot from the table when they run, so slots filled
-// after this check (doorbell path) are seen.
+// Decode plan (one workgroup of 256 threads, <= 8 tokens): residency check + the list of distinct
+// experts (ascending id) with the tokens that chose each (split into tasks of <= kTaskTok
+// tokens), then the shared expert over all tokens.  The FFN kernel resolves each task's slot from
+// the table when it runs, so slots filled after this check (doorbell path) are seen.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict__ ids, int T, int k, int E,
-                                                       int n_shared, const int32_t* __restrict__ table,
-                                                       int n_slots, int32_t* __restrict__ slots_out,
-                                                       int32_t* __restrict__ miss_ids,
-                                                       int32_t* __restrict__ miss_count_out,
-                                                       DecodeTask* __restrict__ tasks,
-                                                       int32_t* __restrict__ ctrl, DoorbellArgs bell) {
-  __shared__ uint32_t tok_mask[kMaxExperts];
-  __shared__ uint8_t choice[kMaxExperts][kMaxDecodeTok];
-  __shared__ int wave_sums[16];
-  __shared__ int s_bad;
-  for (int e = threadIdx.x; e < E; e += blockDim.x) tok_mask[e] = 0;
-  if (threadIdx.x == 0) s_bad = 0;
+struct PlanShared {
+  uint32_t tok_mask[kMaxExperts];
+  uint8_t choice[kMaxExperts][kMaxDecodeTok];
+  int wave_sums[16];
+  int bad;
+};
+
+// Exclusive scan over the block (blockDim.x multiple of 64, <= 1024) of one value per thread.
+MOE_DEV int block_scan_excl(int v, int* wave_sums, int* total) {
+  return block_exclusive_scan(v, wave_sums, total);
+}
+
+MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table, int n_slots,
+                        int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell,
+                        PlanShared& sh) {
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sh.tok_mask[e] = 0;
+  if (threadIdx.x == 0) sh.bad = 0;
   __syncthreads();
   const int n_pairs = T * k;
   for (int p = threadIdx.x; p < n_pairs; p += blockDim.x) {
     const int e = ids[p];
     const int t = p / k, j = p - t * k;
-    int s = -1;
     if (e < 0 || e >= E) {
-      atomicOr(&s_bad, MOE_DERR_EXPERT_ID);
+      atomicOr(&sh.bad, MOE_DERR_EXPERT_ID);
     } else {
-      atomicOr(&tok_mask[e], 1u << t);
-      choice[e][t] = (uint8_t)j;
-      s = table ? table[e] : e;
-      if (s >= n_slots) {
-        atomicOr(&s_bad, MOE_DERR_SLOT);
-        s = -1;
-      }
+      atomicOr(&sh.tok_mask[e], 1u << t);
+      sh.choice[e][t] = (uint8_t)j;
+      const int s = table ? table[e] : e;
+      if (s >= n_slots) atomicOr(&sh.bad, MOE_DERR_SLOT);
     }
-    if (slots_out) slots_out[p] = s;
   }
   __syncthreads();
-  const int e = threadIdx.x;
-  const uint32_t m = e < E ? tok_mask[e] : 0u;
-  const int n_e = __popc(m);
-  const bool used = n_e > 0;
-  int slot_e = -1;
-  if (used) slot_e = table ? table[e] : e;
-  const bool miss = used && slot_e < 0;
+  // each thread owns a run of consecutive experts, so the outputs come out in ascending id
+  const int per = (E + blockDim.x - 1) / blockDim.x;
+  const int e0 = threadIdx.x * per;
+  int n_sub = 0, n_mis = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int c = __popc(sh.tok_mask[e]);
+    if (c) {
+      n_sub += (c + kTaskTok - 1) / kTaskTok;
+      const int s = table ? table[e] : e;
+      if (s < 0) ++n_mis;
+    }
+  }
   int n_tasks, n_miss;
-  const int n_sub = (n_e + kTaskTok - 1) / kTaskTok;  // tasks of at most kTaskTok tokens
-  const int tpos = block_exclusive_scan(n_sub, wave_sums, &n_tasks);
-  const int mpos = block_exclusive_scan(miss ? 1 : 0, wave_sums, &n_miss);
-  if (used) {
+  int tpos = block_scan_excl(n_sub, sh.wave_sums, &n_tasks);
+  int mpos = block_scan_excl(n_mis, sh.wave_sums, &n_miss);
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const uint32_t m = sh.tok_mask[e];
+    if (!m) continue;
+    const int s = table ? table[e] : e;
+    if (s < 0) miss_ids[mpos++] = e;
     DecodeTask tk;
     tk.expert = e;
-    int n = 0, task = tpos;
+    tk.slot = s;
+    int n = 0;
     for (int t = 0; t < T; ++t) {
       if (m & (1u << t)) {
         tk.tok[n] = t;
-        tk.pair[n] = t * k + choice[e][t];
+        tk.pair[n] = t * k + sh.choice[e][t];
         if (++n == kTaskTok) {
           tk.n_tok = n;
-          tasks[task++] = tk;
+          tasks[tpos++] = tk;
           n = 0;
         }
       }
     }
     if (n > 0) {
       tk.n_tok = n;
-      tasks[task] = tk;
+      tasks[tpos++] = tk;
     }
   }
-  if (miss) miss_ids[mpos] = e;
   if (threadIdx.x == 0) {
     int n_all = n_tasks;
     if (n_shared) {
       for (int t0 = 0; t0 < T; t0 += kTaskTok) {
         DecodeTask tk;
         tk.expert = -1;
+        tk.slot = -1;
         tk.n_tok = min(kTaskTok, T - t0);
         for (int n = 0; n < tk.n_tok; ++n) {
           tk.tok[n] = t0 + n;
@@ -321,34 +265,181 @@ __global__ __launch_bounds__(1024) void k_decode_plan(const int32_t* __restrict_
     }
     ctrl[kCtrlNTasks] = n_all;
     ctrl[kCtrlMissCount] = n_miss;
-    if (miss_count_out) *miss_count_out = n_miss;
-    if (s_bad) set_error(ctrl, s_bad);
+    if (sh.bad) set_error(ctrl, sh.bad);
   }
   __threadfence();
   __syncthreads();
   ring_doorbell(bell, miss_ids, n_miss);
 }
 
+__global__ __launch_bounds__(256) void k_decode_plan(const int32_t* __restrict__ ids, int T, int k, int E,
+                                                      int n_shared, const int32_t* __restrict__ table,
+                                                      int n_slots, int32_t* __restrict__ miss_ids,
+                                                      DecodeTask* __restrict__ tasks, int32_t* __restrict__ ctrl,
+                                                      DoorbellArgs bell) {
+  __shared__ PlanShared sh;
+  build_plan(ids, T, k, E, n_shared, table, n_slots, miss_ids, tasks, ctrl, bell, sh);
+}
+
+// ------------------------------------------------------------------------------------------
+// Decode route (<= 8 tokens): a router GEMV over all workgroups (each wave's first router row
+// is loaded before the activations are staged), then one workgroup that selects and plans.  The
+// two are separate launches: a kernel boundary is the cheapest way to make the logits of every
+// XCD visible to one workgroup (an in-kernel release would write back each XCD's L2).
+// ------------------------------------------------------------------------------------------
+struct RouteArgs {
+  const void* x;
+  const void* Wr;
+  const float* bias;
+  int T, E, H, k, n_shared;
+  float* logits;   // [T][E]
+  int32_t* ids;    // [T][k]
+  float* w;        // [T][k]
+  int32_t* ctrl;
+  int plan;        // also build the decode plan
+  const int32_t* table;
+  int n_slots;
+  int32_t* miss_ids;
+  DecodeTask* tasks;
+  DoorbellArgs bell;
+};
+
+MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, float* w_out, int32_t* ctrl) {
+  const int lane = threadIdx.x & 63;
+  constexpr int kPerLane = kMaxExperts / 64;
+  float v[kPerLane];
+  bool nan_seen = false;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int e = lane + 64 * i;
+    float val = -INFINITY;
+    if (e < E) {
+      val = row[e];
+      if (val != val) {
+        nan_seen = true;
+        val = -INFINITY;
+      }
+    }
+    v[i] = val;
+  }
+  if (__any(nan_seen) && lane == 0) set_error(ctrl, MOE_DERR_NAN);
+  uint32_t taken = 0;
+  float my_v = 0.f;
+  int my_i = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) {
+      const int e = lane + 64 * i;
+      if (!(taken & (1u << i)) && e < E && (v[i] > bv || (v[i] == bv && e < bi))) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+    wave_argmax(bv, bi);
+    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if (lane == r) {
+      my_v = bv;
+      my_i = bi;
+    }
+  }
+  const float m = __shfl(my_v, 0, 64);
+  const float ex = lane < k ? expf(my_v - m) : 0.f;
+  float s = 0.f;
+  for (int r = 0; r < k; ++r) s += __shfl(ex, r, 64);
+  if (lane < k) {
+    ids_out[lane] = my_i;
+    w_out[lane] = ex / s;
+  }
+}
+
+template <bool X_BF16, bool R_BF16>
+__global__ __launch_bounds__(256) void k_router_gemv(RouteArgs a) {
+  extern __shared__ float xs[];  // [T][H]
+  const int T = a.T, E = a.E, H = a.H;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int waves_total = gridDim.x * (blockDim.x >> 6);
+  constexpr int kPer = R_BF16 ? 8 : 4;  // elements per 16-byte load
+  const int n_chunks = H / kPer;
+  const int e_first = blockIdx.x * (blockDim.x >> 6) + wave;
+  // first router row's loads go out before the activations are staged
+  constexpr int kMaxChunkPerLane = R_BF16 ? 8 : 16;  // H <= 4096
+  uint4 wpre[kMaxChunkPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxChunkPerLane; ++i) {
+    const int c = lane + 64 * i;
+    if (e_first < E && c < n_chunks) wpre[i] = *((const uint4*)((const uint8_t*)a.Wr + (size_t)e_first * H * (R_BF16 ? 2 : 4)) + c);
+  }
+  for (int i = threadIdx.x; i < T * H; i += blockDim.x) {
+    float v;
+    if (X_BF16) v = __uint_as_float(((uint32_t)((const uint16_t*)a.x)[i]) << 16);
+    else v = ((const float*)a.x)[i];
+    xs[i] = v;
+  }
+  __syncthreads();
+  for (int e = e_first; e < E; e += waves_total) {
+    float acc[kMaxDecodeTok];
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTok; ++t) acc[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxChunkPerLane; ++i) {
+      const int c = lane + 64 * i;
+      if (c >= n_chunks) break;
+      const uint4 q = e == e_first ? wpre[i]
+                                   : *((const uint4*)((const uint8_t*)a.Wr + (size_t)e * H * (R_BF16 ? 2 : 4)) + c);
+      float wv[kPer];
+      if constexpr (R_BF16) {
+        const uint32_t p[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          wv[2 * j] = bf16_lo(p[j]);
+          wv[2 * j + 1] = bf16_hi(p[j]);
+        }
+      } else {
+        wv[0] = __uint_as_float(q.x);
+        wv[1] = __uint_as_float(q.y);
+        wv[2] = __uint_as_float(q.z);
+        wv[3] = __uint_as_float(q.w);
+      }
+#pragma unroll
+      for (int t = 0; t < kMaxDecodeTok; ++t) {
+        if (t < T) {
+          const float* xr = xs + t * H + c * kPer;
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) acc[t] = fmaf(xr[j], wv[j], acc[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kMaxDecodeTok; ++t) {
+      if (t < T) {
+        const float sum = group_sum_dpp(acc[t], 64);
+        if (lane == 63) a.logits[(size_t)t * E + e] = sum + (a.bias ? a.bias[e] : 0.f);
+      }
+    }
+  }
+}
+
+// One workgroup: the top-k of every token (one wave per token, DPP arg-max) and, if asked, the
+// decode plan (residency check, task list, miss list, doorbell).
+__global__ __launch_bounds__(256) void k_decode_select(RouteArgs a) {
+  __shared__ PlanShared sh;
+  __shared__ int32_t s_ids[kMaxDecodeTok * kMaxK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < a.T; t += blockDim.x >> 6) {
+    select_topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.ctrl);
+    if (lane < a.k) s_ids[t * a.k + lane] = a.ids[(size_t)t * a.k + lane];
+  }
+  __syncthreads();
+  if (a.plan)
+    build_plan(s_ids, a.T, a.k, a.E, a.n_shared, a.table, a.n_slots, a.miss_ids, a.tasks, a.ctrl, a.bell, sh);
+}
+
 // ------------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------------
-hipError_t launch_router_gemv(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias,
-                              int T, int E, int H, float* logits, hipStream_t st) {
-  const int waves_per_wg = 4;
-  int grid = (E + waves_per_wg - 1) / waves_per_wg;
-  if (grid > 512) grid = 512;
-  const size_t lds = (size_t)T * H * sizeof(float);
-  if (x_dtype == MOE_BF16 && r_dtype == MOE_BF16)
-    k_router_gemv<true, true><<<grid, 256, lds, st>>>(x, Wr, bias, T, E, H, logits);
-  else if (x_dtype == MOE_BF16)
-    k_router_gemv<true, false><<<grid, 256, lds, st>>>(x, Wr, bias, T, E, H, logits);
-  else if (r_dtype == MOE_BF16)
-    k_router_gemv<false, true><<<grid, 256, lds, st>>>(x, Wr, bias, T, E, H, logits);
-  else
-    k_router_gemv<false, false><<<grid, 256, lds, st>>>(x, Wr, bias, T, E, H, logits);
-  return hipGetLastError();
-}
-
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* ctrl,
                        hipStream_t st) {
   const int grid = (T + 3) / 4;
@@ -372,10 +463,48 @@ hipError_t launch_lookup(const int32_t* ids, int n_pairs, int E, const int32_t* 
 }
 
 hipError_t launch_decode_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table,
-                              int n_slots, int32_t* slots_out, int32_t* miss_ids, int32_t* miss_count_out,
-                              DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell, hipStream_t st) {
-  k_decode_plan<<<1, 1024, 0, st>>>(ids, T, k, E, n_shared, table, n_slots, slots_out, miss_ids,
-                                    miss_count_out, tasks, ctrl, bell);
+                              int n_slots, int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl,
+                              const DoorbellArgs& bell, hipStream_t st) {
+  k_decode_plan<<<1, 256, 0, st>>>(ids, T, k, E, n_shared, table, n_slots, miss_ids, tasks, ctrl, bell);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias, int T,
+                               int E, int H, int k, int n_shared, float* logits, int32_t* ids, float* w,
+                               int32_t* ctrl, bool plan, const int32_t* table, int n_slots, int32_t* miss_ids,
+                               DecodeTask* tasks, const DoorbellArgs& bell, hipStream_t st) {
+  RouteArgs a{};
+  a.x = x;
+  a.Wr = Wr;
+  a.bias = bias;
+  a.T = T;
+  a.E = E;
+  a.H = H;
+  a.k = k;
+  a.n_shared = n_shared;
+  a.logits = logits;
+  a.ids = ids;
+  a.w = w;
+  a.ctrl = ctrl;
+  a.plan = plan ? 1 : 0;
+  a.table = table;
+  a.n_slots = n_slots;
+  a.miss_ids = miss_ids;
+  a.tasks = tasks;
+  a.bell = bell;
+  const int grid = (E + 3) / 4;
+  const uint32_t lds = (uint32_t)(T * H * sizeof(float));
+  hipError_t err;
+  if (x_dtype == MOE_BF16 && r_dtype == MOE_BF16)
+    err = launch_timed(kTimeDecodeRoute, k_router_gemv<true, true>, grid, 256, lds, st, a);
+  else if (x_dtype == MOE_BF16)
+    err = launch_timed(kTimeDecodeRoute, k_router_gemv<true, false>, grid, 256, lds, st, a);
+  else if (r_dtype == MOE_BF16)
+    err = launch_timed(kTimeDecodeRoute, k_router_gemv<false, true>, grid, 256, lds, st, a);
+  else
+    err = launch_timed(kTimeDecodeRoute, k_router_gemv<false, false>, grid, 256, lds, st, a);
+  if (err != hipSuccess) return err;
+  k_decode_select<<<1, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -149,7 +149,7 @@ def moe_check_device_error(ws, stream=None) -> int:
     return bits.value
 
 
-TIME_DECODE_GATE_UP, TIME_DECODE_DOWN, TIME_PREFILL_GATE_UP, TIME_PREFILL_DOWN = 1, 2, 3, 4
+TIME_DECODE_GATE_UP, TIME_DECODE_DOWN, TIME_PREFILL_GATE_UP, TIME_PREFILL_DOWN, TIME_DECODE_ROUTE = 1, 2, 3, 4, 5
 
 
 def moe_debug_kernel_events(which: int, start_event, stop_event):

@@ -130,8 +130,7 @@ MOE_DEV bool row_writer(int lane, int Lp) { return Lp >= 16 ? group_last_lane(la
 
 // ---- gate/up unit: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for the unit's rows ------------
 template <int MAXTOK, int NPART, int BPL, bool X_BF16>
-MOE_DEV void gate_up_unit(const DecodeArgs& a, int task_id, int tile) {
-  const DecodeTask* tk = a.tasks + task_id;
+MOE_DEV void gate_up_unit(const DecodeArgs& a, const DecodeTask* tk, int tile) {
   const uint8_t* blob = task_blob(a.src, *tk);
   if (!blob) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
@@ -220,13 +219,16 @@ MOE_DEV void gate_up_unit(const DecodeArgs& a, int task_id, int tile) {
 template <int MAXTOK, int NPART_X, int BPL, bool X_BF16>
 __global__ __launch_bounds__(256) void k_decode_gate_up(DecodeArgs a) {
   const int task = blockIdx.x / a.tiles_gu;
+  // the descriptor slot always exists (max_tasks of them): load it together with the count
+  const DecodeTask tk = a.tasks[task];
   if (task >= a.ctrl[kCtrlNTasks]) return;
-  gate_up_unit<MAXTOK, NPART_X, BPL, X_BF16>(a, task, blockIdx.x - task * a.tiles_gu);
+  gate_up_unit<MAXTOK, NPART_X, BPL, X_BF16>(a, &tk, blockIdx.x - task * a.tiles_gu);
 }
 
 // ---- down + combine: rows [tile*RW, tile*RW + RW) of y for every token ----------------------
-// RW = kDnPasses * P rows; wave w computes tasks w, w+4, ... for all RW rows.
-template <int MAXTOK, int BPL>
+// RW = kDnPasses * P rows.  Wave w takes tasks w, w+4, ...; it issues the weight and h loads of
+// TS of its tasks before computing any of them, so their latencies overlap.
+template <int MAXTOK, int BPL, int TS>
 __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
   __shared__ float ys[kMaxPairs][kDnPasses * 16];
   const int n_tasks = a.ctrl[kCtrlNTasks];
@@ -239,65 +241,85 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
   const bool active = b0 < L;
   constexpr int NPART = 2;
   const int row0 = blockIdx.x * RW;
-  for (int task = wave; task < n_tasks; task += kDecodeWaves) {
-    const DecodeTask* tk = a.tasks + task;
-    const uint8_t* blob = task_blob(a.src, *tk);
-    if (!blob) {
-      if (lane == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
-      continue;
-    }
-    const int ntok = tk->n_tok;
-    uint4 dc[kDnPasses][BPL];
-    float ds[kDnPasses][BPL];
+  for (int base = wave; base < n_tasks; base += kDecodeWaves * TS) {
+    int ntok[TS];
+    const uint8_t* blob[TS];
+    int pair[TS][MAXTOK];
+    uint4 dc[TS][kDnPasses][BPL];
+    float ds[TS][kDnPasses][BPL];
+    uint32_t xq[TS][MAXTOK][BPL][NPART][16];
+    float xi[TS][MAXTOK][BPL][NPART];
 #pragma unroll
-    for (int i = 0; i < kDnPasses; ++i) {
-      const int r = row0 + i * P + sub;
-#pragma unroll
-      for (int bb = 0; bb < BPL; ++bb) {
-        const int blk = b0 + 64 * bb;
-        if (active && blk < L && r < H) {
-          dc[i][bb] = *(const uint4*)(blob + lay.down_codes + (size_t)r * (F / 2) + (size_t)blk * 16);
-          ds[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.down_scales + ((size_t)r * L + blk) * 2));
+    for (int q = 0; q < TS; ++q) {
+      const int task = base + kDecodeWaves * q;
+      ntok[q] = 0;
+      blob[q] = nullptr;
+      if (task < n_tasks) {
+        const DecodeTask* tk = a.tasks + task;
+        blob[q] = task_blob(a.src, *tk);
+        if (!blob[q]) {
+          if (lane == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
         } else {
-          dc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-          ds[i][bb] = 0.f;
+          ntok[q] = tk->n_tok;
         }
+#pragma unroll
+        for (int n = 0; n < MAXTOK; ++n) pair[q][n] = n < ntok[q] ? tk->pair[n] : 0;
       }
-    }
-    uint32_t xq[MAXTOK][BPL][NPART][16];
-    float xi[MAXTOK][BPL][NPART];
 #pragma unroll
-    for (int n = 0; n < MAXTOK; ++n) {
+      for (int i = 0; i < kDnPasses; ++i) {
+        const int r = row0 + i * P + sub;
 #pragma unroll
-      for (int bb = 0; bb < BPL; ++bb) {
-        if (n < ntok && active && b0 + 64 * bb < L) {
-          const float* hrow = a.h + (size_t)tk->pair[n] * F;
-          load_x_block<NPART, false>(hrow, b0 + 64 * bb, xq[n][bb], xi[n][bb]);
-        } else {
-#pragma unroll
-          for (int p = 0; p < NPART; ++p) {
-            xi[n][bb][p] = 0.f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) xq[n][bb][p][i] = 0u;
+        for (int bb = 0; bb < BPL; ++bb) {
+          const int blk = b0 + 64 * bb;
+          if (ntok[q] > 0 && active && blk < L && r < H) {
+            dc[q][i][bb] = *(const uint4*)(blob[q] + lay.down_codes + (size_t)r * (F / 2) + (size_t)blk * 16);
+            ds[q][i][bb] =
+                fp16_bits_to_f32(*(const uint16_t*)(blob[q] + lay.down_scales + ((size_t)r * L + blk) * 2));
+          } else {
+            dc[q][i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
+            ds[q][i][bb] = 0.f;
           }
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < kDnPasses; ++i) {
+    for (int q = 0; q < TS; ++q) {
 #pragma unroll
       for (int n = 0; n < MAXTOK; ++n) {
-        if (n < ntok) {
-          float yv = 0.f;
 #pragma unroll
-          for (int bb = 0; bb < BPL; ++bb) {
-            float sd = 0.f;
+        for (int bb = 0; bb < BPL; ++bb) {
+          if (n < ntok[q] && active && b0 + 64 * bb < L) {
+            const float* hrow = a.h + (size_t)pair[q][n] * F;
+            load_x_block<NPART, false>(hrow, b0 + 64 * bb, xq[q][n][bb], xi[q][n][bb]);
+          } else {
 #pragma unroll
-            for (int p = 0; p < NPART; ++p) sd += block_dot(dc[i][bb], xq[n][bb][p], xi[n][bb][p]);
-            yv = fmaf(sd, ds[i][bb], yv);
+            for (int p = 0; p < NPART; ++p) {
+              xi[q][n][bb][p] = 0.f;
+#pragma unroll
+              for (int i = 0; i < 16; ++i) xq[q][n][bb][p][i] = 0u;
+            }
           }
-          const float yt = row_sum(yv, Lp);
-          if (row_writer(lane, Lp)) ys[tk->pair[n]][i * P + sub] = yt;
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < TS; ++q) {
+#pragma unroll
+      for (int i = 0; i < kDnPasses; ++i) {
+#pragma unroll
+        for (int n = 0; n < MAXTOK; ++n) {
+          if (n < ntok[q]) {
+            float yv = 0.f;
+#pragma unroll
+            for (int bb = 0; bb < BPL; ++bb) {
+              float sd = 0.f;
+#pragma unroll
+              for (int p = 0; p < NPART; ++p) sd += block_dot(dc[q][i][bb], xq[q][n][bb][p], xi[q][n][bb][p]);
+              yv = fmaf(sd, ds[q][i][bb], yv);
+            }
+            const float yt = row_sum(yv, Lp);
+            if (row_writer(lane, Lp)) ys[pair[q][n]][i * P + sub] = yt;
+          }
         }
       }
     }
@@ -369,8 +391,10 @@ static hipError_t launch_decode_ffn_t(const DecodeArgs& a, int bpl_gu, int bpl_d
     else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 2, false>, grid_gu, 256, 0, st, a);
   }
   if (err != hipSuccess) return err;
-  if (bpl_dn == 1) return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 1>, grid_dn, 256, 0, st, a);
-  return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 2>, grid_dn, 256, 0, st, a);
+  // task slots per wave: as many as the registers allow for MAXTOK tokens per task
+  constexpr int TS = MAXTOK == 1 ? 3 : MAXTOK == 2 ? 2 : 1;
+  if (bpl_dn == 1) return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 1, TS>, grid_dn, 256, 0, st, a);
+  return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 2, TS>, grid_dn, 256, 0, st, a);
 }
 
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,

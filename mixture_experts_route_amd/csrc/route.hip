@@ -9,32 +9,33 @@
 namespace moe {
 
 // ------------------------------------------------------------------------------------------
-// Top-k of E logits per token, one wave per token.  Each lane holds E/64 logits; k rounds of
-// (local best, wave arg-max on (value desc, id asc)) pick the experts in rank order.  The
-// weights are a softmax over the selected logits, summed in selection order.
+// Top-k of E logits per token, one wave per token.  Each lane holds the logits lane + 64 i;
+// k rounds of (local best, DPP wave arg-max on (value desc, id asc)) pick the experts in rank
+// order.  The weights are a softmax over the selected logits, summed in selection order.  NaN
+// logits are flagged and never selected.
 // ------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
-                                               int32_t* __restrict__ ids, float* __restrict__ w,
-                                               int32_t* __restrict__ ctrl) {
+MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, float* w_out, int32_t* ctrl,
+                              int32_t* lds_ids) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  if (t >= T) return;
   constexpr int kPerLane = kMaxExperts / 64;
   float v[kPerLane];
-  const float* row = logits + (size_t)t * E;
+  // all loads are issued before any value is looked at: a clamped index instead of a branch keeps
+  // the compiler from waiting on each load in turn (16 serial memory round trips otherwise)
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = row[e < E ? e : E - 1];
+  }
   bool nan_seen = false;
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int e = lane + 64 * i;
-    float val = -INFINITY;
-    if (e < E) {
-      val = row[e];
-      if (val != val) {
-        nan_seen = true;
-        val = -INFINITY;
-      }
+    if (e >= E) {
+      v[i] = -INFINITY;
+    } else if (v[i] != v[i]) {
+      nan_seen = true;
+      v[i] = -INFINITY;
     }
-    v[i] = val;
   }
   if (__any(nan_seen) && lane == 0) set_error(ctrl, MOE_DERR_NAN);
   uint32_t taken = 0;
@@ -63,9 +64,18 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   float s = 0.f;
   for (int r = 0; r < k; ++r) s += __shfl(ex, r, 64);
   if (lane < k) {
-    ids[(size_t)t * k + lane] = my_i;
-    w[(size_t)t * k + lane] = ex / s;
+    ids_out[lane] = my_i;
+    w_out[lane] = ex / s;
+    if (lds_ids) lds_ids[lane] = my_i;
   }
+}
+
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
+                                               int32_t* __restrict__ ids, float* __restrict__ w,
+                                               int32_t* __restrict__ ctrl) {
+  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  select_topk_wave(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, ctrl, nullptr);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -161,9 +171,11 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
     *miss_count = total;
     ctrl[kCtrlMissCount] = total;
   }
-  __threadfence();
-  __syncthreads();
-  ring_doorbell(bell, miss_ids, total);
+  if (bell.active) {
+    __threadfence();
+    __syncthreads();
+    ring_doorbell(bell, miss_ids, total);
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -174,16 +186,15 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
 // ------------------------------------------------------------------------------------------
 struct PlanShared {
   uint32_t tok_mask[kMaxExperts];
+  int32_t slot_of[kMaxExperts];
   uint8_t choice[kMaxExperts][kMaxDecodeTok];
   int wave_sums[16];
   int bad;
 };
 
-// Exclusive scan over the block (blockDim.x multiple of 64, <= 1024) of one value per thread.
-MOE_DEV int block_scan_excl(int v, int* wave_sums, int* total) {
-  return block_exclusive_scan(v, wave_sums, total);
-}
-
+// ids: the step's [T][k] selections (LDS or global).  One thread per pair fills the per-expert
+// token masks and slots in LDS; then each thread owns a run of consecutive experts, so tasks and
+// misses come out in ascending expert id.  Tasks are written field by field to global memory.
 MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table, int n_slots,
                         int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell,
                         PlanShared& sh) {
@@ -200,11 +211,11 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
       atomicOr(&sh.tok_mask[e], 1u << t);
       sh.choice[e][t] = (uint8_t)j;
       const int s = table ? table[e] : e;
+      sh.slot_of[e] = s;  // every writer of e writes the same value
       if (s >= n_slots) atomicOr(&sh.bad, MOE_DERR_SLOT);
     }
   }
   __syncthreads();
-  // each thread owns a run of consecutive experts, so the outputs come out in ascending id
   const int per = (E + blockDim.x - 1) / blockDim.x;
   const int e0 = threadIdx.x * per;
   int n_sub = 0, n_mis = 0;
@@ -214,62 +225,60 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     const int c = __popc(sh.tok_mask[e]);
     if (c) {
       n_sub += (c + kTaskTok - 1) / kTaskTok;
-      const int s = table ? table[e] : e;
-      if (s < 0) ++n_mis;
+      if (sh.slot_of[e] < 0) ++n_mis;
     }
   }
   int n_tasks, n_miss;
-  int tpos = block_scan_excl(n_sub, sh.wave_sums, &n_tasks);
-  int mpos = block_scan_excl(n_mis, sh.wave_sums, &n_miss);
+  int tpos = block_exclusive_scan(n_sub, sh.wave_sums, &n_tasks);
+  int mpos = block_exclusive_scan(n_mis, sh.wave_sums, &n_miss);
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     const uint32_t m = sh.tok_mask[e];
     if (!m) continue;
-    const int s = table ? table[e] : e;
+    const int s = sh.slot_of[e];
     if (s < 0) miss_ids[mpos++] = e;
-    DecodeTask tk;
-    tk.expert = e;
-    tk.slot = s;
     int n = 0;
     for (int t = 0; t < T; ++t) {
-      if (m & (1u << t)) {
-        tk.tok[n] = t;
-        tk.pair[n] = t * k + sh.choice[e][t];
-        if (++n == kTaskTok) {
-          tk.n_tok = n;
-          tasks[tpos++] = tk;
-          n = 0;
-        }
+      if (!(m & (1u << t))) continue;
+      tasks[tpos].tok[n] = t;
+      tasks[tpos].pair[n] = t * k + sh.choice[e][t];
+      if (++n == kTaskTok || (m >> (t + 1)) == 0) {
+        tasks[tpos].expert = e;
+        tasks[tpos].slot = s;
+        tasks[tpos].n_tok = n;
+        ++tpos;
+        n = 0;
       }
-    }
-    if (n > 0) {
-      tk.n_tok = n;
-      tasks[tpos++] = tk;
     }
   }
   if (threadIdx.x == 0) {
     int n_all = n_tasks;
     if (n_shared) {
       for (int t0 = 0; t0 < T; t0 += kTaskTok) {
-        DecodeTask tk;
-        tk.expert = -1;
-        tk.slot = -1;
-        tk.n_tok = min(kTaskTok, T - t0);
-        for (int n = 0; n < tk.n_tok; ++n) {
-          tk.tok[n] = t0 + n;
-          tk.pair[n] = T * k + t0 + n;
+        const int nt = min(kTaskTok, T - t0);
+        for (int n = 0; n < nt; ++n) {
+          tasks[n_all].tok[n] = t0 + n;
+          tasks[n_all].pair[n] = T * k + t0 + n;
         }
-        tasks[n_all++] = tk;
+        tasks[n_all].expert = -1;
+        tasks[n_all].slot = -1;
+        tasks[n_all].n_tok = nt;
+        ++n_all;
       }
     }
     ctrl[kCtrlNTasks] = n_all;
     ctrl[kCtrlMissCount] = n_miss;
     if (sh.bad) set_error(ctrl, sh.bad);
   }
-  __threadfence();
-  __syncthreads();
-  ring_doorbell(bell, miss_ids, n_miss);
+  if (bell.active) {
+    // the host reads the miss list as soon as the doorbell rings: publish it first.  Without a
+    // doorbell the kernel boundary publishes everything (an agent-scope fence here would write
+    // back every XCD's L2).
+    __threadfence();
+    __syncthreads();
+    ring_doorbell(bell, miss_ids, n_miss);
+  }
 }
 
 __global__ __launch_bounds__(256) void k_decode_plan(const int32_t* __restrict__ ids, int T, int k, int E,
@@ -304,55 +313,6 @@ struct RouteArgs {
   DoorbellArgs bell;
 };
 
-MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, float* w_out, int32_t* ctrl) {
-  const int lane = threadIdx.x & 63;
-  constexpr int kPerLane = kMaxExperts / 64;
-  float v[kPerLane];
-  bool nan_seen = false;
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) {
-    const int e = lane + 64 * i;
-    float val = -INFINITY;
-    if (e < E) {
-      val = row[e];
-      if (val != val) {
-        nan_seen = true;
-        val = -INFINITY;
-      }
-    }
-    v[i] = val;
-  }
-  if (__any(nan_seen) && lane == 0) set_error(ctrl, MOE_DERR_NAN);
-  uint32_t taken = 0;
-  float my_v = 0.f;
-  int my_i = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (!(taken & (1u << i)) && e < E && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == r) {
-      my_v = bv;
-      my_i = bi;
-    }
-  }
-  const float m = __shfl(my_v, 0, 64);
-  const float ex = lane < k ? expf(my_v - m) : 0.f;
-  float s = 0.f;
-  for (int r = 0; r < k; ++r) s += __shfl(ex, r, 64);
-  if (lane < k) {
-    ids_out[lane] = my_i;
-    w_out[lane] = ex / s;
-  }
-}
 
 template <bool X_BF16, bool R_BF16>
 __global__ __launch_bounds__(256) void k_router_gemv(RouteArgs a) {
@@ -427,10 +387,10 @@ __global__ __launch_bounds__(256) void k_router_gemv(RouteArgs a) {
 __global__ __launch_bounds__(256) void k_decode_select(RouteArgs a) {
   __shared__ PlanShared sh;
   __shared__ int32_t s_ids[kMaxDecodeTok * kMaxK];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6;
   for (int t = wave; t < a.T; t += blockDim.x >> 6) {
-    select_topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.ctrl);
-    if (lane < a.k) s_ids[t * a.k + lane] = a.ids[(size_t)t * a.k + lane];
+    select_topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.ctrl,
+                     s_ids + t * a.k);
   }
   __syncthreads();
   if (a.plan)

@@ -36,8 +36,9 @@ The readings taken here:
   experts);
 * R2 the shared expert has weight 1, no gate, the same width and format;
 * R3 4-bit code u in 0..15 stands for q = u - 8; blocks of 32 run along the
-  reduction dimension; one fp16 scale per block; byte layout as in
-  :func:`decode_codes`;
+  reduction dimension; one fp16 scale per block; the code words of each run of
+  four blocks are interleaved as in :func:`decode_codes` (rows hold a multiple
+  of 128 elements);
 * R4 a per-expert bias, when given, is added to the logits before both the
   selection and the weights;
 * R5 equal logits: the lower expert id wins;
@@ -94,19 +95,29 @@ def blob_layout(H: int, F: int) -> dict:
     return out
 
 
-def decode_codes(code_bytes: np.ndarray, rows: int, cols: int) -> np.ndarray:
-    """4-bit codes of a [rows][cols] matrix, as integers 0..15.
+GROUP = 128  # elements per word group: four blocks of 32
 
-    Each row is cols/2 bytes read as little-endian 32-bit words; word d holds
-    elements 8d .. 8d+7 of the row: element 8d+2j in bits 4j..4j+3 and element
-    8d+2j+1 in bits 16+4j..16+4j+3, for j = 0..3.
+
+def decode_codes(code_bytes: np.ndarray, rows: int, cols: int) -> np.ndarray:
+    """4-bit codes of a [rows][cols] matrix, as integers 0..15 (cols a multiple of 128).
+
+    Each row is cols/2 bytes read as little-endian 32-bit words, in groups of 16
+    words that cover 128 elements (four blocks of 32).  Word 4g + i of group c
+    holds the eight elements 128c + 32i + 8g .. 128c + 32i + 8g + 7 (slice g of
+    block i of the group): its element 2j in bits 4j..4j+3 and its element 2j+1
+    in bits 16+4j..16+4j+3, for j = 0..3.
     """
-    b = np.asarray(code_bytes, dtype=np.uint8).reshape(rows, cols // 8, 4).astype(np.uint32)
+    assert cols % GROUP == 0
+    b = np.asarray(code_bytes, dtype=np.uint8).reshape(rows, cols // GROUP, 4, 4, 4).astype(np.uint32)
+    # b[r, c, g, i, byte]: byte `byte` of word 4g + i of group c
     word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
-    u = np.empty((rows, cols // 8, 8), dtype=np.int64)
-    for j in range(4):
-        u[..., 2 * j] = (word >> (4 * j)) & 0xF
-        u[..., 2 * j + 1] = (word >> (16 + 4 * j)) & 0xF
+    u = np.empty((rows, cols // GROUP, 4, 4, 8), dtype=np.int64)  # [r, c, i (block), g (slice), m]
+    for i in range(4):
+        for g in range(4):
+            w = word[:, :, g, i]
+            for j in range(4):
+                u[:, :, i, g, 2 * j] = (w >> (4 * j)) & 0xF
+                u[:, :, i, g, 2 * j + 1] = (w >> (16 + 4 * j)) & 0xF
     return u.reshape(rows, cols)
 
 

@@ -30,37 +30,51 @@ def _rows(name):
 
 # ----------------------------------------------------------------------------- dequant
 
-def test_dequant_hand_encoded_blocks():
+def _codes_field(field):
+    parts = field.split()
+    if parts[0] != "fill":
+        return [int(c) for c in parts]
+    u = [int(parts[1])] * 128
+    for p in parts[2:]:
+        e, v = p.split("=")
+        u[int(e)] = int(v)
+    return u
+
+
+def test_dequant_hand_encoded_groups():
     n = 0
-    for name, bhex, shex, sval, codes in _rows("dequant_blocks.txt"):
+    for name, bhex, shex, svals, codes in _rows("dequant_groups.txt"):
         code_bytes = np.array([int(b, 16) for b in bhex.split()], dtype=np.uint8)
-        scale_bits = int(shex, 16)
-        scale = Fraction(sval)
-        u = [int(c) for c in codes.split()]
-        assert len(code_bytes) == 16 and len(u) == 32
-        # fp16 decoding of the scale is exact, subnormals included
-        assert O.fp16_codes_to_f64(np.array([scale_bits], np.uint16))[0] == float(scale), name
-        scale_bytes = np.array([scale_bits & 0xFF, scale_bits >> 8], dtype=np.uint8)
-        assert list(O.decode_codes(code_bytes, 1, 32)[0]) == u, name
-        w = O.dequant(code_bytes, scale_bytes, 1, 32)[0]
-        want = [float((ui - 8) * scale) for ui in u]
+        scale_bits = [int(h, 16) for h in shex.split()]
+        scales = [Fraction(v) for v in svals.split()]
+        u = _codes_field(codes)
+        assert len(code_bytes) == 64 and len(u) == 128 and len(scale_bits) == 4 == len(scales)
+        # fp16 decoding of the scales is exact, subnormals and sign included
+        assert list(O.fp16_codes_to_f64(np.array(scale_bits, np.uint16))) == [float(v) for v in scales], name
+        scale_bytes = np.array(scale_bits, dtype=np.uint16).view(np.uint8)
+        assert list(O.decode_codes(code_bytes, 1, 128)[0]) == u, name
+        w = O.dequant(code_bytes, scale_bytes, 1, 128)[0]
+        want = [float((ui - 8) * scales[e // 32]) for e, ui in enumerate(u)]
         assert list(w) == want, name
         n += 1
-    assert n >= 12
+    assert n >= 14
 
 
-def test_dequant_rows_and_blocks_are_independent():
-    # two rows, two blocks each: each block takes its own scale, rows do not mix
-    ramp = [0x20, 0x64, 0x31, 0x75, 0xA8, 0xEC, 0xB9, 0xFD] * 2
-    zero = [0x88] * 16
+def test_dequant_rows_and_groups_are_independent():
+    # two rows of two groups: each block takes its own scale, groups and rows do not mix
+    ramp = [0x20, 0x64, 0x31, 0x75] * 4 + [0xA8, 0xEC, 0xB9, 0xFD] * 4
+    ramp = ramp * 2  # slices 0..3 of the four blocks (see dequant_groups.txt)
+    zero = [0x88] * 64
     code_bytes = np.array(ramp + zero + zero + ramp, dtype=np.uint8)
-    scales = np.array([0x3C00, 0x4000, 0x3800, 0x4400], dtype=np.uint16)  # 1, 2, 0.5, 4
-    w = O.dequant(code_bytes, scales.view(np.uint8), 2, 64)
-    q = np.array([(i % 16) - 8 for i in range(32)], dtype=np.float64)
-    assert np.array_equal(w[0, :32], q * 1.0)
-    assert np.array_equal(w[0, 32:], np.zeros(32))
-    assert np.array_equal(w[1, :32], np.zeros(32))
-    assert np.array_equal(w[1, 32:], q * 4.0)
+    scales = np.array([0x3C00, 0x4000, 0x3800, 0x4400] + [0x3C00] * 4 + [0x3C00] * 4 + [0x4000] * 4,
+                      dtype=np.uint16)  # row 0: 1, 2, 0.5, 4, 1...; row 1: 1..., 2, 2, 2, 2
+    w = O.dequant(code_bytes, scales.view(np.uint8), 2, 256)
+    q = np.array([(e % 16) - 8 for e in range(128)], dtype=np.float64)
+    s0 = np.repeat([1.0, 2.0, 0.5, 4.0], 32)
+    assert np.array_equal(w[0, :128], q * s0)
+    assert np.array_equal(w[0, 128:], np.zeros(128))
+    assert np.array_equal(w[1, :128], np.zeros(128))
+    assert np.array_equal(w[1, 128:], q * 2.0)
 
 
 def test_blob_layout_sizes():
@@ -147,7 +161,7 @@ def test_weights_equal_full_softmax_renormalised():
 # ----------------------------------------------------------------------------- FFN
 
 def _hand_blob():
-    H, F = 64, 32
+    H, F = 128, 128
     lay = O.blob_layout(H, F)
     blob = np.zeros(lay["total"][1], dtype=np.uint8)
     for name in ("gate_codes", "up_codes", "down_codes"):

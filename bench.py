@@ -145,34 +145,73 @@ def bench_decode1(args):
     N.moe_workspace_init(ws)
     ids = torch.empty((1, K_TOP), dtype=torch.int32, device=dev)
     tw = torch.empty((1, K_TOP), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-    for s in range(args.warmup):
-        N.moe_layer_forward(d, w, L["table"], xs[s:s + 1], 1, y, ws, topk_ids=ids, topk_w=tw)
-    torch.cuda.synchronize()
-    assert N.moe_check_device_error(ws) == 0
+    st = torch.cuda.Stream()
 
-    timer = KernelTimer(args.steps)
-    st = torch.cuda.current_stream()
+    def steps_on(stream, first, count):
+        for i in range(count):
+            s = first + i
+            N.moe_layer_forward(d, w, L["table"], xs[s:s + 1], 1, y, ws, topk_ids=ids, topk_w=tw, stream=stream)
+
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        s = args.warmup + i
-        N.moe_debug_kernel_events(N.TIME_DECODE_GATE_UP, timer.pairs[i][0], timer.pairs[i][1])
-        N.moe_layer_forward(d, w, L["table"], xs[s:s + 1], 1, y, ws, topk_ids=ids, topk_w=tw, stream=st)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    N.moe_debug_kernel_events(0, None, None)
+    if args.eager:
+        with torch.cuda.stream(st):
+            steps_on(st, 0, args.warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(st):
+            steps_on(st, args.warmup, args.steps)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        # a decode step is a handful of short kernels: the steps are captured in HIP graphs (one for
+        # the warmup steps, one for the timed steps, each step with its own token) and replayed, so the
+        # host's launch rate does not set the pace
+        gw, gt = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=st):
+            steps_on(torch.cuda.current_stream(), 0, args.warmup)
+        with torch.cuda.graph(gt, stream=st):
+            steps_on(torch.cuda.current_stream(), args.warmup, args.steps)
+        torch.cuda.synchronize()
+        gw.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        gt.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     assert N.moe_check_device_error(ws) == 0
-    k_ms = timer.durations_ms()
-    timer.close()
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
+
+    # per-kernel durations of the gate/up and down launches: HIP events around the kernel itself, on
+    # the stream it runs on, over second (eager) passes of the same steps
+    n_k = min(args.steps, 200)
+
+    def kernel_ms(which):
+        timer = KernelTimer(n_k)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            for i in range(n_k):
+                s = args.warmup + i
+                N.moe_debug_kernel_events(which, timer.pairs[i][0], timer.pairs[i][1])
+                N.moe_layer_forward(d, w, L["table"], xs[s:s + 1], 1, y, ws, topk_ids=ids, topk_w=tw, stream=st)
+        torch.cuda.synchronize()
+        N.moe_debug_kernel_events(0, None, None)
+        assert N.moe_check_device_error(ws) == 0
+        out = timer.durations_ms()
+        timer.close()
+        return out
+
+    k_ms = kernel_ms(N.TIME_DECODE_GATE_UP)
+    dn_ms = kernel_ms(N.TIME_DECODE_DOWN)
     # algorithmic bytes of one gate/up launch: 11 experts (10 routed, distinct, + shared), each
-    # reading its gate and up codes and scales once, plus x in and h out
+    # reading its gate and up codes and scales once, plus x in and h out (bf16 hi + lo)
     per_expert = 2 * (F * H // 2 + F * (H // 32) * 2)
     gu_bytes = 11 * per_expert + H * 2 + 11 * F * 4
     gu_avg_s = float(np.mean(k_ms)) * 1e-3
     achieved = gu_bytes / gu_avg_s / 1e9
+    # down: the 11 experts' down codes and scales, h in, each pair's output row out
+    dn_bytes = 11 * (H * F // 2 + H * (F // 32) * 2) + 11 * F * 4 + 11 * H * 4
+    dn_avg_s = float(np.mean(dn_ms)) * 1e-3
     result = {
         "metric": METRIC,
         "value": args.steps / elapsed,
@@ -204,6 +243,11 @@ def bench_decode1(args):
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": gu_avg_s * 1e6,
         },
+        "decode_down": {"bytes_per_launch": dn_bytes, "avg_launch_us": dn_avg_s * 1e6,
+                        "achieved_gbs": dn_bytes / dn_avg_s / 1e9, "frac": dn_bytes / dn_avg_s / 1e9 / HBM_PEAK_GBS},
+        # expert-FFN HBM fraction: both FFN kernels' algorithmic bytes over their summed time
+        "decode_ffn_hbm_frac": (gu_bytes + dn_bytes) / (gu_avg_s + dn_avg_s) / 1e9 / HBM_PEAK_GBS,
+        "timed_region": "eager launches" if args.eager else "HIP graph replay of the timed steps",
     }
     if not args.no_cpu_baseline:
         n = args.cpu_sample
@@ -318,6 +362,7 @@ def main():
     ap.add_argument("--workload", default="decode1", choices=["decode1"])
     ap.add_argument("--cpu-sample", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="launch decode steps one by one instead of replaying graphs")
     ap.add_argument("--prefill", default="4096", help="comma-separated prefill token counts to add ('' = none)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     args = ap.parse_args()

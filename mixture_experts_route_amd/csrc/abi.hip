@@ -17,10 +17,16 @@ struct WsLayout {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Pairs of a decode step of T tokens (routed t*k + j, then shared T*k + t).
+static int decode_pairs(const moe_dims* d, int T) {
+  const int Td = T < kMaxDecodeTok ? T : kMaxDecodeTok;
+  return Td * (d->top_k + d->n_shared);
+}
+
 static WsLayout ws_layout(const moe_dims* d, int T) {
   WsLayout L{};
   const int Td = T < kMaxDecodeTok ? T : kMaxDecodeTok;
-  const int pairs_d = Td * (d->top_k + d->n_shared);
+  const int pairs_d = decode_pairs(d, T);
   size_t off = kCtrlBytes;
   L.miss_flag = 3072;
   L.tasks = off;
@@ -76,11 +82,9 @@ static int check_dims(const moe_dims* d) {
   if (d->n_shared != 0 && d->n_shared != 1) return MOE_EINVAL;
   if (d->top_k > d->n_experts) return MOE_EINVAL;
   if (d->block != kBlock) return MOE_EUNSUPPORTED;
-  if (d->hidden % kBlock || d->ffn % kBlock) return MOE_EINVAL;
-  if (d->hidden < 128 || d->ffn < 128) return MOE_EUNSUPPORTED;  // GEMV row groups need >= 4 blocks
-  if (d->hidden / kBlock > 128 || d->ffn / kBlock > 128) return MOE_EUNSUPPORTED;
-  if (d->hidden / kBlock > 64 && d->hidden / kBlock != 128) return MOE_EUNSUPPORTED;
-  if (d->ffn / kBlock > 64 && d->ffn / kBlock != 128) return MOE_EUNSUPPORTED;
+  // rows are whole groups of 4 blocks (the interleaved code layout)
+  if (d->hidden % kGroupElems || d->ffn % kGroupElems) return MOE_EINVAL;
+  if (d->hidden > 4096 || d->ffn > 4096) return MOE_EUNSUPPORTED;
   if (d->top_k > kMaxK || d->n_experts > kMaxExperts) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
@@ -178,9 +182,12 @@ static int do_decode_ffn(const moe_dims* d, const moe_layer_weights* w, const in
     if (hipStreamWaitValue32(st, bell->ready, bell->epoch, hipStreamWaitValueGte, 0xFFFFFFFFu) != hipSuccess)
       return MOE_EHIP;
   }
+  // h: bf16 hi parts of every pair, then the lo parts
+  uint16_t* h_hi = at<uint16_t>(ws, L.h);
+  uint16_t* h_lo = h_hi + (size_t)decode_pairs(d, T) * d->ffn;
   return hip_status(launch_decode_ffn(d->hidden, d->ffn, d->top_k, d->n_shared, T,
                                       decode_max_tasks(T, d->top_k, d->n_shared), source_of(w, table), x, x_dtype,
-                                      tasks, topk_w, at<float>(ws, L.h), at<float>(ws, L.y_pairs), y, ctrl, st));
+                                      tasks, topk_w, h_hi, h_lo, at<float>(ws, L.y_pairs), y, ctrl, st));
 }
 
 static GroupBuffers group_buffers(const WsLayout& L, void* ws) {

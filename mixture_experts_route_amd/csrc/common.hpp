@@ -49,6 +49,27 @@ __host__ __device__ inline BlobLayout blob_layout(int H, int F) {
 }
 
 // ---------------------------------------------------------------------------------------
+// Matrix-core operand types (v_mfma_f32_16x16x32_{bf16,f16}).  For a 16x16x32 step, lane l
+// supplies row (A) / column (B) l % 16 at k = 8 (l / 16) .. 8 (l / 16) + 7 as 8 packed 16-bit
+// values, and receives D rows 4 (l / 16) .. 4 (l / 16) + 3 of column l % 16.
+// ---------------------------------------------------------------------------------------
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Code words of a 4-bit matrix of R rows: every row is split into groups of 128 elements (4
+// blocks of 32) stored as 64-byte records, group-major: record (c, r) = group c of row r at byte
+// 64 (c R + r), its four fp16 block scales at byte 8 (c R + r) of the scale section.  Word 4g + i
+// of a record holds slice g (elements 8g .. 8g+7) of block i.  A lane that loads bytes 16g..16g+15
+// of a record therefore holds slice g of each of the group's four blocks: exactly its share of
+// four 16x16x32 matrix-core steps, one block (one scale) per step; and 16 rows x 4 lanes read
+// 1 KiB of consecutive records.
+constexpr int kGroupElems = 128;
+constexpr int kGroupBytes = 64;
+constexpr int kGroupScaleBytes = 8;
+
+// ---------------------------------------------------------------------------------------
 // Small numeric helpers
 // ---------------------------------------------------------------------------------------
 MOE_DEV float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }

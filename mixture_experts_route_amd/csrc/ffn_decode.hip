@@ -1,34 +1,42 @@
-// Expert FFNs for a small batch of tokens (decode): 4-bit GEMV, bandwidth-bound.
+// Expert FFNs for a small batch of tokens (decode): 4-bit GEMVs on the matrix cores.
 //
 // Weights: halogen-flash-server README, "Bring your own GGUF" (small set of values x one scale
 // per block, used as stored).  The layer: Betelgeuse news article, "mechanism" (10 routed + 1
 // shared expert per token).  Decode pays per byte of weights read (halogen README, "Bring your
 // own GGUF": an 8-bit trunk costs 2 GB more per token at 240 GB/s), so each selected expert's blob
-// is streamed once from HBM per step.
+// is streamed once from HBM per step, whatever the number of tokens (1..8) that chose it.
 //
-// GEMV design (gfx950): one lane per quantization block of a row.  A row of K inputs has L = K/32
-// blocks; the L lanes of a row group (L rounded up to a power of two Lp, so P = 64/Lp rows per
-// wave pass) each load the block's 16 code bytes with one 128-bit load and its fp16 scale.  The
-// activations of the lane's block live in registers as bf16 pairs, so the inner loop is: one mask
-// per code pair (the pair becomes two bf16 values q + 136, exact), one v_dot2c_f32_bf16 per pair
-// and token, and one scale FMA per block and token.  The +136 offset is removed by starting each
-// block's chain at -136 * sum(x over the block).  fp32 inputs (the FFN intermediate h, fp32
-// activations) are split into two bf16 parts hi + lo (16 significant bits), each run through the
-// same chain.  Row sums are reduced across the Lp lanes with DPP.
+// Design (gfx950).  A VALU GEMV over 4-bit weights spends ~2 vector instructions per weight
+// (unpack, dot, scale) and at one token that is as long as the weight stream itself.  Here the
+// dot products run on the matrix cores: for a 16-row tile of a weight matrix and one block of 32
+// inputs, one v_mfma_f32_16x16x32_bf16 takes
+//   A = the activation rows (one row per token; fp32 inputs as two bf16 rows hi + lo, which
+//       together carry 16 significant bits),
+//   B = the block's codes as bf16 (128 + u) = q + 136, built with one shift and one mask-or per
+//       code pair (exact),
+//   C = -136 * sum_k A[m][k], itself one MFMA of A against a constant -136 operand,
+// so D[m][n] = sum_k A[m][k] * q[n][k] (products exact, fp32 sums), and the block's scale is
+// applied with one FMA per live D register.  The interleaved code layout gives each lane, with
+// one 16-byte load, slice g of four consecutive blocks of its row: its share of four MFMA steps.
+// What is left on the VALU is ~7 instructions per 8 weights of a lane plus the scale FMAs.
 //
-// Two kernels run the FFN of a step and no workgroup depends on another: the gate/up kernel (one
-// workgroup per (task, 16-row tile)) writes h; in the down kernel one workgroup owns a tile of
-// output rows for every task of the step (its waves take the tasks in turn), keeps each pair's
-// partial rows in LDS and combines them for every token in the fixed order j = 0..k-1, then the
-// shared expert.
+// Kernels of a step; no workgroup waits on another:
+//   gate/up: one workgroup per (task, 16-row tile of the F rows).  Its waves split the H inputs
+//     in runs of 4 groups (512 inputs), reduce through LDS, apply SwiGLU and store h = silu(g) * u
+//     of the task's tokens as bf16 hi + lo, ready to be the down projection's A operand.
+//   down: one wave per (task, 16 output rows) over all F inputs.  A rows are the (hi, lo) row
+//     pairs of the task's tokens (<= 8 tokens -> <= 16 rows), so one MFMA per block covers both
+//     parts.  Writes each pair's output row y_e.
+//   combine: y[t] = sum_j w[t][j] * y_{e_j}[t] (j = 0..k-1), then + y_shared[t]: fixed order.
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kDecodeWaves = 4;  // waves per workgroup
-constexpr int kRowsPerWave = 4;  // wave passes per unit (each pass covers P rows)
-constexpr int kDnPasses = 4;     // down: wave passes per task (each pass covers P rows)
-constexpr int kMaxPairs = kMaxDecodeTok * (kMaxK + 1);
+constexpr int kGuQuadsPerWave = 4;                                   // groups of 128 inputs per wave
+constexpr int kMaxGuWaves = 4096 / (kGroupElems * kGuQuadsPerWave);  // H <= 4096
+constexpr int kDnQuadsPerPass = 6;                                   // down: groups per load batch
+constexpr uint32_t kMagicPair = 0x43004300u;                         // bf16 pair (128, 128)
+constexpr uint32_t kNeg136Pair = 0xC308C308u;                        // bf16 pair (-136, -136)
 
 // A task's blob: the shared expert, the slot the plan resolved, or (for an expert that missed when
 // the plan ran and was filled since) the table entry read now.
@@ -40,304 +48,301 @@ MOE_DEV const uint8_t* task_blob(const ExpertSource& s, const DecodeTask& tk) {
   return s.arena + (int64_t)slot * s.slot_stride;
 }
 
-// The 32 activations of block `blk` of row `src` as bf16 pair words (pair i = elements 2i,
-// 2i+1) in NPART parts, and each part's chain start -136 * sum(part over the block).
-template <int NPART, bool SRC_BF16>
-MOE_DEV void load_x_block(const void* src, int blk, uint32_t (&q)[NPART][16], float (&init)[NPART]) {
-  if constexpr (SRC_BF16) {
-    static_assert(NPART == 1, "bf16 activations are one part");
-    const uint4* p = (const uint4*)((const uint16_t*)src + (size_t)blk * kBlock);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = p[i];
-      q[0][4 * i + 0] = v.x;
-      q[0][4 * i + 1] = v.y;
-      q[0][4 * i + 2] = v.z;
-      q[0][4 * i + 3] = v.w;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s += bf16_lo(q[0][i]) + bf16_hi(q[0][i]);
-    init[0] = -136.f * s;
-  } else {
-    const float4* p = (const float4*)((const float*)src + (size_t)blk * kBlock);
-    float s[NPART];
-#pragma unroll
-    for (int pp = 0; pp < NPART; ++pp) s[pp] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float4 v = p[i];
-      const float f[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t hi[2], lo[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const float xv = f[2 * h + e];
-          hi[e] = f32_to_bf16_rne(xv);
-          const float hv = __uint_as_float(hi[e] << 16);
-          lo[e] = f32_to_bf16_rne(xv - hv);
-          s[0] += hv;
-          if constexpr (NPART == 2) s[1] += __uint_as_float(lo[e] << 16);
-        }
-        q[0][2 * i + h] = hi[0] | (hi[1] << 16);
-        if constexpr (NPART == 2) q[1][2 * i + h] = lo[0] | (lo[1] << 16);
-      }
-    }
-#pragma unroll
-    for (int pp = 0; pp < NPART; ++pp) init[pp] = -136.f * s[pp];
-  }
+// One code word (8 elements of a slice) -> B operand: 8 bf16 values q + 136 = 128 + u.  Pair j of
+// the word (its elements 2j and 2j+1 in bits 4j and 16 + 4j) becomes register j.
+MOE_DEV bf16x8 codes_q136(uint32_t w) {
+  uint4 p;
+  p.x = (w & 0x000F000Fu) | kMagicPair;
+  p.y = ((w >> 4) & 0x000F000Fu) | kMagicPair;
+  p.z = ((w >> 8) & 0x000F000Fu) | kMagicPair;
+  p.w = ((w >> 12) & 0x000F000Fu) | kMagicPair;
+  return __builtin_bit_cast(bf16x8, p);
 }
 
-// sum over the block of x * q, for one part: starts at init = -136 * sum(x).
-MOE_DEV float block_dot(const uint4 c, const uint32_t (&xq)[16], float init) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float acc = init;
+MOE_DEV bf16x8 const_neg136() {
+  const uint4 p = make_uint4(kNeg136Pair, kNeg136Pair, kNeg136Pair, kNeg136Pair);
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+MOE_DEV uint32_t word_at(const uint4& c, int i) { return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w; }
+
+// fp16 scale i (0..3) of a group's four block scales.
+MOE_DEV float scale_at(const uint2& s, int i) {
+  const uint32_t w = i < 2 ? s.x : s.y;
+  return fp16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+// Token of slot m of a task: the m-th set bit of its token mask (m < popcount(mask)).
+MOE_DEV int task_token(uint32_t mask, int m) {
+  uint32_t x = mask;
 #pragma unroll
-  for (int d = 0; d < 4; ++d) {
+  for (int j = 0; j < kTaskTok - 1; ++j) x = j < m ? (x & (x - 1u)) : x;
+  return __builtin_ctz(x);
+}
+
+// FFN output row (pair) of token t in a task.
+MOE_DEV int task_pair(const DecodeTask& tk, int t, int T, int k) {
+  return tk.expert < 0 ? T * k + t : t * k + (int)((tk.choice >> (4 * t)) & 15u);
+}
+
+MOE_DEV float4v mfma_bf16(const bf16x8& a, const bf16x8& b, const float4v& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Eight fp32 activations -> one bf16 part (0 = hi, 1 = lo) as an A operand; hi = RNE(x),
+// lo = RNE(x - hi).
+MOE_DEV uint4 split_part(const float4& a, const float4& b, int part) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t q[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc = dot2_bf16(xq[4 * d + j], code_pair_bf16_q136(w[d], j), acc);
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t hi = f32_to_bf16_rne(v[e]);
+    q[e] = part ? f32_to_bf16_rne(v[e] - __uint_as_float(hi << 16)) : hi;
   }
-  return acc;
+  return make_uint4(q[0] | (q[1] << 16), q[2] | (q[3] << 16), q[4] | (q[5] << 16), q[6] | (q[7] << 16));
 }
 
 struct DecodeArgs {
   ExpertSource src;
   const DecodeTask* tasks;
   int32_t* ctrl;
-  const void* x;         // activations [T][H], bf16 or fp32
-  float* h;              // [pairs][F]
-  float* y_pairs;        // [pairs][H]
-  const float* topk_w;   // [T][k]
-  float* y;              // [T][H]
+  const void* x;        // [T][H] bf16 or fp32
+  uint16_t* h_hi;       // [P][F] bf16: SwiGLU output, high part
+  uint16_t* h_lo;       // [P][F] bf16: low part
+  float* y_pairs;       // [P][H] each pair's expert output
+  const float* topk_w;  // [T][k]
+  float* y;             // [T][H]
   int H, F, T, k, n_shared;
-  int tiles_gu, tiles_dn, max_tasks;
+  int tiles_gu;  // F / 16
+  int tiles_dn;  // H / 64
 };
 
-MOE_DEV int lanes_per_row(int L) {
-  int Lp = 1;
-  while (Lp < L && Lp < 64) Lp <<= 1;
-  return Lp;
-}
+// ---- gate/up: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for one task and 16 rows r --------
+// A rows: token slot m of the task (bf16 x) or 2 m + part (fp32 x).  ROWS <= 16.
+template <int MAXTOK, bool X_BF16>
+__global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs a) {
+  constexpr int ROWS = X_BF16 ? MAXTOK : 2 * MAXTOK;
+  constexpr int NR = ROWS < 4 ? ROWS : 4;  // live D registers per lane
+  __shared__ float red[kMaxGuWaves][2][ROWS][16];
 
-// Sum over the Lp lanes of a row group; valid in the group's last lane.
-MOE_DEV float row_sum(float v, int Lp) {
-  if (Lp >= 16) return group_sum_dpp(v, Lp);
-  return group_sum(v, Lp);  // narrow rows (small hidden sizes): shuffles, valid in every lane
-}
-
-MOE_DEV bool row_writer(int lane, int Lp) { return Lp >= 16 ? group_last_lane(lane, Lp) : (lane % Lp) == 0; }
-
-// ---- gate/up unit: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for the unit's rows ------------
-template <int MAXTOK, int NPART, int BPL, bool X_BF16>
-MOE_DEV void gate_up_unit(const DecodeArgs& a, const DecodeTask* tk, int tile) {
-  const uint8_t* blob = task_blob(a.src, *tk);
+  const int task = blockIdx.x / a.tiles_gu;
+  const int tile = blockIdx.x - task * a.tiles_gu;
+  // the descriptor slot always exists (max_tasks of them): load it together with the count
+  const DecodeTask tk = a.tasks[task];
+  if (task >= a.ctrl[kCtrlNTasks]) return;
+  const uint8_t* blob = task_blob(a.src, tk);
   if (!blob) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
     return;
   }
-  const int ntok = tk->n_tok;
-  const int H = a.H, F = a.F, L = H / kBlock;
+  const int H = a.H, F = a.F;
   const BlobLayout lay = blob_layout(H, F);
-  const int Lp = lanes_per_row(L), P = 64 / Lp;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane / Lp, b0 = lane - sub * Lp;
-  const bool active = b0 < L;
-  const int row0 = (tile * kDecodeWaves + wave) * kRowsPerWave * P;
+  const int n = lane & 15, g = lane >> 4;
+  const int row = tile * 16 + n;
+  const int q0 = wave * kGuQuadsPerWave;
+  const int nq = min(kGuQuadsPerWave, H / kGroupElems - q0);
 
-  // weights first: they do not depend on the activations
-  uint4 gc[kRowsPerWave][BPL], uc[kRowsPerWave][BPL];
-  float gs[kRowsPerWave][BPL], us[kRowsPerWave][BPL];
+  // ---- loads, group by group in the order the MFMA steps use them: the activations of the
+  // group (A row m = lane % 16, inputs 32 i + 8 g .. +7), then slice g of the group's record of
+  // row `row` in both matrices, and the record's four scales
+  const int m = n;
+  const int tslot = X_BF16 ? m : (m >> 1);
+  const int n_tok = __builtin_popcount(tk.tok_mask);
+  const bool live = m < ROWS && tslot < n_tok;
+  const int tok = live ? task_token(tk.tok_mask, tslot) : 0;
+  const size_t rec0 = (size_t)q0 * F + row;  // record (q0, row); the next group is F records on
+  const uint8_t* gcode = blob + lay.gate_codes + rec0 * kGroupBytes + 16 * g;
+  const uint8_t* ucode = blob + lay.up_codes + rec0 * kGroupBytes + 16 * g;
+  const uint8_t* gscale = blob + lay.gate_scales + rec0 * kGroupScaleBytes;
+  const uint8_t* uscale = blob + lay.up_scales + rec0 * kGroupScaleBytes;
+  const uint16_t* xr = (const uint16_t*)a.x + (size_t)tok * H + (size_t)q0 * kGroupElems + 8 * g;
+  uint4 cg[kGuQuadsPerWave], cu[kGuQuadsPerWave];
+  uint2 sg[kGuQuadsPerWave], su[kGuQuadsPerWave];
+  uint4 xa[X_BF16 ? kGuQuadsPerWave : 1][4];
 #pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int r = row0 + i * P + sub;
+  for (int qi = 0; qi < kGuQuadsPerWave; ++qi) {
+    if (qi < nq) {
+      if constexpr (X_BF16) {
 #pragma unroll
-    for (int bb = 0; bb < BPL; ++bb) {
-      const int blk = b0 + 64 * bb;
-      if (active && blk < L && r < F) {
-        gc[i][bb] = *(const uint4*)(blob + lay.gate_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
-        uc[i][bb] = *(const uint4*)(blob + lay.up_codes + (size_t)r * (H / 2) + (size_t)blk * 16);
-        gs[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.gate_scales + ((size_t)r * L + blk) * 2));
-        us[i][bb] = fp16_bits_to_f32(*(const uint16_t*)(blob + lay.up_scales + ((size_t)r * L + blk) * 2));
+        for (int i = 0; i < 4; ++i)
+          xa[qi][i] = live ? *(const uint4*)(xr + (size_t)qi * kGroupElems + 32 * i) : make_uint4(0u, 0u, 0u, 0u);
+      }
+      cg[qi] = *(const uint4*)(gcode + (size_t)qi * F * kGroupBytes);
+      cu[qi] = *(const uint4*)(ucode + (size_t)qi * F * kGroupBytes);
+      sg[qi] = *(const uint2*)(gscale + (size_t)qi * F * kGroupScaleBytes);
+      su[qi] = *(const uint2*)(uscale + (size_t)qi * F * kGroupScaleBytes);
+    }
+  }
+
+  const bf16x8 neg = const_neg136();
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  float accg[NR], accu[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) accg[r] = accu[r] = 0.f;
+#pragma unroll
+  for (int qi = 0; qi < kGuQuadsPerWave; ++qi) {
+    if (qi >= nq) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 av;
+      if constexpr (X_BF16) {
+        av = xa[qi][i];
       } else {
-        gc[i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-        uc[i][bb] = gc[i][bb];
-        gs[i][bb] = 0.f;
-        us[i][bb] = 0.f;
+        av = make_uint4(0u, 0u, 0u, 0u);
+        if (live) {
+          const float* xr = (const float*)a.x + (size_t)tok * H + (size_t)(q0 + qi) * kGroupElems + 32 * i + 8 * g;
+          av = split_part(*(const float4*)xr, *(const float4*)(xr + 4), m & 1);
+        }
+      }
+      const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+      const float4v O = mfma_bf16(A, neg, zero);
+      const float4v Dg = mfma_bf16(A, codes_q136(word_at(cg[qi], i)), O);
+      const float4v Du = mfma_bf16(A, codes_q136(word_at(cu[qi], i)), O);
+      const float s_g = scale_at(sg[qi], i), s_u = scale_at(su[qi], i);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        accg[r] = fmaf(s_g, Dg[r], accg[r]);
+        accu[r] = fmaf(s_u, Du[r], accu[r]);
       }
     }
   }
 
-  uint32_t xq[MAXTOK][BPL][NPART][16];
-  float xi[MAXTOK][BPL][NPART];
+  // ---- reduce the waves' K ranges, SwiGLU, store h as bf16 hi + lo ---------------------------
+  // lane (g, n) holds rows 4g + r of column n
 #pragma unroll
-  for (int n = 0; n < MAXTOK; ++n) {
-#pragma unroll
-    for (int bb = 0; bb < BPL; ++bb) {
-      if (n < ntok && active && b0 + 64 * bb < L) {
-        const int t = tk->tok[n];
-        const void* xrow = X_BF16 ? (const void*)((const uint16_t*)a.x + (size_t)t * H)
-                                  : (const void*)((const float*)a.x + (size_t)t * H);
-        load_x_block<NPART, X_BF16>(xrow, b0 + 64 * bb, xq[n][bb], xi[n][bb]);
-      } else {
-#pragma unroll
-        for (int p = 0; p < NPART; ++p) {
-          xi[n][bb][p] = 0.f;
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xq[n][bb][p][i] = 0u;
-        }
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < kRowsPerWave; ++i) {
-    const int r = row0 + i * P + sub;
-#pragma unroll
-    for (int n = 0; n < MAXTOK; ++n) {
-      if (n < ntok) {
-        float g = 0.f, u = 0.f;
-#pragma unroll
-        for (int bb = 0; bb < BPL; ++bb) {
-          float sg = 0.f, su = 0.f;
-#pragma unroll
-          for (int p = 0; p < NPART; ++p) {
-            sg += block_dot(gc[i][bb], xq[n][bb][p], xi[n][bb][p]);
-            su += block_dot(uc[i][bb], xq[n][bb][p], xi[n][bb][p]);
-          }
-          g = fmaf(sg, gs[i][bb], g);
-          u = fmaf(su, us[i][bb], u);
-        }
-        const float gt = row_sum(g, Lp);
-        const float ut = row_sum(u, Lp);
-        if (row_writer(lane, Lp) && r < F) a.h[(size_t)tk->pair[n] * F + r] = silu(gt) * ut;
-      }
-    }
-  }
-}
-
-template <int MAXTOK, int NPART_X, int BPL, bool X_BF16>
-__global__ __launch_bounds__(256) void k_decode_gate_up(DecodeArgs a) {
-  const int task = blockIdx.x / a.tiles_gu;
-  // the descriptor slot always exists (max_tasks of them): load it together with the count
-  const DecodeTask tk = a.tasks[task];
-  if (task >= a.ctrl[kCtrlNTasks]) return;
-  gate_up_unit<MAXTOK, NPART_X, BPL, X_BF16>(a, &tk, blockIdx.x - task * a.tiles_gu);
-}
-
-// ---- down + combine: rows [tile*RW, tile*RW + RW) of y for every token ----------------------
-// RW = kDnPasses * P rows.  Wave w takes tasks w, w+4, ...; it issues the weight and h loads of
-// TS of its tasks before computing any of them, so their latencies overlap.
-template <int MAXTOK, int BPL, int TS>
-__global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
-  __shared__ float ys[kMaxPairs][kDnPasses * 16];
-  const int n_tasks = a.ctrl[kCtrlNTasks];
-  const int H = a.H, F = a.F, L = F / kBlock;
-  const BlobLayout lay = blob_layout(H, F);
-  const int Lp = lanes_per_row(L), P = 64 / Lp;
-  const int RW = kDnPasses * P;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane / Lp, b0 = lane - sub * Lp;
-  const bool active = b0 < L;
-  constexpr int NPART = 2;
-  const int row0 = blockIdx.x * RW;
-  for (int base = wave; base < n_tasks; base += kDecodeWaves * TS) {
-    int ntok[TS];
-    const uint8_t* blob[TS];
-    int pair[TS][MAXTOK];
-    uint4 dc[TS][kDnPasses][BPL];
-    float ds[TS][kDnPasses][BPL];
-    uint32_t xq[TS][MAXTOK][BPL][NPART][16];
-    float xi[TS][MAXTOK][BPL][NPART];
-#pragma unroll
-    for (int q = 0; q < TS; ++q) {
-      const int task = base + kDecodeWaves * q;
-      ntok[q] = 0;
-      blob[q] = nullptr;
-      if (task < n_tasks) {
-        const DecodeTask* tk = a.tasks + task;
-        blob[q] = task_blob(a.src, *tk);
-        if (!blob[q]) {
-          if (lane == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
-        } else {
-          ntok[q] = tk->n_tok;
-        }
-#pragma unroll
-        for (int n = 0; n < MAXTOK; ++n) pair[q][n] = n < ntok[q] ? tk->pair[n] : 0;
-      }
-#pragma unroll
-      for (int i = 0; i < kDnPasses; ++i) {
-        const int r = row0 + i * P + sub;
-#pragma unroll
-        for (int bb = 0; bb < BPL; ++bb) {
-          const int blk = b0 + 64 * bb;
-          if (ntok[q] > 0 && active && blk < L && r < H) {
-            dc[q][i][bb] = *(const uint4*)(blob[q] + lay.down_codes + (size_t)r * (F / 2) + (size_t)blk * 16);
-            ds[q][i][bb] =
-                fp16_bits_to_f32(*(const uint16_t*)(blob[q] + lay.down_scales + ((size_t)r * L + blk) * 2));
-          } else {
-            dc[q][i][bb] = make_uint4(0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u);
-            ds[q][i][bb] = 0.f;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < TS; ++q) {
-#pragma unroll
-      for (int n = 0; n < MAXTOK; ++n) {
-#pragma unroll
-        for (int bb = 0; bb < BPL; ++bb) {
-          if (n < ntok[q] && active && b0 + 64 * bb < L) {
-            const float* hrow = a.h + (size_t)pair[q][n] * F;
-            load_x_block<NPART, false>(hrow, b0 + 64 * bb, xq[q][n][bb], xi[q][n][bb]);
-          } else {
-#pragma unroll
-            for (int p = 0; p < NPART; ++p) {
-              xi[q][n][bb][p] = 0.f;
-#pragma unroll
-              for (int i = 0; i < 16; ++i) xq[q][n][bb][p][i] = 0u;
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < TS; ++q) {
-#pragma unroll
-      for (int i = 0; i < kDnPasses; ++i) {
-#pragma unroll
-        for (int n = 0; n < MAXTOK; ++n) {
-          if (n < ntok[q]) {
-            float yv = 0.f;
-#pragma unroll
-            for (int bb = 0; bb < BPL; ++bb) {
-              float sd = 0.f;
-#pragma unroll
-              for (int p = 0; p < NPART; ++p) sd += block_dot(dc[q][i][bb], xq[q][n][bb][p], xi[q][n][bb][p]);
-              yv = fmaf(sd, ds[q][i][bb], yv);
-            }
-            const float yt = row_sum(yv, Lp);
-            if (row_writer(lane, Lp)) ys[pair[q][n]][i * P + sub] = yt;
-          }
-        }
-      }
+  for (int r = 0; r < NR; ++r) {
+    const int mr = 4 * g + r;
+    if (mr < ROWS) {
+      red[wave][0][mr][n] = accg[r];
+      red[wave][1][mr][n] = accu[r];
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < a.T * RW; idx += blockDim.x) {
-    const int t = idx / RW, rr = idx - t * RW, o = row0 + rr;
-    if (o >= H) continue;
-    float acc = 0.f;
-    for (int j = 0; j < a.k; ++j) acc = fmaf(a.topk_w[t * a.k + j], ys[t * a.k + j][rr], acc);
-    if (a.n_shared) acc += ys[a.T * a.k + t][rr];
-    a.y[(size_t)t * H + o] = acc;
+  const int nw = blockDim.x >> 6;
+  if ((int)threadIdx.x < 16 * MAXTOK) {
+    const int ts = threadIdx.x >> 4, c = threadIdx.x & 15;
+    if (ts < n_tok) {
+      float gs = 0.f, us = 0.f;
+      for (int w = 0; w < nw; ++w) {
+        if constexpr (X_BF16) {
+          gs += red[w][0][ts][c];
+          us += red[w][1][ts][c];
+        } else {
+          gs += red[w][0][2 * ts][c] + red[w][0][2 * ts + 1][c];
+          us += red[w][1][2 * ts][c] + red[w][1][2 * ts + 1][c];
+        }
+      }
+      const float h = silu(gs) * us;
+      const uint32_t hi = f32_to_bf16_rne(h);
+      const uint32_t lo = f32_to_bf16_rne(h - __uint_as_float(hi << 16));
+      const size_t o = (size_t)task_pair(tk, task_token(tk.tok_mask, ts), a.T, a.k) * F + tile * 16 + c;
+      a.h_hi[o] = (uint16_t)hi;
+      a.h_lo[o] = (uint16_t)lo;
+    }
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// Test entry: dequantize one matrix of a blob to fp32 (exact).
-// ------------------------------------------------------------------------------------------
+// ---- down: y_e[pair][o] = Wd[o] . h[pair] for one task and 16 output rows per wave ----------
+// A rows 2 s + part: token slot s, part 0 = h_hi, 1 = h_lo.
+template <int MAXTOK>
+__global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
+  constexpr int ROWS = 2 * MAXTOK;
+  constexpr int NR = ROWS < 4 ? ROWS : 4;
+  const int task = blockIdx.x / a.tiles_dn;
+  const int tile = blockIdx.x - task * a.tiles_dn;
+  const DecodeTask tk = a.tasks[task];
+  if (task >= a.ctrl[kCtrlNTasks]) return;
+  const uint8_t* blob = task_blob(a.src, tk);
+  if (!blob) {
+    if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+    return;
+  }
+  const int H = a.H, F = a.F;
+  const BlobLayout lay = blob_layout(H, F);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int row = (tile * 4 + wave) * 16 + n;
+  const int NQ = F / kGroupElems;
+
+  // record (q, row) of the down matrix (H rows) is at 64 (q H + row)
+  const uint8_t* dcode = blob + lay.down_codes + (size_t)row * kGroupBytes + 16 * g;
+  const uint8_t* dscale = blob + lay.down_scales + (size_t)row * kGroupScaleBytes;
+  const int m = n, ts = m >> 1;
+  const int n_tok = __builtin_popcount(tk.tok_mask);
+  const bool live = m < ROWS && ts < n_tok;
+  const int hpair = live ? task_pair(tk, task_token(tk.tok_mask, ts), a.T, a.k) : 0;
+  const uint16_t* hrow = ((m & 1) ? a.h_lo : a.h_hi) + (size_t)hpair * F + 8 * g;
+
+  const bf16x8 neg = const_neg136();
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  float acc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
+  for (int q0 = 0; q0 < NQ; q0 += kDnQuadsPerPass) {
+    const int nq = min(kDnQuadsPerPass, NQ - q0);
+    uint4 cd[kDnQuadsPerPass], ha[kDnQuadsPerPass][4];
+    uint2 sd[kDnQuadsPerPass];
+    // loads group by group in the order of use: h (A operands), then the record and its scales
+#pragma unroll
+    for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
+      if (qi < nq) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ha[qi][i] = live ? *(const uint4*)(hrow + (size_t)(q0 + qi) * kGroupElems + 32 * i) : make_uint4(0u, 0u, 0u, 0u);
+        cd[qi] = *(const uint4*)(dcode + (size_t)(q0 + qi) * H * kGroupBytes);
+        sd[qi] = *(const uint2*)(dscale + (size_t)(q0 + qi) * H * kGroupScaleBytes);
+      }
+    }
+#pragma unroll
+    for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
+      if (qi >= nq) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 A = __builtin_bit_cast(bf16x8, ha[qi][i]);
+        const float4v O = mfma_bf16(A, neg, zero);
+        const float4v D = mfma_bf16(A, codes_q136(word_at(cd[qi], i)), O);
+        const float s = scale_at(sd[qi], i);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r] = fmaf(s, D[r], acc[r]);
+      }
+    }
+  }
+  // lane (g, n) holds rows 4g + r: token slots 2g (r = 0, 1) and 2g + 1 (r = 2, 3)
+#pragma unroll
+  for (int s2 = 0; s2 < NR / 2; ++s2) {
+    const int slot = 2 * g + s2;
+    if (slot < n_tok)
+      a.y_pairs[(size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + row] = acc[2 * s2] + acc[2 * s2 + 1];
+  }
+}
+
+// ---- combine: y[t][o] = sum_j w[t][j] * y_pairs[t k + j][o] (+ y_pairs[T k + t][o]) ----------
+__global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a) {
+  const int per_tok = a.H / 4;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= a.T * per_tok) return;
+  const int t = i / per_tok, o = (i - t * per_tok) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < a.k; ++j) {
+    const float w = a.topk_w[t * a.k + j];
+    const float4 v = *(const float4*)(a.y_pairs + (size_t)(t * a.k + j) * a.H + o);
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  if (a.n_shared) {
+    const float4 v = *(const float4*)(a.y_pairs + (size_t)(a.T * a.k + t) * a.H + o);
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+  }
+  *(float4*)(a.y + (size_t)t * a.H + o) = acc;
+}
+
+// ---- dequantization check: one thread per code word, the same unpacking as the FFN kernels --
 __global__ __launch_bounds__(256) void k_debug_dequant(int H, int F, const uint8_t* __restrict__ blob,
                                                         int matrix, float* __restrict__ out) {
   const BlobLayout lay = blob_layout(H, F);
@@ -346,15 +351,18 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int H, int F, const uint8
   const int64_t scales = matrix == 0 ? lay.gate_scales : matrix == 1 ? lay.up_scales : lay.down_scales;
   const int n_words = rows * cols / 8;
   for (int wi = blockIdx.x * blockDim.x + threadIdx.x; wi < n_words; wi += gridDim.x * blockDim.x) {
-    const int r = wi / (cols / 8), d = wi - r * (cols / 8);
+    const int rec = wi >> 4, p = wi & 15, g = p >> 2, i = p & 3;  // word 4g + i of record rec
+    const int grp = rec / rows, r = rec - grp * rows;            // record (grp, r)
+    const int blk = 4 * grp + i;
+    const int c0 = blk * kBlock + 8 * g;
     const uint32_t w = *(const uint32_t*)(blob + codes + (size_t)wi * 4);
-    const int c0 = d * 8;
-    const float s = fp16_bits_to_f32(*(const uint16_t*)(blob + scales + ((size_t)r * (cols / kBlock) + c0 / kBlock) * 2));
+    const float s = fp16_bits_to_f32(*(const uint16_t*)(blob + scales + (size_t)rec * kGroupScaleBytes + 2 * i));
+    const uint4 q = __builtin_bit_cast(uint4, codes_q136(w));
+    const uint32_t pr[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t pr = code_pair_bf16_q136(w, j);
-      out[(size_t)r * cols + c0 + 2 * j] = (bf16_lo(pr) - 136.f) * s;
-      out[(size_t)r * cols + c0 + 2 * j + 1] = (bf16_hi(pr) - 136.f) * s;
+      out[(size_t)r * cols + c0 + 2 * j] = (bf16_lo(pr[j]) - 136.f) * s;
+      out[(size_t)r * cols + c0 + 2 * j + 1] = (bf16_hi(pr[j]) - 136.f) * s;
     }
   }
 }
@@ -366,46 +374,32 @@ __global__ void k_fill_zero(uint32_t* p, size_t n) {
 // ------------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------------
-static int lanes_per_row_host(int K) {
-  const int L = K / kBlock;
-  int Lp = 1;
-  while (Lp < L && Lp < 64) Lp <<= 1;
-  return Lp;
-}
-
-// gate/up: rows per workgroup; down: rows per workgroup (one tile of y for all tasks)
-static int rows_per_unit(int K) { return kDecodeWaves * kRowsPerWave * (64 / lanes_per_row_host(K)); }
-static int rows_per_down_tile(int F) { return kDnPasses * (64 / lanes_per_row_host(F)); }
-
-int decode_tiles_dn(int H, int F) { return (H + rows_per_down_tile(F) - 1) / rows_per_down_tile(F); }
-
 template <int MAXTOK>
-static hipError_t launch_decode_ffn_t(const DecodeArgs& a, int bpl_gu, int bpl_dn, bool xb, hipStream_t st) {
-  const int grid_gu = a.max_tasks * a.tiles_gu, grid_dn = a.tiles_dn;
+static hipError_t launch_decode_ffn_t(const DecodeArgs& a, int max_tasks, bool xb, hipStream_t st) {
+  const int gu_waves = (a.H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
+  const int grid_gu = max_tasks * a.tiles_gu, grid_dn = max_tasks * a.tiles_dn;
   hipError_t err;
-  if (xb) {
-    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 1, true>, grid_gu, 256, 0, st, a);
-    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 1, 2, true>, grid_gu, 256, 0, st, a);
-  } else {
-    if (bpl_gu == 1) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 1, false>, grid_gu, 256, 0, st, a);
-    else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, 2, 2, false>, grid_gu, 256, 0, st, a);
-  }
+  if (xb) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true>, grid_gu, 64 * gu_waves, 0, st, a);
+  else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false>, grid_gu, 64 * gu_waves, 0, st, a);
   if (err != hipSuccess) return err;
-  // task slots per wave: as many as the registers allow for MAXTOK tokens per task
-  constexpr int TS = MAXTOK == 1 ? 3 : MAXTOK == 2 ? 2 : 1;
-  if (bpl_dn == 1) return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 1, TS>, grid_dn, 256, 0, st, a);
-  return launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, 2, TS>, grid_dn, 256, 0, st, a);
+  err = launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK>, grid_dn, 256, 0, st, a);
+  if (err != hipSuccess) return err;
+  const int n4 = a.T * a.H / 4;
+  k_decode_combine<<<(n4 + 255) / 256, 256, 0, st>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
                              const void* x, int x_dtype, const DecodeTask* tasks, const float* topk_w,
-                             float* h, float* y_pairs, float* y, int32_t* ctrl, hipStream_t st) {
+                             uint16_t* h_hi, uint16_t* h_lo, float* y_pairs, float* y, int32_t* ctrl,
+                             hipStream_t st) {
   DecodeArgs a{};
   a.src = src;
   a.tasks = tasks;
   a.ctrl = ctrl;
   a.x = x;
-  a.h = h;
+  a.h_hi = h_hi;
+  a.h_lo = h_lo;
   a.y_pairs = y_pairs;
   a.topk_w = topk_w;
   a.y = y;
@@ -414,16 +408,14 @@ hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_t
   a.T = T;
   a.k = k;
   a.n_shared = n_shared;
-  a.tiles_gu = (F + rows_per_unit(H) - 1) / rows_per_unit(H);
-  a.tiles_dn = decode_tiles_dn(H, F);
-  a.max_tasks = max_tasks;
-  const int bpl_gu = (H / kBlock) > 64 ? 2 : 1;
-  const int bpl_dn = (F / kBlock) > 64 ? 2 : 1;
+  a.tiles_gu = F / 16;
+  a.tiles_dn = H / 64;
   const bool xb = x_dtype == MOE_BF16;
-  static_assert(kTaskTok == 4, "instantiations below cover tasks of up to 4 tokens");
-  if (T <= 1) return launch_decode_ffn_t<1>(a, bpl_gu, bpl_dn, xb, st);
-  if (T <= 2) return launch_decode_ffn_t<2>(a, bpl_gu, bpl_dn, xb, st);
-  return launch_decode_ffn_t<4>(a, bpl_gu, bpl_dn, xb, st);
+  static_assert(kTaskTok == kMaxDecodeTok, "a decode task holds every token of the step that chose its expert");
+  if (T <= 1) return launch_decode_ffn_t<1>(a, max_tasks, xb, st);
+  if (T <= 2) return launch_decode_ffn_t<2>(a, max_tasks, xb, st);
+  if (T <= 4) return launch_decode_ffn_t<4>(a, max_tasks, xb, st);
+  return launch_decode_ffn_t<8>(a, max_tasks, xb, st);
 }
 
 hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st) {

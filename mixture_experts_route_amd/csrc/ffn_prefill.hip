@@ -11,13 +11,14 @@
 //   A (activations, fp16): staged global -> LDS (double-buffered, 16-byte padded rows), read
 //     back as 16x16x32 MFMA fragments (one 16-byte LDS read per lane per MFMA, reused by the
 //     wave's 4 subtiles);
-//   B (weights): each lane loads the 16 code bytes + fp16 scale of one quantization block of its
-//     weight row straight into registers (lane group g takes block 4c+g) and dequantizes to fp16
-//     in registers, q * scale rounded once: two bit operations build (1024 + u) in fp16, one
-//     packed subtract gives q exactly, one packed multiply applies the scale.
-//   MFMA v_mfma_f32_16x16x32_f16, fp32 accumulation.  MFMA d (0..3) of a chunk pairs word d of
-//   every lane's block with the matching 8 activations of that block, so each B register is
-//   used as loaded.
+//   B (weights): each lane loads 16 code bytes (slice g = lane / 16 of the chunk's four blocks,
+//     the interleaved code layout) and the four block scales of its weight row straight into
+//     registers and dequantizes to fp16 in registers, q * scale rounded once: two bit operations
+//     build (1024 + u) in fp16, one packed subtract gives q exactly, one packed multiply applies
+//     the scale.
+//   MFMA v_mfma_f32_16x16x32_f16, fp32 accumulation.  MFMA d (0..3) of a chunk covers block d of
+//   the chunk: word d of every lane's 16 bytes with activations 32 d + 8 g .. +7, so each B
+//   register is used as loaded and each MFMA sees one scale per weight row.
 // Rows of an item are processed in 16-row subtiles up to the item's row count (no work on
 // padding beyond the last 16-row subtile).  fp16 (11 significant bits) instead of bf16 (8) for
 // the dequantized weights and the SwiGLU intermediate keeps the layer within a 2e-3 relative
@@ -27,11 +28,6 @@
 #include "kernels.hpp"
 
 namespace moe {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 constexpr int kKC = 128;                  // K per pipeline stage (4 quantization blocks)
 constexpr int kAStride = kKC + 8;         // LDS row stride in 16-bit elements (16-byte pad)
@@ -66,7 +62,7 @@ MOE_DEV const uint8_t* bucket_blob(const ExpertSource& s, int bucket, int E) {
   return s.arena + (int64_t)slot * s.slot_stride;
 }
 
-// Word d of a block's codes -> the 8 fp16 weights (elements 8d..8d+7) of MFMA d.
+// One code word (8 elements of a slice) -> the 8 fp16 weights q * scale of an MFMA step.
 MOE_DEV half8 dequant_word(uint32_t w, half2v s2) {
   const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
   half8 r;
@@ -125,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   const int H = a.H, F = a.F;
   const int K = MODE == kDown ? F : H;
   const int nk = K / kKC;
-  const int L = K / kBlock;
+  const int wrows = MODE == kDown ? H : F;  // rows of the weight matrix
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int ms = (it.rows + 15) >> 4;
@@ -161,8 +157,9 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
         sb = lay.down_scales;
       }
       bvalid[s] = true;
-      coff[s] = (uint32_t)(cb + (int64_t)row * (K / 2));
-      soff[s] = (uint32_t)(sb + (int64_t)row * L * 2);
+      // record (kc, row) of a matrix of R rows: codes at 64 (kc R + row), scales at 8 (kc R + row)
+      coff[s] = (uint32_t)(cb + (int64_t)row * kGroupBytes);
+      soff[s] = (uint32_t)(sb + (int64_t)row * kGroupScaleBytes);
     }
   }
 
@@ -189,19 +186,19 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   // ---- B registers --------------------------------------------------------------------------
   constexpr int kBW = MODE == kRouter ? 4 : 1;  // 16-byte loads per subtile per chunk
   uint4 braw[4][kBW];
-  uint32_t bsc[4];
+  uint2 bsc[4];  // the four block scales (fp16) of the chunk
   auto load_b = [&](int kc) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if constexpr (MODE == kRouter) {
 #pragma unroll
         for (int d = 0; d < 4; ++d)
-          braw[s][d] = bvalid[s] ? *(const uint4*)(bbase + coff[s] + ((size_t)kc * kKC + g * 32 + 8 * d) * 2)
+          braw[s][d] = bvalid[s] ? *(const uint4*)(bbase + coff[s] + ((size_t)kc * kKC + 32 * d + 8 * g) * 2)
                                  : make_uint4(0u, 0u, 0u, 0u);
-        bsc[s] = 0;
+        bsc[s] = make_uint2(0u, 0u);
       } else {
-        braw[s][0] = *(const uint4*)(bbase + coff[s] + (size_t)(kc * 4 + g) * 16);
-        bsc[s] = *(const uint16_t*)(bbase + soff[s] + (size_t)(kc * 4 + g) * 2);
+        braw[s][0] = *(const uint4*)(bbase + coff[s] + (size_t)kc * wrows * kGroupBytes + 16 * g);
+        bsc[s] = *(const uint2*)(bbase + soff[s] + (size_t)kc * wrows * kGroupScaleBytes);
       }
     }
   };
@@ -220,13 +217,12 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   for (int kc = 0; kc < nk; ++kc) {
     uint16_t* Ab = (kc & 1) ? As1 : As0;
     uint4 bcur[4][kBW];
-    half2v s2[4];
+    uint2 scur[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int d = 0; d < kBW; ++d) bcur[s][d] = braw[s][d];
-      const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)bsc[s]);
-      s2[s] = (half2v){sv, sv};
+      scur[s] = bsc[s];
     }
     if (kc + 1 < nk) {
       issue_a(kc + 1, (kc & 1) ? As0 : As1);
@@ -234,8 +230,9 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      // fragment read: row 16i + n, logical chunk 4g + d -> physical (4g + d) ^ n
-      const int pcol = (((4 * g + d) ^ n) * 8);
+      // fragment read: row 16i + n, inputs 32 d + 8 g .. +7 = logical chunk 4d + g -> physical
+      // chunk (4d + g) ^ n
+      const int pcol = (((4 * d + g) ^ n) * 8);
       if constexpr (MODE == kRouter) {
 #pragma unroll
         for (int i = 0; i < kMSub; ++i) {
@@ -250,7 +247,11 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
       } else {
         half8 bf[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) bf[s] = dequant_word(word_of(bcur[s][0], d), s2[s]);
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t sw = d < 2 ? scur[s].x : scur[s].y;
+          const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)((d & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+          bf[s] = dequant_word(word_of(bcur[s][0], d), (half2v){sv, sv});
+        }
 #pragma unroll
         for (int i = 0; i < kMSub; ++i) {
           if (i < ms) {

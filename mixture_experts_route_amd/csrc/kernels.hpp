@@ -26,23 +26,22 @@ hipError_t launch_timed(int which, K kernel, dim3 grid, dim3 block, uint32_t lds
   return hipGetLastError();
 }
 
-// One expert's work in a decode step: the tokens that chose it and, for each, the pair
-// index whose FFN output row it owns (routed pair t*k + j, shared pair T*k + t).
-constexpr int kTaskTok = 4;  // tokens per decode task (an expert chosen by more is split)
+// One expert's work in a decode step: the tokens that chose it (a bitmask; a task holds every
+// token of the step that chose its expert, so each expert's weights are read once) and, for a
+// routed expert, the position j of the expert in each token's top-k list (4 bits per token).
+// Token t of a routed task owns FFN output row (pair) t*k + j; of the shared task, T*k + t.
+constexpr int kTaskTok = kMaxDecodeTok;
 
 struct DecodeTask {
-  int32_t expert;  // routed expert id, or -1 for the shared expert
-  int32_t slot;    // slot resolved by the plan, or -1: look the table up when the FFN runs (a miss)
-  int32_t n_tok;
-  int32_t tok[kTaskTok];
-  int32_t pair[kTaskTok];
+  int32_t expert;     // routed expert id, or -1 for the shared expert
+  int32_t slot;       // slot resolved by the plan, or -1: look the table up when the FFN runs (a miss)
+  uint32_t tok_mask;  // bit t: token t chose the expert
+  uint32_t choice;    // bits 4t..4t+3: j of token t (routed tasks)
 };
 
-// Upper bound on decode tasks for T tokens: every routed task holds >= 1 pair, and the
-// shared expert's T tokens make ceil(T / kTaskTok) tasks.
-inline int decode_max_tasks(int T, int k, int n_shared) {
-  return T * k + (n_shared ? (T + kTaskTok - 1) / kTaskTok : 0);
-}
+// Upper bound on decode tasks for T tokens: every routed task holds >= 1 pair, plus one task
+// for the shared expert.
+inline int decode_max_tasks(int T, int k, int n_shared) { return T * k + (n_shared ? 1 : 0); }
 
 struct DoorbellArgs {
   int active;
@@ -107,7 +106,8 @@ hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r
 // ffn_decode.hip
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
                              const void* x, int x_dtype, const DecodeTask* tasks, const float* topk_w,
-                             float* h, float* y_pairs, float* y, int32_t* ctrl, hipStream_t st);
+                             uint16_t* h_hi, uint16_t* h_lo, float* y_pairs, float* y, int32_t* ctrl,
+                             hipStream_t st);
 // group.hip
 hipError_t launch_group(const int32_t* ids, const float* topk_w, int T, int k, int E, int n_shared,
                         const GroupBuffers& g, int32_t* ctrl, int32_t* counts_out, int32_t* offsets_out,

@@ -179,10 +179,10 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode plan (one workgroup of 256 threads, <= 8 tokens): residency check + the list of distinct
-// experts (ascending id) with the tokens that chose each (split into tasks of <= kTaskTok
-// tokens), then the shared expert over all tokens.  The FFN kernel resolves each task's slot from
-// the table when it runs, so slots filled after this check (doorbell path) are seen.
+// Decode plan (one workgroup of 256 threads, <= 8 tokens): residency check + one task per
+// distinct expert (ascending id) with the tokens that chose it, then the shared expert over all
+// tokens.  A task whose expert missed keeps slot -1 and the FFN kernels read the table entry when
+// they run, so slots filled after this check (doorbell path) are seen.
 // ------------------------------------------------------------------------------------------
 struct PlanShared {
   uint32_t tok_mask[kMaxExperts];
@@ -194,7 +194,7 @@ struct PlanShared {
 
 // ids: the step's [T][k] selections (LDS or global).  One thread per pair fills the per-expert
 // token masks and slots in LDS; then each thread owns a run of consecutive experts, so tasks and
-// misses come out in ascending expert id.  Tasks are written field by field to global memory.
+// misses come out in ascending expert id.
 MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table, int n_slots,
                         int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell,
                         PlanShared& sh) {
@@ -222,9 +222,8 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
-    const int c = __popc(sh.tok_mask[e]);
-    if (c) {
-      n_sub += (c + kTaskTok - 1) / kTaskTok;
+    if (sh.tok_mask[e]) {
+      ++n_sub;
       if (sh.slot_of[e] < 0) ++n_mis;
     }
   }
@@ -238,34 +237,25 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     if (!m) continue;
     const int s = sh.slot_of[e];
     if (s < 0) miss_ids[mpos++] = e;
-    int n = 0;
-    for (int t = 0; t < T; ++t) {
-      if (!(m & (1u << t))) continue;
-      tasks[tpos].tok[n] = t;
-      tasks[tpos].pair[n] = t * k + sh.choice[e][t];
-      if (++n == kTaskTok || (m >> (t + 1)) == 0) {
-        tasks[tpos].expert = e;
-        tasks[tpos].slot = s;
-        tasks[tpos].n_tok = n;
-        ++tpos;
-        n = 0;
-      }
-    }
+    uint32_t choice = 0;
+    for (int t = 0; t < T; ++t)
+      if (m & (1u << t)) choice |= (uint32_t)sh.choice[e][t] << (4 * t);
+    DecodeTask tk;
+    tk.expert = e;
+    tk.slot = s;
+    tk.tok_mask = m;
+    tk.choice = choice;
+    tasks[tpos++] = tk;
   }
   if (threadIdx.x == 0) {
     int n_all = n_tasks;
     if (n_shared) {
-      for (int t0 = 0; t0 < T; t0 += kTaskTok) {
-        const int nt = min(kTaskTok, T - t0);
-        for (int n = 0; n < nt; ++n) {
-          tasks[n_all].tok[n] = t0 + n;
-          tasks[n_all].pair[n] = T * k + t0 + n;
-        }
-        tasks[n_all].expert = -1;
-        tasks[n_all].slot = -1;
-        tasks[n_all].n_tok = nt;
-        ++n_all;
-      }
+      DecodeTask tk;
+      tk.expert = -1;
+      tk.slot = -1;
+      tk.tok_mask = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
+      tk.choice = 0;
+      tasks[n_all++] = tk;
     }
     ctrl[kCtrlNTasks] = n_all;
     ctrl[kCtrlMissCount] = n_miss;

@@ -37,8 +37,8 @@ The readings taken here:
 * R2 the shared expert has weight 1, no gate, the same width and format;
 * R3 4-bit code u in 0..15 stands for q = u - 8; blocks of 32 run along the
   reduction dimension; one fp16 scale per block; the code words of each run of
-  four blocks are interleaved as in :func:`decode_codes` (rows hold a multiple
-  of 128 elements);
+  four blocks are interleaved and the runs stored group-major as in
+  :func:`decode_codes` (rows hold a multiple of 128 elements);
 * R4 a per-expert bias, when given, is added to the logits before both the
   selection and the weights;
 * R5 equal logits: the lower expert id wins;
@@ -78,9 +78,11 @@ def fp16_codes_to_f64(codes) -> np.ndarray:
 def blob_layout(H: int, F: int) -> dict:
     """Byte offsets of the six sections of one expert blob.
 
-    Order: gate codes [F][H/2], up codes [F][H/2], down codes [H][F/2], then the
-    fp16 scales gate [F][H/32], up [F][H/32], down [H][F/32].  (Layout is ours:
-    [HG] "Bring your own GGUF" repacks a file's values into the kernels' layout.)
+    Order: gate codes (F rows of H), up codes (F rows of H), down codes (H rows
+    of F), each F*H/2 bytes, then the fp16 scales of gate, up and down, F*H/32 * 2
+    bytes each; codes and scales group-major (:func:`decode_codes`,
+    :func:`decode_scales`).  (Layout is ours: [HG] "Bring your own GGUF" repacks
+    a file's values into the kernels' layout.)
     """
     sizes = [
         ("gate_codes", F * H // 2), ("up_codes", F * H // 2), ("down_codes", H * F // 2),
@@ -101,30 +103,42 @@ GROUP = 128  # elements per word group: four blocks of 32
 def decode_codes(code_bytes: np.ndarray, rows: int, cols: int) -> np.ndarray:
     """4-bit codes of a [rows][cols] matrix, as integers 0..15 (cols a multiple of 128).
 
-    Each row is cols/2 bytes read as little-endian 32-bit words, in groups of 16
-    words that cover 128 elements (four blocks of 32).  Word 4g + i of group c
-    holds the eight elements 128c + 32i + 8g .. 128c + 32i + 8g + 7 (slice g of
-    block i of the group): its element 2j in bits 4j..4j+3 and its element 2j+1
-    in bits 16+4j..16+4j+3, for j = 0..3.
+    The codes are stored group-major: the cols/128 groups of 128 elements (four
+    blocks of 32) of every row form 64-byte records, record (c, r) = group c of
+    row r at byte 64 (c * rows + r).  A record is 16 little-endian 32-bit words;
+    word 4g + i holds the eight elements 128c + 32i + 8g .. 128c + 32i + 8g + 7
+    (slice g of block i of the group): its element 2j in bits 4j..4j+3 and its
+    element 2j+1 in bits 16+4j..16+4j+3, for j = 0..3.
     """
     assert cols % GROUP == 0
-    b = np.asarray(code_bytes, dtype=np.uint8).reshape(rows, cols // GROUP, 4, 4, 4).astype(np.uint32)
-    # b[r, c, g, i, byte]: byte `byte` of word 4g + i of group c
+    b = np.asarray(code_bytes, dtype=np.uint8).reshape(cols // GROUP, rows, 4, 4, 4).astype(np.uint32)
+    # b[c, r, g, i, byte]: byte `byte` of word 4g + i of record (c, r)
     word = b[..., 0] | (b[..., 1] << 8) | (b[..., 2] << 16) | (b[..., 3] << 24)
     u = np.empty((rows, cols // GROUP, 4, 4, 8), dtype=np.int64)  # [r, c, i (block), g (slice), m]
     for i in range(4):
         for g in range(4):
-            w = word[:, :, g, i]
+            w = word[:, :, g, i].T  # [r, c]
             for j in range(4):
                 u[:, :, i, g, 2 * j] = (w >> (4 * j)) & 0xF
                 u[:, :, i, g, 2 * j + 1] = (w >> (16 + 4 * j)) & 0xF
     return u.reshape(rows, cols)
 
 
+def decode_scales(scale_bytes, rows: int, cols: int) -> np.ndarray:
+    """fp16 block scales of a [rows][cols] matrix -> float64 [rows][cols/32].
+
+    Stored group-major like the codes: record (c, r) = the four scales of group c
+    of row r (blocks 4c .. 4c+3) at byte 8 (c * rows + r).
+    """
+    s = fp16_codes_to_f64(np.asarray(scale_bytes, dtype=np.uint8).view(np.uint16))
+    s = s.reshape(cols // GROUP, rows, 4)  # [c, r, i]
+    return s.transpose(1, 0, 2).reshape(rows, cols // BLOCK)
+
+
 def dequant(code_bytes, scale_bytes, rows: int, cols: int) -> np.ndarray:
     """w[r][c] = (u[r][c] - 8) * scale[r][c // 32]  ([HG]: small set x block scale)."""
     u = decode_codes(code_bytes, rows, cols)
-    s = fp16_codes_to_f64(np.asarray(scale_bytes, dtype=np.uint8).view(np.uint16)).reshape(rows, cols // BLOCK)
+    s = decode_scales(scale_bytes, rows, cols)
     return (u - 8).astype(np.float64) * np.repeat(s, BLOCK, axis=1)
 
 

@@ -49,12 +49,13 @@ def test_blob_and_workspace_sizes(N):
 @pytest.mark.parametrize("bad,code", [
     (dict(block=16), -2),             # unsupported block size, refused by name
     (dict(hidden=100), -1),           # not a multiple of 32
+    (dict(ffn=32 * 5), -1),           # whole blocks, but not whole groups of four blocks
     (dict(top_k=0), -1),
     (dict(top_k=600), -1),            # k > E
     (dict(n_shared=2), -1),
     (dict(n_experts=2048), -2),       # beyond the selection kernel's 1024
     (dict(top_k=17, n_experts=64), -2),
-    (dict(hidden=32 * 96), -2),       # 96 blocks per row: not a layout the GEMV maps
+    (dict(hidden=4096 + 128), -2),    # beyond the 4096-wide rows the kernels are built for
 ])
 def test_invalid_dims_rejected_on_host(N, bad, code):
     args = dict(hidden=2048, ffn=768, n_experts=512, top_k=10, n_shared=1, block=32)

@@ -61,20 +61,41 @@ def test_dequant_hand_encoded_groups():
 
 
 def test_dequant_rows_and_groups_are_independent():
-    # two rows of two groups: each block takes its own scale, groups and rows do not mix
+    # two rows of two groups, stored group-major: record (group c, row r) at 64 (2 c + r).
+    # Each block takes its own scale; groups and rows do not mix.  No two records agree, so a
+    # row-major reading fails.
     ramp = [0x20, 0x64, 0x31, 0x75] * 4 + [0xA8, 0xEC, 0xB9, 0xFD] * 4
     ramp = ramp * 2  # slices 0..3 of the four blocks (see dequant_groups.txt)
     zero = [0x88] * 64
-    code_bytes = np.array(ramp + zero + zero + ramp, dtype=np.uint8)
-    scales = np.array([0x3C00, 0x4000, 0x3800, 0x4400] + [0x3C00] * 4 + [0x3C00] * 4 + [0x4000] * 4,
-                      dtype=np.uint16)  # row 0: 1, 2, 0.5, 4, 1...; row 1: 1..., 2, 2, 2, 2
+    probe = list(zero)
+    probe[20] = 0x8A  # element 40 of the group = 10 (dequant_groups.txt, only_el40)
+    # records: (c0, r0) ramp, (c0, r1) zero, (c1, r0) probe, (c1, r1) ramp
+    code_bytes = np.array(ramp + zero + probe + ramp, dtype=np.uint8)
+    # scale records (c, r) of four fp16 each, in the same order
+    scales = np.array([0x3C00, 0x4000, 0x3800, 0x4400] + [0x3C00] * 4 + [0x4400] * 4 + [0x4000] * 4,
+                      dtype=np.uint16)  # (1, 2, 0.5, 4), 1..., 4..., 2...
     w = O.dequant(code_bytes, scales.view(np.uint8), 2, 256)
     q = np.array([(e % 16) - 8 for e in range(128)], dtype=np.float64)
     s0 = np.repeat([1.0, 2.0, 0.5, 4.0], 32)
     assert np.array_equal(w[0, :128], q * s0)
-    assert np.array_equal(w[0, 128:], np.zeros(128))
+    want01 = np.zeros(128)
+    want01[40] = (10 - 8) * 4.0
+    assert np.array_equal(w[0, 128:], want01)
     assert np.array_equal(w[1, :128], np.zeros(128))
     assert np.array_equal(w[1, 128:], q * 2.0)
+
+
+def test_dequant_group_major_three_rows():
+    # three rows of one group each: records are consecutive rows, scales likewise
+    zero = [0x88] * 64
+    probe = list(zero)
+    probe[20] = 0x8A  # element 40 of the group = 10 (dequant_groups.txt, only_el40)
+    code_bytes = np.array(zero + probe + zero, dtype=np.uint8)
+    scales = np.array([0x3C00] * 4 + [0x3C00, 0x4400, 0x3C00, 0x3C00] + [0x3C00] * 4, dtype=np.uint16)
+    w = O.dequant(code_bytes, scales.view(np.uint8), 3, 128)
+    want = np.zeros((3, 128))
+    want[1, 40] = (10 - 8) * 4.0  # block 1 of row 1 has scale 4
+    assert np.array_equal(w, want)
 
 
 def test_blob_layout_sizes():

@@ -354,6 +354,135 @@ def bench_prefill(T: int, steps: int, warmup: int, cpu_sample: int | None):
     return out
 
 
+def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
+    """Batched decode through all 48 layers: 8 tokens per step, every layer's 512 + 1 experts resident
+    in HBM (one 65 GB arena), per-layer Zipf(1.1) router bias, fresh seeded tokens per (step, layer)."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_route_amd import native as N
+    from mixture_experts_route_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    n_layers, T, cfg = 48, 8, 3
+    stride = (S.blob_bytes(H, F) + 4095) // 4096 * 4096
+    per_layer = E + 1  # routed experts in slots 0..E-1, the shared expert after them
+    arena = torch.empty((n_layers * per_layer, stride), dtype=torch.uint8, device=dev)
+    for layer in range(n_layers):
+        keys = [S.stream_key(0, cfg, "blob", layer, e) for e in range(E)] + [S.stream_key(0, cfg, "shared", layer, 0)]
+        S.expert_blobs_torch_batch(keys, H, F, arena[layer * per_layer:(layer + 1) * per_layer])
+    routers = [S.bf16_normal_torch(S.stream_key(0, cfg, "router", layer, 0), (E, H), 0.02, dev)
+               for layer in range(n_layers)]
+    biases = [torch.from_numpy(S.zipf_bias(S.rank_permutation(0, cfg, layer, 0, E), S.ZIPF_C)).to(dev)
+              for layer in range(n_layers)]
+    n_steps = warmup + steps
+    xs = [S.bf16_normal_torch(S.stream_key(0, cfg, "x", layer, X_STREAM), (n_steps * T, H), 1.0, dev)
+          for layer in range(n_layers)]
+    d = N.dims(H, F, E, K_TOP, 1)
+    ws_t = [N.layer_weights(routers[l], arena[l * per_layer:], stride, E, arena[l * per_layer + E], biases[l])
+            for l in range(n_layers)]
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(N.moe_workspace_bytes(d, T) // 4 + 64, dtype=torch.int32, device=dev)
+    N.moe_workspace_init(ws)
+    st = torch.cuda.Stream()
+
+    def run_steps(stream, first, count, ids_out=None):
+        for i in range(count):
+            s = first + i
+            for layer in range(n_layers):
+                ids = ids_out[i][layer] if ids_out is not None else None
+                N.moe_layer_forward(d, ws_t[layer], None, xs[layer][s * T:(s + 1) * T], T, y, ws, topk_ids=ids,
+                                    stream=stream)
+
+    torch.cuda.synchronize()
+    if graph:
+        chunk = 16
+        graphs = []
+        for first in range(warmup, warmup + steps, chunk):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=st):
+                run_steps(torch.cuda.current_stream(), first, min(chunk, warmup + steps - first))
+            graphs.append(g)
+        with torch.cuda.stream(st):
+            run_steps(st, 0, warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    else:
+        with torch.cuda.stream(st):
+            run_steps(st, 0, warmup)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(st):
+            run_steps(st, warmup, steps)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+    assert N.moe_check_device_error(ws) == 0
+    elapsed = t1 - t0
+
+    # per-kernel durations (HIP events around each gate/up and down launch of `time_steps` eager steps)
+    # and the algorithmic bytes of each launch from its own routing (distinct experts U + shared)
+    ids_out = [[torch.empty((T, K_TOP), dtype=torch.int32, device=dev) for _ in range(n_layers)]
+               for _ in range(time_steps)]
+    res_k = {}
+    for which in (N.TIME_DECODE_GATE_UP, N.TIME_DECODE_DOWN):
+        timer = KernelTimer(time_steps * n_layers)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            for i in range(time_steps):
+                for layer in range(n_layers):
+                    pr = timer.pairs[i * n_layers + layer]
+                    N.moe_debug_kernel_events(which, pr[0], pr[1])
+                    s = warmup + i
+                    N.moe_layer_forward(d, ws_t[layer], None, xs[layer][s * T:(s + 1) * T], T, y, ws,
+                                        topk_ids=ids_out[i][layer], stream=st)
+        torch.cuda.synchronize()
+        N.moe_debug_kernel_events(0, None, None)
+        res_k[which] = timer.durations_ms()
+        timer.close()
+    assert N.moe_check_device_error(ws) == 0
+    u = np.array([len(np.unique(ids_out[i][l].cpu().numpy())) for i in range(time_steps) for l in range(n_layers)])
+    gu_exp = 2 * (F * H // 2 + F * (H // 32) * 2)
+    dn_exp = H * F // 2 + H * (F // 32) * 2
+    pairs = T * (K_TOP + 1)
+    gu_bytes = (u + 1) * gu_exp + T * H * 2 + pairs * F * 4
+    dn_bytes = (u + 1) * dn_exp + pairs * F * 4 + pairs * H * 4
+    gu_s = np.array(res_k[N.TIME_DECODE_GATE_UP]) * 1e-3
+    dn_s = np.array(res_k[N.TIME_DECODE_DOWN]) * 1e-3
+    gu_gbs = gu_bytes.sum() / gu_s.sum() / 1e9
+    dn_gbs = dn_bytes.sum() / dn_s.sum() / 1e9
+    ffn_gbs = (gu_bytes.sum() + dn_bytes.sum()) / (gu_s.sum() + dn_s.sum()) / 1e9
+    step_bytes = float(np.mean(u + 1)) * 2_654_208 * n_layers + n_layers * (E * H * 2)
+    return {
+        "workload": "batched decode through 48 layers: 8 tokens per step, 48 x (512 routed + 1 shared) experts "
+                    "resident in HBM (65.4 GB of 4-bit weights), per-layer Zipf(1.1) router bias, top-10 + shared, "
+                    "hidden 2048, expert FFN 768, fresh bf16 tokens per (step, layer)",
+        "tokens_per_s": T * steps / elapsed,
+        "ms_per_step": elapsed * 1e3 / steps,
+        "steps": steps,
+        "timed_region": "HIP graph replay of the timed steps" if graph else "eager launches",
+        "distinct_experts_per_layer": float(np.mean(u)),
+        "approx_weight_bytes_per_step": step_bytes,
+        "roofline": {
+            "kernel": "k_decode_gate_up (matrix-core 4-bit GEMV gate+up, SwiGLU fused), 8 tokens",
+            "bound": "hbm",
+            "achieved": gu_gbs,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": gu_gbs / HBM_PEAK_GBS,
+            "traffic": None,
+            "bytes_per_launch": float(gu_bytes.mean()),
+            "avg_launch_us": float(gu_s.mean() * 1e6),
+        },
+        "decode_down": {"achieved_gbs": dn_gbs, "frac": dn_gbs / HBM_PEAK_GBS, "bytes_per_launch": float(dn_bytes.mean()),
+                        "avg_launch_us": float(dn_s.mean() * 1e6)},
+        "decode_ffn_hbm_frac": ffn_gbs / HBM_PEAK_GBS,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -365,12 +494,15 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch decode steps one by one instead of replaying graphs")
     ap.add_argument("--prefill", default="4096", help="comma-separated prefill token counts to add ('' = none)")
     ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--decode48-steps", type=int, default=64, help="steps of the 48-layer batched decode (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's data-parallel scale-out has no exchange on the path, "
               "so only --gpus 1 is run here", file=sys.stderr)
         sys.exit(2)
     res = bench_decode1(args)
+    if args.decode48_steps > 0:
+        res["decode_8tok_48layers"] = bench_decode48(args.decode48_steps, 4, not args.eager)
     for T in [int(v) for v in args.prefill.split(",") if v.strip()]:
         steps = args.prefill_steps if T <= 8192 else max(4, args.prefill_steps // 4)
         sample = None if args.no_cpu_baseline else (48 if T == 4096 else None)

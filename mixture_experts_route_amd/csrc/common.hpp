@@ -157,6 +157,36 @@ MOE_DEV float group_sum_dpp(float v, int width) {
 
 MOE_DEV bool group_last_lane(int lane, int width) { return (lane & (width - 1)) == width - 1; }
 
+// Wave-wide maximum of a 64-bit key (DPP, no branches); returned to every lane.
+MOE_DEV uint64_t wave_max_u64(uint64_t key) {
+#define MOE_MAX64_STEP(C, M)                                                              \
+  {                                                                                       \
+    const uint32_t lo = (uint32_t)dpp_i<C, M>((int)(uint32_t)key);                        \
+    const uint32_t hi = (uint32_t)dpp_i<C, M>((int)(uint32_t)(key >> 32));                \
+    const uint64_t other = ((uint64_t)hi << 32) | lo;                                     \
+    key = other > key ? other : key;                                                      \
+  }
+  MOE_MAX64_STEP(kDppQuadXor1, 0xF)
+  MOE_MAX64_STEP(kDppQuadXor2, 0xF)
+  MOE_MAX64_STEP(kDppRowRor4, 0xF)
+  MOE_MAX64_STEP(kDppRowRor8, 0xF)
+  MOE_MAX64_STEP(kDppRowBcast15, 0xA)
+  MOE_MAX64_STEP(kDppRowBcast31, 0xC)
+#undef MOE_MAX64_STEP
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Order-preserving map of a float to uint32 (a > b as floats <=> map(a) > map(b); no NaN).
+MOE_DEV uint32_t f32_order_key(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+MOE_DEV float f32_from_order_key(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // Wave-wide arg-max on (value desc, index asc); the result is returned to every lane.
 MOE_DEV void wave_argmax(float& v, int& i) {
 #define MOE_ARGMAX_STEP(C, M)                                        \

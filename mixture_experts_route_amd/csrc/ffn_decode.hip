@@ -85,6 +85,14 @@ MOE_DEV int task_pair(const DecodeTask& tk, int t, int T, int k) {
   return tk.expert < 0 ? T * k + t : t * k + (int)((tk.choice >> (4 * t)) & 15u);
 }
 
+// Keeps every load above it ahead of the code below it: the loads of a wave's whole tile go out
+// together, and the waits the compiler inserts before each group's MFMA steps then cover only
+// that group's data (loads complete in order).
+MOE_DEV void issue_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 MOE_DEV float4v mfma_bf16(const bf16x8& a, const bf16x8& b, const float4v& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -145,34 +153,42 @@ __global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs 
 
   // ---- loads, group by group in the order the MFMA steps use them: the activations of the
   // group (A row m = lane % 16, inputs 32 i + 8 g .. +7), then slice g of the group's record of
-  // row `row` in both matrices, and the record's four scales
+  // row `row` in both matrices, and the record's four scales.  No load sits under a branch (dead
+  // lanes and groups past the wave's range load valid, clamped addresses and are masked after),
+  // so the compiler can wait for each group's data alone.
   const int m = n;
   const int tslot = X_BF16 ? m : (m >> 1);
   const int n_tok = __builtin_popcount(tk.tok_mask);
   const bool live = m < ROWS && tslot < n_tok;
   const int tok = live ? task_token(tk.tok_mask, tslot) : 0;
-  const size_t rec0 = (size_t)q0 * F + row;  // record (q0, row); the next group is F records on
-  const uint8_t* gcode = blob + lay.gate_codes + rec0 * kGroupBytes + 16 * g;
-  const uint8_t* ucode = blob + lay.up_codes + rec0 * kGroupBytes + 16 * g;
-  const uint8_t* gscale = blob + lay.gate_scales + rec0 * kGroupScaleBytes;
-  const uint8_t* uscale = blob + lay.up_scales + rec0 * kGroupScaleBytes;
-  const uint16_t* xr = (const uint16_t*)a.x + (size_t)tok * H + (size_t)q0 * kGroupElems + 8 * g;
+  const uint8_t* gcode = blob + lay.gate_codes + (size_t)row * kGroupBytes + 16 * g;
+  const uint8_t* ucode = blob + lay.up_codes + (size_t)row * kGroupBytes + 16 * g;
+  const uint8_t* gscale = blob + lay.gate_scales + (size_t)row * kGroupScaleBytes;
+  const uint8_t* uscale = blob + lay.up_scales + (size_t)row * kGroupScaleBytes;
+  const uint16_t* xr = (const uint16_t*)a.x + (size_t)tok * H + 8 * g;
+  const int NQ = H / kGroupElems;
   uint4 cg[kGuQuadsPerWave], cu[kGuQuadsPerWave];
   uint2 sg[kGuQuadsPerWave], su[kGuQuadsPerWave];
   uint4 xa[X_BF16 ? kGuQuadsPerWave : 1][4];
 #pragma unroll
   for (int qi = 0; qi < kGuQuadsPerWave; ++qi) {
-    if (qi < nq) {
-      if constexpr (X_BF16) {
+    const int qq = min(q0 + qi, NQ - 1);  // record (qq, row) at 64 (qq F + row)
+    if constexpr (X_BF16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          xa[qi][i] = live ? *(const uint4*)(xr + (size_t)qi * kGroupElems + 32 * i) : make_uint4(0u, 0u, 0u, 0u);
-      }
-      cg[qi] = *(const uint4*)(gcode + (size_t)qi * F * kGroupBytes);
-      cu[qi] = *(const uint4*)(ucode + (size_t)qi * F * kGroupBytes);
-      sg[qi] = *(const uint2*)(gscale + (size_t)qi * F * kGroupScaleBytes);
-      su[qi] = *(const uint2*)(uscale + (size_t)qi * F * kGroupScaleBytes);
+      for (int i = 0; i < 4; ++i) xa[qi][i] = *(const uint4*)(xr + (size_t)qq * kGroupElems + 32 * i);
     }
+    cg[qi] = *(const uint4*)(gcode + (size_t)qq * F * kGroupBytes);
+    cu[qi] = *(const uint4*)(ucode + (size_t)qq * F * kGroupBytes);
+    sg[qi] = *(const uint2*)(gscale + (size_t)qq * F * kGroupScaleBytes);
+    su[qi] = *(const uint2*)(uscale + (size_t)qq * F * kGroupScaleBytes);
+  }
+  issue_fence();
+  if constexpr (X_BF16) {
+#pragma unroll
+    for (int qi = 0; qi < kGuQuadsPerWave; ++qi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!live) xa[qi][i] = make_uint4(0u, 0u, 0u, 0u);
   }
 
   const bf16x8 neg = const_neg136();
@@ -182,7 +198,7 @@ __global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs 
   for (int r = 0; r < NR; ++r) accg[r] = accu[r] = 0.f;
 #pragma unroll
   for (int qi = 0; qi < kGuQuadsPerWave; ++qi) {
-    if (qi >= nq) break;
+    if (qi >= nq) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint4 av;
@@ -191,8 +207,8 @@ __global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs 
       } else {
         av = make_uint4(0u, 0u, 0u, 0u);
         if (live) {
-          const float* xr = (const float*)a.x + (size_t)tok * H + (size_t)(q0 + qi) * kGroupElems + 32 * i + 8 * g;
-          av = split_part(*(const float4*)xr, *(const float4*)(xr + 4), m & 1);
+          const float* xf = (const float*)a.x + (size_t)tok * H + (size_t)(q0 + qi) * kGroupElems + 32 * i + 8 * g;
+          av = split_part(*(const float4*)xf, *(const float4*)(xf + 4), m & 1);
         }
       }
       const bf16x8 A = __builtin_bit_cast(bf16x8, av);
@@ -283,20 +299,25 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
     const int nq = min(kDnQuadsPerPass, NQ - q0);
     uint4 cd[kDnQuadsPerPass], ha[kDnQuadsPerPass][4];
     uint2 sd[kDnQuadsPerPass];
-    // loads group by group in the order of use: h (A operands), then the record and its scales
+    // loads group by group in the order of use: h (A operands), then the record and its scales;
+    // unconditional (clamped addresses, dead lanes masked after) so each group is waited for alone
 #pragma unroll
     for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
-      if (qi < nq) {
+      const int qq = min(q0 + qi, NQ - 1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          ha[qi][i] = live ? *(const uint4*)(hrow + (size_t)(q0 + qi) * kGroupElems + 32 * i) : make_uint4(0u, 0u, 0u, 0u);
-        cd[qi] = *(const uint4*)(dcode + (size_t)(q0 + qi) * H * kGroupBytes);
-        sd[qi] = *(const uint2*)(dscale + (size_t)(q0 + qi) * H * kGroupScaleBytes);
-      }
+      for (int i = 0; i < 4; ++i) ha[qi][i] = *(const uint4*)(hrow + (size_t)qq * kGroupElems + 32 * i);
+      cd[qi] = *(const uint4*)(dcode + (size_t)qq * H * kGroupBytes);
+      sd[qi] = *(const uint2*)(dscale + (size_t)qq * H * kGroupScaleBytes);
     }
+    issue_fence();
+#pragma unroll
+    for (int qi = 0; qi < kDnQuadsPerPass; ++qi)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (!live) ha[qi][i] = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
     for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
-      if (qi >= nq) break;
+      if (qi >= nq) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 A = __builtin_bit_cast(bf16x8, ha[qi][i]);

@@ -14,68 +14,69 @@ namespace moe {
 // order.  The weights are a softmax over the selected logits, summed in selection order.  NaN
 // logits are flagged and never selected.
 // ------------------------------------------------------------------------------------------
+// NPER = logits per lane, 64 * NPER >= E (8 for E <= 512, 16 for E <= 1024).
+template <int NPER>
 MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, float* w_out, int32_t* ctrl,
                               int32_t* lds_ids) {
+  constexpr int kPerLane = NPER;
   const int lane = threadIdx.x & 63;
-  constexpr int kPerLane = kMaxExperts / 64;
   float v[kPerLane];
   // all loads are issued before any value is looked at: a clamped index instead of a branch keeps
-  // the compiler from waiting on each load in turn (16 serial memory round trips otherwise)
+  // the compiler from waiting on each load in turn
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int e = lane + 64 * i;
     v[i] = row[e < E ? e : E - 1];
   }
+  // key = (order-preserving value bits, ~id): a larger key is a larger logit, then a lower id.
+  // NaN ranks as -inf (and is reported); ids >= E get key 0, below every real key.
+  uint64_t key[kPerLane];
   bool nan_seen = false;
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int e = lane + 64 * i;
-    if (e >= E) {
-      v[i] = -INFINITY;
-    } else if (v[i] != v[i]) {
-      nan_seen = true;
-      v[i] = -INFINITY;
-    }
+    const bool nan = v[i] != v[i];
+    nan_seen |= nan && e < E;
+    const float f = nan ? -INFINITY : v[i];
+    key[i] = e < E ? (((uint64_t)f32_order_key(f) << 32) | (uint32_t)~e) : 0ull;
   }
   if (__any(nan_seen) && lane == 0) set_error(ctrl, MOE_DERR_NAN);
-  uint32_t taken = 0;
-  float my_v = 0.f;
-  int my_i = 0;
+  uint64_t best = 0;
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) best = key[i] > best ? key[i] : best;
+  uint64_t mine = 0;  // lane r keeps the r-th selection
   for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    const uint64_t win = wave_max_u64(best);
+    mine = lane == r ? win : mine;
+    // the lane holding the winner drops it; every lane recomputes its best (no branches)
+    best = 0;
 #pragma unroll
     for (int i = 0; i < kPerLane; ++i) {
-      const int e = lane + 64 * i;
-      if (!(taken & (1u << i)) && e < E && (v[i] > bv || (v[i] == bv && e < bi))) {
-        bv = v[i];
-        bi = e;
-      }
-    }
-    wave_argmax(bv, bi);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (lane == r) {
-      my_v = bv;
-      my_i = bi;
+      key[i] = key[i] == win ? 0ull : key[i];
+      best = key[i] > best ? key[i] : best;
     }
   }
-  const float m = __shfl(my_v, 0, 64);
+  const int my_i = (int)~(uint32_t)mine;
+  const float my_v = f32_from_order_key((uint32_t)(mine >> 32));
+  // weights: softmax over the selected logits, denominator summed in selection order
+  const float m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(my_v)));
   const float ex = lane < k ? expf(my_v - m) : 0.f;
-  float s = 0.f;
-  for (int r = 0; r < k; ++r) s += __shfl(ex, r, 64);
+  float sum = 0.f;
+  for (int r = 0; r < k; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), r));
   if (lane < k) {
     ids_out[lane] = my_i;
-    w_out[lane] = ex / s;
+    w_out[lane] = ex / sum;
     if (lds_ids) lds_ids[lane] = my_i;
   }
 }
 
+template <int NPER>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                                int32_t* __restrict__ ids, float* __restrict__ w,
                                                int32_t* __restrict__ ctrl) {
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;
-  select_topk_wave(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, ctrl, nullptr);
+  select_topk_wave<NPER>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, ctrl, nullptr);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -372,15 +373,98 @@ __global__ __launch_bounds__(256) void k_router_gemv(RouteArgs a) {
   }
 }
 
+// Router GEMV on the matrix cores (bf16 router): one workgroup per 16 router rows, its 8 waves
+// split the H inputs and reduce through LDS.  A = activation rows (one per token; fp32 inputs as
+// bf16 hi + lo rows), B = 16 router rows, 32 inputs per v_mfma_f32_16x16x32_bf16 step; each lane
+// loads 16 contiguous bytes of its router row per step (the row's 4 lanes read 64 bytes).
+constexpr int kRouterWaves = 8;
+constexpr int kRouterMaxSteps = 4096 / 32 / kRouterWaves;  // H <= 4096
+
+MOE_DEV uint4 split_bf16_part(const float4& a, const float4& b, int part) {
+  const float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t q[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t hi = f32_to_bf16_rne(v[e]);
+    q[e] = part ? f32_to_bf16_rne(v[e] - __uint_as_float(hi << 16)) : hi;
+  }
+  return make_uint4(q[0] | (q[1] << 16), q[2] | (q[3] << 16), q[4] | (q[5] << 16), q[6] | (q[7] << 16));
+}
+
+template <bool X_BF16>
+__global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(RouteArgs a) {
+  __shared__ float red[kRouterWaves][16][16];  // [wave][A row][router row]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int T = a.T, E = a.E, H = a.H;
+  const int e0 = blockIdx.x * 16;
+  const int e = e0 + n;
+  const int NB = H / 32;
+  const int spw = (NB + kRouterWaves - 1) / kRouterWaves;  // 32-input steps per wave
+  const int b0 = wave * spw;
+  const int nb = min(spw, NB - b0);
+  const int rows = X_BF16 ? T : 2 * T;
+  const int m = n;  // A row of this lane
+  const bool live = m < rows;
+  const int tok = X_BF16 ? m : (m >> 1);
+  const uint16_t* wr = (const uint16_t*)a.Wr + (size_t)(e < E ? e : 0) * H + 8 * g;
+  uint4 wb[kRouterMaxSteps];
+  uint4 xa[X_BF16 ? kRouterMaxSteps : 1];
+#pragma unroll
+  for (int j = 0; j < kRouterMaxSteps; ++j) {
+    if (j < nb) {
+      if constexpr (X_BF16)
+        xa[j] = live ? *(const uint4*)((const uint16_t*)a.x + (size_t)tok * H + (b0 + j) * 32 + 8 * g)
+                     : make_uint4(0u, 0u, 0u, 0u);
+      wb[j] = e < E ? *(const uint4*)(wr + (size_t)(b0 + j) * 32) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  float4v acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kRouterMaxSteps; ++j) {
+    if (j < nb) {
+      uint4 av;
+      if constexpr (X_BF16) {
+        av = xa[j];
+      } else {
+        av = make_uint4(0u, 0u, 0u, 0u);
+        if (live) {
+          const float* xr = (const float*)a.x + (size_t)tok * H + (b0 + j) * 32 + 8 * g;
+          av = split_bf16_part(*(const float4*)xr, *(const float4*)(xr + 4), m & 1);
+        }
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, wb[j]),
+                                                    acc, 0, 0, 0);
+    }
+  }
+  // lane (g, n) holds A rows 4g + r of router row n
+#pragma unroll
+  for (int r = 0; r < 4; ++r) red[wave][4 * g + r][n] = acc[r];
+  __syncthreads();
+  if ((int)threadIdx.x < 16 * T) {
+    const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
+    const int ee = e0 + c;
+    if (ee < E) {
+      float sum = 0.f;
+      for (int w = 0; w < kRouterWaves; ++w) {
+        if constexpr (X_BF16) sum += red[w][t][c];
+        else sum += red[w][2 * t][c] + red[w][2 * t + 1][c];
+      }
+      a.logits[(size_t)t * E + ee] = sum + (a.bias ? a.bias[ee] : 0.f);
+    }
+  }
+}
+
 // One workgroup: the top-k of every token (one wave per token, DPP arg-max) and, if asked, the
 // decode plan (residency check, task list, miss list, doorbell).
-__global__ __launch_bounds__(256) void k_decode_select(RouteArgs a) {
+template <int NPER>
+__global__ __launch_bounds__(64 * kMaxDecodeTok) void k_decode_select(RouteArgs a) {
   __shared__ PlanShared sh;
   __shared__ int32_t s_ids[kMaxDecodeTok * kMaxK];
   const int wave = threadIdx.x >> 6;
   for (int t = wave; t < a.T; t += blockDim.x >> 6) {
-    select_topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k, a.ctrl,
-                     s_ids + t * a.k);
+    select_topk_wave<NPER>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k,
+                           a.ctrl, s_ids + t * a.k);
   }
   __syncthreads();
   if (a.plan)
@@ -393,7 +477,8 @@ __global__ __launch_bounds__(256) void k_decode_select(RouteArgs a) {
 hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w, int32_t* ctrl,
                        hipStream_t st) {
   const int grid = (T + 3) / 4;
-  k_topk<<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, ctrl);
+  if (E <= 512) k_topk<8><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, ctrl);
+  else k_topk<16><<<grid, 256, 0, st>>>(logits, T, E, k, ids, w, ctrl);
   return hipGetLastError();
 }
 
@@ -442,19 +527,24 @@ hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r
   a.miss_ids = miss_ids;
   a.tasks = tasks;
   a.bell = bell;
-  const int grid = (E + 3) / 4;
-  const uint32_t lds = (uint32_t)(T * H * sizeof(float));
   hipError_t err;
-  if (x_dtype == MOE_BF16 && r_dtype == MOE_BF16)
-    err = launch_timed(kTimeDecodeRoute, k_router_gemv<true, true>, grid, 256, lds, st, a);
-  else if (x_dtype == MOE_BF16)
-    err = launch_timed(kTimeDecodeRoute, k_router_gemv<true, false>, grid, 256, lds, st, a);
-  else if (r_dtype == MOE_BF16)
-    err = launch_timed(kTimeDecodeRoute, k_router_gemv<false, true>, grid, 256, lds, st, a);
-  else
-    err = launch_timed(kTimeDecodeRoute, k_router_gemv<false, false>, grid, 256, lds, st, a);
+  if (r_dtype == MOE_BF16) {
+    // bf16 router: matrix-core GEMV
+    const int grid = (E + 15) / 16;
+    if (x_dtype == MOE_BF16) err = launch_timed(kTimeDecodeRoute, k_router_mfma<true>, grid, 64 * kRouterWaves, 0, st, a);
+    else err = launch_timed(kTimeDecodeRoute, k_router_mfma<false>, grid, 64 * kRouterWaves, 0, st, a);
+  } else {
+    // fp32 router: exact fp32 FMA GEMV
+    const int grid = (E + 3) / 4;
+    const uint32_t lds = (uint32_t)(T * H * sizeof(float));
+    if (x_dtype == MOE_BF16) err = launch_timed(kTimeDecodeRoute, k_router_gemv<true, false>, grid, 256, lds, st, a);
+    else err = launch_timed(kTimeDecodeRoute, k_router_gemv<false, false>, grid, 256, lds, st, a);
+  }
   if (err != hipSuccess) return err;
-  k_decode_select<<<1, 256, 0, st>>>(a);
+  // one wave per token (at least 4 waves for the plan)
+  const int threads = 64 * (T > 4 ? T : 4);
+  if (E <= 512) k_decode_select<8><<<1, threads, 0, st>>>(a);
+  else k_decode_select<16><<<1, threads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -257,6 +257,35 @@ def expert_blobs_torch(keys, H: int, F: int, out, scale_sigma: float = 0.02):
     return out
 
 
+def expert_blobs_torch_batch(keys, H: int, F: int, out, scale_sigma: float = 0.02, batch: int = 64):
+    """:func:`expert_blobs_torch` for many keys at once (``batch`` blobs per pass); same bytes."""
+    import torch
+
+    nb, ns = _blob_counts(H, F)
+    dev = out.device
+    tt = torch.from_numpy(_halfnormal_fp16_table(float(scale_sigma))[0]).to(dev)
+    cc = torch.from_numpy(_halfnormal_fp16_table(float(scale_sigma))[1].astype(np.int32)).to(dev)
+    n_code_words = nb // 8
+    n_scale_words = (ns + 1) // 2
+    n_words = n_code_words + n_scale_words
+    idx = torch.arange(1, n_words + 1, dtype=torch.int64, device=dev) * _signed64(GOLDEN)
+    for b0 in range(0, len(keys), batch):
+        kk = torch.tensor([_signed64(k) for k in keys[b0:b0 + batch]], dtype=torch.int64, device=dev)
+        z = idx.unsqueeze(0) + kk.unsqueeze(1)
+        z = (z ^ _lsr_t(z, 30)) * _signed64(0xBF58476D1CE4E5B9)
+        z = (z ^ _lsr_t(z, 27)) * _signed64(0x94D049BB133111EB)
+        z = z ^ _lsr_t(z, 31)
+        rows = out[b0:b0 + len(kk)]
+        rows[:, :nb].copy_(z[:, :n_code_words].contiguous().view(torch.uint8))
+        w = z[:, n_code_words:]
+        u = torch.stack([w & 0xFFFFFFFF, _lsr_t(w, 32)], dim=2).reshape(len(kk), -1)[:, :ns]
+        sc = cc[torch.searchsorted(tt, u.contiguous(), right=True)]
+        sc = torch.where(sc >= 0x8000, sc - 0x10000, sc).to(torch.int16)
+        rows[:, nb:nb + 2 * ns].copy_(sc.view(torch.uint8).reshape(len(kk), 2 * ns))
+        del z, w, u, sc
+    return out
+
+
 def rank_permutation(seed: int, cfg: int, layer: int, topic: int, E: int) -> np.ndarray:
     """Popularity rank (1 = hottest) of each expert for one (layer, topic)."""
     g = np.random.Generator(np.random.PCG64(stream_key(seed, cfg, "rank", layer, topic)))

@@ -136,6 +136,24 @@ def test_layer_model_shape_decode(N, dev, model_layer, T):
     _layer_check(N, dev, model_layer, T, step=11 + T)
 
 
+def test_layer_batched_decode_zipf_layers(N, dev):
+    """The 48-layer batched decode's shape: 8 tokens per step through layers with their own
+    Zipf(1.1) router bias (popular experts shared by several tokens of a step), one step in each
+    of two layers."""
+    from mixture_experts_route_amd import synth as S
+
+    spec = dict(MODEL, cfg=3)
+    for layer_id in (0, 47):
+        layer = Layer(spec, dev, seed=0, layer=layer_id, bias_c=S.ZIPF_C)
+        x, x64 = layer.x(8, 0, dev)
+        ref = layer.oracle(x64)
+        # the step really shares experts between tokens (tasks of several tokens)
+        assert len(np.unique(ref["ids"])) < 8 * layer.k
+        _layer_check(N, dev, layer, 8, 0)
+        del layer
+        torch.cuda.empty_cache()
+
+
 def test_ffn_decode_entry_point(N, dev, model_layer):
     _layer_check(N, dev, model_layer, 3, step=2, via_layer=False)
 

@@ -77,3 +77,17 @@ def test_zipf_bias_gives_zipf_11_popularity():
     r = np.arange(5, 201)
     slope = np.polyfit(np.log(r), np.log(np.maximum(cnt[r - 1], 1)), 1)[0]
     assert -1.2 < slope < -1.0
+
+
+def test_batched_torch_blobs_equal_single():
+    import torch
+
+    H, F = 256, 128
+    keys = [S.stream_key(0, 3, "blob", 5, e) for e in range(5)]
+    stride = (S.blob_bytes(H, F) + 4095) // 4096 * 4096
+    a = torch.zeros((5, stride), dtype=torch.uint8)
+    b = torch.zeros((5, stride), dtype=torch.uint8)
+    S.expert_blobs_torch(keys, H, F, a)
+    S.expert_blobs_torch_batch(keys, H, F, b, batch=2)
+    assert torch.equal(a, b)
+    assert np.array_equal(b[3, :S.blob_bytes(H, F)].numpy(), S.expert_blob_np(keys[3], H, F))

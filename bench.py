@@ -126,6 +126,29 @@ def cpu_baseline_decode(n_tokens: int, seed=0, cfg=2, layer=0):
     return n_tokens / dt, dt
 
 
+def measured_traffic(path="profiles/decode1_gate_up_traffic.txt"):
+    """HBM bytes per launch of the decode gate/up kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy), or None once the kernel's sources
+    differ from the ones the counters were taken on."""
+    import hashlib
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    try:
+        fields = {}
+        for line in open(os.path.join(root, path)):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+        h = hashlib.sha256()
+        for f in fields["source_files"].split():
+            h.update(open(os.path.join(root, f), "rb").read())
+        if h.hexdigest() != fields["source_sha256"]:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def bench_decode1(args):
     import numpy as np
     import torch
@@ -239,7 +262,7 @@ def bench_decode1(args):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "bytes_per_launch": gu_bytes,
             "avg_launch_us": gu_avg_s * 1e6,
         },
@@ -495,12 +518,23 @@ def main():
     ap.add_argument("--prefill", default="4096", help="comma-separated prefill token counts to add ('' = none)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--decode48-steps", type=int, default=64, help="steps of the 48-layer batched decode (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the layer's data-parallel scale-out has no exchange on the path, "
               "so only --gpus 1 is run here", file=sys.stderr)
         sys.exit(2)
     res = bench_decode1(args)
+    if args.copy_calibration:
+        import torch
+
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(4):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        res["copy_calibration_bytes"] = 256 << 20
     if args.decode48_steps > 0:
         res["decode_8tok_48layers"] = bench_decode48(args.decode48_steps, 4, not args.eager)
     for T in [int(v) for v in args.prefill.split(",") if v.strip()]:

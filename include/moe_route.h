@@ -121,17 +121,23 @@ typedef struct moe_layer_weights {
 /* Miss notification for a slot pool served by the host (Betelgeuse article, "mechanism":
  * the in-stream check rings a host doorbell only on a miss).
  *   host_miss_ids    host-mapped pinned int32[E]: the step's miss list (ascending ids).
- *   host_miss_count  host-mapped pinned int32[2]: [0] = number of misses, [1] = epoch,
- *                    written after the list (the host polls [1] == epoch).
+ *   host_miss_count  host-mapped pinned int32[3]: [0] = number of misses, [2] = number of
+ *                    selections written to host_step_ids, [1] = epoch, written last (the
+ *                    host polls [1] == epoch, then reads the rest).
  *   ready            device-visible uint32 the stream waits on: work after the check
  *                    runs once *ready >= epoch.  With no miss the check kernel writes
  *                    *ready = epoch itself; otherwise the host writes it after the fills.
- *   epoch            this call's epoch (strictly increasing over calls). */
+ *   epoch            this call's epoch (strictly increasing over calls).
+ *   host_step_ids    optional host-mapped pinned int32[n_tokens * k] (or NULL): the step's
+ *                    selections in (token, choice) order, written by the decode path
+ *                    (<= MOE_DECODE_MAX_TOKENS tokens) before the epoch; a pool's
+ *                    recency policy needs the hits as well as the misses. */
 typedef struct moe_doorbell {
   int32_t* host_miss_ids;
   int32_t* host_miss_count;
   uint32_t* ready;
   uint32_t epoch;
+  int32_t* host_step_ids;
 } moe_doorbell;
 
 /* Bytes of one expert blob (layout above) for `dims`; 0 if dims are invalid. */
@@ -153,8 +159,8 @@ MOE_API int moe_workspace_init(void* ws, size_t ws_bytes, void* stream);
 MOE_API int moe_check_device_error(void* ws, void* stream, int32_t* bits_out);
 
 /* Profiling aid.  Until the next call, every launch of kernel `which` (1 = decode gate/up GEMV,
- * 2 = decode down GEMV (+ combine), 3 = prefill gate/up grouped GEMM, 4 = prefill down grouped
- * GEMM, 5 = decode route (router GEMV, top-k, residency check and plan); 0 = off) records the hipEvent_t `start_event` / `stop_event` (created by the caller with
+ * 2 = decode down GEMV, 3 = prefill gate/up grouped GEMM, 4 = prefill down grouped
+ * GEMM, 5 = decode router GEMV; 0 = off) records the hipEvent_t `start_event` / `stop_event` (created by the caller with
  * timing enabled) around that kernel alone, via hipExtLaunchKernel.  Process-wide setting,
  * not for concurrent use from several threads. */
 MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop_event);
@@ -230,6 +236,71 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w,
                               const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
                               int32_t* topk_ids_out_or_null, float* topk_w_out_or_null,
                               void* ws, size_t ws_bytes, void* stream);
+
+/* ---- Host service of a per-layer expert-slot pool (decode calls) ----------------------------
+ * Betelgeuse news article, section "mechanism: VRAM expert-slot pool, in-stream doorbell and
+ * victim cache": a layer keeps a fixed number of HBM slots, the in-stream check rings the host
+ * only on a miss, a miss is filled from host memory, and the HBM and host copies of an expert
+ * are exclusive.  Policy (the article names none): least recently used among the slots whose
+ * expert is not selected in the step, ties to the lower slot; misses placed in ascending id
+ * order; recency stamped per selection in (token, choice) order.
+ *
+ * Use per layer call: moe_pool_arm -> moe_layer_forward(..., table, &bell, ...) on the compute
+ * stream -> moe_pool_serve on the host (it blocks until the call's check has run, then
+ * enqueues the copies, the table update and the release of the compute stream on
+ * `copy_stream`).  Several layers' calls may be enqueued before their serves; serve them in
+ * the same order.  A pool is used from one host thread and one copy stream. */
+typedef struct moe_pool moe_pool;
+
+typedef struct moe_pool_stats {
+  int64_t calls;       /* served calls */
+  int64_t selections;  /* (token, choice) selections seen */
+  int64_t misses;      /* distinct misses filled */
+  int64_t bytes_h2d;   /* expert bytes copied host -> HBM */
+  int64_t bytes_d2h;   /* expert bytes copied HBM -> host (exclusive swap) */
+} moe_pool_stats;
+
+/* Creates the service for one layer.  All memory is the caller's and must outlive the pool:
+ *   arena, slot_stride, n_slots  device slots (as in moe_layer_weights), n_slots <= E;
+ *   table          device int32[E]: written here (slot of each expert, -1 elsewhere) and kept
+ *                  up to date by moe_pool_serve; pass it as the layer_table of the calls;
+ *   initial        host int32[n_slots]: the distinct expert held by each slot, hottest first
+ *                  (colder ones are evicted first); their blobs must already be in the slots;
+ *   host_home      host array [E] of pinned host pointers: the blob of every expert not in
+ *                  `initial`, NULL for those in it (the pool permutes these buffers);
+ *   spare          one pinned host buffer of a blob's size, holding no expert;
+ *   host_miss_ids  host-mapped pinned int32[E]; host_counts host-mapped pinned int32[3];
+ *   host_step_ids  host-mapped pinned int32[MOE_DECODE_MAX_TOKENS * k];
+ *   ready          device uint32 (set to 0 here).
+ * Copies the table and the ready word synchronously.  Returns MOE_EINVAL on inconsistent
+ * arguments (a slot holding an id out of range or twice, an expert with no or two homes). */
+MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_stride, int32_t n_slots,
+                            int32_t* table, const int32_t* initial, uint8_t* const* host_home, uint8_t* spare,
+                            int32_t* host_miss_ids, int32_t* host_counts, int32_t* host_step_ids,
+                            uint32_t* ready, moe_pool** pool_out);
+
+/* Frees the pool object (not the caller's memory). */
+MOE_API int moe_pool_destroy(moe_pool* pool);
+
+/* The doorbell of the pool's next call (next epoch).  MOE_EINVAL if the previous call was
+ * armed but not served. */
+MOE_API int moe_pool_arm(moe_pool* pool, moe_doorbell* bell_out);
+
+/* Serves the armed call: waits on the host until the check kernel has written the epoch
+ * (polling host memory, at most timeout_us microseconds if > 0), places every miss, and on
+ * copy_stream enqueues per miss a device->host copy of the victim and a host->device copy of
+ * the missed expert, then the table and *ready = epoch.  fills_out (host int32[E][3] or NULL)
+ * receives (expert, slot, evicted expert) per fill, n_fills_out their number.  On a timeout,
+ * a bad doorbell or a failed copy the compute stream is still released (*ready = epoch), the
+ * fill error bit is set in ws (when not NULL) and MOE_EFILL is returned. */
+MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, int32_t* fills_out,
+                           int32_t* n_fills_out, int64_t timeout_us);
+
+/* Counters since creation. */
+MOE_API int moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* out);
+
+/* The pool's current slot table (host int32[E]). */
+MOE_API int moe_pool_get_table(const moe_pool* pool, int32_t* table_out);
 
 #ifdef __cplusplus
 }

@@ -123,6 +123,7 @@ static DoorbellArgs bell_args(const moe_doorbell* b) {
     a.active = 1;
     a.host_miss_ids = b->host_miss_ids;
     a.host_miss_count = b->host_miss_count;
+    a.host_step_ids = b->host_step_ids;
     a.ready = b->ready;
     a.epoch = b->epoch;
   }

@@ -47,6 +47,7 @@ struct DoorbellArgs {
   int active;
   int32_t* host_miss_ids;
   int32_t* host_miss_count;
+  int32_t* host_step_ids;  // may be null
   uint32_t* ready;
   uint32_t epoch;
 };

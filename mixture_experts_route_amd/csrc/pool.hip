@@ -1,0 +1,236 @@
+// Host service of a per-layer expert-slot pool (decode path).
+//
+// Betelgeuse news article, section "mechanism: VRAM expert-slot pool, in-stream doorbell and
+// victim cache": each layer keeps a fixed number of HBM slots; the GPU-side check finds the
+// misses and rings the host only then; a miss is filled from host memory, and the HBM and host
+// copies of an expert are exclusive (the expert a fill displaces moves to the host).  The policy
+// is unnamed there; this service uses least-recently-used over slots not selected in the step,
+// ties to the lower slot, misses placed in ascending id order (the oracle's SlotPoolLRU).
+//
+// One call of the layer with this pool:
+//   moe_pool_arm      -> the doorbell for the next call (epoch + 1);
+//   moe_layer_forward -> enqueues route + check (the check kernel writes the miss list, the
+//                        step's selections and the epoch into host-mapped memory; with no miss it
+//                        also writes *ready = epoch), a stream wait on *ready >= epoch, the FFNs;
+//   moe_pool_serve    -> polls the epoch, places the misses, and on `copy_stream`: per miss one
+//                        device->host copy of the victim into the spare host buffer and one
+//                        host->device copy of the missing expert into the victim's slot, then the
+//                        updated slot table, then *ready = epoch.  The spare buffer and the filled
+//                        expert's old host buffer trade places (the exclusive swap).
+// The FFN kernels read the slot of a missed expert from the table when they run, after the wait.
+#include <atomic>
+#include <chrono>
+#include <cstring>
+#include <new>
+#include <thread>
+#include <vector>
+
+#include "kernels.hpp"
+
+namespace moe {
+__global__ void k_set_error_bits(int32_t* ctrl, int bits) {
+  if (threadIdx.x == 0) atomicOr(&ctrl[kCtrlError], bits);
+}
+}  // namespace moe
+
+using namespace moe;
+
+struct moe_pool {
+  int E = 0, k = 0;
+  int64_t blob_bytes = 0, stride = 0;
+  int n_slots = 0;
+  uint8_t* arena = nullptr;
+  int32_t* table_dev = nullptr;
+  int32_t* table_host = nullptr;  // pinned mirror, copied to table_dev after fills
+  std::vector<int32_t> holder;    // expert in each slot
+  std::vector<int64_t> last_use;  // recency stamp of each slot
+  int64_t clock = 0;
+  std::vector<uint8_t*> home;     // pinned host blob of every expert not in a slot
+  uint8_t* spare = nullptr;       // pinned host blob with no expert in it
+  int32_t* host_miss_ids = nullptr;
+  int32_t* host_counts = nullptr;
+  int32_t* host_step_ids = nullptr;
+  uint32_t* ready = nullptr;
+  uint32_t epoch = 0;
+  bool armed = false;
+  moe_pool_stats stats{};
+};
+
+static bool hip_ok(hipError_t e) { return e == hipSuccess; }
+
+extern "C" {
+
+MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_stride, int32_t n_slots, int32_t* table,
+                            const int32_t* initial, uint8_t* const* host_home, uint8_t* spare, int32_t* host_miss_ids,
+                            int32_t* host_counts, int32_t* host_step_ids, uint32_t* ready, moe_pool** pool_out) {
+  if (!pool_out) return MOE_EINVAL;
+  *pool_out = nullptr;
+  const size_t blob = moe_expert_blob_bytes(dims);
+  if (!blob) return MOE_EINVAL;
+  if (!arena || !table || !initial || !host_home || !spare || !host_miss_ids || !host_counts || !host_step_ids ||
+      !ready)
+    return MOE_EINVAL;
+  if (n_slots < 1 || n_slots > dims->n_experts || slot_stride < (int64_t)blob || slot_stride % 4096) return MOE_EINVAL;
+  const int E = dims->n_experts;
+  std::vector<int32_t> tab(E, -1);
+  for (int s = 0; s < n_slots; ++s) {
+    const int e = initial[s];
+    if (e < 0 || e >= E || tab[e] >= 0) return MOE_EINVAL;  // each slot holds a distinct expert
+    tab[e] = s;
+  }
+  for (int e = 0; e < E; ++e)
+    if ((tab[e] < 0) != (host_home[e] != nullptr)) return MOE_EINVAL;  // exactly one home per expert
+  moe_pool* p = new (std::nothrow) moe_pool();
+  if (!p) return MOE_EINVAL;
+  p->E = E;
+  p->k = dims->top_k;
+  p->blob_bytes = (int64_t)blob;
+  p->stride = slot_stride;
+  p->n_slots = n_slots;
+  p->arena = arena;
+  p->table_dev = table;
+  p->holder.assign(initial, initial + n_slots);
+  p->last_use.resize(n_slots);
+  for (int s = 0; s < n_slots; ++s) p->last_use[s] = -(int64_t)(s + 1);  // hottest first: colder evicted first
+  p->home.assign(host_home, host_home + E);
+  p->spare = spare;
+  p->host_miss_ids = host_miss_ids;
+  p->host_counts = host_counts;
+  p->host_step_ids = host_step_ids;
+  p->ready = ready;
+  if (!hip_ok(hipHostMalloc((void**)&p->table_host, sizeof(int32_t) * E, hipHostMallocDefault))) {
+    delete p;
+    return MOE_EHIP;
+  }
+  std::memcpy(p->table_host, tab.data(), sizeof(int32_t) * E);
+  const uint32_t zero = 0;
+  if (!hip_ok(hipMemcpy(table, p->table_host, sizeof(int32_t) * E, hipMemcpyHostToDevice)) ||
+      !hip_ok(hipMemcpy(ready, &zero, sizeof(zero), hipMemcpyHostToDevice))) {
+    (void)hipHostFree(p->table_host);
+    delete p;
+    return MOE_EHIP;
+  }
+  host_counts[1] = 0;
+  *pool_out = p;
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_destroy(moe_pool* pool) {
+  if (!pool) return MOE_EINVAL;
+  (void)hipHostFree(pool->table_host);
+  delete pool;
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_arm(moe_pool* pool, moe_doorbell* bell_out) {
+  if (!pool || !bell_out) return MOE_EINVAL;
+  if (pool->armed) return MOE_EINVAL;  // the previous call was not served
+  pool->epoch += 1;
+  pool->armed = true;
+  bell_out->host_miss_ids = pool->host_miss_ids;
+  bell_out->host_miss_count = pool->host_counts;
+  bell_out->ready = pool->ready;
+  bell_out->epoch = pool->epoch;
+  bell_out->host_step_ids = pool->host_step_ids;
+  return MOE_OK;
+}
+
+// Releases the waiting stream with the fill error flagged (and the table as it stands).
+static int release_with_error(moe_pool* p, void* ws, hipStream_t cs) {
+  if (ws) k_set_error_bits<<<1, 64, 0, cs>>>((int32_t*)ws, MOE_DERR_FILL);
+  (void)hipStreamWriteValue32(cs, p->ready, p->epoch, 0);
+  p->armed = false;
+  return MOE_EFILL;
+}
+
+MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, int32_t* fills_out,
+                           int32_t* n_fills_out, int64_t timeout_us) {
+  if (!pool || !pool->armed) return MOE_EINVAL;
+  moe_pool* p = pool;
+  hipStream_t cs = (hipStream_t)copy_stream;
+  if (n_fills_out) *n_fills_out = 0;
+  // wait for the check kernel's doorbell (the epoch is written after the lists)
+  volatile int32_t* counts = p->host_counts;
+  const auto t0 = std::chrono::steady_clock::now();
+  while ((uint32_t)counts[1] != p->epoch) {
+    if (timeout_us > 0 &&
+        std::chrono::duration_cast<std::chrono::microseconds>(std::chrono::steady_clock::now() - t0).count() >
+            timeout_us)
+      return release_with_error(p, ws_or_null, cs);
+    std::this_thread::yield();
+  }
+  std::atomic_thread_fence(std::memory_order_acquire);
+  const int n_miss = counts[0];
+  const int n_sel = counts[2];
+  if (n_miss < 0 || n_miss > p->E || n_sel < 0 || n_sel > kMaxDecodeTok * kMaxK)
+    return release_with_error(p, ws_or_null, cs);
+  std::vector<int32_t> miss(n_miss), sel(n_sel);
+  for (int i = 0; i < n_miss; ++i) miss[i] = ((volatile int32_t*)p->host_miss_ids)[i];
+  for (int i = 0; i < n_sel; ++i) sel[i] = ((volatile int32_t*)p->host_step_ids)[i];
+  std::vector<char> selected(p->E, 0);
+  for (int e : sel) {
+    if (e < 0 || e >= p->E) return release_with_error(p, ws_or_null, cs);
+    selected[e] = 1;
+  }
+  int n_fills = 0;
+  for (int e : miss) {
+    if (e < 0 || e >= p->E || p->table_host[e] >= 0 || !p->home[e]) return release_with_error(p, ws_or_null, cs);
+    selected[e] = 1;
+    // victim: the least recently used slot whose expert is not selected in this step
+    int best = -1;
+    for (int s = 0; s < p->n_slots; ++s) {
+      if (selected[p->holder[s]]) continue;
+      if (best < 0 || p->last_use[s] < p->last_use[best]) best = s;
+    }
+    if (best < 0) return release_with_error(p, ws_or_null, cs);  // fewer slots than the step's experts
+    const int old = p->holder[best];
+    uint8_t* slot = p->arena + (int64_t)best * p->stride;
+    // exclusive swap: the victim goes to the spare host buffer, the missing expert to the slot
+    if (!hip_ok(hipMemcpyAsync(p->spare, slot, p->blob_bytes, hipMemcpyDeviceToHost, cs)) ||
+        !hip_ok(hipMemcpyAsync(slot, p->home[e], p->blob_bytes, hipMemcpyHostToDevice, cs)))
+      return release_with_error(p, ws_or_null, cs);
+    p->home[old] = p->spare;
+    p->spare = p->home[e];
+    p->home[e] = nullptr;
+    p->table_host[old] = -1;
+    p->table_host[e] = best;
+    p->holder[best] = e;
+    if (fills_out) {
+      fills_out[3 * n_fills + 0] = e;
+      fills_out[3 * n_fills + 1] = best;
+      fills_out[3 * n_fills + 2] = old;
+    }
+    ++n_fills;
+    p->stats.bytes_h2d += p->blob_bytes;
+    p->stats.bytes_d2h += p->blob_bytes;
+  }
+  if (n_miss > 0) {
+    if (!hip_ok(hipMemcpyAsync(p->table_dev, p->table_host, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, cs)) ||
+        !hip_ok(hipStreamWriteValue32(cs, p->ready, p->epoch, 0)))
+      return release_with_error(p, ws_or_null, cs);
+  }
+  // recency: every selection of the step, in (token, choice) order
+  for (int e : sel) p->last_use[p->table_host[e]] = ++p->clock;
+  if (n_sel == 0)
+    for (int i = 0; i < n_miss; ++i) p->last_use[p->table_host[miss[i]]] = ++p->clock;
+  p->stats.calls += 1;
+  p->stats.selections += n_sel;
+  p->stats.misses += n_miss;
+  if (n_fills_out) *n_fills_out = n_fills;
+  p->armed = false;
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* out) {
+  if (!pool || !out) return MOE_EINVAL;
+  *out = pool->stats;
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_get_table(const moe_pool* pool, int32_t* table_out) {
+  if (!pool || !table_out) return MOE_EINVAL;
+  std::memcpy(table_out, pool->table_host, sizeof(int32_t) * pool->E);
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -107,15 +107,21 @@ MOE_DEV int block_exclusive_scan(int v, int* lds_wave_sums, int* total) {
 // Doorbell: publish the miss list to host-mapped memory, then the count, then the epoch;
 // with no miss, release the stream's wait directly.
 // ------------------------------------------------------------------------------------------
-MOE_DEV void ring_doorbell(const DoorbellArgs& bell, const int32_t* miss_ids, int n_miss) {
+MOE_DEV void ring_doorbell(const DoorbellArgs& bell, const int32_t* miss_ids, int n_miss, const int32_t* step_ids,
+                           int n_sel) {
   if (!bell.active) return;
   volatile int32_t* hids = bell.host_miss_ids;
   for (int i = threadIdx.x; i < n_miss; i += blockDim.x) hids[i] = miss_ids[i];
+  if (bell.host_step_ids && step_ids) {
+    volatile int32_t* hs = bell.host_step_ids;
+    for (int i = threadIdx.x; i < n_sel; i += blockDim.x) hs[i] = step_ids[i];
+  }
   __threadfence_system();
   __syncthreads();
   if (threadIdx.x == 0) {
     volatile int32_t* hcnt = bell.host_miss_count;
     hcnt[0] = n_miss;
+    hcnt[2] = (bell.host_step_ids && step_ids) ? n_sel : 0;
     __threadfence_system();
     hcnt[1] = (int32_t)bell.epoch;
     __threadfence_system();
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
   if (bell.active) {
     __threadfence();
     __syncthreads();
-    ring_doorbell(bell, miss_ids, total);
+    ring_doorbell(bell, miss_ids, total, nullptr, 0);
   }
 }
 
@@ -268,7 +274,7 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     // back every XCD's L2).
     __threadfence();
     __syncthreads();
-    ring_doorbell(bell, miss_ids, n_miss);
+    ring_doorbell(bell, miss_ids, n_miss, ids, T * k);
   }
 }
 

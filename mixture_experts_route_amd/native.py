@@ -30,6 +30,8 @@ EXPORTS = [
     "moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_workspace_init",
     "moe_check_device_error", "moe_debug_kernel_events", "moe_debug_dequant", "moe_route", "moe_slot_lookup", "moe_group_tokens",
     "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "moe_layer_forward",
+    "moe_pool_create", "moe_pool_destroy", "moe_pool_arm", "moe_pool_serve", "moe_pool_get_stats",
+    "moe_pool_get_table",
 ]
 
 
@@ -46,7 +48,12 @@ class moe_layer_weights(ctypes.Structure):
 
 class moe_doorbell(ctypes.Structure):
     _fields_ = [("host_miss_ids", ctypes.c_void_p), ("host_miss_count", ctypes.c_void_p),
-                ("ready", ctypes.c_void_p), ("epoch", ctypes.c_uint32)]
+                ("ready", ctypes.c_void_p), ("epoch", ctypes.c_uint32), ("host_step_ids", ctypes.c_void_p)]
+
+
+class moe_pool_stats(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_int64), ("selections", ctypes.c_int64), ("misses", ctypes.c_int64),
+                ("bytes_h2d", ctypes.c_int64), ("bytes_d2h", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):
@@ -61,6 +68,7 @@ _SZ = ctypes.c_size_t
 _D = ctypes.POINTER(moe_dims)
 _W = ctypes.POINTER(moe_layer_weights)
 _B = ctypes.POINTER(moe_doorbell)
+_PP = ctypes.POINTER(ctypes.c_void_p)
 
 _sig = {
     "moe_expert_blob_bytes": (_SZ, [_D]),
@@ -76,6 +84,12 @@ _sig = {
     "moe_expert_ffn_decode": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn_prefill": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward": (ctypes.c_int, [_D, _W, _P, _B, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_pool_create": (ctypes.c_int, [_D, _P, ctypes.c_int64, _I, _P, _P, _PP, _P, _P, _P, _P, _P, _PP]),
+    "moe_pool_destroy": (ctypes.c_int, [_P]),
+    "moe_pool_arm": (ctypes.c_int, [_P, _B]),
+    "moe_pool_serve": (ctypes.c_int, [_P, _P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64]),
+    "moe_pool_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(moe_pool_stats)]),
+    "moe_pool_get_table": (ctypes.c_int, [_P, _P]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -209,3 +223,108 @@ def moe_layer_forward(d: moe_dims, w: moe_layer_weights, table, x, n_tokens: int
 def raw(name: str):
     """The raw ctypes function (for tests of the C-level validation)."""
     return getattr(_lib, name)
+
+
+# ---------------------------------------------------------------------------------------------
+# slot-pool service (host side)
+# ---------------------------------------------------------------------------------------------
+
+def _hiprt():
+    lib = ctypes.CDLL("libamdhip64.so.7")
+    lib.hipHostMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t, ctypes.c_uint]
+    lib.hipHostFree.argtypes = [ctypes.c_void_p]
+    lib.hipStreamCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+    lib.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def new_stream():
+    """A fresh non-blocking HIP stream at the default priority, as a torch stream object.
+
+    A pool's compute stream waits (in-stream) for a value its copy stream writes; the two must
+    not share a hardware queue, so they are created here rather than taken from torch's stream
+    pool (whose streams share the few hardware queues round-robin).  Free with free_stream."""
+    s = ctypes.c_void_p()
+    rc = _hiprt().hipStreamCreateWithFlags(ctypes.byref(s), 0x1)
+    if rc != 0:
+        raise MoeError(MOE_EHIP, f"hipStreamCreateWithFlags = {rc}")
+    return torch.cuda.ExternalStream(s.value)
+
+
+def free_stream(stream):
+    torch.cuda.synchronize()
+    _hiprt().hipStreamDestroy(stream.cuda_stream)
+
+
+HIP_HOST_MALLOC_MAPPED, HIP_HOST_MALLOC_COHERENT = 0x2, 0x40000000
+
+
+class HostBuffer:
+    """Pinned, device-mapped, coherent host memory (for doorbell words the GPU writes and the
+    host polls).  ``.ptr`` is the address both sides use; ``.view(dtype)`` a numpy view."""
+
+    def __init__(self, nbytes: int):
+        import numpy as np
+
+        self._hip = _hiprt()
+        p = ctypes.c_void_p()
+        rc = self._hip.hipHostMalloc(ctypes.byref(p), nbytes, HIP_HOST_MALLOC_MAPPED | HIP_HOST_MALLOC_COHERENT)
+        if rc != 0:
+            raise MoeError(MOE_EHIP, f"hipHostMalloc({nbytes}) = {rc}")
+        self.ptr, self.nbytes = p.value, nbytes
+        self._np = np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(self.ptr))
+        self._np[:] = 0
+
+    def view(self, dtype):
+        return self._np.view(dtype)
+
+    def free(self):
+        if self.ptr:
+            self._hip.hipHostFree(self.ptr)
+            self.ptr = 0
+
+
+def moe_pool_create(d: moe_dims, arena, slot_stride: int, n_slots: int, table, initial, host_home, spare,
+                    host_miss_ids: int, host_counts: int, host_step_ids: int, ready):
+    """Returns the pool handle (int).  ``initial``: sequence of n_slots expert ids; ``host_home``:
+    sequence of E addresses (0 for experts in ``initial``); other pointers as in the header."""
+    init = (ctypes.c_int32 * n_slots)(*[int(e) for e in initial])
+    homes = (ctypes.c_void_p * len(host_home))(*[int(a) if a else None for a in host_home])
+    out = ctypes.c_void_p()
+    _check(_lib.moe_pool_create(ctypes.byref(d), _ptr(arena), int(slot_stride), int(n_slots), _ptr(table), init,
+                                homes, _ptr(spare), host_miss_ids, host_counts, host_step_ids, _ptr(ready),
+                                ctypes.byref(out)), "moe_pool_create")
+    return out.value
+
+
+def moe_pool_destroy(pool: int):
+    _check(_lib.moe_pool_destroy(pool), "moe_pool_destroy")
+
+
+def moe_pool_arm(pool: int) -> moe_doorbell:
+    bell = moe_doorbell()
+    _check(_lib.moe_pool_arm(pool, ctypes.byref(bell)), "moe_pool_arm")
+    return bell
+
+
+def moe_pool_serve(pool: int, ws=None, copy_stream=None, n_experts: int = 0, timeout_us: int = 20_000_000):
+    """Serves the armed call; returns the fills [(expert, slot, evicted)].  Raises on MOE_EFILL."""
+    fills = (ctypes.c_int32 * (3 * max(1, n_experts)))()
+    n = ctypes.c_int32()
+    _check(_lib.moe_pool_serve(pool, _ptr(ws), _stream(copy_stream), fills if n_experts else None, ctypes.byref(n),
+                               int(timeout_us)), "moe_pool_serve")
+    return [(fills[3 * i], fills[3 * i + 1], fills[3 * i + 2]) for i in range(n.value)] if n_experts else n.value
+
+
+def moe_pool_get_stats(pool: int) -> moe_pool_stats:
+    st = moe_pool_stats()
+    _check(_lib.moe_pool_get_stats(pool, ctypes.byref(st)), "moe_pool_get_stats")
+    return st
+
+
+def moe_pool_get_table(pool: int, n_experts: int):
+    import numpy as np
+
+    out = np.zeros(n_experts, dtype=np.int32)
+    _check(_lib.moe_pool_get_table(pool, out.ctypes.data), "moe_pool_get_table")
+    return out

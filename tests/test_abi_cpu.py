@@ -102,3 +102,28 @@ def test_strerror(N):
     for c in range(-6, 1):
         assert isinstance(N.strerror(c), str) and N.strerror(c)
     assert N.strerror(42) == "unknown status code"
+
+
+def test_pool_create_rejects_inconsistent_residency(N):
+    """The host pool service refuses, before touching any memory, a slot list with a repeated or
+    out-of-range expert and an expert with no host home or with two homes (exclusive tiers)."""
+    d = N.dims(2048, 768, 512, 10, 1)
+    stride = 648 * 4096
+    fake = 1 << 30  # never dereferenced: every case fails validation first
+
+    def create(initial, homes):
+        init = (ctypes.c_int32 * len(initial))(*initial)
+        hh = (ctypes.c_void_p * 512)(*[h if h else None for h in homes])
+        out = ctypes.c_void_p()
+        return N.raw("moe_pool_create")(ctypes.byref(d), fake, stride, len(initial), fake, init, hh, fake, fake,
+                                        fake, fake, fake, ctypes.byref(out))
+
+    homes = [0 if e < 4 else fake + 4096 * e for e in range(512)]
+    assert create([0, 1, 2, 2], homes) == -1            # expert 2 in two slots
+    assert create([0, 1, 2, 600], homes) == -1          # id out of range
+    assert create([0, 1, 2, 3], [0] * 512) == -1        # experts 4.. have no home
+    both = list(homes)
+    both[0] = fake
+    assert create([0, 1, 2, 3], both) == -1             # expert 0 in a slot and on the host
+    assert N.raw("moe_pool_arm")(None, None) == -1
+    assert N.raw("moe_pool_serve")(None, None, None, None, None, 0) == -1

@@ -506,6 +506,127 @@ def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
     }
 
 
+def pool_slots(layer: int) -> int:
+    """HBM slots of a layer in the slot-pool workload: 240 / 92 / 60 for early / middle / late
+    layers (10 x 240 + 10 x 92 + 28 x 60 = 5,000)."""
+    return 240 if layer < 10 else 92 if layer < 20 else 60
+
+
+def bench_pool(steps: int, topic_every: int = 128, n_layers: int = 48):
+    """Single-token decode through 48 layers whose experts live in 5,000 HBM slots and pinned host
+    memory (exclusive tiers); per-layer Zipf(1.1) bias redrawn every `topic_every` steps; misses
+    filled from the host by the pool service on a copy stream."""
+    import numpy as np
+    import torch
+
+    from mixture_experts_route_amd import native as N
+    from mixture_experts_route_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    cfg, T = 5, 1
+    stride = (S.blob_bytes(H, F) + 4095) // 4096 * 4096
+    blob = S.blob_bytes(H, F)
+    d = N.dims(H, F, E, K_TOP, 1)
+    n_topics = (steps + 2 + topic_every - 1) // topic_every + 1
+    layers = []
+    tmp = torch.empty((E, stride), dtype=torch.uint8, device=dev)
+    for layer in range(n_layers):
+        keys = [S.stream_key(0, cfg, "blob", layer, e) for e in range(E)]
+        S.expert_blobs_torch_batch(keys, H, F, tmp)
+        ranks = [S.rank_permutation(0, cfg, layer, t, E) for t in range(n_topics)]
+        n_slots = pool_slots(layer)
+        initial = [int(e) for e in np.argsort(ranks[0], kind="stable")[:n_slots]]
+        arena = tmp[torch.as_tensor(initial, device=dev, dtype=torch.long)].contiguous()
+        away = [e for e in range(E) if e not in set(initial)]
+        homes = N.HostBuffer((len(away) + 1) * stride, flags=0)
+        hv = torch.from_numpy(homes.view(np.uint8)).view(len(away) + 1, stride)
+        hv[:len(away)].copy_(tmp[torch.as_tensor(away, device=dev, dtype=torch.long)])
+        home_addr = [0] * E
+        for i, e in enumerate(away):
+            home_addr[e] = homes.ptr + i * stride
+        shared = torch.empty((stride,), dtype=torch.uint8, device=dev)
+        S.expert_blobs_torch([S.stream_key(0, cfg, "shared", layer, 0)], H, F, shared.view(1, -1))
+        router = S.bf16_normal_torch(S.stream_key(0, cfg, "router", layer, 0), (E, H), 0.02, dev)
+        biases = [torch.from_numpy(S.zipf_bias(r, S.ZIPF_C)).to(dev) for r in ranks]
+        table = torch.full((E,), -1, dtype=torch.int32, device=dev)
+        ready = torch.zeros((64,), dtype=torch.int32, device=dev)
+        hb = [N.HostBuffer(4 * E), N.HostBuffer(64), N.HostBuffer(4 * 8 * K_TOP)]
+        pool = N.moe_pool_create(d, arena, stride, n_slots, table, initial, home_addr, homes.ptr + len(away) * stride,
+                                 hb[0].ptr, hb[1].ptr, hb[2].ptr, ready)
+        layers.append(dict(arena=arena, homes=homes, shared=shared, router=router, biases=biases, table=table,
+                           ready=ready, hb=hb, pool=pool, n_slots=n_slots))
+    del tmp
+    torch.cuda.empty_cache()
+    xs = [S.bf16_normal_torch(S.stream_key(0, cfg, "x", layer, X_STREAM), (steps + 2, H), 1.0, dev)
+          for layer in range(n_layers)]
+    y = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(N.moe_workspace_bytes(d, T) // 4 + 64, dtype=torch.int32, device=dev)
+    N.moe_workspace_init(ws)
+    compute, copy = N.new_stream(), N.new_stream()
+
+    def step(s):
+        topic = s // topic_every
+        for layer, L in enumerate(layers):
+            bell = N.moe_pool_arm(L["pool"])
+            w = N.layer_weights(L["router"], L["arena"], stride, L["n_slots"], L["shared"], L["biases"][topic])
+            N.moe_layer_forward(d, w, L["table"], xs[layer][s:s + 1], T, y, ws, bell=bell, stream=compute)
+        for L in layers:
+            N.moe_pool_serve(L["pool"], ws, copy)
+
+    torch.cuda.synchronize()
+    for s in range(2):
+        step(s)
+    compute.synchronize()
+    st0 = [N.moe_pool_get_stats(L["pool"]) for L in layers]
+    t0 = time.perf_counter()
+    for s in range(2, steps + 2):
+        step(s)
+    compute.synchronize()
+    copy.synchronize()
+    t1 = time.perf_counter()
+    assert N.moe_check_device_error(ws) == 0
+    st1 = [N.moe_pool_get_stats(L["pool"]) for L in layers]
+    sel = sum(b.selections - a.selections for a, b in zip(st0, st1))
+    mis = sum(b.misses - a.misses for a, b in zip(st0, st1))
+    h2d = sum(b.bytes_h2d - a.bytes_h2d for a, b in zip(st0, st1))
+    d2h = sum(b.bytes_d2h - a.bytes_d2h for a, b in zip(st0, st1))
+    # pinned host <-> HBM copy rate for one expert blob, same process (the fills' bound)
+    hb = N.HostBuffer(blob * 8, flags=0)
+    dbuf = torch.empty((blob * 8,), dtype=torch.uint8, device=dev)
+    hip = N._hiprt()
+    hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    rates = {}
+    for kind, name in ((1, "h2d"), (2, "d2h")):
+        torch.cuda.synchronize()
+        c0 = time.perf_counter()
+        for rep in range(8):
+            dst = dbuf.data_ptr() + rep * blob if kind == 1 else hb.ptr + rep * blob
+            src = hb.ptr + rep * blob if kind == 1 else dbuf.data_ptr() + rep * blob
+            hip.hipMemcpyAsync(dst, src, blob, kind, copy.cuda_stream)
+        copy.synchronize()
+        rates[name] = 8 * blob / (time.perf_counter() - c0) / 1e9
+    hb.free()
+    for L in layers:
+        N.moe_pool_destroy(L["pool"])
+    N.free_stream(compute)
+    N.free_stream(copy)
+    elapsed = t1 - t0
+    return {
+        "workload": "single-token decode through 48 layers with 5,000 HBM expert slots (240 / 92 / 60 per early / "
+                    "middle / late layer) and the other 19,576 experts in pinned host memory (exclusive tiers); "
+                    f"per-layer Zipf(1.1) router bias with a topic shift every {topic_every} steps; misses filled "
+                    "by the host pool service on a copy stream while the compute stream waits in-stream",
+        "tokens_per_s": steps / elapsed,
+        "ms_per_token": elapsed * 1e3 / steps,
+        "steps": steps,
+        "hit_rate": 1.0 - mis / max(1, sel),
+        "misses_per_token": mis / steps,
+        "pcie_mib_per_token": (h2d + d2h) / steps / 2**20,
+        "pcie_rate_gbs_per_blob_copy": rates,
+        "fill_time_bound_ms_per_token": (h2d / rates["h2d"] + d2h / rates["d2h"]) / 1e6 / steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -518,6 +639,7 @@ def main():
     ap.add_argument("--prefill", default="4096", help="comma-separated prefill token counts to add ('' = none)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--decode48-steps", type=int, default=64, help="steps of the 48-layer batched decode (0 = skip)")
+    ap.add_argument("--pool-steps", type=int, default=512, help="steps of the slot-pool decode workload (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
@@ -537,6 +659,11 @@ def main():
         res["copy_calibration_bytes"] = 256 << 20
     if args.decode48_steps > 0:
         res["decode_8tok_48layers"] = bench_decode48(args.decode48_steps, 4, not args.eager)
+        import torch
+
+        torch.cuda.empty_cache()
+    if args.pool_steps > 0:
+        res["decode_slot_pool_48layers"] = bench_pool(args.pool_steps)
     for T in [int(v) for v in args.prefill.split(",") if v.strip()]:
         steps = args.prefill_steps if T <= 8192 else max(4, args.prefill_steps // 4)
         sample = None if args.no_cpu_baseline else (48 if T == 4096 else None)

@@ -260,20 +260,22 @@ HIP_HOST_MALLOC_MAPPED, HIP_HOST_MALLOC_COHERENT = 0x2, 0x40000000
 
 
 class HostBuffer:
-    """Pinned, device-mapped, coherent host memory (for doorbell words the GPU writes and the
-    host polls).  ``.ptr`` is the address both sides use; ``.view(dtype)`` a numpy view."""
+    """Pinned host memory: by default device-mapped and coherent (for doorbell words the GPU
+    writes and the host polls); ``flags=0`` for bulk copy buffers.  ``.ptr`` is the address both
+    sides use; ``.view(dtype)`` a numpy view."""
 
-    def __init__(self, nbytes: int):
+    def __init__(self, nbytes: int, flags: int = HIP_HOST_MALLOC_MAPPED | HIP_HOST_MALLOC_COHERENT):
         import numpy as np
 
         self._hip = _hiprt()
         p = ctypes.c_void_p()
-        rc = self._hip.hipHostMalloc(ctypes.byref(p), nbytes, HIP_HOST_MALLOC_MAPPED | HIP_HOST_MALLOC_COHERENT)
+        rc = self._hip.hipHostMalloc(ctypes.byref(p), nbytes, flags)
         if rc != 0:
             raise MoeError(MOE_EHIP, f"hipHostMalloc({nbytes}) = {rc}")
         self.ptr, self.nbytes = p.value, nbytes
         self._np = np.ctypeslib.as_array((ctypes.c_uint8 * nbytes).from_address(self.ptr))
-        self._np[:] = 0
+        if flags & HIP_HOST_MALLOC_COHERENT:
+            self._np[:] = 0
 
     def view(self, dtype):
         return self._np.view(dtype)

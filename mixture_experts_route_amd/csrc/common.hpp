@@ -56,6 +56,8 @@ __host__ __device__ inline BlobLayout blob_layout(int H, int F) {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // Code words of a 4-bit matrix of R rows: every row is split into groups of 128 elements (4
@@ -68,6 +70,12 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 constexpr int kGroupElems = 128;
 constexpr int kGroupBytes = 64;
 constexpr int kGroupScaleBytes = 8;
+
+// Asynchronous global -> LDS copy of 16 bytes per active lane: lane l's bytes land at
+// lds_base + 16 l (lds_base wave-uniform).  Counted by vmcnt like any vector load.
+MOE_DEV void lds_dma16(const void* gsrc, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
 
 // ---------------------------------------------------------------------------------------
 // Small numeric helpers

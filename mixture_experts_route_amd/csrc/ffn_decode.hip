@@ -28,13 +28,24 @@
 //     pairs of the task's tokens (<= 8 tokens -> <= 16 rows), so one MFMA per block covers both
 //     parts.  Writes each pair's output row y_e.
 //   combine: y[t] = sum_j w[t][j] * y_{e_j}[t] (j = 0..k-1), then + y_shared[t]: fixed order.
+#include <utility>
+
 #include "kernels.hpp"
 
 namespace moe {
 
-constexpr int kGuQuadsPerWave = 4;                                   // groups of 128 inputs per wave
-constexpr int kMaxGuWaves = 4096 / (kGroupElems * kGuQuadsPerWave);  // H <= 4096
-constexpr int kDnQuadsPerPass = 6;                                   // down: groups per load batch
+constexpr int kGuQuadsPerWave = 4;  // gate/up: groups of 128 inputs per wave
+constexpr int kGuRG = 2;            // gate/up: row groups of 16 per workgroup
+constexpr int kDnQuadsPerPass = 6;  // down: groups per load batch
+constexpr int kDnWaves = 8;         // down: waves per workgroup
+// down: row groups of 16 per wave (more output rows per staged activation tile when the tasks
+// carry more tokens)
+template <int MAXTOK>
+constexpr int kDnRGW = MAXTOK >= 4 ? 2 : 1;
+// down: h chunks (16 bytes) per thread held in registers while staging; sized so that F <= 1536
+// needs no second pass
+template <int MAXTOK>
+constexpr int kDnStageChunks = (2 * MAXTOK * (1536 / 8) + 64 * kDnWaves - 1) / (64 * kDnWaves);
 constexpr uint32_t kMagicPair = 0x43004300u;                         // bf16 pair (128, 128)
 constexpr uint32_t kNeg136Pair = 0xC308C308u;                        // bf16 pair (-136, -136)
 
@@ -48,8 +59,29 @@ MOE_DEV const uint8_t* task_blob(const ExpertSource& s, const DecodeTask& tk) {
   return s.arena + (int64_t)slot * s.slot_stride;
 }
 
+// The two constants of the code unpacking, held in registers (the nibble mask in a scalar register,
+// the bf16 pair (128, 128) in a vector register) so that each output register is one
+// v_and_or_b32 (plus a shift): with literal operands the compiler splits it into an and and an or.
+struct Unpack {
+  uint32_t mask, magic;
+};
+MOE_DEV Unpack make_unpack() {
+  Unpack u;
+  asm("s_mov_b32 %0, 0xf000f" : "=s"(u.mask));
+  asm("v_mov_b32 %0, 0x43004300" : "=v"(u.magic));
+  return u;
+}
+
 // One code word (8 elements of a slice) -> B operand: 8 bf16 values q + 136 = 128 + u.  Pair j of
 // the word (its elements 2j and 2j+1 in bits 4j and 16 + 4j) becomes register j.
+MOE_DEV bf16x8 codes_q136(uint32_t w, const Unpack& k) {
+  uint4 p;
+  p.x = (w & k.mask) | k.magic;
+  p.y = ((w >> 4) & k.mask) | k.magic;
+  p.z = ((w >> 8) & k.mask) | k.magic;
+  p.w = ((w >> 12) & k.mask) | k.magic;
+  return __builtin_bit_cast(bf16x8, p);
+}
 MOE_DEV bf16x8 codes_q136(uint32_t w) {
   uint4 p;
   p.x = (w & 0x000F000Fu) | kMagicPair;
@@ -65,11 +97,29 @@ MOE_DEV bf16x8 const_neg136() {
 }
 
 MOE_DEV uint32_t word_at(const uint4& c, int i) { return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w; }
+MOE_DEV uint32_t word_at(const u32x4& c, int i) { return c[i]; }
 
 // fp16 scale i (0..3) of a group's four block scales.
 MOE_DEV float scale_at(const uint2& s, int i) {
   const uint32_t w = i < 2 ? s.x : s.y;
   return fp16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+MOE_DEV float scale_at(const u32x2& s, int i) {
+  const uint32_t w = s[i >> 1];
+  return fp16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xFFFFu));
+}
+
+// A blob as a buffer resource: loads take a per-lane 32-bit offset and a wave-uniform one, so a
+// wave's addresses cost one register instead of a 64-bit pointer per load; reads past `bytes`
+// return zero.  Word 3 = 0x00020000: 32-bit data format, the value raw loads need on this family.
+MOE_DEV __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t* blob, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)blob, 0, (int)bytes, 0x00020000);
+}
+MOE_DEV u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+MOE_DEV u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
 }
 
 // Token of slot m of a task: the m-th set bit of its token mask (m < popcount(mask)).
@@ -121,17 +171,91 @@ struct DecodeArgs {
   const float* topk_w;  // [T][k]
   float* y;             // [T][H]
   int H, F, T, k, n_shared;
-  int tiles_gu;  // F / 16
-  int tiles_dn;  // H / 64
+  int tiles_gu;  // workgroups per task, gate/up
+  int tiles_dn;  // workgroups per task, down
 };
 
-// ---- gate/up: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for one task and 16 rows r --------
-// A rows: token slot m of the task (bf16 x) or 2 m + part (fp32 x).  ROWS <= 16.
+// ---- activation rows in LDS -----------------------------------------------------------------
+// A task's A-operand rows (bf16) are copied once per workgroup into LDS, row m at m * (K + 8)
+// elements: the 16-byte pad puts the 16 rows an MFMA fragment reads into 16 different bank
+// groups.  Each thread loads its chunks (8 elements, 16 bytes) into registers before the weight
+// loads are issued and writes them to LDS after: waiting for these loads (loads complete in order)
+// then leaves the weight loads in flight.  (LDS DMA would save the registers, but the compiler
+// cannot tell which outstanding load wrote LDS and waits for all of them before any LDS read.)
+MOE_DEV int lds_row_stride(int K) { return K + 8; }
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>): indexes into a register array
+// that are constants from the start, so the array never lives in scratch memory.
+template <typename Fn, int... I>
+MOE_DEV void static_for_impl(Fn&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+MOE_DEV void static_for(Fn&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Chunk c of this thread: index threadIdx.x + c * blockDim.x over rows * K / 8 chunks; row m,
+// column col.
+MOE_DEV void chunk_pos(int idx, int K, int& m, int& col) {
+  m = idx / (K / 8);
+  col = (idx - m * (K / 8)) * 8;
+}
+
+// Loads this thread's first MAXC chunks (clamped: no load under a branch).  Row m of the staged
+// operand comes from src_row(m) (K bf16 elements).
+template <int MAXC, typename SrcRow>
+MOE_DEV void stage_load(u32x4 (&v)[MAXC], int rows, int K, SrcRow src_row) {
+  const int n_chunks = rows * (K / 8);
+  static_for<MAXC>([&](auto c) {
+    const int idx = min((int)(threadIdx.x + c.value * blockDim.x), n_chunks - 1);
+    int m, col;
+    chunk_pos(idx, K, m, col);
+    v[c.value] = *(const u32x4*)(src_row(m) + col);
+  });
+  __builtin_amdgcn_sched_barrier(0);  // these loads go out before the weight loads
+}
+
+// Writes the chunks to LDS (with MAY_OVERFLOW, any beyond MAXC per thread are copied directly), then a plain
+// workgroup barrier (__syncthreads would also wait for every weight load still in flight).
+template <bool MAY_OVERFLOW, int MAXC, typename SrcRow>
+MOE_DEV void stage_store_sync(const u32x4 (&v)[MAXC], uint16_t* lds, int rows, int K, SrcRow src_row) {
+  const int n_chunks = rows * (K / 8);
+  static_for<MAXC>([&](auto c) {
+    const int idx = threadIdx.x + c.value * blockDim.x;
+    int m, col;
+    chunk_pos(min(idx, n_chunks - 1), K, m, col);
+    if (idx < n_chunks) *(u32x4*)(lds + m * lds_row_stride(K) + col) = v[c.value];
+  });
+  if constexpr (MAY_OVERFLOW) {
+    for (int idx = threadIdx.x + MAXC * blockDim.x; idx < n_chunks; idx += blockDim.x) {
+      int m, col;
+      chunk_pos(idx, K, m, col);
+      *(u32x4*)(lds + m * lds_row_stride(K) + col) = *(const u32x4*)(src_row(m) + col);
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A fragment for one 16x16x32 step: lane (g, m) takes inputs k0 + 8 g .. +7 of row m (zero for
+// rows >= rows).
+MOE_DEV bf16x8 lds_fragment(const uint16_t* lds, int rows, int K, int m, int g, int k0) {
+  const int mr = m < rows ? m : 0;
+  uint4 v = *(const uint4*)(lds + mr * lds_row_stride(K) + k0 + 8 * g);
+  if (m >= rows) v = make_uint4(0u, 0u, 0u, 0u);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---- gate/up: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for one task and 32 rows r ------------
+// Workgroup = kGuRG row groups of 16 rows x KS waves splitting the H inputs in runs of 4 groups
+// (KS = H / 512).  A rows: token slot m of the task (bf16 x) or 2 m + part (fp32 x, hi / lo).
 template <int MAXTOK, bool X_BF16>
-__global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs a) {
+__global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   constexpr int ROWS = X_BF16 ? MAXTOK : 2 * MAXTOK;
-  constexpr int NR = ROWS < 4 ? ROWS : 4;  // live D registers per lane
-  __shared__ float red[kMaxGuWaves][2][ROWS][16];
+  constexpr int NR = ROWS < 4 ? ROWS : 4;                    // live D registers per lane
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
 
   const int task = blockIdx.x / a.tiles_gu;
   const int tile = blockIdx.x - task * a.tiles_gu;
@@ -147,48 +271,56 @@ __global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs 
   const BlobLayout lay = blob_layout(H, F);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int row = tile * 16 + n;
-  const int q0 = wave * kGuQuadsPerWave;
-  const int nq = min(kGuQuadsPerWave, H / kGroupElems - q0);
-
-  // ---- loads, group by group in the order the MFMA steps use them: the activations of the
-  // group (A row m = lane % 16, inputs 32 i + 8 g .. +7), then slice g of the group's record of
-  // row `row` in both matrices, and the record's four scales.  No load sits under a branch (dead
-  // lanes and groups past the wave's range load valid, clamped addresses and are masked after),
-  // so the compiler can wait for each group's data alone.
-  const int m = n;
-  const int tslot = X_BF16 ? m : (m >> 1);
+  const int NQ = H / kGroupElems;
+  const int KS = (NQ + kGuQuadsPerWave - 1) / kGuQuadsPerWave;  // waves per row group
+  const int rg = wave / KS, kq = wave - rg * KS;
+  const int row = (tile * kGuRG + rg) * 16 + n;
+  const int q0 = kq * kGuQuadsPerWave;
+  const int nq = min(kGuQuadsPerWave, NQ - q0);
   const int n_tok = __builtin_popcount(tk.tok_mask);
-  const bool live = m < ROWS && tslot < n_tok;
-  const int tok = live ? task_token(tk.tok_mask, tslot) : 0;
+
+  // ---- activations -> LDS: bf16 rows loaded first and stored once the weight loads are issued;
+  // fp32 rows (small shapes only) split into hi / lo bf16 rows by the threads right away
+  auto x_row = [&](int m) {
+    const int tok = task_token(tk.tok_mask, m < n_tok ? m : 0);
+    return (const uint16_t*)a.x + (size_t)tok * H;
+  };
+  // bf16: ROWS * H / 8 chunks over 64 kGuRG H / 512 threads is at most MAXTOK / 2 per thread
+  u32x4 xv[(MAXTOK + 1) / 2];
+  if constexpr (X_BF16) {
+    stage_load(xv, ROWS, H, x_row);
+  } else {
+    for (int c = threadIdx.x; c < ROWS * (H / 8); c += blockDim.x) {
+      const int m = c / (H / 8), col = (c - m * (H / 8)) * 8;
+      const int slot = m >> 1;
+      const int tok = task_token(tk.tok_mask, slot < n_tok ? slot : 0);
+      const float* xf = (const float*)a.x + (size_t)tok * H + col;
+      *(uint4*)(smem + m * lds_row_stride(H) + col) = split_part(*(const float4*)xf, *(const float4*)(xf + 4), m & 1);
+    }
+  }
+
+  // ---- weights: slice g of each group record of row `row` in this wave's K range, both
+  // matrices, and the records' scales; unconditional (clamped groups), all issued now
   const uint8_t* gcode = blob + lay.gate_codes + (size_t)row * kGroupBytes + 16 * g;
   const uint8_t* ucode = blob + lay.up_codes + (size_t)row * kGroupBytes + 16 * g;
   const uint8_t* gscale = blob + lay.gate_scales + (size_t)row * kGroupScaleBytes;
   const uint8_t* uscale = blob + lay.up_scales + (size_t)row * kGroupScaleBytes;
-  const uint16_t* xr = (const uint16_t*)a.x + (size_t)tok * H + 8 * g;
-  const int NQ = H / kGroupElems;
   uint4 cg[kGuQuadsPerWave], cu[kGuQuadsPerWave];
   uint2 sg[kGuQuadsPerWave], su[kGuQuadsPerWave];
-  uint4 xa[X_BF16 ? kGuQuadsPerWave : 1][4];
 #pragma unroll
   for (int qi = 0; qi < kGuQuadsPerWave; ++qi) {
     const int qq = min(q0 + qi, NQ - 1);  // record (qq, row) at 64 (qq F + row)
-    if constexpr (X_BF16) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) xa[qi][i] = *(const uint4*)(xr + (size_t)qq * kGroupElems + 32 * i);
-    }
     cg[qi] = *(const uint4*)(gcode + (size_t)qq * F * kGroupBytes);
     cu[qi] = *(const uint4*)(ucode + (size_t)qq * F * kGroupBytes);
     sg[qi] = *(const uint2*)(gscale + (size_t)qq * F * kGroupScaleBytes);
     su[qi] = *(const uint2*)(uscale + (size_t)qq * F * kGroupScaleBytes);
+    __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
   }
   issue_fence();
   if constexpr (X_BF16) {
-#pragma unroll
-    for (int qi = 0; qi < kGuQuadsPerWave; ++qi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!live) xa[qi][i] = make_uint4(0u, 0u, 0u, 0u);
+    stage_store_sync<false>(xv, smem, ROWS, H, x_row);
+  } else {
+    __syncthreads();
   }
 
   const bf16x8 neg = const_neg136();
@@ -201,17 +333,7 @@ __global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs 
     if (qi >= nq) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      uint4 av;
-      if constexpr (X_BF16) {
-        av = xa[qi][i];
-      } else {
-        av = make_uint4(0u, 0u, 0u, 0u);
-        if (live) {
-          const float* xf = (const float*)a.x + (size_t)tok * H + (size_t)(q0 + qi) * kGroupElems + 32 * i + 8 * g;
-          av = split_part(*(const float4*)xf, *(const float4*)(xf + 4), m & 1);
-        }
-      }
-      const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+      const bf16x8 A = lds_fragment(smem, ROWS, H, n, g, (q0 + qi) * kGroupElems + 32 * i);
       const float4v O = mfma_bf16(A, neg, zero);
       const float4v Dg = mfma_bf16(A, codes_q136(word_at(cg[qi], i)), O);
       const float4v Du = mfma_bf16(A, codes_q136(word_at(cu[qi], i)), O);
@@ -224,47 +346,54 @@ __global__ __launch_bounds__(64 * kMaxGuWaves) void k_decode_gate_up(DecodeArgs 
     }
   }
 
-  // ---- reduce the waves' K ranges, SwiGLU, store h as bf16 hi + lo ---------------------------
-  // lane (g, n) holds rows 4g + r of column n
+  // ---- reduce the K waves of each row group (LDS reused), SwiGLU, store h as bf16 hi + lo ----
+  __syncthreads();
+  float* red = (float*)smem;  // [wave][2][ROWS][16]
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int mr = 4 * g + r;
+    const int mr = 4 * g + r;  // lane (g, n) holds rows 4g + r of column n
     if (mr < ROWS) {
-      red[wave][0][mr][n] = accg[r];
-      red[wave][1][mr][n] = accu[r];
+      red[((wave * 2 + 0) * ROWS + mr) * 16 + n] = accg[r];
+      red[((wave * 2 + 1) * ROWS + mr) * 16 + n] = accu[r];
     }
   }
   __syncthreads();
-  const int nw = blockDim.x >> 6;
-  if ((int)threadIdx.x < 16 * MAXTOK) {
-    const int ts = threadIdx.x >> 4, c = threadIdx.x & 15;
-    if (ts < n_tok) {
-      float gs = 0.f, us = 0.f;
-      for (int w = 0; w < nw; ++w) {
-        if constexpr (X_BF16) {
-          gs += red[w][0][ts][c];
-          us += red[w][1][ts][c];
-        } else {
-          gs += red[w][0][2 * ts][c] + red[w][0][2 * ts + 1][c];
-          us += red[w][1][2 * ts][c] + red[w][1][2 * ts + 1][c];
-        }
+  for (int idx = threadIdx.x; idx < kGuRG * 16 * MAXTOK; idx += blockDim.x) {
+    const int r16 = idx / (16 * MAXTOK), rem = idx - r16 * 16 * MAXTOK;
+    const int ts = rem >> 4, c = rem & 15;
+    if (ts >= n_tok) continue;
+    float gs = 0.f, us = 0.f;
+    for (int w = r16 * KS; w < (r16 + 1) * KS; ++w) {
+      if constexpr (X_BF16) {
+        gs += red[((w * 2 + 0) * ROWS + ts) * 16 + c];
+        us += red[((w * 2 + 1) * ROWS + ts) * 16 + c];
+      } else {
+        gs += red[((w * 2 + 0) * ROWS + 2 * ts) * 16 + c] + red[((w * 2 + 0) * ROWS + 2 * ts + 1) * 16 + c];
+        us += red[((w * 2 + 1) * ROWS + 2 * ts) * 16 + c] + red[((w * 2 + 1) * ROWS + 2 * ts + 1) * 16 + c];
       }
-      const float h = silu(gs) * us;
-      const uint32_t hi = f32_to_bf16_rne(h);
-      const uint32_t lo = f32_to_bf16_rne(h - __uint_as_float(hi << 16));
-      const size_t o = (size_t)task_pair(tk, task_token(tk.tok_mask, ts), a.T, a.k) * F + tile * 16 + c;
-      a.h_hi[o] = (uint16_t)hi;
-      a.h_lo[o] = (uint16_t)lo;
     }
+    const float h = silu(gs) * us;
+    const uint32_t hi = f32_to_bf16_rne(h);
+    const uint32_t lo = f32_to_bf16_rne(h - __uint_as_float(hi << 16));
+    const size_t o = (size_t)task_pair(tk, task_token(tk.tok_mask, ts), a.T, a.k) * F + (tile * kGuRG + r16) * 16 + c;
+    a.h_hi[o] = (uint16_t)hi;
+    a.h_lo[o] = (uint16_t)lo;
   }
 }
 
-// ---- down: y_e[pair][o] = Wd[o] . h[pair] for one task and 16 output rows per wave ----------
-// A rows 2 s + part: token slot s, part 0 = h_hi, 1 = h_lo.
-template <int MAXTOK>
-__global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
+static size_t gate_up_lds_bytes(int H, int rows, int waves) {
+  const size_t xs = (size_t)rows * (H + 8) * 2;
+  const size_t red = (size_t)waves * 2 * rows * 16 * 4;
+  return xs > red ? xs : red;
+}
+
+// ---- down: y_e[pair][o] = Wd[o] . h[pair] for one task; RGW row groups of 16 per wave ----------
+// A rows 2 s + part: token slot s, part 0 = h_hi, 1 = h_lo, staged in LDS once per workgroup.
+template <int MAXTOK, int RGW>
+__global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
   constexpr int ROWS = 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int task = blockIdx.x / a.tiles_dn;
   const int tile = blockIdx.x - task * a.tiles_dn;
   const DecodeTask tk = a.tasks[task];
@@ -278,63 +407,339 @@ __global__ __launch_bounds__(256) void k_decode_down(DecodeArgs a) {
   const BlobLayout lay = blob_layout(H, F);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
-  const int row = (tile * 4 + wave) * 16 + n;
   const int NQ = F / kGroupElems;
-
-  // record (q, row) of the down matrix (H rows) is at 64 (q H + row)
-  const uint8_t* dcode = blob + lay.down_codes + (size_t)row * kGroupBytes + 16 * g;
-  const uint8_t* dscale = blob + lay.down_scales + (size_t)row * kGroupScaleBytes;
-  const int m = n, ts = m >> 1;
   const int n_tok = __builtin_popcount(tk.tok_mask);
-  const bool live = m < ROWS && ts < n_tok;
-  const int hpair = live ? task_pair(tk, task_token(tk.tok_mask, ts), a.T, a.k) : 0;
-  const uint16_t* hrow = ((m & 1) ? a.h_lo : a.h_hi) + (size_t)hpair * F + 8 * g;
 
+  auto h_row = [&](int m) {
+    const int slot = m >> 1;
+    const int pair = task_pair(tk, task_token(tk.tok_mask, slot < n_tok ? slot : 0), a.T, a.k);
+    return (const uint16_t*)((m & 1) ? a.h_lo : a.h_hi) + (size_t)pair * F;
+  };
+  u32x4 hv[kDnStageChunks<MAXTOK>];
+  stage_load(hv, ROWS, F, h_row);
+
+  int rows[RGW];
+  const uint8_t* dcode[RGW];
+  const uint8_t* dscale[RGW];
+  bool rg_live[RGW];  // row groups past H (a ragged last workgroup) load row 0 and store nothing
+#pragma unroll
+  for (int r = 0; r < RGW; ++r) {
+    const int r0 = ((tile * kDnWaves + wave) * RGW + r) * 16;
+    rg_live[r] = r0 < H;
+    rows[r] = (rg_live[r] ? r0 : 0) + n;
+    // record (q, row) of the down matrix (H rows) is at 64 (q H + row)
+    dcode[r] = blob + lay.down_codes + (size_t)rows[r] * kGroupBytes + 16 * g;
+    dscale[r] = blob + lay.down_scales + (size_t)rows[r] * kGroupScaleBytes;
+  }
   const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
-  float acc[NR];
+  float acc[RGW][NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) acc[r] = 0.f;
-  for (int q0 = 0; q0 < NQ; q0 += kDnQuadsPerPass) {
+  for (int r = 0; r < RGW; ++r)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[r][j] = 0.f;
+  // one batch of kDnQuadsPerPass groups: every load issued, then the MFMA steps group by group
+  auto batch = [&](int q0, bool first) {
     const int nq = min(kDnQuadsPerPass, NQ - q0);
-    uint4 cd[kDnQuadsPerPass], ha[kDnQuadsPerPass][4];
-    uint2 sd[kDnQuadsPerPass];
-    // loads group by group in the order of use: h (A operands), then the record and its scales;
-    // unconditional (clamped addresses, dead lanes masked after) so each group is waited for alone
+    uint4 cd[RGW][kDnQuadsPerPass];
+    uint2 sd[RGW][kDnQuadsPerPass];
 #pragma unroll
     for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
       const int qq = min(q0 + qi, NQ - 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ha[qi][i] = *(const uint4*)(hrow + (size_t)qq * kGroupElems + 32 * i);
-      cd[qi] = *(const uint4*)(dcode + (size_t)qq * H * kGroupBytes);
-      sd[qi] = *(const uint2*)(dscale + (size_t)qq * H * kGroupScaleBytes);
+      for (int r = 0; r < RGW; ++r) {
+        cd[r][qi] = *(const uint4*)(dcode[r] + (size_t)qq * H * kGroupBytes);
+        sd[r][qi] = *(const uint2*)(dscale[r] + (size_t)qq * H * kGroupScaleBytes);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
     }
     issue_fence();
-#pragma unroll
-    for (int qi = 0; qi < kDnQuadsPerPass; ++qi)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (!live) ha[qi][i] = make_uint4(0u, 0u, 0u, 0u);
+    if (first) stage_store_sync<true>(hv, smem, ROWS, F, h_row);
 #pragma unroll
     for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
       if (qi >= nq) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 A = __builtin_bit_cast(bf16x8, ha[qi][i]);
+        const bf16x8 A = lds_fragment(smem, ROWS, F, n, g, (q0 + qi) * kGroupElems + 32 * i);
         const float4v O = mfma_bf16(A, neg, zero);
-        const float4v D = mfma_bf16(A, codes_q136(word_at(cd[qi], i)), O);
-        const float s = scale_at(sd[qi], i);
 #pragma unroll
-        for (int r = 0; r < NR; ++r) acc[r] = fmaf(s, D[r], acc[r]);
+        for (int r = 0; r < RGW; ++r) {
+          const float4v D = mfma_bf16(A, codes_q136(word_at(cd[r][qi], i)), O);
+          const float s = scale_at(sd[r][qi], i);
+#pragma unroll
+          for (int j = 0; j < NR; ++j) acc[r][j] = fmaf(s, D[j], acc[r][j]);
+        }
       }
     }
-  }
-  // lane (g, n) holds rows 4g + r: token slots 2g (r = 0, 1) and 2g + 1 (r = 2, 3)
+  };
+  batch(0, true);  // peeled: a loop head would wait for every outstanding load, the staging too
+  for (int q0 = kDnQuadsPerPass; q0 < NQ; q0 += kDnQuadsPerPass) batch(q0, false);
+  // lane (g, n) holds rows 4g + j: token slots 2g (j = 0, 1) and 2g + 1 (j = 2, 3)
 #pragma unroll
-  for (int s2 = 0; s2 < NR / 2; ++s2) {
-    const int slot = 2 * g + s2;
-    if (slot < n_tok)
-      a.y_pairs[(size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + row] = acc[2 * s2] + acc[2 * s2 + 1];
+  for (int r = 0; r < RGW; ++r) {
+#pragma unroll
+    for (int s2 = 0; s2 < NR / 2; ++s2) {
+      const int slot = 2 * g + s2;
+      if (rg_live[r] && slot < n_tok)
+        a.y_pairs[(size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r]] =
+            acc[r][2 * s2] + acc[r][2 * s2 + 1];
+    }
+  }
+}
+
+// ---- pipelined variants for tasks of up to 4 or 8 bf16 tokens ----------------------------------
+// Each wave owns whole row groups (16 output rows over the full input range), so there is no
+// reduction across waves, and walks the input range in UNITS chunks whose loads go out one chunk
+// ahead of the MFMA work: the wave always has weight loads in flight, and the grid (a workgroup per
+// 64 gate/up rows or 256 down rows of one task) fits the chip in one round.
+constexpr int kPipeGuWaves = 4;   // gate/up: waves (= row groups of 16) per workgroup
+constexpr int kPipeGuGroups = 2;  // gate/up: groups of 128 inputs per chunk
+constexpr int kPipeDnWaves = 8;   // down: waves per workgroup
+constexpr int kPipeDnRGW = 2;     // down: row groups per wave (at most 2: one offset register each)
+static_assert(kPipeDnRGW >= 1 && kPipeDnRGW <= 2, "down row groups per wave");
+constexpr int kPipeDnGroups = 3;  // down: groups of 128 inputs per chunk
+
+// gate/up: H = 128 kPipeGuGroups UNITS; A rows = token slots of the task (bf16 x).
+template <int MAXTOK, int UNITS>
+__global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_gate_up_pipe(DecodeArgs a) {
+  constexpr int ROWS = MAXTOK;
+  constexpr int NR = ROWS < 4 ? ROWS : 4;
+  constexpr int QG = kPipeGuGroups;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int task = blockIdx.x / a.tiles_gu;
+  const int tile = blockIdx.x - task * a.tiles_gu;
+  const DecodeTask tk = a.tasks[task];
+  if (task >= a.ctrl[kCtrlNTasks]) return;
+  const uint8_t* blob = task_blob(a.src, tk);
+  if (!blob) {
+    if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+    return;
+  }
+  constexpr int H = 128 * QG * UNITS;
+  const int F = a.F;
+  const BlobLayout lay = blob_layout(H, F);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int row = (tile * kPipeGuWaves + wave) * 16 + n;
+  const int n_tok = __builtin_popcount(tk.tok_mask);
+  const Unpack uk = make_unpack();
+
+  auto x_row = [&](int m) {
+    const int tok = task_token(tk.tok_mask, m < n_tok ? m : 0);
+    return (const uint16_t*)a.x + (size_t)tok * H;
+  };
+  // ROWS * H / 8 chunks over 64 kPipeGuWaves threads
+  constexpr int XC = (ROWS * (H / 8) + 64 * kPipeGuWaves - 1) / (64 * kPipeGuWaves);
+  u32x4 xv[XC];
+  stage_load(xv, ROWS, H, x_row);
+
+  const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob, lay.total);
+  const int voff_c = row * kGroupBytes + 16 * g, voff_s = row * kGroupScaleBytes;
+  u32x4 cg[2][QG], cu[2][QG];
+  u32x2 sg[2][QG], su[2][QG];
+  // chunk u into buffer b: record (q, row) at 64 (q F + row), its scales at 8 (q F + row)
+  auto load_chunk = [&](auto bc, int u) {
+    constexpr int b = decltype(bc)::value;
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi) {
+      const int q = (u * QG + qi) * F;
+      cg[b][qi] = buf_load16(rs, voff_c, (int)lay.gate_codes + q * kGroupBytes);
+      cu[b][qi] = buf_load16(rs, voff_c, (int)lay.up_codes + q * kGroupBytes);
+      sg[b][qi] = buf_load8(rs, voff_s, (int)lay.gate_scales + q * kGroupScaleBytes);
+      su[b][qi] = buf_load8(rs, voff_s, (int)lay.up_scales + q * kGroupScaleBytes);
+      __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
+    }
+  };
+  load_chunk(std::integral_constant<int, 0>{}, 0);
+  issue_fence();
+  stage_store_sync<false>(xv, smem, ROWS, H, x_row);
+  if constexpr (UNITS > 1) {
+    load_chunk(std::integral_constant<int, 1>{}, 1);
+    issue_fence();
+  }
+
+  const bf16x8 neg = const_neg136();
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  // Summation order of the split kernel above (a partial sum per range of kGuQuadsPerWave groups,
+  // the partials added in range order), so a token's h is bitwise the same whichever kernel the
+  // size of its step selects.
+  constexpr int CPR = kGuQuadsPerWave / QG;  // chunks per range
+  static_assert(kGuQuadsPerWave % QG == 0 && UNITS % CPR == 0, "whole ranges per chunk walk");
+  float accg[NR], accu[NR], totg[NR], totu[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) accg[r] = accu[r] = totg[r] = totu[r] = 0.f;
+  static_for<UNITS>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    constexpr int b = u & 1;
+    if constexpr (u % CPR == 0) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) accg[r] = accu[r] = 0.f;
+    }
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 A = lds_fragment(smem, ROWS, H, n, g, (u * QG + qi) * kGroupElems + 32 * i);
+        const float4v O = mfma_bf16(A, neg, zero);
+        const float4v Dg = mfma_bf16(A, codes_q136(word_at(cg[b][qi], i), uk), O);
+        const float4v Du = mfma_bf16(A, codes_q136(word_at(cu[b][qi], i), uk), O);
+        const float s_g = scale_at(sg[b][qi], i), s_u = scale_at(su[b][qi], i);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          accg[r] = fmaf(s_g, Dg[r], accg[r]);
+          accu[r] = fmaf(s_u, Du[r], accu[r]);
+        }
+      }
+      // one group at a time: an unbounded schedule hoists every MFMA and spills their results
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (u % CPR == CPR - 1) {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        totg[r] += accg[r];
+        totu[r] += accu[r];
+      }
+    }
+    if constexpr (u + 2 < UNITS) {
+      load_chunk(std::integral_constant<int, b>{}, u + 2);
+      issue_fence();
+    }
+  });
+
+  // The sums are final here: without this the compiler sinks the whole accumulation chain into
+  // the conditional stores below, after every MFMA, and spills the MFMA results.
+#pragma unroll
+  for (int r = 0; r < NR; ++r) asm volatile("" : "+v"(totg[r]), "+v"(totu[r]));
+  // lane (g, n) holds token slots 4 g + r of row `row`: SwiGLU, h as bf16 hi + lo
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    const int slot = 4 * g + r;
+    if (slot < n_tok) {
+      const float h = silu(totg[r]) * totu[r];
+      const uint32_t hi = f32_to_bf16_rne(h);
+      const uint32_t lo = f32_to_bf16_rne(h - __uint_as_float(hi << 16));
+      const size_t o = (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * F + row;
+      a.h_hi[o] = (uint16_t)hi;
+      a.h_lo[o] = (uint16_t)lo;
+    }
+  }
+}
+
+// down: F = 128 kPipeDnGroups UNITS; A rows 2 s + part (token slot s, h hi / lo).
+template <int MAXTOK, int UNITS>
+__global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_down_pipe(DecodeArgs a) {
+  constexpr int ROWS = 2 * MAXTOK;
+  constexpr int NR = ROWS < 4 ? ROWS : 4;
+  constexpr int QG = kPipeDnGroups;
+  constexpr int RGW = kPipeDnRGW;
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int task = blockIdx.x / a.tiles_dn;
+  const int tile = blockIdx.x - task * a.tiles_dn;
+  const DecodeTask tk = a.tasks[task];
+  if (task >= a.ctrl[kCtrlNTasks]) return;
+  const uint8_t* blob = task_blob(a.src, tk);
+  if (!blob) {
+    if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+    return;
+  }
+  constexpr int F = 128 * QG * UNITS;
+  const int H = a.H;
+  const BlobLayout lay = blob_layout(H, F);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int n_tok = __builtin_popcount(tk.tok_mask);
+  const Unpack uk = make_unpack();
+
+  auto h_row = [&](int m) {
+    const int slot = m >> 1;
+    const int pair = task_pair(tk, task_token(tk.tok_mask, slot < n_tok ? slot : 0), a.T, a.k);
+    return (const uint16_t*)((m & 1) ? a.h_lo : a.h_hi) + (size_t)pair * F;
+  };
+  constexpr int HC = (ROWS * (F / 8) + 64 * kPipeDnWaves - 1) / (64 * kPipeDnWaves);
+  u32x4 hv[HC];
+  stage_load(hv, ROWS, F, h_row);
+
+  const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob, lay.total);
+  // the wave's row groups are consecutive: row group r of the wave at voff + 16 r records
+  const int r0 = ((tile * kPipeDnWaves + wave) * RGW) * 16;
+  bool rg_live[RGW];  // row groups past H (a ragged last workgroup) load row 0 and store nothing
+  int rows[RGW];
+#pragma unroll
+  for (int r = 0; r < RGW; ++r) {
+    rg_live[r] = r0 + 16 * r < H;
+    rows[r] = (rg_live[r] ? r0 + 16 * r : 0) + n;
+  }
+  const int voff_c0 = rows[0] * kGroupBytes + 16 * g, voff_s0 = rows[0] * kGroupScaleBytes;
+  const int voff_c1 = rows[RGW - 1] * kGroupBytes + 16 * g, voff_s1 = rows[RGW - 1] * kGroupScaleBytes;
+  u32x4 cd[2][RGW][QG];
+  u32x2 sd[2][RGW][QG];
+  auto load_chunk = [&](auto bc, int u) {
+    constexpr int b = decltype(bc)::value;
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi) {
+      const int q = (u * QG + qi) * H;  // record (q, row) of the down matrix (H rows)
+#pragma unroll
+      for (int r = 0; r < RGW; ++r) {
+        cd[b][r][qi] = buf_load16(rs, r == 0 ? voff_c0 : voff_c1, (int)lay.down_codes + q * kGroupBytes);
+        sd[b][r][qi] = buf_load8(rs, r == 0 ? voff_s0 : voff_s1, (int)lay.down_scales + q * kGroupScaleBytes);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  load_chunk(std::integral_constant<int, 0>{}, 0);
+  issue_fence();
+  stage_store_sync<false>(hv, smem, ROWS, F, h_row);
+  if constexpr (UNITS > 1) {
+    load_chunk(std::integral_constant<int, 1>{}, 1);
+    issue_fence();
+  }
+
+  const bf16x8 neg = const_neg136();
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  float acc[RGW][NR];
+#pragma unroll
+  for (int r = 0; r < RGW; ++r)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) acc[r][j] = 0.f;
+  static_for<UNITS>([&](auto uc) {
+    constexpr int u = decltype(uc)::value;
+    constexpr int b = u & 1;
+#pragma unroll
+    for (int qi = 0; qi < QG; ++qi) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 A = lds_fragment(smem, ROWS, F, n, g, (u * QG + qi) * kGroupElems + 32 * i);
+        const float4v O = mfma_bf16(A, neg, zero);
+#pragma unroll
+        for (int r = 0; r < RGW; ++r) {
+          const float4v D = mfma_bf16(A, codes_q136(word_at(cd[b][r][qi], i), uk), O);
+          const float s = scale_at(sd[b][r][qi], i);
+#pragma unroll
+          for (int j = 0; j < NR; ++j) acc[r][j] = fmaf(s, D[j], acc[r][j]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one group at a time
+    }
+    if constexpr (u + 2 < UNITS) {
+      load_chunk(std::integral_constant<int, b>{}, u + 2);
+      issue_fence();
+    }
+  });
+  // final accumulators (kept from being sunk into the conditional stores)
+#pragma unroll
+  for (int r = 0; r < RGW; ++r)
+#pragma unroll
+    for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(acc[r][j]));
+  // lane (g, n) holds rows 4g + j: token slots 2g (j = 0, 1) and 2g + 1 (j = 2, 3)
+#pragma unroll
+  for (int r = 0; r < RGW; ++r) {
+#pragma unroll
+    for (int s2 = 0; s2 < NR / 2; ++s2) {
+      const int slot = 2 * g + s2;
+      if (rg_live[r] && slot < n_tok)
+        a.y_pairs[(size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r]] =
+            acc[r][2 * s2] + acc[r][2 * s2 + 1];
+    }
   }
 }
 
@@ -395,15 +800,67 @@ __global__ void k_fill_zero(uint32_t* p, size_t n) {
 // ------------------------------------------------------------------------------------------
 // Launchers
 // ------------------------------------------------------------------------------------------
+// Pipelined kernels: input ranges of 4, 8 or 16 gate/up chunks (H = 1024, 2048, 4096) and 2 or 4
+// down chunks (F = 768, 1536); 0 = not covered.
+static int gate_up_pipe_units(int H) {
+  const int u = H / (kGroupElems * kPipeGuGroups);
+  return H % (kGroupElems * kPipeGuGroups) == 0 && (u == 4 || u == 8 || u == 16) ? u : 0;
+}
+static int down_pipe_units(int F) {
+  const int u = F / (kGroupElems * kPipeDnGroups);
+  return F % (kGroupElems * kPipeDnGroups) == 0 && (u == 2 || u == 4) ? u : 0;
+}
+
 template <int MAXTOK>
-static hipError_t launch_decode_ffn_t(const DecodeArgs& a, int max_tasks, bool xb, hipStream_t st) {
-  const int gu_waves = (a.H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
-  const int grid_gu = max_tasks * a.tiles_gu, grid_dn = max_tasks * a.tiles_dn;
-  hipError_t err;
-  if (xb) err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true>, grid_gu, 64 * gu_waves, 0, st, a);
-  else err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false>, grid_gu, 64 * gu_waves, 0, st, a);
+static hipError_t launch_gate_up_pipe(DecodeArgs a, int max_tasks, int units, hipStream_t st) {
+  a.tiles_gu = a.F / (16 * kPipeGuWaves);
+  const int grid = max_tasks * a.tiles_gu, threads = 64 * kPipeGuWaves;
+  const uint32_t lds = (uint32_t)(MAXTOK * (a.H + 8) * 2);
+  if (units == 4) return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 4>, grid, threads, lds, st, a);
+  if (units == 8) return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 8>, grid, threads, lds, st, a);
+  return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 16>, grid, threads, lds, st, a);
+}
+
+template <int MAXTOK>
+static hipError_t launch_down_pipe(DecodeArgs a, int max_tasks, int units, hipStream_t st) {
+  const int rows = 16 * kPipeDnWaves * kPipeDnRGW;
+  a.tiles_dn = (a.H + rows - 1) / rows;
+  const int grid = max_tasks * a.tiles_dn, threads = 64 * kPipeDnWaves;
+  const uint32_t lds = (uint32_t)(2 * MAXTOK * (a.F + 8) * 2);
+  if (units == 2) return launch_timed(kTimeDecodeDown, k_decode_down_pipe<MAXTOK, 2>, grid, threads, lds, st, a);
+  return launch_timed(kTimeDecodeDown, k_decode_down_pipe<MAXTOK, 4>, grid, threads, lds, st, a);
+}
+
+template <int MAXTOK>
+static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipStream_t st) {
+  hipError_t err = hipSuccess;
+  // tasks of more than 2 tokens (bf16 x) at the covered shapes: the pipelined kernels
+  const int gu_units = (MAXTOK >= 4 && xb) ? gate_up_pipe_units(a.H) : 0;
+  if (gu_units) {
+    if constexpr (MAXTOK >= 4) err = launch_gate_up_pipe<MAXTOK>(a, max_tasks, gu_units, st);
+  } else {
+    const int ks = (a.H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
+    const int gu_threads = 64 * kGuRG * ks;
+    a.tiles_gu = a.F / (16 * kGuRG);
+    const int grid_gu = max_tasks * a.tiles_gu;
+    if (xb)
+      err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true>, grid_gu, gu_threads,
+                         (uint32_t)gate_up_lds_bytes(a.H, MAXTOK, kGuRG * ks), st, a);
+    else
+      err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false>, grid_gu, gu_threads,
+                         (uint32_t)gate_up_lds_bytes(a.H, 2 * MAXTOK, kGuRG * ks), st, a);
+  }
   if (err != hipSuccess) return err;
-  err = launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK>, grid_dn, 256, 0, st, a);
+  const int dn_units = MAXTOK >= 4 ? down_pipe_units(a.F) : 0;
+  if (dn_units) {
+    if constexpr (MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);
+  } else {
+    const int dn_rows = 16 * kDnWaves * kDnRGW<MAXTOK>;
+    a.tiles_dn = (a.H + dn_rows - 1) / dn_rows;
+    const uint32_t dn_lds = (uint32_t)(2 * MAXTOK * (a.F + 8) * 2);
+    err = launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, kDnRGW<MAXTOK>>, max_tasks * a.tiles_dn, 64 * kDnWaves,
+                       dn_lds, st, a);
+  }
   if (err != hipSuccess) return err;
   const int n4 = a.T * a.H / 4;
   k_decode_combine<<<(n4 + 255) / 256, 256, 0, st>>>(a);
@@ -429,8 +886,6 @@ hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_t
   a.T = T;
   a.k = k;
   a.n_shared = n_shared;
-  a.tiles_gu = F / 16;
-  a.tiles_dn = H / 64;
   const bool xb = x_dtype == MOE_BF16;
   static_assert(kTaskTok == kMaxDecodeTok, "a decode task holds every token of the step that chose its expert");
   if (T <= 1) return launch_decode_ffn_t<1>(a, max_tasks, xb, st);

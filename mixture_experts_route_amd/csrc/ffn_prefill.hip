@@ -79,10 +79,6 @@ MOE_DEV half8 dequant_word(uint32_t w, half2v s2) {
 
 MOE_DEV uint32_t word_of(const uint4& c, int d) { return d == 0 ? c.x : d == 1 ? c.y : d == 2 ? c.z : c.w; }
 
-// Asynchronous global -> LDS copy of 16 bytes per lane: lane l's bytes land at lds_base + 16 l.
-MOE_DEV void lds_dma16(const void* gsrc, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
 
 MOE_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 

@@ -494,10 +494,12 @@ __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
 // 64 gate/up rows or 256 down rows of one task) fits the chip in one round.
 constexpr int kPipeGuWaves = 4;   // gate/up: waves (= row groups of 16) per workgroup
 constexpr int kPipeGuGroups = 2;  // gate/up: groups of 128 inputs per chunk
+constexpr int kPipeGuBufs = 3;    // gate/up: chunks in flight
 constexpr int kPipeDnWaves = 8;   // down: waves per workgroup
 constexpr int kPipeDnRGW = 2;     // down: row groups per wave (at most 2: one offset register each)
 static_assert(kPipeDnRGW >= 1 && kPipeDnRGW <= 2, "down row groups per wave");
 constexpr int kPipeDnGroups = 3;  // down: groups of 128 inputs per chunk
+constexpr int kPipeDnBufs = 2;    // down: chunks in flight
 
 // gate/up: H = 128 kPipeGuGroups UNITS; A rows = token slots of the task (bf16 x).
 template <int MAXTOK, int UNITS>
@@ -531,12 +533,14 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   // ROWS * H / 8 chunks over 64 kPipeGuWaves threads
   constexpr int XC = (ROWS * (H / 8) + 64 * kPipeGuWaves - 1) / (64 * kPipeGuWaves);
   u32x4 xv[XC];
+  // chunks in flight (fewer when the staged rows need many registers)
+  constexpr int NBUF = XC > 8 ? 2 : kPipeGuBufs;
   stage_load(xv, ROWS, H, x_row);
 
   const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob, lay.total);
   const int voff_c = row * kGroupBytes + 16 * g, voff_s = row * kGroupScaleBytes;
-  u32x4 cg[2][QG], cu[2][QG];
-  u32x2 sg[2][QG], su[2][QG];
+  u32x4 cg[NBUF][QG], cu[NBUF][QG];
+  u32x2 sg[NBUF][QG], su[NBUF][QG];
   // chunk u into buffer b: record (q, row) at 64 (q F + row), its scales at 8 (q F + row)
   auto load_chunk = [&](auto bc, int u) {
     constexpr int b = decltype(bc)::value;
@@ -550,13 +554,11 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
       __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
     }
   };
-  load_chunk(std::integral_constant<int, 0>{}, 0);
+  // the first chunks go out before the staged rows are stored (the store waits for the staging
+  // loads only, issued first)
+  static_for<(NBUF < UNITS ? NBUF : UNITS)>([&](auto uc) { load_chunk(uc, decltype(uc)::value); });
   issue_fence();
   stage_store_sync<false>(xv, smem, ROWS, H, x_row);
-  if constexpr (UNITS > 1) {
-    load_chunk(std::integral_constant<int, 1>{}, 1);
-    issue_fence();
-  }
 
   const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -570,7 +572,7 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   for (int r = 0; r < NR; ++r) accg[r] = accu[r] = totg[r] = totu[r] = 0.f;
   static_for<UNITS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    constexpr int b = u & 1;
+    constexpr int b = u % NBUF;
     if constexpr (u % CPR == 0) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) accg[r] = accu[r] = 0.f;
@@ -600,8 +602,8 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
         totu[r] += accu[r];
       }
     }
-    if constexpr (u + 2 < UNITS) {
-      load_chunk(std::integral_constant<int, b>{}, u + 2);
+    if constexpr (u + NBUF < UNITS) {
+      load_chunk(std::integral_constant<int, b>{}, u + NBUF);
       issue_fence();
     }
   });
@@ -671,8 +673,8 @@ __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_
   }
   const int voff_c0 = rows[0] * kGroupBytes + 16 * g, voff_s0 = rows[0] * kGroupScaleBytes;
   const int voff_c1 = rows[RGW - 1] * kGroupBytes + 16 * g, voff_s1 = rows[RGW - 1] * kGroupScaleBytes;
-  u32x4 cd[2][RGW][QG];
-  u32x2 sd[2][RGW][QG];
+  u32x4 cd[kPipeDnBufs][RGW][QG];
+  u32x2 sd[kPipeDnBufs][RGW][QG];
   auto load_chunk = [&](auto bc, int u) {
     constexpr int b = decltype(bc)::value;
 #pragma unroll
@@ -686,13 +688,11 @@ __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  load_chunk(std::integral_constant<int, 0>{}, 0);
+  // the first chunks go out before the staged rows are stored (the store waits for the staging
+  // loads only, issued first)
+  static_for<(kPipeDnBufs < UNITS ? kPipeDnBufs : UNITS)>([&](auto uc) { load_chunk(uc, decltype(uc)::value); });
   issue_fence();
   stage_store_sync<false>(hv, smem, ROWS, F, h_row);
-  if constexpr (UNITS > 1) {
-    load_chunk(std::integral_constant<int, 1>{}, 1);
-    issue_fence();
-  }
 
   const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
@@ -703,7 +703,7 @@ __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_
     for (int j = 0; j < NR; ++j) acc[r][j] = 0.f;
   static_for<UNITS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
-    constexpr int b = u & 1;
+    constexpr int b = u % kPipeDnBufs;
 #pragma unroll
     for (int qi = 0; qi < QG; ++qi) {
 #pragma unroll
@@ -720,8 +720,8 @@ __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_
       }
       __builtin_amdgcn_sched_barrier(0);  // one group at a time
     }
-    if constexpr (u + 2 < UNITS) {
-      load_chunk(std::integral_constant<int, b>{}, u + 2);
+    if constexpr (u + kPipeDnBufs < UNITS) {
+      load_chunk(std::integral_constant<int, b>{}, u + kPipeDnBufs);
       issue_fence();
     }
   });

@@ -90,10 +90,14 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t As0[kTileRows * kKC];
   __shared__ __attribute__((aligned(1024))) uint16_t As1[kTileRows * kKC];
 
-  // XCD-aware work index: blockIdx i runs on XCD i % 8; give each XCD a contiguous range.
-  const int per_xcd = gridDim.x >> 3;
-  const int work = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (work >= a.n_works) return;
+  // XCD-aware work index: blockIdx i runs on XCD i % 8; each XCD gets a contiguous eighth of the
+  // works that exist (the item count is known on the device only; the grid covers the bound).
+  int n_works = a.n_works;
+  if constexpr (MODE != kRouter) n_works = min(*a.n_items * a.n_ntiles, a.n_works);
+  const int per_xcd = (n_works + 7) >> 3;
+  const int local = (int)(blockIdx.x >> 3);
+  const int work = (int)(blockIdx.x & 7) * per_xcd + local;
+  if (local >= per_xcd || work >= n_works) return;
   const int item_id = work / a.n_ntiles;
   const int ntile = work - item_id * a.n_ntiles;
 
@@ -105,7 +109,6 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
     it.rows = min(kTileRows, a.T - it.row0);
     if (it.rows <= 0) return;
   } else {
-    if (item_id >= *a.n_items) return;
     it = a.items[item_id];
     blob = bucket_blob(a.src, it.bucket, a.E);
     if (!blob) {

@@ -204,7 +204,7 @@ struct PlanShared {
 // misses come out in ascending expert id.
 MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table, int n_slots,
                         int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell,
-                        PlanShared& sh) {
+                        PlanShared& sh, bool slots_staged = false) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) sh.tok_mask[e] = 0;
   if (threadIdx.x == 0) sh.bad = 0;
   __syncthreads();
@@ -217,8 +217,8 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     } else {
       atomicOr(&sh.tok_mask[e], 1u << t);
       sh.choice[e][t] = (uint8_t)j;
-      const int s = table ? table[e] : e;
-      sh.slot_of[e] = s;  // every writer of e writes the same value
+      const int s = slots_staged ? sh.slot_of[e] : table ? table[e] : e;
+      if (!slots_staged) sh.slot_of[e] = s;  // every writer of e writes the same value
       if (s >= n_slots) atomicOr(&sh.bad, MOE_DERR_SLOT);
     }
   }
@@ -468,13 +468,27 @@ __global__ __launch_bounds__(64 * kMaxDecodeTok) void k_decode_select(RouteArgs 
   __shared__ PlanShared sh;
   __shared__ int32_t s_ids[kMaxDecodeTok * kMaxK];
   const int wave = threadIdx.x >> 6;
+  // the slot table is loaded with the logits (issued first: one wait covers both) and goes to LDS
+  // after the selections, so the plan makes no dependent global load
+  constexpr int kTabPer = kMaxExperts / 256;  // blockDim.x >= 256
+  int32_t tab[kTabPer];
+#pragma unroll
+  for (int i = 0; i < kTabPer; ++i) {
+    const int e = min((int)(threadIdx.x + i * blockDim.x), a.E - 1);
+    tab[i] = a.table ? a.table[e] : e;
+  }
   for (int t = wave; t < a.T; t += blockDim.x >> 6) {
     select_topk_wave<NPER>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k,
                            a.ctrl, s_ids + t * a.k);
   }
+#pragma unroll
+  for (int i = 0; i < kTabPer; ++i) {
+    const int e = threadIdx.x + i * blockDim.x;
+    if (e < a.E) sh.slot_of[e] = tab[i];
+  }
   __syncthreads();
   if (a.plan)
-    build_plan(s_ids, a.T, a.k, a.E, a.n_shared, a.table, a.n_slots, a.miss_ids, a.tasks, a.ctrl, a.bell, sh);
+    build_plan(s_ids, a.T, a.k, a.E, a.n_shared, a.table, a.n_slots, a.miss_ids, a.tasks, a.ctrl, a.bell, sh, true);
 }
 
 // ------------------------------------------------------------------------------------------

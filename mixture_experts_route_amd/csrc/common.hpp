@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #include "../../include/moe_route.h"
 
 #define MOE_DEV __device__ __forceinline__
@@ -214,6 +216,30 @@ MOE_DEV void wave_argmax(float& v, int& i) {
 #undef MOE_ARGMAX_STEP
   v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
   i = __builtin_amdgcn_readlane(i, 63);
+}
+
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>): indexes into a register array
+// that are constants from the start, so the array never lives in scratch memory.
+template <typename Fn, int... I>
+MOE_DEV void static_for_impl(Fn&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename Fn>
+MOE_DEV void static_for(Fn&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// A blob as a buffer resource: loads take a per-lane 32-bit offset and a wave-uniform one, so a
+// wave's addresses cost one register instead of a 64-bit pointer per load; reads past `bytes`
+// return zero.  Word 3 = 0x00020000: 32-bit data format, the value raw loads need on this family.
+MOE_DEV __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t* blob, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)blob, 0, (int)bytes, 0x00020000);
+}
+MOE_DEV u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+MOE_DEV u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
 }
 
 }  // namespace moe

@@ -28,8 +28,6 @@
 //     pairs of the task's tokens (<= 8 tokens -> <= 16 rows), so one MFMA per block covers both
 //     parts.  Writes each pair's output row y_e.
 //   combine: y[t] = sum_j w[t][j] * y_{e_j}[t] (j = 0..k-1), then + y_shared[t]: fixed order.
-#include <utility>
-
 #include "kernels.hpp"
 
 namespace moe {
@@ -109,18 +107,6 @@ MOE_DEV float scale_at(const u32x2& s, int i) {
   return fp16_bits_to_f32((i & 1) ? (w >> 16) : (w & 0xFFFFu));
 }
 
-// A blob as a buffer resource: loads take a per-lane 32-bit offset and a wave-uniform one, so a
-// wave's addresses cost one register instead of a 64-bit pointer per load; reads past `bytes`
-// return zero.  Word 3 = 0x00020000: 32-bit data format, the value raw loads need on this family.
-MOE_DEV __amdgpu_buffer_rsrc_t blob_rsrc(const uint8_t* blob, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)blob, 0, (int)bytes, 0x00020000);
-}
-MOE_DEV u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
-MOE_DEV u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-}
 
 // Token of slot m of a task: the m-th set bit of its token mask (m < popcount(mask)).
 MOE_DEV int task_token(uint32_t mask, int m) {
@@ -184,16 +170,6 @@ struct DecodeArgs {
 // cannot tell which outstanding load wrote LDS and waits for all of them before any LDS read.)
 MOE_DEV int lds_row_stride(int K) { return K + 8; }
 
-// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>): indexes into a register array
-// that are constants from the start, so the array never lives in scratch memory.
-template <typename Fn, int... I>
-MOE_DEV void static_for_impl(Fn&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename Fn>
-MOE_DEV void static_for(Fn&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 // Chunk c of this thread: index threadIdx.x + c * blockDim.x over rows * K / 8 chunks; row m,
 // column col.

@@ -77,6 +77,33 @@ MOE_DEV half8 dequant_word(uint32_t w, half2v s2) {
   return r;
 }
 
+// The constants of dequant_word in registers (the nibble mask in a scalar register, the fp16 pair
+// (1024, 1024) in a vector register): each pair is then one v_and_or_b32 (plus a shift), where
+// literal operands make the compiler split it into an and and an or.
+struct DequantConsts {
+  uint32_t mask, magic, off;
+};
+MOE_DEV DequantConsts make_dequant_consts() {
+  DequantConsts c;
+  asm("s_mov_b32 %0, 0xf000f" : "=s"(c.mask));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(c.magic));
+  asm("s_mov_b32 %0, 0x64086408" : "=s"(c.off));  // fp16 pair (1032, 1032)
+  return c;
+}
+MOE_DEV half8 dequant_word_k(uint32_t w, half2v s2, const DequantConsts& c) {
+  const half2v off = __builtin_bit_cast(half2v, c.off);
+  half8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = ((w >> (4 * j)) & c.mask) | c.magic;  // fp16 (1024 + u) pair
+    const half2v q = __builtin_bit_cast(half2v, t) - off;   // q = u - 8, exact
+    const half2v v = q * s2;                                // fp16(q * scale)
+    r[2 * j] = v.x;
+    r[2 * j + 1] = v.y;
+  }
+  return r;
+}
+
 MOE_DEV uint32_t word_of(const uint4& c, int d) { return d == 0 ? c.x : d == 1 ? c.y : d == 2 ? c.z : c.w; }
 
 
@@ -303,6 +330,190 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   }
 }
 
+// ---- pipelined variant (the model's K: NK chunks of 128) ----------------------------------------
+// Workgroup = 8 waves over 512 weight rows (gate/up: 256 gate + 256 up rows = 256 h columns; down:
+// 512 output columns) of one item; each wave keeps the 128 x 64 tile of the scalar kernel above.
+// The activation tile goes through a 3-stage LDS ring, loaded through registers 3 chunks before
+// its MFMA work (written to LDS one chunk after its loads were issued, so the wait is for those
+// loads alone); weights go through a 3-slot register ring, 2 chunks ahead.  One barrier per chunk
+// and no wait for all loads: the weight stream never drains inside a work.
+constexpr int kPWaves = 8;
+constexpr int kPNTile = 64 * kPWaves;                       // weight rows per workgroup
+constexpr int kPAPer = kTileRows * (kKC / 8) / (64 * kPWaves);  // A 16-byte pieces per thread per chunk
+static_assert(kPAPer * 64 * kPWaves == kTileRows * (kKC / 8), "A pieces split evenly");
+
+template <int MODE, int NK>
+__global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a) {
+  static_assert(MODE == kGateUp || MODE == kDown, "expert GEMMs only");
+  static_assert(NK >= 3, "pipeline depth");
+  __shared__ __attribute__((aligned(1024))) uint16_t As[3][kTileRows * kKC];
+
+  const int n_works = min(*a.n_items * a.n_ntiles, a.n_works);
+  const int per_xcd = (n_works + 7) >> 3;
+  const int local = (int)(blockIdx.x >> 3);
+  const int work = (int)(blockIdx.x & 7) * per_xcd + local;
+  if (local >= per_xcd || work >= n_works) return;
+  const int item_id = work / a.n_ntiles;
+  const int ntile = work - item_id * a.n_ntiles;
+  const TileItem it = a.items[item_id];
+  const uint8_t* blob = bucket_blob(a.src, it.bucket, a.E);
+  if (!blob) {
+    if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+    return;
+  }
+  const int H = a.H, F = a.F;
+  constexpr int K = NK * kKC;
+  const int wrows = MODE == kDown ? H : F;
+  const BlobLayout lay = blob_layout(H, F);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int ms = (it.rows + 15) >> 4;
+  const DequantConsts uk = make_dequant_consts();
+
+  // ---- weights: subtile s of this wave, row `row`, through the blob's buffer resource ----------
+  const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob, lay.total);
+  // subtile s = rows row0 + 16 s (down) or gate rows row0 + 16 (s & 1), up rows likewise (gate/up):
+  // one per-lane offset per stream, the rest is uniform (scalar offset) or an immediate
+  int row0;
+  int32_t cb0, sb0, cb_up = 0, sb_up = 0;
+  if constexpr (MODE == kGateUp) {
+    row0 = ntile * (kPNTile / 2) + wave * 32 + n;
+    cb0 = (int32_t)lay.gate_codes;
+    sb0 = (int32_t)lay.gate_scales;
+    cb_up = (int32_t)(lay.up_codes - lay.gate_codes);
+    sb_up = (int32_t)(lay.up_scales - lay.gate_scales);
+  } else {
+    row0 = ntile * kPNTile + wave * 64 + n;
+    cb0 = (int32_t)lay.down_codes;
+    sb0 = (int32_t)lay.down_scales;
+  }
+  // record (kc, row): codes at 64 (kc R + row), scales at 8 (kc R + row)
+  const int voff_c = row0 * kGroupBytes + 16 * g, voff_s = row0 * kGroupScaleBytes;
+  u32x4 bc[2][4];
+  u32x2 bs[2][4];
+  auto load_b = [&](auto slot_c, int kc) {
+    constexpr int sl = decltype(slot_c)::value;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int rsub = MODE == kGateUp ? 16 * (s & 1) : 16 * s;  // row offset of the subtile
+      const bool up = MODE == kGateUp && s >= 2;
+      bc[sl][s] = buf_load16(rs, voff_c + rsub * kGroupBytes, cb0 + (up ? cb_up : 0) + kc * wrows * kGroupBytes);
+      bs[sl][s] = buf_load8(rs, voff_s + rsub * kGroupScaleBytes, sb0 + (up ? sb_up : 0) + kc * wrows * kGroupScaleBytes);
+    }
+  };
+
+  // ---- activations: piece j of this thread = row r_j, logical 16-byte chunk lc of the K chunk ----
+  const int a_ld = MODE == kDown ? F : H;
+  const int lc = threadIdx.x & 15;
+  int a_src[kPAPer];  // element offset of the piece in the activation matrix
+  // LDS element offset of piece j: row r_j = r_0 + 32 j has the same r & 15, so only the row moves
+  const int a_dst0 = (threadIdx.x >> 4) * kKC + ((lc ^ ((threadIdx.x >> 4) & 15)) * 8);
+  constexpr int kRowStep = 64 * kPWaves / 16;
+  static_assert(kRowStep % 16 == 0, "pieces keep their chunk swizzle");
+#pragma unroll
+  for (int j = 0; j < kPAPer; ++j) {
+    const int r = (threadIdx.x >> 4) + kRowStep * j;
+    const int rr = r < it.rows ? r : 0;  // padding rows copy row 0 (their outputs are dropped)
+    const int src = MODE == kGateUp ? a.row_tok[it.row0 + rr] : it.row0 + rr;
+    a_src[j] = src * a_ld + lc * 8;
+  }
+  auto load_a = [&](u32x4 (&v)[kPAPer], int kc) {
+#pragma unroll
+    for (int j = 0; j < kPAPer; ++j) v[j] = *(const u32x4*)(a.a16 + a_src[j] + kc * kKC);
+  };
+  auto store_a = [&](const u32x4 (&v)[kPAPer], uint16_t* buf) {
+#pragma unroll
+    for (int j = 0; j < kPAPer; ++j) *(u32x4*)(buf + a_dst0 + kRowStep * kKC * j) = v[j];
+  };
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  float4v acc[kMSub][4];
+#pragma unroll
+  for (int i = 0; i < kMSub; ++i)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[i][s] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  // ---- prologue: A(0), A(1) in LDS, A(2) and B(0) in flight -------------------------------------
+  u32x4 av[kPAPer];
+  {
+    u32x4 a0[kPAPer];
+    load_a(a0, 0);
+    load_a(av, 1);
+    load_b(std::integral_constant<int, 0>{}, 0);
+    store_a(a0, As[0]);
+    store_a(av, As[1]);
+    load_a(av, 2);
+    barrier();
+  }
+
+  static_for<NK>([&](auto kc_c) {
+    constexpr int kc = decltype(kc_c)::value;
+    constexpr int sl = kc % 2;
+    if constexpr (kc + 1 < NK) load_b(std::integral_constant<int, (kc + 1) % 2>{}, kc + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* Ab = As[kc % 3];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      // fragment read: row 16i + n, inputs 32 d + 8 g .. +7 = logical chunk 4d + g -> physical
+      // chunk (4d + g) ^ n
+      const int pcol = ((4 * d + g) ^ n) * 8;
+      half8 bf[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint32_t sw = bs[sl][s][d >> 1];
+        const uint32_t sv = (d & 1) ? (sw >> 16) : (sw & 0xFFFFu);
+        bf[s] = dequant_word_k(bc[sl][s][d], __builtin_bit_cast(half2v, sv | (sv << 16)), uk);
+      }
+#pragma unroll
+      for (int i = 0; i < kMSub; ++i) {
+        if (i < ms) {
+          const half8 af = *(const half8*)(Ab + (16 * i + n) * kKC + pcol);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+            acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[s], acc[i][s], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kc + 2 < NK) {
+      store_a(av, As[(kc + 2) % 3]);  // its stage was last read in chunk kc - 1
+      if constexpr (kc + 3 < NK) load_a(av, kc + 3);
+    }
+    if constexpr (kc + 1 < NK) barrier();
+  });
+
+  // ---- epilogue: lane holds D[16i + 4g + r][16s + n] -----------------------------------------
+#pragma unroll
+  for (int i = 0; i < kMSub; ++i) {
+    if (i >= ms) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * i + 4 * g + r;
+      if (row >= it.rows) continue;
+      if constexpr (MODE == kGateUp) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const float gv = acc[i][s][r], uv = acc[i][s + 2][r];
+          const int col = ntile * (kPNTile / 2) + wave * 32 + 16 * s + n;
+          a.h_out[(size_t)(it.row0 + row) * F + col] = (_Float16)(silu(gv) * uv);
+        }
+      } else {
+        const float wv = a.row_w[it.row0 + row];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const int col = ntile * kPNTile + wave * 64 + 16 * s + n;
+          a.y_out[(size_t)(it.row0 + row) * H + col] = acc[i][s][r] * wv;
+        }
+      }
+    }
+  }
+  (void)K;
+}
+
 // x (bf16) -> fp16, exact for values inside the fp16 normal range.
 __global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* __restrict__ x, _Float16* __restrict__ y,
                                                      size_t n) {
@@ -357,22 +568,34 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   a.F = F;
   a.T = T;
 
-  // gate/up + SwiGLU: h16[row][F]
-  a.n_ntiles = F / (kNTileW / 2);
-  a.n_works = max_items * a.n_ntiles;
+  // gate/up + SwiGLU: h16[row][F]; the pipelined kernel at H = 2048 (16 chunks), F % 256 == 0
   a.a16 = (const uint16_t*)b.x16;
   a.row_tok = g.row_tok;
   a.h_out = b.h16;
-  err = launch_timed(kTimePrefillGateUp, k_expert_gemm<kGateUp>, round8(a.n_works), 256, 0, st, a);
+  if (H == 16 * kKC && F % (kPNTile / 2) == 0) {
+    a.n_ntiles = F / (kPNTile / 2);
+    a.n_works = max_items * a.n_ntiles;
+    err = launch_timed(kTimePrefillGateUp, k_expert_gemm_pipe<kGateUp, 16>, round8(a.n_works), 64 * kPWaves, 0, st, a);
+  } else {
+    a.n_ntiles = F / (kNTileW / 2);
+    a.n_works = max_items * a.n_ntiles;
+    err = launch_timed(kTimePrefillGateUp, k_expert_gemm<kGateUp>, round8(a.n_works), 256, 0, st, a);
+  }
   if (err != hipSuccess) return err;
 
-  // down: y_rows[row][H] = w_row * (Wd h)
-  a.n_ntiles = H / kNTileW;
-  a.n_works = max_items * a.n_ntiles;
+  // down: y_rows[row][H] = w_row * (Wd h); the pipelined kernel at F = 768 (6 chunks), H % 512 == 0
   a.a16 = (const uint16_t*)b.h16;
   a.row_w = g.row_w;
   a.y_out = b.y_rows;
-  err = launch_timed(kTimePrefillDown, k_expert_gemm<kDown>, round8(a.n_works), 256, 0, st, a);
+  if (F == 6 * kKC && H % kPNTile == 0) {
+    a.n_ntiles = H / kPNTile;
+    a.n_works = max_items * a.n_ntiles;
+    err = launch_timed(kTimePrefillDown, k_expert_gemm_pipe<kDown, 6>, round8(a.n_works), 64 * kPWaves, 0, st, a);
+  } else {
+    a.n_ntiles = H / kNTileW;
+    a.n_works = max_items * a.n_ntiles;
+    err = launch_timed(kTimePrefillDown, k_expert_gemm<kDown>, round8(a.n_works), 256, 0, st, a);
+  }
   if (err != hipSuccess) return err;
 
   const size_t nc = (size_t)T * (H / 4);

@@ -41,19 +41,44 @@ MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, 
     key[i] = e < E ? (((uint64_t)f32_order_key(f) << 32) | (uint32_t)~e) : 0ull;
   }
   if (__any(nan_seen) && lane == 0) set_error(ctrl, MOE_DERR_NAN);
-  uint64_t best = 0;
-#pragma unroll
-  for (int i = 0; i < kPerLane; ++i) best = key[i] > best ? key[i] : best;
   uint64_t mine = 0;  // lane r keeps the r-th selection
-  for (int r = 0; r < k; ++r) {
-    const uint64_t win = wave_max_u64(best);
-    mine = lane == r ? win : mine;
-    // the lane holding the winner drops it; every lane recomputes its best (no branches)
-    best = 0;
+  if constexpr (kPerLane == 8) {
+    // each lane sorts its 8 keys (descending, odd-even merge network); a round takes the wave
+    // maximum of the lanes' heads and the winning lane shifts its list by one
+    auto cx = [&](int a, int b) {
+      const uint64_t hi = key[a] > key[b] ? key[a] : key[b];
+      const uint64_t lo = key[a] > key[b] ? key[b] : key[a];
+      key[a] = hi;
+      key[b] = lo;
+    };
+    cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+    cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+    cx(1, 2); cx(5, 6);
+    cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+    cx(2, 4); cx(3, 5);
+    cx(1, 2); cx(3, 4); cx(5, 6);
+    for (int r = 0; r < k; ++r) {
+      const uint64_t win = wave_max_u64(key[0]);
+      mine = lane == r ? win : mine;
+      const bool took = key[0] == win;  // one lane: keys are distinct
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      key[i] = key[i] == win ? 0ull : key[i];
-      best = key[i] > best ? key[i] : best;
+      for (int i = 0; i < kPerLane - 1; ++i) key[i] = took ? key[i + 1] : key[i];
+      key[kPerLane - 1] = took ? 0ull : key[kPerLane - 1];
+    }
+  } else {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kPerLane; ++i) best = key[i] > best ? key[i] : best;
+    for (int r = 0; r < k; ++r) {
+      const uint64_t win = wave_max_u64(best);
+      mine = lane == r ? win : mine;
+      // the lane holding the winner drops it; every lane recomputes its best (no branches)
+      best = 0;
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) {
+        key[i] = key[i] == win ? 0ull : key[i];
+        best = key[i] > best ? key[i] : best;
+      }
     }
   }
   const int my_i = (int)~(uint32_t)mine;
@@ -91,6 +116,32 @@ MOE_DEV int block_exclusive_scan(int v, int* lds_wave_sums, int* total) {
     if (lane >= o) incl += u;
   }
   if (lane == 63) lds_wave_sums[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < n_waves; ++i) {
+    const int s = lds_wave_sums[i];
+    if (i < wave) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+// The same scan with DPP lane moves (no LDS crossbar round trips inside the wave): inclusive
+// within each row of 16 by shifts of 1, 2, 4, 8, then rows 1 and 3 add lane 15 of the row
+// before, rows 2 and 3 add lane 31.
+MOE_DEV int block_exclusive_scan_dpp(int v, int* lds_wave_sums, int* total) {
+  const int wave = threadIdx.x >> 6, n_waves = blockDim.x >> 6;
+  int incl = v;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);  // row_shr:8
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  const int wave_total = __builtin_amdgcn_readlane(incl, 63);
+  if ((threadIdx.x & 63) == 0) lds_wave_sums[wave] = wave_total;
   __syncthreads();
   int base = 0, tot = 0;
   for (int i = 0; i < n_waves; ++i) {
@@ -194,7 +245,7 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
 struct PlanShared {
   uint32_t tok_mask[kMaxExperts];
   int32_t slot_of[kMaxExperts];
-  uint8_t choice[kMaxExperts][kMaxDecodeTok];
+  uint32_t choice[kMaxExperts];  // 4 bits per token: position j of the expert in its top-k
   int wave_sums[16];
   int bad;
 };
@@ -205,7 +256,7 @@ struct PlanShared {
 MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table, int n_slots,
                         int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell,
                         PlanShared& sh, bool slots_staged = false) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) sh.tok_mask[e] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sh.tok_mask[e] = sh.choice[e] = 0;
   if (threadIdx.x == 0) sh.bad = 0;
   __syncthreads();
   const int n_pairs = T * k;
@@ -216,7 +267,7 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
       atomicOr(&sh.bad, MOE_DERR_EXPERT_ID);
     } else {
       atomicOr(&sh.tok_mask[e], 1u << t);
-      sh.choice[e][t] = (uint8_t)j;
+      atomicOr(&sh.choice[e], (uint32_t)j << (4 * t));
       const int s = slots_staged ? sh.slot_of[e] : table ? table[e] : e;
       if (!slots_staged) sh.slot_of[e] = s;  // every writer of e writes the same value
       if (s >= n_slots) atomicOr(&sh.bad, MOE_DERR_SLOT);
@@ -234,9 +285,11 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
       if (sh.slot_of[e] < 0) ++n_mis;
     }
   }
-  int n_tasks, n_miss;
-  int tpos = block_exclusive_scan(n_sub, sh.wave_sums, &n_tasks);
-  int mpos = block_exclusive_scan(n_mis, sh.wave_sums, &n_miss);
+  // task and miss positions from one scan of the packed pair (n_sub, n_mis): totals stay < 2^16
+  int packed_total;
+  const int packed = block_exclusive_scan_dpp(n_sub | (n_mis << 16), sh.wave_sums, &packed_total);
+  int tpos = packed & 0xFFFF, mpos = packed >> 16;
+  const int n_tasks = packed_total & 0xFFFF, n_miss = packed_total >> 16;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
@@ -244,9 +297,7 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     if (!m) continue;
     const int s = sh.slot_of[e];
     if (s < 0) miss_ids[mpos++] = e;
-    uint32_t choice = 0;
-    for (int t = 0; t < T; ++t)
-      if (m & (1u << t)) choice |= (uint32_t)sh.choice[e][t] << (4 * t);
+    const uint32_t choice = sh.choice[e];
     DecodeTask tk;
     tk.expert = e;
     tk.slot = s;

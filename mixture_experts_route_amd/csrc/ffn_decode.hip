@@ -27,7 +27,9 @@
 //   down: one wave per (task, 16 output rows) over all F inputs.  A rows are the (hi, lo) row
 //     pairs of the task's tokens (<= 8 tokens -> <= 16 rows), so one MFMA per block covers both
 //     parts.  Writes each pair's output row y_e.
-//   combine: y[t] = sum_j w[t][j] * y_{e_j}[t] (j = 0..k-1), then + y_shared[t]: fixed order.
+//   combine: y[t] = sum_j w[t][j] * y_{e_j}[t] (j = 0..k-1), then + y_shared[t]: fixed order,
+//     done inside the down launch by the last workgroup to finish each row tile (a counter per
+//     tile; the pair rows go through agent-scope stores and loads).
 #include "kernels.hpp"
 
 namespace moe {
@@ -159,6 +161,7 @@ struct DecodeArgs {
   int H, F, T, k, n_shared;
   int tiles_gu;  // workgroups per task, gate/up
   int tiles_dn;  // workgroups per task, down
+  int32_t* tile_done;  // per down row tile: workgroups finished (control words, zero between calls)
 };
 
 // ---- activation rows in LDS -----------------------------------------------------------------
@@ -363,17 +366,69 @@ static size_t gate_up_lds_bytes(int H, int rows, int waves) {
   return xs > red ? xs : red;
 }
 
+// ---- combine inside the down kernels ------------------------------------------------------------
+// Each down workgroup writes its rows of every pair with agent-scope stores (written through to
+// the coherence point the XCDs share), waits for them, and counts itself in its row tile's
+// counter; the workgroup that completes a tile's count (every task's workgroup for those rows has
+// finished) combines the tile's rows after an agent-scope acquire:
+// y[t][o] = sum_j w[t][j] * y_pair[t k + j][o], then + y_pair[T k + t][o], in that order.
+// No workgroup waits on another.
+MOE_DEV void store_pair(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+MOE_DEV void combine_tile_if_last(const DecodeArgs& a, int tile, int tile_rows) {
+  __shared__ int s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's pair stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int n_wg = (int)gridDim.x / a.tiles_dn;  // one workgroup per task slot for this tile
+    const int old = __hip_atomic_fetch_add(&a.tile_done[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == n_wg - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(&a.tile_done[tile], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // acquire: drop this XCD's cached copies, so the plain loads below see the pairs just written
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const int r0 = tile * tile_rows;
+  const int rr4 = min(tile_rows, a.H - r0) / 4;
+  for (int i = threadIdx.x; i < a.T * rr4; i += blockDim.x) {
+    const int t = i / rr4, o = r0 + 4 * (i - t * rr4);
+    // every load in flight at once (rows and weights past k clamped to j = 0, then not used)
+    float4 v[kMaxK + 1];
+    float w[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      const int jj = j < a.k ? j : 0;
+      w[j] = a.topk_w[t * a.k + jj];
+      v[j] = *(const float4*)(a.y_pairs + (size_t)(t * a.k + jj) * a.H + o);
+    }
+    v[kMaxK] = *(const float4*)(a.y_pairs + (size_t)(a.T * a.k + (a.n_shared ? t : 0)) * a.H + o);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) {
+      const bool use = j < a.k;
+      acc.x = use ? fmaf(w[j], v[j].x, acc.x) : acc.x;
+      acc.y = use ? fmaf(w[j], v[j].y, acc.y) : acc.y;
+      acc.z = use ? fmaf(w[j], v[j].z, acc.z) : acc.z;
+      acc.w = use ? fmaf(w[j], v[j].w, acc.w) : acc.w;
+    }
+    if (a.n_shared) {
+      acc.x += v[kMaxK].x;
+      acc.y += v[kMaxK].y;
+      acc.z += v[kMaxK].z;
+      acc.w += v[kMaxK].w;
+    }
+    *(float4*)(a.y + (size_t)t * a.H + o) = acc;
+  }
+}
+
 // ---- down: y_e[pair][o] = Wd[o] . h[pair] for one task; RGW row groups of 16 per wave ----------
 // A rows 2 s + part: token slot s, part 0 = h_hi, 1 = h_lo, staged in LDS once per workgroup.
 template <int MAXTOK, int RGW>
-__global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
+MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) {
   constexpr int ROWS = 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int task = blockIdx.x / a.tiles_dn;
-  const int tile = blockIdx.x - task * a.tiles_dn;
   const DecodeTask tk = a.tasks[task];
-  if (task >= a.ctrl[kCtrlNTasks]) return;
   const uint8_t* blob = task_blob(a.src, tk);
   if (!blob) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
@@ -457,10 +512,19 @@ __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
     for (int s2 = 0; s2 < NR / 2; ++s2) {
       const int slot = 2 * g + s2;
       if (rg_live[r] && slot < n_tok)
-        a.y_pairs[(size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r]] =
-            acc[r][2 * s2] + acc[r][2 * s2 + 1];
+        store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
+                   acc[r][2 * s2] + acc[r][2 * s2 + 1]);
     }
   }
+}
+
+template <int MAXTOK, int RGW>
+__global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int task = blockIdx.x / a.tiles_dn;
+  const int tile = blockIdx.x - task * a.tiles_dn;
+  if (task < a.ctrl[kCtrlNTasks]) down_body<MAXTOK, RGW>(a, task, tile, smem);
+  combine_tile_if_last(a, tile, 16 * kDnWaves * RGW);
 }
 
 // ---- pipelined variants for tasks of up to 4 or 8 bf16 tokens ----------------------------------
@@ -605,16 +669,12 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
 
 // down: F = 128 kPipeDnGroups UNITS; A rows 2 s + part (token slot s, h hi / lo).
 template <int MAXTOK, int UNITS>
-__global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_down_pipe(DecodeArgs a) {
+MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) {
   constexpr int ROWS = 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
   constexpr int QG = kPipeDnGroups;
   constexpr int RGW = kPipeDnRGW;
-  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
-  const int task = blockIdx.x / a.tiles_dn;
-  const int tile = blockIdx.x - task * a.tiles_dn;
   const DecodeTask tk = a.tasks[task];
-  if (task >= a.ctrl[kCtrlNTasks]) return;
   const uint8_t* blob = task_blob(a.src, tk);
   if (!blob) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
@@ -713,35 +773,19 @@ __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_
     for (int s2 = 0; s2 < NR / 2; ++s2) {
       const int slot = 2 * g + s2;
       if (rg_live[r] && slot < n_tok)
-        a.y_pairs[(size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r]] =
-            acc[r][2 * s2] + acc[r][2 * s2 + 1];
+        store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
+                   acc[r][2 * s2] + acc[r][2 * s2 + 1]);
     }
   }
 }
 
-// ---- combine: y[t][o] = sum_j w[t][j] * y_pairs[t k + j][o] (+ y_pairs[T k + t][o]) ----------
-__global__ __launch_bounds__(256) void k_decode_combine(DecodeArgs a) {
-  const int per_tok = a.H / 4;
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= a.T * per_tok) return;
-  const int t = i / per_tok, o = (i - t * per_tok) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < a.k; ++j) {
-    const float w = a.topk_w[t * a.k + j];
-    const float4 v = *(const float4*)(a.y_pairs + (size_t)(t * a.k + j) * a.H + o);
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
-  }
-  if (a.n_shared) {
-    const float4 v = *(const float4*)(a.y_pairs + (size_t)(a.T * a.k + t) * a.H + o);
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
-  }
-  *(float4*)(a.y + (size_t)t * a.H + o) = acc;
+template <int MAXTOK, int UNITS>
+__global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_down_pipe(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  const int task = blockIdx.x / a.tiles_dn;
+  const int tile = blockIdx.x - task * a.tiles_dn;
+  if (task < a.ctrl[kCtrlNTasks]) down_pipe_body<MAXTOK, UNITS>(a, task, tile, smem);
+  combine_tile_if_last(a, tile, 16 * kPipeDnWaves * kPipeDnRGW);
 }
 
 // ---- dequantization check: one thread per code word, the same unpacking as the FFN kernels --
@@ -837,10 +881,7 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
     err = launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, kDnRGW<MAXTOK>>, max_tasks * a.tiles_dn, 64 * kDnWaves,
                        dn_lds, st, a);
   }
-  if (err != hipSuccess) return err;
-  const int n4 = a.T * a.H / 4;
-  k_decode_combine<<<(n4 + 255) / 256, 256, 0, st>>>(a);
-  return hipGetLastError();
+  return err;
 }
 
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
@@ -862,6 +903,7 @@ hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_t
   a.T = T;
   a.k = k;
   a.n_shared = n_shared;
+  a.tile_done = ctrl + kCtrlTileDone;
   const bool xb = x_dtype == MOE_BF16;
   static_assert(kTaskTok == kMaxDecodeTok, "a decode task holds every token of the step that chose its expert");
   if (T <= 1) return launch_decode_ffn_t<1>(a, max_tasks, xb, st);

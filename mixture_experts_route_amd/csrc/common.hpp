@@ -26,6 +26,7 @@ enum CtrlWord {
   kCtrlNTasks = 1,     // decode: number of expert tasks
   kCtrlMissCount = 2,  // residency: number of misses
   kCtrlNTiles = 3,     // prefill: number of m-tiles in the work list
+  kCtrlRouteDone = 4,  // decode route: router workgroups finished (zero between calls)
   kCtrlTileDone = 64,  // decode down: 64 per-row-tile counters (words 64..127), zero between calls
 };
 

@@ -340,9 +340,10 @@ __global__ __launch_bounds__(256) void k_decode_plan(const int32_t* __restrict__
 
 // ------------------------------------------------------------------------------------------
 // Decode route (<= 8 tokens): a router GEMV over all workgroups (each wave's first router row
-// is loaded before the activations are staged), then one workgroup that selects and plans.  The
-// two are separate launches: a kernel boundary is the cheapest way to make the logits of every
-// XCD visible to one workgroup (an in-kernel release would write back each XCD's L2).
+// is loaded before the activations are staged); the last workgroup to finish then selects and
+// plans, in the same launch.  The logits cross the XCDs through agent-scope stores and an
+// agent-scope acquire in that workgroup (a release fence in every workgroup would write back each
+// XCD's L2 many times over).
 // ------------------------------------------------------------------------------------------
 struct RouteArgs {
   const void* x;
@@ -362,7 +363,59 @@ struct RouteArgs {
 };
 
 
-template <bool X_BF16, bool R_BF16>
+// One workgroup: the top-k of every token (one wave per token, DPP arg-max) and, if asked, the
+// decode plan (residency check, task list, miss list, doorbell).  Needs >= 256 threads.
+template <int NPER>
+MOE_DEV void select_and_plan(const RouteArgs& a) {
+  __shared__ PlanShared sh;
+  __shared__ int32_t s_ids[kMaxDecodeTok * kMaxK];
+  const int wave = threadIdx.x >> 6;
+  // the slot table is loaded with the logits (issued first: one wait covers both) and goes to LDS
+  // after the selections, so the plan makes no dependent global load
+  constexpr int kTabPer = kMaxExperts / 256;  // blockDim.x >= 256
+  int32_t tab[kTabPer];
+#pragma unroll
+  for (int i = 0; i < kTabPer; ++i) {
+    const int e = min((int)(threadIdx.x + i * blockDim.x), a.E - 1);
+    tab[i] = a.table ? a.table[e] : e;
+  }
+  for (int t = wave; t < a.T; t += blockDim.x >> 6) {
+    select_topk_wave<NPER>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k,
+                           a.ctrl, s_ids + t * a.k);
+  }
+#pragma unroll
+  for (int i = 0; i < kTabPer; ++i) {
+    const int e = threadIdx.x + i * blockDim.x;
+    if (e < a.E) sh.slot_of[e] = tab[i];
+  }
+  __syncthreads();
+  if (a.plan)
+    build_plan(s_ids, a.T, a.k, a.E, a.n_shared, a.table, a.n_slots, a.miss_ids, a.tasks, a.ctrl, a.bell, sh, true);
+}
+
+// End of a router workgroup: its logits went out as agent-scope stores (written through to the
+// coherence point the XCDs share); it waits for them and counts itself; the workgroup that
+// completes the count (every router row is then written) acquires at agent scope and runs the
+// selection and the plan.  No workgroup waits on another.
+MOE_DEV void store_logit(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+template <int NPER>
+MOE_DEV void route_tail(const RouteArgs& a) {
+  __shared__ int s_last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's logit stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(&a.ctrl[kCtrlRouteDone], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = old == (int)gridDim.x - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0) __hip_atomic_store(&a.ctrl[kCtrlRouteDone], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  select_and_plan<NPER>(a);
+}
+
+template <bool X_BF16, bool R_BF16, int NPER>
 __global__ __launch_bounds__(256) void k_router_gemv(RouteArgs a) {
   extern __shared__ float xs[];  // [T][H]
   const int T = a.T, E = a.E, H = a.H;
@@ -424,10 +477,11 @@ __global__ __launch_bounds__(256) void k_router_gemv(RouteArgs a) {
     for (int t = 0; t < kMaxDecodeTok; ++t) {
       if (t < T) {
         const float sum = group_sum_dpp(acc[t], 64);
-        if (lane == 63) a.logits[(size_t)t * E + e] = sum + (a.bias ? a.bias[e] : 0.f);
+        if (lane == 63) store_logit(a.logits + (size_t)t * E + e, sum + (a.bias ? a.bias[e] : 0.f));
       }
     }
   }
+  route_tail<NPER>(a);
 }
 
 // Router GEMV on the matrix cores (bf16 router): one workgroup per 16 router rows, its 8 waves
@@ -448,7 +502,7 @@ MOE_DEV uint4 split_bf16_part(const float4& a, const float4& b, int part) {
   return make_uint4(q[0] | (q[1] << 16), q[2] | (q[3] << 16), q[4] | (q[5] << 16), q[6] | (q[7] << 16));
 }
 
-template <bool X_BF16>
+template <bool X_BF16, int NPER>
 __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(RouteArgs a) {
   __shared__ float red[kRouterWaves][16][16];  // [wave][A row][router row]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -507,39 +561,10 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(RouteArgs a) 
         if constexpr (X_BF16) sum += red[w][t][c];
         else sum += red[w][2 * t][c] + red[w][2 * t + 1][c];
       }
-      a.logits[(size_t)t * E + ee] = sum + (a.bias ? a.bias[ee] : 0.f);
+      store_logit(a.logits + (size_t)t * E + ee, sum + (a.bias ? a.bias[ee] : 0.f));
     }
   }
-}
-
-// One workgroup: the top-k of every token (one wave per token, DPP arg-max) and, if asked, the
-// decode plan (residency check, task list, miss list, doorbell).
-template <int NPER>
-__global__ __launch_bounds__(64 * kMaxDecodeTok) void k_decode_select(RouteArgs a) {
-  __shared__ PlanShared sh;
-  __shared__ int32_t s_ids[kMaxDecodeTok * kMaxK];
-  const int wave = threadIdx.x >> 6;
-  // the slot table is loaded with the logits (issued first: one wait covers both) and goes to LDS
-  // after the selections, so the plan makes no dependent global load
-  constexpr int kTabPer = kMaxExperts / 256;  // blockDim.x >= 256
-  int32_t tab[kTabPer];
-#pragma unroll
-  for (int i = 0; i < kTabPer; ++i) {
-    const int e = min((int)(threadIdx.x + i * blockDim.x), a.E - 1);
-    tab[i] = a.table ? a.table[e] : e;
-  }
-  for (int t = wave; t < a.T; t += blockDim.x >> 6) {
-    select_topk_wave<NPER>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k,
-                           a.ctrl, s_ids + t * a.k);
-  }
-#pragma unroll
-  for (int i = 0; i < kTabPer; ++i) {
-    const int e = threadIdx.x + i * blockDim.x;
-    if (e < a.E) sh.slot_of[e] = tab[i];
-  }
-  __syncthreads();
-  if (a.plan)
-    build_plan(s_ids, a.T, a.k, a.E, a.n_shared, a.table, a.n_slots, a.miss_ids, a.tasks, a.ctrl, a.bell, sh, true);
+  route_tail<NPER>(a);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -575,6 +600,22 @@ hipError_t launch_decode_plan(const int32_t* ids, int T, int k, int E, int n_sha
   return hipGetLastError();
 }
 
+template <int NPER>
+static hipError_t launch_router(const RouteArgs& a, int x_dtype, int r_dtype, hipStream_t st) {
+  if (r_dtype == MOE_BF16) {
+    // bf16 router: matrix-core GEMV
+    const int grid = (a.E + 15) / 16;
+    if (x_dtype == MOE_BF16)
+      return launch_timed(kTimeDecodeRoute, k_router_mfma<true, NPER>, grid, 64 * kRouterWaves, 0, st, a);
+    return launch_timed(kTimeDecodeRoute, k_router_mfma<false, NPER>, grid, 64 * kRouterWaves, 0, st, a);
+  }
+  // fp32 router: exact fp32 FMA GEMV
+  const int grid = (a.E + 3) / 4;
+  const uint32_t lds = (uint32_t)(a.T * a.H * sizeof(float));
+  if (x_dtype == MOE_BF16) return launch_timed(kTimeDecodeRoute, k_router_gemv<true, false, NPER>, grid, 256, lds, st, a);
+  return launch_timed(kTimeDecodeRoute, k_router_gemv<false, false, NPER>, grid, 256, lds, st, a);
+}
+
 hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias, int T,
                                int E, int H, int k, int n_shared, float* logits, int32_t* ids, float* w,
                                int32_t* ctrl, bool plan, const int32_t* table, int n_slots, int32_t* miss_ids,
@@ -598,25 +639,9 @@ hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r
   a.miss_ids = miss_ids;
   a.tasks = tasks;
   a.bell = bell;
-  hipError_t err;
-  if (r_dtype == MOE_BF16) {
-    // bf16 router: matrix-core GEMV
-    const int grid = (E + 15) / 16;
-    if (x_dtype == MOE_BF16) err = launch_timed(kTimeDecodeRoute, k_router_mfma<true>, grid, 64 * kRouterWaves, 0, st, a);
-    else err = launch_timed(kTimeDecodeRoute, k_router_mfma<false>, grid, 64 * kRouterWaves, 0, st, a);
-  } else {
-    // fp32 router: exact fp32 FMA GEMV
-    const int grid = (E + 3) / 4;
-    const uint32_t lds = (uint32_t)(T * H * sizeof(float));
-    if (x_dtype == MOE_BF16) err = launch_timed(kTimeDecodeRoute, k_router_gemv<true, false>, grid, 256, lds, st, a);
-    else err = launch_timed(kTimeDecodeRoute, k_router_gemv<false, false>, grid, 256, lds, st, a);
-  }
-  if (err != hipSuccess) return err;
-  // one wave per token (at least 4 waves for the plan)
-  const int threads = 64 * (T > 4 ? T : 4);
-  if (E <= 512) k_decode_select<8><<<1, threads, 0, st>>>(a);
-  else k_decode_select<16><<<1, threads, 0, st>>>(a);
-  return hipGetLastError();
+  // the router launch also selects and plans (its last workgroup); 8 or 16 logits per lane
+  if (E <= 512) return launch_router<8>(a, x_dtype, r_dtype, st);
+  return launch_router<16>(a, x_dtype, r_dtype, st);
 }
 
 }  // namespace moe

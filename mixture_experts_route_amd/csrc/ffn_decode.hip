@@ -238,6 +238,15 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
 
   const int task = blockIdx.x / a.tiles_gu;
   const int tile = blockIdx.x - task * a.tiles_gu;
+  const int H = a.H, F = a.F;
+  // ---- bf16 activations: the rows of every token of the step (row t = token t) are loaded
+  // before the task is known (they do not depend on it) and stored to LDS once the weight loads
+  // are issued; a lane picks its token slot's row when it reads its fragment.  fp32 rows (small
+  // shapes only) are split into hi / lo bf16 rows of the task's tokens by the threads below.
+  auto x_row = [&](int m) { return (const uint16_t*)a.x + (size_t)(m < a.T ? m : 0) * H; };
+  // bf16: ROWS * H / 8 chunks over 64 kGuRG H / 512 threads is at most MAXTOK / 2 per thread
+  u32x4 xv[(MAXTOK + 1) / 2];
+  if constexpr (X_BF16) stage_load(xv, ROWS, H, x_row);
   // the descriptor slot always exists (max_tasks of them): load it together with the count
   const DecodeTask tk = a.tasks[task];
   if (task >= a.ctrl[kCtrlNTasks]) return;
@@ -246,7 +255,6 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
     return;
   }
-  const int H = a.H, F = a.F;
   const BlobLayout lay = blob_layout(H, F);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
@@ -257,18 +265,10 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   const int q0 = kq * kGuQuadsPerWave;
   const int nq = min(kGuQuadsPerWave, NQ - q0);
   const int n_tok = __builtin_popcount(tk.tok_mask);
+  // A row of this lane in LDS: bf16, the token of slot n (none past the task's tokens); fp32, row n
+  const int arow = X_BF16 ? (n < n_tok ? task_token(tk.tok_mask, n) : ROWS) : n;
 
-  // ---- activations -> LDS: bf16 rows loaded first and stored once the weight loads are issued;
-  // fp32 rows (small shapes only) split into hi / lo bf16 rows by the threads right away
-  auto x_row = [&](int m) {
-    const int tok = task_token(tk.tok_mask, m < n_tok ? m : 0);
-    return (const uint16_t*)a.x + (size_t)tok * H;
-  };
-  // bf16: ROWS * H / 8 chunks over 64 kGuRG H / 512 threads is at most MAXTOK / 2 per thread
-  u32x4 xv[(MAXTOK + 1) / 2];
-  if constexpr (X_BF16) {
-    stage_load(xv, ROWS, H, x_row);
-  } else {
+  if constexpr (!X_BF16) {
     for (int c = threadIdx.x; c < ROWS * (H / 8); c += blockDim.x) {
       const int m = c / (H / 8), col = (c - m * (H / 8)) * 8;
       const int slot = m >> 1;
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
     if (qi >= nq) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bf16x8 A = lds_fragment(smem, ROWS, H, n, g, (q0 + qi) * kGroupElems + 32 * i);
+      const bf16x8 A = lds_fragment(smem, ROWS, H, arow, g, (q0 + qi) * kGroupElems + 32 * i);
       const float4v O = mfma_bf16(A, neg, zero);
       const float4v Dg = mfma_bf16(A, codes_q136(word_at(cg[qi], i)), O);
       const float4v Du = mfma_bf16(A, codes_q136(word_at(cu[qi], i)), O);
@@ -550,6 +550,15 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int task = blockIdx.x / a.tiles_gu;
   const int tile = blockIdx.x - task * a.tiles_gu;
+  constexpr int H = 128 * QG * UNITS;
+  // the rows of every token of the step (row t = token t), loaded before the task is known
+  auto x_row = [&](int m) { return (const uint16_t*)a.x + (size_t)(m < a.T ? m : 0) * H; };
+  // ROWS * H / 8 chunks over 64 kPipeGuWaves threads
+  constexpr int XC = (ROWS * (H / 8) + 64 * kPipeGuWaves - 1) / (64 * kPipeGuWaves);
+  u32x4 xv[XC];
+  // chunks in flight (fewer when the staged rows need many registers)
+  constexpr int NBUF = XC > 8 ? 2 : kPipeGuBufs;
+  stage_load(xv, ROWS, H, x_row);
   const DecodeTask tk = a.tasks[task];
   if (task >= a.ctrl[kCtrlNTasks]) return;
   const uint8_t* blob = task_blob(a.src, tk);
@@ -557,25 +566,14 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
     return;
   }
-  constexpr int H = 128 * QG * UNITS;
   const int F = a.F;
   const BlobLayout lay = blob_layout(H, F);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int row = (tile * kPipeGuWaves + wave) * 16 + n;
   const int n_tok = __builtin_popcount(tk.tok_mask);
+  const int arow = n < n_tok ? task_token(tk.tok_mask, n) : ROWS;  // LDS row of this lane's slot
   const Unpack uk = make_unpack();
-
-  auto x_row = [&](int m) {
-    const int tok = task_token(tk.tok_mask, m < n_tok ? m : 0);
-    return (const uint16_t*)a.x + (size_t)tok * H;
-  };
-  // ROWS * H / 8 chunks over 64 kPipeGuWaves threads
-  constexpr int XC = (ROWS * (H / 8) + 64 * kPipeGuWaves - 1) / (64 * kPipeGuWaves);
-  u32x4 xv[XC];
-  // chunks in flight (fewer when the staged rows need many registers)
-  constexpr int NBUF = XC > 8 ? 2 : kPipeGuBufs;
-  stage_load(xv, ROWS, H, x_row);
 
   const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob, lay.total);
   const int voff_c = row * kGroupBytes + 16 * g, voff_s = row * kGroupScaleBytes;
@@ -621,7 +619,7 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
     for (int qi = 0; qi < QG; ++qi) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 A = lds_fragment(smem, ROWS, H, n, g, (u * QG + qi) * kGroupElems + 32 * i);
+        const bf16x8 A = lds_fragment(smem, ROWS, H, arow, g, (u * QG + qi) * kGroupElems + 32 * i);
         const float4v O = mfma_bf16(A, neg, zero);
         const float4v Dg = mfma_bf16(A, codes_q136(word_at(cg[b][qi], i), uk), O);
         const float4v Du = mfma_bf16(A, codes_q136(word_at(cu[b][qi], i), uk), O);

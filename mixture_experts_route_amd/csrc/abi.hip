@@ -71,7 +71,7 @@ static WsLayout ws_layout(const moe_dims* d, int T) {
   L.h16 = off;
   off = align256(off + 2 * P * d->ffn);
   L.y_rows = off;
-  off = align256(off + 4 * P * d->hidden);
+  off = align256(off + 2 * P * d->hidden);
   L.total = off;
   return L;
 }
@@ -220,7 +220,7 @@ static int do_prefill_ffn(const moe_dims* d, const moe_layer_weights* w, const i
   PrefillBuffers b;
   b.x16 = at<_Float16>(ws, L.x16);
   b.h16 = at<_Float16>(ws, L.h16);
-  b.y_rows = at<float>(ws, L.y_rows);
+  b.y_rows = at<_Float16>(ws, L.y_rows);
   return hip_status(launch_prefill_ffn(d->hidden, d->ffn, d->top_k, d->n_experts, d->n_shared, T, source_of(w, table),
                                        x, g, b, y, ctrl, st));
 }

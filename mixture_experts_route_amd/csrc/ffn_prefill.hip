@@ -35,6 +35,9 @@ constexpr int kMSub = kTileRows / 16;     // 16-row subtiles per item
 constexpr int kNTileW = 256;              // weight rows per workgroup (4 waves x 64)
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
+// Router GEMM rows per work: 32 (not a full 128-row tile), so that a 4K-token call has 256 works
+// (x 2 router tiles) instead of 64 and the router streams through every CU.
+constexpr int kRouterTileRows = 32;
 
 struct GemmArgs {
   ExpertSource src;
@@ -52,7 +55,8 @@ struct GemmArgs {
   const uint16_t* wr;      // router: Wr bf16 [E][H]
   const float* bias;       // router: bias [E] or null
   _Float16* h_out;         // gate/up: h16 [P][F]
-  float* y_out;            // down: y_rows [P][H]; router: logits [T][E]
+  float* y_out;            // router: logits [T][E]
+  _Float16* y16_out;       // down: y_rows [P][H], router-weighted, fp16
 };
 
 MOE_DEV const uint8_t* bucket_blob(const ExpertSource& s, int bucket, int E) {
@@ -132,8 +136,8 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   const uint8_t* blob = nullptr;
   if constexpr (MODE == kRouter) {
     it.bucket = 0;
-    it.row0 = item_id * kTileRows;
-    it.rows = min(kTileRows, a.T - it.row0);
+    it.row0 = item_id * kRouterTileRows;
+    it.rows = min(kRouterTileRows, a.T - it.row0);
     if (it.rows <= 0) return;
   } else {
     it = a.items[item_id];
@@ -316,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int col = ntile * kNTileW + wave * 64 + 16 * s + n;
-          a.y_out[(size_t)(it.row0 + row) * H + col] = acc[i][s][r] * wv;
+          a.y16_out[(size_t)(it.row0 + row) * H + col] = (_Float16)(acc[i][s][r] * wv);
         }
       } else {
 #pragma unroll
@@ -506,7 +510,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int col = ntile * kPNTile + wave * 64 + 16 * s + n;
-          a.y_out[(size_t)(it.row0 + row) * H + col] = acc[i][s][r] * wv;
+          a.y16_out[(size_t)(it.row0 + row) * H + col] = (_Float16)(acc[i][s][r] * wv);
         }
       }
     }
@@ -521,25 +525,34 @@ __global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* __restrict_
     y[i] = (_Float16)__uint_as_float((uint32_t)x[i] << 16);
 }
 
-// y[t] = sum_{j<k} y_rows[inv[t*k+j]] + y_rows[inv[T*k+t]] (rows already weighted), fixed order.
-__global__ __launch_bounds__(256) void k_prefill_combine(const float* __restrict__ y_rows,
+// y[t] = sum_{j<k} y_rows[inv[t*k+j]] + y_rows[inv[T*k+t]] (rows already weighted, fp16), fixed
+// order, fp32 sums.  Every row position and every row of a thread's outputs is loaded before any
+// is added (no chain of dependent loads).
+__global__ __launch_bounds__(256) void k_prefill_combine(const _Float16* __restrict__ y_rows,
                                                           const int32_t* __restrict__ inv, int T, int k,
                                                           int n_shared, int H, float* __restrict__ y) {
+  typedef _Float16 half4v __attribute__((ext_vector_type(4)));
   const int H4 = H / 4;
   for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)T * H4;
        idx += (size_t)gridDim.x * blockDim.x) {
     const int t = (int)(idx / H4), o4 = (int)(idx - (size_t)t * H4);
+    int pos[kMaxK + 1];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) pos[j] = j < k ? inv[t * k + (j < k ? j : 0)] : -1;
+    pos[kMaxK] = n_shared ? inv[T * k + t] : -1;
+    half4v v[kMaxK + 1];
+#pragma unroll
+    for (int j = 0; j <= kMaxK; ++j)
+      v[j] = ((const half4v*)(y_rows + (size_t)(pos[j] < 0 ? 0 : pos[j]) * H))[o4];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int pos = inv[t * k + j];
-      if (pos < 0) continue;
-      const float4 v = ((const float4*)(y_rows + (size_t)pos * H))[o4];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-    }
-    if (n_shared) {
-      const int pos = inv[T * k + t];
-      const float4 v = ((const float4*)(y_rows + (size_t)pos * H))[o4];
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+#pragma unroll
+    for (int j = 0; j <= kMaxK; ++j) {
+      if (pos[j] >= 0) {
+        acc.x += (float)v[j].x;
+        acc.y += (float)v[j].y;
+        acc.z += (float)v[j].z;
+        acc.w += (float)v[j].w;
+      }
     }
     ((float4*)(y + (size_t)t * H))[o4] = acc;
   }
@@ -586,7 +599,7 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   // down: y_rows[row][H] = w_row * (Wd h); the pipelined kernel at F = 768 (6 chunks), H % 512 == 0
   a.a16 = (const uint16_t*)b.h16;
   a.row_w = g.row_w;
-  a.y_out = b.y_rows;
+  a.y16_out = b.y_rows;
   if (F == 6 * kKC && H % kPNTile == 0) {
     a.n_ntiles = H / kPNTile;
     a.n_works = max_items * a.n_ntiles;
@@ -616,7 +629,7 @@ hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const flo
   a.bias = bias;
   a.y_out = logits;
   a.n_ntiles = (E + kNTileW - 1) / kNTileW;
-  a.n_works = ((T + kTileRows - 1) / kTileRows) * a.n_ntiles;
+  a.n_works = ((T + kRouterTileRows - 1) / kRouterTileRows) * a.n_ntiles;
   k_expert_gemm<kRouter><<<round8(a.n_works), 256, 0, st>>>(a);
   return hipGetLastError();
 }

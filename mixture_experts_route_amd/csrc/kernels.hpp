@@ -118,7 +118,7 @@ hipError_t launch_group(const int32_t* ids, const float* topk_w, int T, int k, i
 struct PrefillBuffers {
   _Float16* x16;   // [T][H]
   _Float16* h16;   // [P][F]
-  float* y_rows;   // [P][H]
+  _Float16* y_rows;  // [P][H] router-weighted expert outputs (fp16)
 };
 hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, const ExpertSource& src,
                               const void* x_bf16, const GroupBuffers& g, const PrefillBuffers& b, float* y,

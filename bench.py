@@ -127,9 +127,9 @@ def cpu_baseline_decode(n_tokens: int, seed=0, cfg=2, layer=0):
 
 
 def measured_traffic(path="profiles/decode1_gate_up_traffic.txt"):
-    """HBM bytes per launch of the decode gate/up kernel from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy), or None once the kernel's sources
-    differ from the ones the counters were taken on."""
+    """HBM bytes per launch of a decode gate/up kernel from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy; for the 48-layer decode the mean over
+    its launches), or None once the kernel's sources differ from the ones the counters were taken on."""
     import hashlib
 
     root = os.path.dirname(os.path.abspath(__file__))
@@ -394,6 +394,9 @@ def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
     for layer in range(n_layers):
         keys = [S.stream_key(0, cfg, "blob", layer, e) for e in range(E)] + [S.stream_key(0, cfg, "shared", layer, 0)]
         S.expert_blobs_torch_batch(keys, H, F, arena[layer * per_layer:(layer + 1) * per_layer])
+        if layer % 12 == 11:
+            torch.cuda.synchronize()
+            print(f"bench: 48-layer arena, {layer + 1} layers generated", file=sys.stderr, flush=True)
     routers = [S.bf16_normal_torch(S.stream_key(0, cfg, "router", layer, 0), (E, H), 0.02, dev)
                for layer in range(n_layers)]
     biases = [torch.from_numpy(S.zipf_bias(S.rank_permutation(0, cfg, layer, 0, E), S.ZIPF_C)).to(dev)
@@ -496,7 +499,7 @@ def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": gu_gbs / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic("profiles/decode48_gate_up_traffic.txt"),
             "bytes_per_launch": float(gu_bytes.mean()),
             "avg_launch_us": float(gu_s.mean() * 1e6),
         },
@@ -647,6 +650,10 @@ def main():
         print("bench.py measures one GPU: the layer's data-parallel scale-out has no exchange on the path, "
               "so only --gpus 1 is run here", file=sys.stderr)
         sys.exit(2)
+    def progress(msg):
+        print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+    progress("single-token decode")
     res = bench_decode1(args)
     if args.copy_calibration:
         import torch
@@ -658,15 +665,18 @@ def main():
         torch.cuda.synchronize()
         res["copy_calibration_bytes"] = 256 << 20
     if args.decode48_steps > 0:
+        progress("48-layer batched decode")
         res["decode_8tok_48layers"] = bench_decode48(args.decode48_steps, 4, not args.eager)
         import torch
 
         torch.cuda.empty_cache()
     if args.pool_steps > 0:
+        progress("slot-pool decode")
         res["decode_slot_pool_48layers"] = bench_pool(args.pool_steps)
     for T in [int(v) for v in args.prefill.split(",") if v.strip()]:
         steps = args.prefill_steps if T <= 8192 else max(4, args.prefill_steps // 4)
         sample = None if args.no_cpu_baseline else (48 if T == 4096 else None)
+        progress(f"{T}-token prefill")
         res[f"prefill_{T}"] = bench_prefill(T, steps, max(2, steps // 5), sample)
     print(json.dumps(res), flush=True)
 

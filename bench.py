@@ -515,7 +515,7 @@ def pool_slots(layer: int) -> int:
     return 240 if layer < 10 else 92 if layer < 20 else 60
 
 
-def bench_pool(steps: int, topic_every: int = 128, n_layers: int = 48):
+def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
     """Single-token decode through 48 layers whose experts live in 5,000 HBM slots and pinned host
     memory (exclusive tiers); per-layer Zipf(1.1) bias redrawn every `topic_every` steps; misses
     filled from the host by the pool service on a copy stream."""
@@ -565,7 +565,7 @@ def bench_pool(steps: int, topic_every: int = 128, n_layers: int = 48):
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     ws = torch.zeros(N.moe_workspace_bytes(d, T) // 4 + 64, dtype=torch.int32, device=dev)
     N.moe_workspace_init(ws)
-    compute, copy = N.new_stream(), N.new_stream()
+    compute, copy = streams
 
     def step(s):
         topic = s // topic_every
@@ -573,8 +573,15 @@ def bench_pool(steps: int, topic_every: int = 128, n_layers: int = 48):
             bell = N.moe_pool_arm(L["pool"])
             w = N.layer_weights(L["router"], L["arena"], stride, L["n_slots"], L["shared"], L["biases"][topic])
             N.moe_layer_forward(d, w, L["table"], xs[layer][s:s + 1], T, y, ws, bell=bell, stream=compute)
-        for L in layers:
-            N.moe_pool_serve(L["pool"], ws, copy)
+        for i, L in enumerate(layers):
+            try:
+                N.moe_pool_serve(L["pool"], ws, copy)
+            except N.MoeError:
+                # a stream that waits on the pool cannot drain once its fill failed: report and leave
+                # without the runtime's teardown (which would wait for that stream)
+                print(f"bench: slot-pool step {s} layer {i}: serve failed; control words "
+                      f"{ws[:8].cpu().tolist()}", file=sys.stderr, flush=True)
+                os._exit(3)
 
     torch.cuda.synchronize()
     for s in range(2):
@@ -611,8 +618,6 @@ def bench_pool(steps: int, topic_every: int = 128, n_layers: int = 48):
     hb.free()
     for L in layers:
         N.moe_pool_destroy(L["pool"])
-    N.free_stream(compute)
-    N.free_stream(copy)
     elapsed = t1 - t0
     return {
         "workload": "single-token decode through 48 layers with 5,000 HBM expert slots (240 / 92 / 60 per early / "
@@ -653,6 +658,14 @@ def main():
     def progress(msg):
         print(f"bench: {msg}", file=sys.stderr, flush=True)
 
+    # The slot pool's compute and copy streams are created first, while no other stream exists:
+    # the runtime spreads streams over a few hardware queues, and the compute stream's in-stream
+    # wait must not sit in front of the copies on a shared queue.
+    pool_streams = None
+    if args.pool_steps > 0:
+        from mixture_experts_route_amd import native as N
+
+        pool_streams = (N.new_stream(), N.new_stream())
     progress("single-token decode")
     res = bench_decode1(args)
     if args.copy_calibration:
@@ -672,7 +685,7 @@ def main():
         torch.cuda.empty_cache()
     if args.pool_steps > 0:
         progress("slot-pool decode")
-        res["decode_slot_pool_48layers"] = bench_pool(args.pool_steps)
+        res["decode_slot_pool_48layers"] = bench_pool(args.pool_steps, pool_streams)
     for T in [int(v) for v in args.prefill.split(",") if v.strip()]:
         steps = args.prefill_steps if T <= 8192 else max(4, args.prefill_steps // 4)
         sample = None if args.no_cpu_baseline else (48 if T == 4096 else None)

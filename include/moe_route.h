@@ -249,7 +249,14 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w,
  * stream -> moe_pool_serve on the host (it blocks until the call's check has run, then
  * enqueues the copies, the table update and the release of the compute stream on
  * `copy_stream`).  Several layers' calls may be enqueued before their serves; serve them in
- * the same order.  A pool is used from one host thread and one copy stream. */
+ * the same order.  A pool is used from one host thread and one copy stream.
+ *
+ * The compute stream's wait stalls whatever the runtime has queued behind it on the same
+ * hardware queue, and the runtime spreads streams over a few such queues (4 by default).
+ * Create the compute and copy streams as a pair, non-blocking, before other streams (a
+ * framework's stream pool, graph capture streams) exist: a copy stream that ends up behind
+ * the wait never runs, and the next serve then times out.  Each serve failure is also
+ * reported on stderr with its epoch and reason. */
 typedef struct moe_pool moe_pool;
 
 typedef struct moe_pool_stats {

@@ -115,6 +115,8 @@ MOE_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
+  // 16-row subtiles per work: a 128-row item, or a 32-row router work
+  constexpr int MSUB = MODE == kRouter ? kRouterTileRows / 16 : kMSub;
   // A tile: 128 rows x 128 16-bit elements per stage, two stages.  16-byte chunk c of row r is
   // stored at chunk c ^ (r & 15) of the row, so the 16 lanes of a fragment read (16 rows, one
   // chunk) hit 16 different chunk slots.
@@ -196,9 +198,9 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   // ---- A staging by DMA: instruction i of wave w fills rows 16i + 4w + (lane >> 4) ---------
   const int a_ld = MODE == kDown ? F : H;
   const int a_pc = lane & 15;  // physical chunk written by this lane
-  int32_t a_src[kMSub];        // source row (token or sorted row) of this lane's row per instruction
+  int32_t a_src[MSUB];        // source row (token or sorted row) of this lane's row per instruction
 #pragma unroll
-  for (int i = 0; i < kMSub; ++i) {
+  for (int i = 0; i < MSUB; ++i) {
     const int r = 16 * i + 4 * wave + (lane >> 4);
     const int rr = r < it.rows ? r : 0;  // padding rows copy row 0 (their outputs are dropped)
     if constexpr (MODE == kGateUp) a_src[i] = a.row_tok[it.row0 + rr];
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   const int a_lc = a_pc ^ ((4 * wave + (lane >> 4)) & 15);  // logical chunk: row & 15 = (4w + l/16) & 15
   auto issue_a = [&](int kc, uint16_t* buf) {
 #pragma unroll
-    for (int i = 0; i < kMSub; ++i) {
+    for (int i = 0; i < MSUB; ++i) {
       if (i < ms)
         lds_dma16(a.a16 + (size_t)a_src[i] * a_ld + kc * kKC + a_lc * 8, buf + (16 * i + 4 * wave) * kKC);
     }
@@ -233,9 +235,9 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
     }
   };
 
-  float4v acc[kMSub][4];
+  float4v acc[MSUB][4];
 #pragma unroll
-  for (int i = 0; i < kMSub; ++i)
+  for (int i = 0; i < MSUB; ++i)
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[i][s] = (float4v){0.f, 0.f, 0.f, 0.f};
 
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
     }
     if (kc + 1 < nk) {
       issue_a(kc + 1, (kc & 1) ? As0 : As1);
-      if constexpr (MODE != kRouter) load_b(kc + 1);
+      load_b(kc + 1);
     }
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
@@ -265,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
       const int pcol = (((4 * d + g) ^ n) * 8);
       if constexpr (MODE == kRouter) {
 #pragma unroll
-        for (int i = 0; i < kMSub; ++i) {
+        for (int i = 0; i < MSUB; ++i) {
           if (i < ms) {
             const bf16x8 af = *(const bf16x8*)(Ab + (16 * i + n) * kKC + pcol);
 #pragma unroll
@@ -283,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
           bf[s] = dequant_word(word_of(bcur[s][0], d), (half2v){sv, sv});
         }
 #pragma unroll
-        for (int i = 0; i < kMSub; ++i) {
+        for (int i = 0; i < MSUB; ++i) {
           if (i < ms) {
             const half8 af = *(const half8*)(Ab + (16 * i + n) * kKC + pcol);
 #pragma unroll
@@ -293,16 +295,13 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
         }
       }
     }
-    if constexpr (MODE == kRouter) {
-      if (kc + 1 < nk) load_b(kc + 1);
-    }
     wait_vm();
     __syncthreads();
   }
 
   // ---- epilogue: lane holds D[16i + 4g + r][16s + n] -----------------------------------------
 #pragma unroll
-  for (int i = 0; i < kMSub; ++i) {
+  for (int i = 0; i < MSUB; ++i) {
     if (i >= ms) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {

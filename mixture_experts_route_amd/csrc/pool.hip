@@ -19,6 +19,7 @@
 //                        expert's old host buffer trade places (the exclusive swap).
 // The FFN kernels read the slot of a missed expert from the table when they run, after the wait.
 #include <atomic>
+#include <cstdio>
 #include <chrono>
 #include <cstring>
 #include <new>
@@ -135,8 +136,10 @@ MOE_API int moe_pool_arm(moe_pool* pool, moe_doorbell* bell_out) {
   return MOE_OK;
 }
 
-// Releases the waiting stream with the fill error flagged (and the table as it stands).
-static int release_with_error(moe_pool* p, void* ws, hipStream_t cs) {
+// Releases the waiting stream with the fill error flagged (and the table as it stands); the reason
+// goes to stderr (the return code is the same for every reason).
+static int release_with_error(moe_pool* p, void* ws, hipStream_t cs, const char* why, long v0 = 0, long v1 = 0) {
+  fprintf(stderr, "moe_pool_serve: epoch %u: %s (%ld, %ld)\n", p->epoch, why, v0, v1);
   if (ws) k_set_error_bits<<<1, 64, 0, cs>>>((int32_t*)ws, MOE_DERR_FILL);
   (void)hipStreamWriteValue32(cs, p->ready, p->epoch, 0);
   p->armed = false;
@@ -156,25 +159,26 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, 
     if (timeout_us > 0 &&
         std::chrono::duration_cast<std::chrono::microseconds>(std::chrono::steady_clock::now() - t0).count() >
             timeout_us)
-      return release_with_error(p, ws_or_null, cs);
+      return release_with_error(p, ws_or_null, cs, "no doorbell before the timeout", (long)counts[1], (long)p->epoch);
     std::this_thread::yield();
   }
   std::atomic_thread_fence(std::memory_order_acquire);
   const int n_miss = counts[0];
   const int n_sel = counts[2];
   if (n_miss < 0 || n_miss > p->E || n_sel < 0 || n_sel > kMaxDecodeTok * kMaxK)
-    return release_with_error(p, ws_or_null, cs);
+    return release_with_error(p, ws_or_null, cs, "counts out of range", n_miss, n_sel);
   std::vector<int32_t> miss(n_miss), sel(n_sel);
   for (int i = 0; i < n_miss; ++i) miss[i] = ((volatile int32_t*)p->host_miss_ids)[i];
   for (int i = 0; i < n_sel; ++i) sel[i] = ((volatile int32_t*)p->host_step_ids)[i];
   std::vector<char> selected(p->E, 0);
   for (int e : sel) {
-    if (e < 0 || e >= p->E) return release_with_error(p, ws_or_null, cs);
+    if (e < 0 || e >= p->E) return release_with_error(p, ws_or_null, cs, "selected id out of range", e, n_sel);
     selected[e] = 1;
   }
   int n_fills = 0;
   for (int e : miss) {
-    if (e < 0 || e >= p->E || p->table_host[e] >= 0 || !p->home[e]) return release_with_error(p, ws_or_null, cs);
+    if (e < 0 || e >= p->E || p->table_host[e] >= 0 || !p->home[e])
+      return release_with_error(p, ws_or_null, cs, "miss id not away", e, (e >= 0 && e < p->E) ? p->table_host[e] : -9);
     selected[e] = 1;
     // victim: the least recently used slot whose expert is not selected in this step
     int best = -1;
@@ -182,13 +186,13 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, 
       if (selected[p->holder[s]]) continue;
       if (best < 0 || p->last_use[s] < p->last_use[best]) best = s;
     }
-    if (best < 0) return release_with_error(p, ws_or_null, cs);  // fewer slots than the step's experts
+    if (best < 0) return release_with_error(p, ws_or_null, cs, "no victim slot", n_miss, n_sel);
     const int old = p->holder[best];
     uint8_t* slot = p->arena + (int64_t)best * p->stride;
     // exclusive swap: the victim goes to the spare host buffer, the missing expert to the slot
     if (!hip_ok(hipMemcpyAsync(p->spare, slot, p->blob_bytes, hipMemcpyDeviceToHost, cs)) ||
         !hip_ok(hipMemcpyAsync(slot, p->home[e], p->blob_bytes, hipMemcpyHostToDevice, cs)))
-      return release_with_error(p, ws_or_null, cs);
+      return release_with_error(p, ws_or_null, cs, "copy enqueue failed", e, best);
     p->home[old] = p->spare;
     p->spare = p->home[e];
     p->home[e] = nullptr;
@@ -207,7 +211,7 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, 
   if (n_miss > 0) {
     if (!hip_ok(hipMemcpyAsync(p->table_dev, p->table_host, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, cs)) ||
         !hip_ok(hipStreamWriteValue32(cs, p->ready, p->epoch, 0)))
-      return release_with_error(p, ws_or_null, cs);
+      return release_with_error(p, ws_or_null, cs, "table copy or release enqueue failed");
   }
   // recency: every selection of the step, in (token, choice) order
   for (int e : sel) p->last_use[p->table_host[e]] = ++p->clock;

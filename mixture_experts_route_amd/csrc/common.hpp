@@ -190,6 +190,25 @@ MOE_DEV uint64_t wave_max_u64(uint64_t key) {
   return ((uint64_t)hi << 32) | lo;
 }
 
+// Wave-wide maximum of a 32-bit key (DPP, no branches); returned to every lane.  Lanes a DPP
+// step does not write read 0, the identity of the unsigned maximum, so each step can fold into
+// one v_max_u32 with a DPP source.
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+#define MOE_MAX32_STEP(C, M)                               \
+  {                                                        \
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, C, M, 0xF, false); \
+    v = o > v ? o : v;                                     \
+  }
+  MOE_MAX32_STEP(kDppQuadXor1, 0xF)
+  MOE_MAX32_STEP(kDppQuadXor2, 0xF)
+  MOE_MAX32_STEP(kDppRowRor4, 0xF)
+  MOE_MAX32_STEP(kDppRowRor8, 0xF)
+  MOE_MAX32_STEP(kDppRowBcast15, 0xA)
+  MOE_MAX32_STEP(kDppRowBcast31, 0xC)
+#undef MOE_MAX32_STEP
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Order-preserving map of a float to uint32 (a > b as floats <=> map(a) > map(b); no NaN).
 MOE_DEV uint32_t f32_order_key(float f) {
   const uint32_t u = __float_as_uint(f);

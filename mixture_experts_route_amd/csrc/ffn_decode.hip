@@ -464,11 +464,11 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
   }
   const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
-  float acc[RGW][NR];
+  float acc[RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
 #pragma unroll
   for (int r = 0; r < RGW; ++r)
 #pragma unroll
-    for (int j = 0; j < NR; ++j) acc[r][j] = 0.f;
+    for (int j = 0; j < NR / 2; ++j) acc[r][j] = 0.f;
   // one batch of kDnQuadsPerPass groups: every load issued, then the MFMA steps group by group
   auto batch = [&](int q0, bool first) {
     const int nq = min(kDnQuadsPerPass, NQ - q0);
@@ -489,6 +489,11 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
 #pragma unroll
     for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
       if (qi >= nq) continue;
+      float part[RGW][NR];
+#pragma unroll
+      for (int r = 0; r < RGW; ++r)
+#pragma unroll
+        for (int j = 0; j < NR; ++j) part[r][j] = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 A = lds_fragment(smem, ROWS, F, n, g, (q0 + qi) * kGroupElems + 32 * i);
@@ -498,9 +503,13 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
           const float4v D = mfma_bf16(A, codes_q136(word_at(cd[r][qi], i)), O);
           const float s = scale_at(sd[r][qi], i);
 #pragma unroll
-          for (int j = 0; j < NR; ++j) acc[r][j] = fmaf(s, D[j], acc[r][j]);
+          for (int j = 0; j < NR; ++j) part[r][j] = fmaf(s, D[j], part[r][j]);
         }
       }
+#pragma unroll
+      for (int r = 0; r < RGW; ++r)
+#pragma unroll
+        for (int j = 0; j < NR / 2; ++j) acc[r][j] += part[r][2 * j] + part[r][2 * j + 1];
     }
   };
   batch(0, true);  // peeled: a loop head would wait for every outstanding load, the staging too
@@ -513,7 +522,7 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
       const int slot = 2 * g + s2;
       if (rg_live[r] && slot < n_tok)
         store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
-                   acc[r][2 * s2] + acc[r][2 * s2 + 1]);
+                   acc[r][s2]);
     }
   }
 }
@@ -525,6 +534,151 @@ __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
   const int tile = blockIdx.x - task * a.tiles_dn;
   if (task < a.ctrl[kCtrlNTasks]) down_body<MAXTOK, RGW>(a, task, tile, smem);
   combine_tile_if_last(a, tile, 16 * kDnWaves * RGW);
+}
+
+// ---- down for one token: output rows outermost, every task inside, no pair rows -------------------
+// One workgroup of 8 waves per RT (8 or 16) output rows.  The work is (task, group of 128 F inputs) items;
+// wave w takes items w, w + 8, ... (at most MAXI), so each wave issues all of its weight loads (one
+// 16-byte code load and one 8-byte scale load per lane per item) at once and the waves carry equal
+// shares.  A rows 0 and 1 are the token's h_hi and h_lo (the other rows zero).  An item's result is
+// the group partial of its task's pair value; the workgroup then forms every pair value and the
+// combine in the same order as the per-pair rows and the combine of the other decode kernels, and
+// stores y directly: no per-pair rows and no cross-workgroup combine.
+template <int MAXT, int MAXI, int RT>
+__global__ __launch_bounds__(512) void k_decode_down_rows1(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t hs[8][MAXI][2][kGroupElems];  // [wave][item][part][input]
+  __shared__ float red[8][MAXT + 1][16];  // [group][task][row]: group partials (task MAXT: unused items)
+  __shared__ float pv[MAXT][16];      // [task][row]: pair values
+  __shared__ int s_inv[kMaxK];        // task of each top-k position j
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int H = a.H, F = a.F;
+  const int NW = F / kGroupElems;  // groups of F inputs (<= 8)
+  // RT output rows per workgroup; with RT = 8 lanes n and n + 8 load the same row (the upper
+  // half of D is not used)
+  const int row = blockIdx.x * RT + (n & (RT - 1));
+  const BlobLayout lay = blob_layout(H, F);
+  // task descriptors: lane t loads task t (the task list always has room for MAXT entries), so one
+  // vector load brings them all; the per-task values are then read from those lanes
+  const int n_tasks = min(a.ctrl[kCtrlNTasks], MAXT);
+  const u32x4 tv = *(const u32x4*)&a.tasks[lane < MAXT ? lane : MAXT - 1];
+  const float l_w = a.topk_w[lane < a.k ? lane : 0];  // lane j: the token's weight j
+  const int l_expert = (int)tv[0];
+  int l_slot = (int)tv[1];
+  // an expert that missed when the plan ran: its table entry now (filled by the pool since)
+  const bool l_routed = lane < n_tasks && l_expert >= 0;
+  if (__any(l_routed && l_slot < 0)) {
+    if (l_routed && l_slot < 0) l_slot = a.src.table ? a.src.table[l_expert] : l_expert;
+  }
+  const bool l_ok = l_routed && l_slot >= 0 && l_slot < a.src.n_slots;
+  if (__any(l_routed && !l_ok) && threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
+  // items past the count (and experts not resident, reported above) load a valid blob and row
+  // and are not computed
+  const uint8_t* const fallback = a.src.shared_blob ? a.src.shared_blob : a.src.arena;
+  const int n_items = n_tasks * NW;
+  const uint8_t* blob[MAXI];
+  int it_t[MAXI], it_q[MAXI], it_pair[MAXI];
+  bool use[MAXI];
+  static_for<MAXI>([&](auto c) {
+    constexpr int m = c.value;
+    const int i = wave + 8 * m;
+    const bool live = i < n_items;
+    const int t = live ? i / NW : 0;
+    it_t[m] = t;
+    it_q[m] = live ? i - t * NW : 0;
+    const int expert = __builtin_amdgcn_readlane(l_expert, t);
+    const int slot = __builtin_amdgcn_readlane(l_slot, t);
+    const int ok = __builtin_amdgcn_readlane((int)l_ok, t);
+    const int choice = __builtin_amdgcn_readlane((int)tv[3], t);
+    const bool routed = live && expert >= 0;
+    const bool shared = live && expert < 0 && a.src.shared_blob;
+    blob[m] = live && ok ? a.src.arena + (int64_t)slot * a.src.slot_stride : fallback;
+    it_pair[m] = routed ? (choice & 15) : shared ? a.T * a.k : 0;
+    use[m] = live && (ok || shared);
+  });
+  // h slices of the items: chunk c = lane + 64 i is item c / 32, part (c / 16) & 1, 8 inputs
+  constexpr int HC = (MAXI * 32 + 63) / 64;
+  u32x4 hv[HC];
+  static_for<HC>([&](auto c) {
+    constexpr int i = c.value;
+    constexpr int m0 = 2 * i < MAXI ? 2 * i : MAXI - 1, m1 = 2 * i + 1 < MAXI ? 2 * i + 1 : MAXI - 1;
+    const int pr = lane < 32 ? it_pair[m0] : it_pair[m1];
+    const int qq = lane < 32 ? it_q[m0] : it_q[m1];
+    const int part = (lane >> 4) & 1;
+    hv[i] = *(const u32x4*)((part ? a.h_lo : a.h_hi) + (size_t)pr * F + qq * kGroupElems + (lane & 15) * 8);
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  // weights of every item: record (q, row) of the down matrix
+  u32x4 cd[MAXI];
+  u32x2 sd[MAXI];
+  static_for<MAXI>([&](auto c) {
+    constexpr int m = c.value;
+    cd[m] = *(const u32x4*)(blob[m] + lay.down_codes + ((size_t)it_q[m] * H + row) * kGroupBytes + 16 * g);
+    sd[m] = *(const u32x2*)(blob[m] + lay.down_scales + ((size_t)it_q[m] * H + row) * kGroupScaleBytes);
+  });
+  issue_fence();
+  static_for<HC>([&](auto c) {
+    constexpr int i = c.value;
+    const int cc = lane + 64 * i;
+    if (cc < MAXI * 32) *(u32x4*)&hs[wave][cc >> 5][(cc >> 4) & 1][(cc & 15) * 8] = hv[i];
+  });
+  asm volatile("" ::: "memory");  // the wave reads back only its own slices: LDS order suffices
+  if (wave == 0 && lane < n_tasks && l_expert >= 0) s_inv[tv[3] & 15u] = lane;
+  const Unpack uk = make_unpack();
+  const bf16x8 neg = const_neg136();
+  const float4v zero = {0.f, 0.f, 0.f, 0.f};
+  // every item is computed (one basic block, so the MFMA chains of different items interleave);
+  // unused items write their result to the spare task row
+  static_for<MAXI>([&](auto c) {
+    constexpr int m = c.value;
+    float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 av = *(const uint4*)&hs[wave][m][n & 1][32 * i + 8 * g];
+      if (n >= 2) av = make_uint4(0u, 0u, 0u, 0u);
+      const bf16x8 A = __builtin_bit_cast(bf16x8, av);
+      const float4v O = mfma_bf16(A, neg, zero);
+      const float4v D = mfma_bf16(A, codes_q136(word_at(cd[m], i), uk), O);
+      const float sc = scale_at(sd[m], i);
+      acc0 = fmaf(sc, D[0], acc0);
+      acc1 = fmaf(sc, D[1], acc1);
+    }
+    // lanes 0..15 hold rows 0 and 1 of D (the token's hi and lo parts) for output row n
+    if (lane < RT) red[use[m] ? it_q[m] : 0][use[m] ? it_t[m] : MAXT][n] = acc0 + acc1;
+  });
+  __syncthreads();
+  // the same arithmetic as the per-pair rows and the combine of the other decode kernels: a pair
+  // value is the sum of its group partials in group order; y = sum_j w_j * pair_j in j order, then
+  // + the shared expert's pair
+  // (every load of a step is issued before the sums that use it)
+  for (int idx = threadIdx.x; idx < 16 * MAXT; idx += blockDim.x) {
+    const int t = idx >> 4, r = idx & 15;
+    if (r >= RT) continue;
+    float v[8];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) v[w] = red[w < NW ? w : 0][t][r];
+    float p = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) p = w < NW ? p + v[w] : p;
+    pv[t][r] = p;
+  }
+  __syncthreads();
+  if (threadIdx.x < RT) {
+    int inv[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) inv[j] = s_inv[j < a.k ? j : 0];
+    float v[kMaxK];
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j) v[j] = pv[inv[j]][threadIdx.x];
+    const float vs = pv[a.n_shared ? n_tasks - 1 : 0][threadIdx.x];
+    float y = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxK; ++j)
+      y = j < a.k ? fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_w), j)), v[j], y) : y;
+    if (a.n_shared) y += vs;
+    a.y[blockIdx.x * RT + threadIdx.x] = y;
+  }
 }
 
 // ---- pipelined variants for tasks of up to 4 or 8 bf16 tokens ----------------------------------
@@ -730,16 +884,21 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
 
   const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
-  float acc[RGW][NR];
+  float acc[RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
 #pragma unroll
   for (int r = 0; r < RGW; ++r)
 #pragma unroll
-    for (int j = 0; j < NR; ++j) acc[r][j] = 0.f;
+    for (int j = 0; j < NR / 2; ++j) acc[r][j] = 0.f;
   static_for<UNITS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
     constexpr int b = u % kPipeDnBufs;
 #pragma unroll
     for (int qi = 0; qi < QG; ++qi) {
+      float part[RGW][NR];
+#pragma unroll
+      for (int r = 0; r < RGW; ++r)
+#pragma unroll
+        for (int j = 0; j < NR; ++j) part[r][j] = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 A = lds_fragment(smem, ROWS, F, n, g, (u * QG + qi) * kGroupElems + 32 * i);
@@ -749,9 +908,13 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
           const float4v D = mfma_bf16(A, codes_q136(word_at(cd[b][r][qi], i), uk), O);
           const float s = scale_at(sd[b][r][qi], i);
 #pragma unroll
-          for (int j = 0; j < NR; ++j) acc[r][j] = fmaf(s, D[j], acc[r][j]);
+          for (int j = 0; j < NR; ++j) part[r][j] = fmaf(s, D[j], part[r][j]);
         }
       }
+#pragma unroll
+      for (int r = 0; r < RGW; ++r)
+#pragma unroll
+        for (int j = 0; j < NR / 2; ++j) acc[r][j] += part[r][2 * j] + part[r][2 * j + 1];
       __builtin_amdgcn_sched_barrier(0);  // one group at a time
     }
     if constexpr (u + kPipeDnBufs < UNITS) {
@@ -763,7 +926,7 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
 #pragma unroll
   for (int r = 0; r < RGW; ++r)
 #pragma unroll
-    for (int j = 0; j < NR; ++j) asm volatile("" : "+v"(acc[r][j]));
+    for (int j = 0; j < NR / 2; ++j) asm volatile("" : "+v"(acc[r][j]));
   // lane (g, n) holds rows 4g + j: token slots 2g (j = 0, 1) and 2g + 1 (j = 2, 3)
 #pragma unroll
   for (int r = 0; r < RGW; ++r) {
@@ -772,7 +935,7 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
       const int slot = 2 * g + s2;
       if (rg_live[r] && slot < n_tok)
         store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
-                   acc[r][2 * s2] + acc[r][2 * s2 + 1]);
+                   acc[r][s2]);
     }
   }
 }
@@ -870,6 +1033,13 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
   }
   if (err != hipSuccess) return err;
   const int dn_units = MAXTOK >= 4 ? down_pipe_units(a.F) : 0;
+  if (MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
+    // one token: output rows outermost, (task, group) items spread over 8 waves, no pair rows
+    const int grid = a.H / 8, items = max_tasks * (a.F / kGroupElems);
+    if (max_tasks <= 11 && items <= 8 * 9)
+      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 9, 8>, grid, 512, 0, st, a);
+    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 8>, grid, 512, 0, st, a);
+  }
   if (dn_units) {
     if constexpr (MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);
   } else {

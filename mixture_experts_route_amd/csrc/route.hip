@@ -15,9 +15,15 @@ namespace moe {
 // logits are flagged and never selected.
 // ------------------------------------------------------------------------------------------
 // NPER = logits per lane, 64 * NPER >= E (8 for E <= 512, 16 for E <= 1024).
-template <int NPER>
+struct NoOp {
+  MOE_DEV void operator()() const {}
+};
+
+// Results go to ids_out / w_out, or (ids_out null) to lds_ids / lds_w.  after_loads() runs once
+// the row's logits are in registers: work on other loads issued before the call waits there.
+template <int NPER, typename AfterLoads = NoOp>
 MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, float* w_out, int32_t* ctrl,
-                              int32_t* lds_ids) {
+                              int32_t* lds_ids = nullptr, float* lds_w = nullptr, AfterLoads&& after_loads = NoOp{}) {
   constexpr int kPerLane = NPER;
   const int lane = threadIdx.x & 63;
   float v[kPerLane];
@@ -40,11 +46,12 @@ MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, 
     const float f = nan ? -INFINITY : v[i];
     key[i] = e < E ? (((uint64_t)f32_order_key(f) << 32) | (uint32_t)~e) : 0ull;
   }
+  after_loads();
   if (__any(nan_seen) && lane == 0) set_error(ctrl, MOE_DERR_NAN);
   uint64_t mine = 0;  // lane r keeps the r-th selection
   if constexpr (kPerLane == 8) {
     // each lane sorts its 8 keys (descending, odd-even merge network); a round takes the wave
-    // maximum of the lanes' heads and the winning lane shifts its list by one
+    // maximum of the lanes' heads and the winning lane shifts its list by one.
     auto cx = [&](int a, int b) {
       const uint64_t hi = key[a] > key[b] ? key[a] : key[b];
       const uint64_t lo = key[a] > key[b] ? key[b] : key[a];
@@ -57,13 +64,35 @@ MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, 
     cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
     cx(2, 4); cx(3, 5);
     cx(1, 2); cx(3, 4); cx(5, 6);
-    for (int r = 0; r < k; ++r) {
-      const uint64_t win = wave_max_u64(key[0]);
-      mine = lane == r ? win : mine;
-      const bool took = key[0] == win;  // one lane: keys are distinct
+    // A round reduces the heads' high words (the values) only; the lanes holding that value are
+    // a ballot, and only when there are several (equal logits) does a second reduction over their
+    // low words (the complemented ids) pick the lowest id.
+    uint32_t hi[kPerLane], lo[kPerLane];
 #pragma unroll
-      for (int i = 0; i < kPerLane - 1; ++i) key[i] = took ? key[i + 1] : key[i];
-      key[kPerLane - 1] = took ? 0ull : key[kPerLane - 1];
+    for (int i = 0; i < kPerLane; ++i) {
+      hi[i] = (uint32_t)(key[i] >> 32);
+      lo[i] = (uint32_t)key[i];
+    }
+    for (int r = 0; r < k; ++r) {
+      const uint32_t wh = wave_max_u32(hi[0]);
+      const uint64_t tied = __builtin_amdgcn_ballot_w64(hi[0] == wh);
+      int win_lane;
+      if (__builtin_popcountll(tied) == 1) {
+        win_lane = __builtin_ctzll(tied);
+      } else {
+        const uint32_t wl = wave_max_u32(hi[0] == wh ? lo[0] : 0u);
+        win_lane = __builtin_ctzll(__builtin_amdgcn_ballot_w64(hi[0] == wh && lo[0] == wl));
+      }
+      const uint32_t wlo = (uint32_t)__builtin_amdgcn_readlane((int)lo[0], win_lane);
+      mine = lane == r ? (((uint64_t)wh << 32) | wlo) : mine;
+      const bool took = lane == win_lane;
+#pragma unroll
+      for (int i = 0; i < kPerLane - 1; ++i) {
+        hi[i] = took ? hi[i + 1] : hi[i];
+        lo[i] = took ? lo[i + 1] : lo[i];
+      }
+      hi[kPerLane - 1] = took ? 0u : hi[kPerLane - 1];
+      lo[kPerLane - 1] = took ? 0u : lo[kPerLane - 1];
     }
   } else {
     uint64_t best = 0;
@@ -89,9 +118,13 @@ MOE_DEV void select_topk_wave(const float* row, int E, int k, int32_t* ids_out, 
   float sum = 0.f;
   for (int r = 0; r < k; ++r) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), r));
   if (lane < k) {
-    ids_out[lane] = my_i;
-    w_out[lane] = ex / sum;
-    if (lds_ids) lds_ids[lane] = my_i;
+    if (ids_out) {
+      ids_out[lane] = my_i;
+      w_out[lane] = ex / sum;
+    } else {
+      lds_ids[lane] = my_i;
+      lds_w[lane] = ex / sum;
+    }
   }
 }
 
@@ -101,7 +134,7 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
                                                int32_t* __restrict__ ctrl) {
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
   if (t >= T) return;
-  select_topk_wave<NPER>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, ctrl, nullptr);
+  select_topk_wave<NPER>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, ctrl);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -242,7 +275,7 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
 // tokens.  A task whose expert missed keeps slot -1 and the FFN kernels read the table entry when
 // they run, so slots filled after this check (doorbell path) are seen.
 // ------------------------------------------------------------------------------------------
-struct PlanShared {
+struct alignas(16) PlanShared {
   uint32_t tok_mask[kMaxExperts];
   int32_t slot_of[kMaxExperts];
   uint32_t choice[kMaxExperts];  // 4 bits per token: position j of the expert in its top-k
@@ -363,12 +396,106 @@ struct RouteArgs {
 };
 
 
+// The decode plan by one wave, from the step's selections in LDS (s_ids, [T][k], valid ids):
+// lane l owns experts NPER*l .. NPER*l + NPER - 1.  The wave clears its experts' token masks and
+// top-k positions, sets them with LDS atomics per (token, choice), reads its experts back, and one
+// wave scan of the packed (tasks, misses) counts places tasks and misses in ascending expert id.
+// A wave's LDS operations take effect in the order it issues them, so no barrier is needed.
+template <int NPER>
+MOE_DEV void plan_wave(const RouteArgs& a, PlanShared& sh, const int32_t* s_ids, int32_t* s_miss, int* s_nmiss) {
+  const int lane = threadIdx.x & 63;
+  const int e0 = NPER * lane;
+#pragma unroll
+  for (int i = 0; i < NPER; i += 4) {
+    *(uint4*)&sh.tok_mask[e0 + i] = make_uint4(0u, 0u, 0u, 0u);
+    *(uint4*)&sh.choice[e0 + i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  asm volatile("" ::: "memory");  // keep the LDS phases in program order
+  const int n_pairs = a.T * a.k;
+  for (int p = lane; p < n_pairs; p += 64) {
+    const int e = s_ids[p];
+    const int t = p / a.k, j = p - t * a.k;
+    __hip_atomic_fetch_or(&sh.tok_mask[e], 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_or(&sh.choice[e], (uint32_t)j << (4 * t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  asm volatile("" ::: "memory");
+  uint32_t m[NPER], c[NPER];
+  int32_t sl[NPER];
+#pragma unroll
+  for (int i = 0; i < NPER; i += 4) {
+    const uint4 mv = *(const uint4*)&sh.tok_mask[e0 + i];
+    const uint4 cv = *(const uint4*)&sh.choice[e0 + i];
+    const int4 sv = *(const int4*)&sh.slot_of[e0 + i];
+    m[i] = mv.x, m[i + 1] = mv.y, m[i + 2] = mv.z, m[i + 3] = mv.w;
+    c[i] = cv.x, c[i + 1] = cv.y, c[i + 2] = cv.z, c[i + 3] = cv.w;
+    sl[i] = sv.x, sl[i + 1] = sv.y, sl[i + 2] = sv.z, sl[i + 3] = sv.w;
+  }
+  int n_sub = 0, n_mis = 0;
+  bool bad = false;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    const bool used = m[i] != 0u;  // experts >= E are never selected
+    n_sub += used;
+    n_mis += used && sl[i] < 0;
+    bad |= used && sl[i] >= a.n_slots;
+  }
+  // wave exclusive scan of the packed counts (totals stay < 2^16)
+  const int v = n_sub | (n_mis << 16);
+  int incl = v;
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x111, 0xF, 0xF, false);  // row_shr:1
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x112, 0xF, 0xF, false);  // row_shr:2
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x114, 0xF, 0xF, false);  // row_shr:4
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x118, 0xF, 0xF, false);  // row_shr:8
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  incl += __builtin_amdgcn_update_dpp(0, incl, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  const int total = __builtin_amdgcn_readlane(incl, 63);
+  const int excl = incl - v;
+  int tpos = excl & 0xFFFF, mpos = excl >> 16;
+  const int n_tasks = total & 0xFFFF, n_miss = total >> 16;
+#pragma unroll
+  for (int i = 0; i < NPER; ++i) {
+    if (m[i] != 0u) {
+      const int e = e0 + i;
+      if (sl[i] < 0) {
+        a.miss_ids[mpos] = e;
+        s_miss[mpos] = e;
+        ++mpos;
+      }
+      DecodeTask tk;
+      tk.expert = e;
+      tk.slot = sl[i];
+      tk.tok_mask = m[i];
+      tk.choice = c[i];
+      a.tasks[tpos++] = tk;
+    }
+  }
+  const bool any_bad = __any(bad);
+  if (lane == 0) {
+    int n_all = n_tasks;
+    if (a.n_shared) {
+      DecodeTask tk;
+      tk.expert = -1;
+      tk.slot = -1;
+      tk.tok_mask = (a.T >= 32) ? 0xFFFFFFFFu : ((1u << a.T) - 1u);
+      tk.choice = 0;
+      a.tasks[n_all++] = tk;
+    }
+    a.ctrl[kCtrlNTasks] = n_all;
+    a.ctrl[kCtrlMissCount] = n_miss;
+    if (any_bad) set_error(a.ctrl, MOE_DERR_SLOT);
+    *s_nmiss = n_miss;
+  }
+}
+
 // One workgroup: the top-k of every token (one wave per token, DPP arg-max) and, if asked, the
 // decode plan (residency check, task list, miss list, doorbell).  Needs >= 256 threads.
 template <int NPER>
 MOE_DEV void select_and_plan(const RouteArgs& a) {
   __shared__ PlanShared sh;
   __shared__ int32_t s_ids[kMaxDecodeTok * kMaxK];
+  __shared__ float s_w[kMaxDecodeTok * kMaxK];
+  __shared__ int32_t s_miss[kMaxDecodeTok * kMaxK];
+  __shared__ int s_nmiss;
   const int wave = threadIdx.x >> 6;
   // the slot table is loaded with the logits (issued first: one wait covers both) and goes to LDS
   // after the selections, so the plan makes no dependent global load
@@ -379,18 +506,41 @@ MOE_DEV void select_and_plan(const RouteArgs& a) {
     const int e = min((int)(threadIdx.x + i * blockDim.x), a.E - 1);
     tab[i] = a.table ? a.table[e] : e;
   }
-  for (int t = wave; t < a.T; t += blockDim.x >> 6) {
-    select_topk_wave<NPER>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + (size_t)t * a.k, a.w + (size_t)t * a.k,
-                           a.ctrl, s_ids + t * a.k);
-  }
+  // The slots go to LDS as soon as the wait for the logits has covered them.  The selections
+  // stay in LDS until the plan has read its LDS: a store still in flight when a later LDS read
+  // reuses its data register makes the compiler wait for every outstanding memory operation.
+  auto stage_slots = [&]() {
 #pragma unroll
-  for (int i = 0; i < kTabPer; ++i) {
-    const int e = threadIdx.x + i * blockDim.x;
-    if (e < a.E) sh.slot_of[e] = tab[i];
+    for (int i = 0; i < kTabPer; ++i) {
+      const int e = threadIdx.x + i * blockDim.x;
+      if (e < a.E) sh.slot_of[e] = tab[i];
+    }
+  };
+  if (wave < a.T) {
+    select_topk_wave<NPER>(a.logits + (size_t)wave * a.E, a.E, a.k, nullptr, nullptr, a.ctrl, s_ids + wave * a.k,
+                           s_w + wave * a.k, stage_slots);
+    for (int t = wave + (blockDim.x >> 6); t < a.T; t += blockDim.x >> 6) {
+      select_topk_wave<NPER>(a.logits + (size_t)t * a.E, a.E, a.k, nullptr, nullptr, a.ctrl, s_ids + t * a.k,
+                             s_w + t * a.k);
+    }
+  } else {
+    stage_slots();
   }
   __syncthreads();
-  if (a.plan)
-    build_plan(s_ids, a.T, a.k, a.E, a.n_shared, a.table, a.n_slots, a.miss_ids, a.tasks, a.ctrl, a.bell, sh, true);
+  if (wave == 0) {
+    if (a.plan) plan_wave<NPER>(a, sh, s_ids, s_miss, &s_nmiss);
+    for (int p = threadIdx.x; p < a.T * a.k; p += 64) {
+      a.ids[p] = s_ids[p];
+      a.w[p] = s_w[p];
+    }
+  }
+  if (!a.plan) return;
+  if (a.bell.active) {
+    // the host reads the miss list and the selections as soon as the doorbell rings: both go
+    // to host memory from LDS before the count and the epoch
+    __syncthreads();
+    ring_doorbell(a.bell, s_miss, s_nmiss, s_ids, a.T * a.k);
+  }
 }
 
 // End of a router workgroup: its logits went out as agent-scope stores (written through to the

@@ -100,6 +100,70 @@ def test_route_model_shape(N, dev, model_layer, T):
     assert ties <= T  # near ties are rare at this logit spread
 
 
+def _tied_router(dev, H, E):
+    """bf16 router whose rows come in equal pairs (2i, 2i + 1), plus a run of 8 equal rows: the
+    GPU's logits for equal rows are bitwise equal, so the selection meets exact ties."""
+    from mixture_experts_route_amd import synth as S
+
+    codes = S.bf16_normal_np(S.stream_key(3, 2, "router", 0, 0), (E, H), 0.02)
+    codes[1::2] = codes[0::2]
+    codes[40:48] = codes[40]
+    return torch.from_numpy(codes.view(np.int16)).to(dev)
+
+
+@pytest.mark.parametrize("T", [1, 5, 8, 300])
+def test_topk_exact_ties_lower_id_first(N, dev, T):
+    """Selection on the GPU's own fp32 logits equals the oracle's ranking (logit desc, id asc)
+    exactly when many logits are equal (decode route for T <= 8, prefill top-k above)."""
+    from mixture_experts_route_amd import synth as S
+
+    H, F, E, k = 2048, 768, 512, 10
+    d = N.dims(H, F, E, k, 1)
+    router = _tied_router(dev, H, E)
+    x = torch.from_numpy(S.bf16_normal_np(S.stream_key(3, 2, "x", 0, T), (T, H), 1.0).view(np.int16)).to(dev)
+    ws = _ws(N, d, T, dev)
+    ids = torch.full((T, k), -7, dtype=torch.int32, device=dev)
+    w = torch.zeros((T, k), dtype=torch.float32, device=dev)
+    logits = torch.zeros((T, E), dtype=torch.float32, device=dev)
+    N.moe_route(d, x, T, router, None, ids, w, logits, ws)
+    torch.cuda.synchronize()
+    _check_no_device_error(N, ws)
+    lg = logits.cpu().numpy()
+    assert np.array_equal(lg[:, 1::2], lg[:, 0::2]), "equal router rows must give equal logits"
+    got = ids.cpu().numpy()
+    ref = O.select_topk(lg, k)
+    assert np.array_equal(got, ref)
+    assert np.max(np.abs(w.cpu().numpy() - O.route_weights(lg, ref))) <= 1e-6
+    # the selections really contain tied pairs, ranked lower id first
+    tied = sum(int(np.isin(row ^ 1, row).sum()) for row in got)
+    assert tied >= T
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_layer_forward_exact_ties(N, dev, model_layer, T):
+    """The decode plan path (router launch with selection and plan) ranks exact ties as moe_route."""
+    layer = model_layer
+    d = layer.dims()
+    router = _tied_router(dev, layer.H, layer.E)
+    x, _ = layer.x(T, 5, dev)
+    from mixture_experts_route_amd import native as NN
+
+    wts = NN.layer_weights(router, layer.arena, layer.stride, layer.n_slots, layer.shared, None)
+    ws = _ws(N, d, T, dev)
+    y = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
+    ids = torch.zeros((T, layer.k), dtype=torch.int32, device=dev)
+    w = torch.zeros((T, layer.k), dtype=torch.float32, device=dev)
+    N.moe_layer_forward(d, wts, None, x, T, y, ws, topk_ids=ids, topk_w=w)
+    ids2 = torch.zeros_like(ids)
+    w2 = torch.zeros_like(w)
+    logits = torch.zeros((T, layer.E), dtype=torch.float32, device=dev)
+    N.moe_route(d, x, T, router, None, ids2, w2, logits, _ws(N, d, T, dev))
+    torch.cuda.synchronize()
+    _check_no_device_error(N, ws)
+    assert np.array_equal(ids.cpu().numpy(), O.select_topk(logits.cpu().numpy(), layer.k))
+    assert torch.equal(ids, ids2) and torch.equal(w, w2)
+
+
 def _layer_check(N, dev, layer, T, step, table=None, via_layer=True):
     d = layer.dims()
     x, x64 = layer.x(T, step, dev)

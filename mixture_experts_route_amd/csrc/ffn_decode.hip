@@ -36,6 +36,7 @@ namespace moe {
 
 constexpr int kGuQuadsPerWave = 4;  // gate/up: groups of 128 inputs per wave
 constexpr int kGuRG = 2;            // gate/up: row groups of 16 per workgroup
+constexpr int kGuRG1 = 1;           // gate/up, one token: row groups of 16 per workgroup
 constexpr int kDnQuadsPerPass = 6;  // down: groups per load batch
 constexpr int kDnWaves = 8;         // down: waves per workgroup
 // down: row groups of 16 per wave (more output rows per staged activation tile when the tasks
@@ -228,9 +229,9 @@ MOE_DEV bf16x8 lds_fragment(const uint16_t* lds, int rows, int K, int m, int g, 
 }
 
 // ---- gate/up: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for one task and 32 rows r ------------
-// Workgroup = kGuRG row groups of 16 rows x KS waves splitting the H inputs in runs of 4 groups
+// Workgroup = RG row groups of 16 rows x KS waves splitting the H inputs in runs of 4 groups
 // (KS = H / 512).  A rows: token slot m of the task (bf16 x) or 2 m + part (fp32 x, hi / lo).
-template <int MAXTOK, bool X_BF16>
+template <int MAXTOK, bool X_BF16, int RG>
 __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   constexpr int ROWS = X_BF16 ? MAXTOK : 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;                    // live D registers per lane
@@ -244,8 +245,8 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   // are issued; a lane picks its token slot's row when it reads its fragment.  fp32 rows (small
   // shapes only) are split into hi / lo bf16 rows of the task's tokens by the threads below.
   auto x_row = [&](int m) { return (const uint16_t*)a.x + (size_t)(m < a.T ? m : 0) * H; };
-  // bf16: ROWS * H / 8 chunks over 64 kGuRG H / 512 threads is at most MAXTOK / 2 per thread
-  u32x4 xv[(MAXTOK + 1) / 2];
+  // bf16: ROWS * H / 8 chunks over 64 RG H / 512 threads is at most MAXTOK / RG per thread
+  u32x4 xv[(MAXTOK + RG - 1) / RG];
   if constexpr (X_BF16) stage_load(xv, ROWS, H, x_row);
   // the descriptor slot always exists (max_tasks of them): load it together with the count
   const DecodeTask tk = a.tasks[task];
@@ -261,7 +262,7 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   const int NQ = H / kGroupElems;
   const int KS = (NQ + kGuQuadsPerWave - 1) / kGuQuadsPerWave;  // waves per row group
   const int rg = wave / KS, kq = wave - rg * KS;
-  const int row = (tile * kGuRG + rg) * 16 + n;
+  const int row = (tile * RG + rg) * 16 + n;
   const int q0 = kq * kGuQuadsPerWave;
   const int nq = min(kGuQuadsPerWave, NQ - q0);
   const int n_tok = __builtin_popcount(tk.tok_mask);
@@ -337,7 +338,7 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < kGuRG * 16 * MAXTOK; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < RG * 16 * MAXTOK; idx += blockDim.x) {
     const int r16 = idx / (16 * MAXTOK), rem = idx - r16 * 16 * MAXTOK;
     const int ts = rem >> 4, c = rem & 15;
     if (ts >= n_tok) continue;
@@ -354,7 +355,7 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
     const float h = silu(gs) * us;
     const uint32_t hi = f32_to_bf16_rne(h);
     const uint32_t lo = f32_to_bf16_rne(h - __uint_as_float(hi << 16));
-    const size_t o = (size_t)task_pair(tk, task_token(tk.tok_mask, ts), a.T, a.k) * F + (tile * kGuRG + r16) * 16 + c;
+    const size_t o = (size_t)task_pair(tk, task_token(tk.tok_mask, ts), a.T, a.k) * F + (tile * RG + r16) * 16 + c;
     a.h_hi[o] = (uint16_t)hi;
     a.h_lo[o] = (uint16_t)lo;
   }
@@ -1021,15 +1022,21 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
     if constexpr (MAXTOK >= 4) err = launch_gate_up_pipe<MAXTOK>(a, max_tasks, gu_units, st);
   } else {
     const int ks = (a.H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
-    const int gu_threads = 64 * kGuRG * ks;
-    a.tiles_gu = a.F / (16 * kGuRG);
-    const int grid_gu = max_tasks * a.tiles_gu;
-    if (xb)
-      err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true>, grid_gu, gu_threads,
-                         (uint32_t)gate_up_lds_bytes(a.H, MAXTOK, kGuRG * ks), st, a);
+    auto launch_rg = [&](auto rgc) {
+      constexpr int RG = decltype(rgc)::value;
+      const int gu_threads = 64 * RG * ks;
+      a.tiles_gu = a.F / (16 * RG);
+      const int grid_gu = max_tasks * a.tiles_gu;
+      if (xb)
+        return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true, RG>, grid_gu, gu_threads,
+                            (uint32_t)gate_up_lds_bytes(a.H, MAXTOK, RG * ks), st, a);
+      return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false, RG>, grid_gu, gu_threads,
+                          (uint32_t)gate_up_lds_bytes(a.H, 2 * MAXTOK, RG * ks), st, a);
+    };
+    if (MAXTOK == 1 && a.F % (16 * kGuRG1) == 0 && kGuRG1 * ks <= 16)
+      err = launch_rg(std::integral_constant<int, kGuRG1>{});
     else
-      err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false>, grid_gu, gu_threads,
-                         (uint32_t)gate_up_lds_bytes(a.H, 2 * MAXTOK, kGuRG * ks), st, a);
+      err = launch_rg(std::integral_constant<int, kGuRG>{});
   }
   if (err != hipSuccess) return err;
   const int dn_units = MAXTOK >= 4 ? down_pipe_units(a.F) : 0;

@@ -471,13 +471,19 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
         const uint32_t sv = (d & 1) ? (sw >> 16) : (sw & 0xFFFFu);
         bf[s] = dequant_word_k(bc[sl][s][d], __builtin_bit_cast(half2v, sv | (sv << 16)), uk);
       }
+      // each subtile's MFMAs run while the next subtile's fragment is read (the read of the
+      // last one is clamped and not used), so the LDS latency is not paid once per subtile
+      half8 af = *(const half8*)(Ab + n * kKC + pcol);
 #pragma unroll
       for (int i = 0; i < kMSub; ++i) {
         if (i < ms) {
-          const half8 af = *(const half8*)(Ab + (16 * i + n) * kKC + pcol);
+          const int inext = i + 1 < kMSub ? i + 1 : i;
+          half8 af_next = *(const half8*)(Ab + (16 * inext + n) * kKC + pcol);
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[s], acc[i][s], 0, 0, 0);
+          asm volatile("" : "+v"(af_next));  // read inside this subtile's block, not sunk into the next
+          af = af_next;
         }
       }
       __builtin_amdgcn_sched_barrier(0);

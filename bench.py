@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the routed MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode1|decode8x48|prefill4k|prefill32k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill 4096,32768]
 
 A step is one pass of the whole layer (router -> top-k -> residency check -> expert FFNs ->
 combine) through ``moe_layer_forward`` over one batch of seeded synthetic input that is
@@ -644,7 +644,7 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=40)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch decode steps one by one instead of replaying graphs")
-    ap.add_argument("--prefill", default="4096", help="comma-separated prefill token counts to add ('' = none)")
+    ap.add_argument("--prefill", default="4096,32768", help="comma-separated prefill token counts to add ('' = none)")
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--decode48-steps", type=int, default=64, help="steps of the 48-layer batched decode (0 = skip)")
     ap.add_argument("--pool-steps", type=int, default=512, help="steps of the slot-pool decode workload (0 = skip)")

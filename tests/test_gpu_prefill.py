@@ -128,6 +128,16 @@ def test_prefill_4k_sampled(N, dev, model_layer):
     _prefill_check(N, dev, model_layer, 4096, step=4096, sample=sample)
 
 
+def test_prefill_32k_sampled_zipf(N, dev):
+    """The long prefill shape (32,768 tokens) with Zipf(1.1)-skewed routing (hot experts with
+    thousands of rows), on sampled tokens including both ends."""
+    layer = Layer(MODEL, dev, seed=4, bias_c=S.ZIPF_C)
+    T = 32768
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 13, replace=False)]))
+    _prefill_check(N, dev, layer, T, step=T, sample=sample)
+
+
 def test_prefill_skewed_zipf_routing(N, dev):
     """Zipf(1.1)-skewed routing (uneven groups, several 128-row items per hot expert)."""
     layer = Layer(MODEL, dev, seed=3, bias_c=S.ZIPF_C)

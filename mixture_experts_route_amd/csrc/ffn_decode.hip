@@ -376,14 +376,15 @@ static size_t gate_up_lds_bytes(int H, int rows, int waves) {
 // No workgroup waits on another.
 MOE_DEV void store_pair(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
-MOE_DEV void combine_tile_if_last(const DecodeArgs& a, int tile, int tile_rows) {
+// n_tasks: the step's task count (one counting workgroup per task for this tile; the slots past
+// it return at once).
+MOE_DEV void combine_tile_if_last(const DecodeArgs& a, int tile, int tile_rows, int n_tasks) {
   __shared__ int s_last;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's pair stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int n_wg = (int)gridDim.x / a.tiles_dn;  // one workgroup per task slot for this tile
     const int old = __hip_atomic_fetch_add(&a.tile_done[tile], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = old == n_wg - 1;
+    s_last = old == n_tasks - 1;
   }
   __syncthreads();
   if (!s_last) return;
@@ -533,8 +534,10 @@ __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int task = blockIdx.x / a.tiles_dn;
   const int tile = blockIdx.x - task * a.tiles_dn;
-  if (task < a.ctrl[kCtrlNTasks]) down_body<MAXTOK, RGW>(a, task, tile, smem);
-  combine_tile_if_last(a, tile, 16 * kDnWaves * RGW);
+  const int n_tasks = a.ctrl[kCtrlNTasks];
+  if (task >= n_tasks) return;  // task slots past the step's count neither compute nor count
+  down_body<MAXTOK, RGW>(a, task, tile, smem);
+  combine_tile_if_last(a, tile, 16 * kDnWaves * RGW, n_tasks);
 }
 
 // ---- down for one token: output rows outermost, every task inside, no pair rows -------------------
@@ -946,8 +949,10 @@ __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int task = blockIdx.x / a.tiles_dn;
   const int tile = blockIdx.x - task * a.tiles_dn;
-  if (task < a.ctrl[kCtrlNTasks]) down_pipe_body<MAXTOK, UNITS>(a, task, tile, smem);
-  combine_tile_if_last(a, tile, 16 * kPipeDnWaves * kPipeDnRGW);
+  const int n_tasks = a.ctrl[kCtrlNTasks];
+  if (task >= n_tasks) return;  // task slots past the step's count neither compute nor count
+  down_pipe_body<MAXTOK, UNITS>(a, task, tile, smem);
+  combine_tile_if_last(a, tile, 16 * kPipeDnWaves * kPipeDnRGW, n_tasks);
 }
 
 // ---- dequantization check: one thread per code word, the same unpacking as the FFN kernels --

@@ -127,9 +127,9 @@ def cpu_baseline_decode(n_tokens: int, seed=0, cfg=2, layer=0):
 
 
 def measured_traffic(path="profiles/decode1_gate_up_traffic.txt"):
-    """HBM bytes per launch of a decode gate/up kernel from a committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy; for the 48-layer decode the mean over
-    its launches), or None once the kernel's sources differ from the ones the counters were taken on."""
+    """HBM bytes per launch of a gate/up kernel (decode or prefill) from a committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE passes, scaled by a plain copy; the mean over the launches),
+    or None once the kernel's sources differ from the ones the counters were taken on."""
     import hashlib
 
     root = os.path.dirname(os.path.abspath(__file__))
@@ -361,7 +361,7 @@ def bench_prefill(T: int, steps: int, warmup: int, cpu_sample: int | None):
             "peak": FP16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": gu_flop / gu_s / 1e12 / FP16_MFMA_PEAK_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic("profiles/prefill4k_gate_up_traffic.txt") if T == 4096 else None,
             "flop_per_launch": gu_flop,
             "avg_launch_us": gu_s * 1e6,
         },

@@ -232,8 +232,9 @@ def bench_decode1(args):
     gu_bytes = 11 * per_expert + H * 2 + 11 * F * 4
     gu_avg_s = float(np.mean(k_ms)) * 1e-3
     achieved = gu_bytes / gu_avg_s / 1e9
-    # down: the 11 experts' down codes and scales, h in, each pair's output row out
-    dn_bytes = 11 * (H * F // 2 + H * (F // 32) * 2) + 11 * F * 4 + 11 * H * 4
+    # down (one token: the weighted combine is inside the launch): the 11 experts' down codes and
+    # scales, h in, y out
+    dn_bytes = 11 * (H * F // 2 + H * (F // 32) * 2) + 11 * F * 4 + H * 4
     dn_avg_s = float(np.mean(dn_ms)) * 1e-3
     result = {
         "metric": METRIC,

@@ -1047,10 +1047,10 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
   const int dn_units = MAXTOK >= 4 ? down_pipe_units(a.F) : 0;
   if (MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
     // one token: output rows outermost, (task, group) items spread over 8 waves, no pair rows
-    const int grid = a.H / 8, items = max_tasks * (a.F / kGroupElems);
+    const int grid = a.H / 16, items = max_tasks * (a.F / kGroupElems);
     if (max_tasks <= 11 && items <= 8 * 9)
-      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 9, 8>, grid, 512, 0, st, a);
-    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 8>, grid, 512, 0, st, a);
+      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 9, 16>, grid, 512, 0, st, a);
+    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16>, grid, 512, 0, st, a);
   }
   if (dn_units) {
     if constexpr (MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);

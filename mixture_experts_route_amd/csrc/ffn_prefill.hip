@@ -36,8 +36,11 @@ constexpr int kNTileW = 256;              // weight rows per workgroup (4 waves 
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
 // Router GEMM rows per work: 32 (not a full 128-row tile), so that a 4K-token call has 256 works
-// (x 2 router tiles) instead of 64 and the router streams through every CU.
+// (x 2 router tiles) instead of 64 and the router streams through every CU; above kRouterTallFrom
+// tokens there are works enough with kRouterTallRows rows, which read the router weights fewer times.
 constexpr int kRouterTileRows = 32;
+constexpr int kRouterTallRows = 64;
+constexpr int kRouterTallFrom = 16384;
 
 struct GemmArgs {
   ExpertSource src;
@@ -113,10 +116,12 @@ MOE_DEV uint32_t word_of(const uint4& c, int d) { return d == 0 ? c.x : d == 1 ?
 
 MOE_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int MODE>
+// RROWS: rows of a router work (the router's weights are read once per work: longer calls take
+// taller works)
+template <int MODE, int RROWS = kRouterTileRows>
 __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
-  // 16-row subtiles per work: a 128-row item, or a 32-row router work
-  constexpr int MSUB = MODE == kRouter ? kRouterTileRows / 16 : kMSub;
+  // 16-row subtiles per work: a 128-row item, or a router work
+  constexpr int MSUB = MODE == kRouter ? RROWS / 16 : kMSub;
   // A tile: 128 rows x 128 16-bit elements per stage, two stages.  16-byte chunk c of row r is
   // stored at chunk c ^ (r & 15) of the row, so the 16 lanes of a fragment read (16 rows, one
   // chunk) hit 16 different chunk slots.
@@ -138,8 +143,8 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   const uint8_t* blob = nullptr;
   if constexpr (MODE == kRouter) {
     it.bucket = 0;
-    it.row0 = item_id * kRouterTileRows;
-    it.rows = min(kRouterTileRows, a.T - it.row0);
+    it.row0 = item_id * RROWS;
+    it.rows = min(RROWS, a.T - it.row0);
     if (it.rows <= 0) return;
   } else {
     it = a.items[item_id];
@@ -634,8 +639,13 @@ hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const flo
   a.bias = bias;
   a.y_out = logits;
   a.n_ntiles = (E + kNTileW - 1) / kNTileW;
-  a.n_works = ((T + kRouterTileRows - 1) / kRouterTileRows) * a.n_ntiles;
-  k_expert_gemm<kRouter><<<round8(a.n_works), 256, 0, st>>>(a);
+  if (T > kRouterTallFrom) {
+    a.n_works = ((T + kRouterTallRows - 1) / kRouterTallRows) * a.n_ntiles;
+    k_expert_gemm<kRouter, kRouterTallRows><<<round8(a.n_works), 256, 0, st>>>(a);
+  } else {
+    a.n_works = ((T + kRouterTileRows - 1) / kRouterTileRows) * a.n_ntiles;
+    k_expert_gemm<kRouter><<<round8(a.n_works), 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

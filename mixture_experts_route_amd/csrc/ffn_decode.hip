@@ -548,9 +548,9 @@ __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
 // the group partial of its task's pair value; the workgroup then forms every pair value and the
 // combine in the same order as the per-pair rows and the combine of the other decode kernels, and
 // stores y directly: no per-pair rows and no cross-workgroup combine.
-template <int MAXT, int MAXI, int RT>
-__global__ __launch_bounds__(512) void k_decode_down_rows1(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t hs[8][MAXI][2][kGroupElems];  // [wave][item][part][input]
+template <int MAXT, int MAXI, int RT, int NWV>
+__global__ __launch_bounds__(64 * NWV) void k_decode_down_rows1(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t hs[NWV][MAXI][2][kGroupElems];  // [wave][item][part][input]
   __shared__ float red[8][MAXT + 1][16];  // [group][task][row]: group partials (task MAXT: unused items)
   __shared__ float pv[MAXT][16];      // [task][row]: pair values
   __shared__ int s_inv[kMaxK];        // task of each top-k position j
@@ -586,7 +586,7 @@ __global__ __launch_bounds__(512) void k_decode_down_rows1(DecodeArgs a) {
   bool use[MAXI];
   static_for<MAXI>([&](auto c) {
     constexpr int m = c.value;
-    const int i = wave + 8 * m;
+    const int i = wave + NWV * m;
     const bool live = i < n_items;
     const int t = live ? i / NW : 0;
     it_t[m] = t;
@@ -1048,9 +1048,9 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
   if (MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
     // one token: output rows outermost, (task, group) items spread over 8 waves, no pair rows
     const int grid = a.H / 16, items = max_tasks * (a.F / kGroupElems);
-    if (max_tasks <= 11 && items <= 8 * 9)
-      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 9, 16>, grid, 512, 0, st, a);
-    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16>, grid, 512, 0, st, a);
+    if (max_tasks <= 11 && items <= 16 * 5)
+      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16>, grid, 1024, 0, st, a);
+    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16, 8>, grid, 512, 0, st, a);
   }
   if (dn_units) {
     if constexpr (MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);

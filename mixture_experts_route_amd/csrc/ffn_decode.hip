@@ -541,10 +541,11 @@ __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
 }
 
 // ---- down for one token: output rows outermost, every task inside, no pair rows -------------------
-// One workgroup of 8 waves per RT (8 or 16) output rows.  The work is (task, group of 128 F inputs) items;
-// wave w takes items w, w + 8, ... (at most MAXI), so each wave issues all of its weight loads (one
-// 16-byte code load and one 8-byte scale load per lane per item) at once and the waves carry equal
-// shares.  A rows 0 and 1 are the token's h_hi and h_lo (the other rows zero).  An item's result is
+// One workgroup of NWV waves per RT (8 or 16) output rows.  The work is (task, group of 128 F inputs)
+// items; wave w takes items w, w + NWV, ... (at most MAXI), so each wave issues all of its weight
+// loads (one 16-byte code load and one 8-byte scale load per lane per item) at once and the waves
+// carry equal shares (16 waves of 4-5 items at the model shape: four waves per SIMD hide each
+// other's MFMA chains).  A rows 0 and 1 are the token's h_hi and h_lo (the other rows zero).  An item's result is
 // the group partial of its task's pair value; the workgroup then forms every pair value and the
 // combine in the same order as the per-pair rows and the combine of the other decode kernels, and
 // stores y directly: no per-pair rows and no cross-workgroup combine.
@@ -1046,11 +1047,11 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
   if (err != hipSuccess) return err;
   const int dn_units = MAXTOK >= 4 ? down_pipe_units(a.F) : 0;
   if (MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
-    // one token: output rows outermost, (task, group) items spread over 8 waves, no pair rows
-    const int grid = a.H / 16, items = max_tasks * (a.F / kGroupElems);
+    // one token: output rows outermost, (task, group) items spread over the waves, no pair rows
+    const int items = max_tasks * (a.F / kGroupElems);
     if (max_tasks <= 11 && items <= 16 * 5)
-      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16>, grid, 1024, 0, st, a);
-    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16, 8>, grid, 512, 0, st, a);
+      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16>, a.H / 16, 1024, 0, st, a);
+    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16, 8>, a.H / 16, 512, 0, st, a);
   }
   if (dn_units) {
     if constexpr (MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);

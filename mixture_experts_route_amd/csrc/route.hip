@@ -634,11 +634,13 @@ __global__ __launch_bounds__(256) void k_router_gemv(RouteArgs a) {
   route_tail<NPER>(a);
 }
 
-// Router GEMV on the matrix cores (bf16 router): one workgroup per 16 router rows, its 8 waves
-// split the H inputs and reduce through LDS.  A = activation rows (one per token; fp32 inputs as
-// bf16 hi + lo rows), B = 16 router rows, 32 inputs per v_mfma_f32_16x16x32_bf16 step; each lane
-// loads 16 contiguous bytes of its router row per step (the row's 4 lanes read 64 bytes).
+// Router GEMV on the matrix cores (bf16 router): one workgroup per kRouterRows router rows (8: 64
+// workgroups share the 2 MB of weights, so each CU reads 32 KB), its 8 waves split the H inputs and
+// reduce through LDS.  A = activation rows (one per token; fp32 inputs as bf16 hi + lo rows), B = the
+// router rows in the MFMA's first kRouterRows columns, 32 inputs per v_mfma_f32_16x16x32_bf16 step;
+// each lane loads 16 contiguous bytes of its router row per step (the row's 4 lanes read 64 bytes).
 constexpr int kRouterWaves = 8;
+constexpr int kRouterRows = 8;  // router rows per workgroup (of the MFMA's 16 columns)
 constexpr int kRouterMaxSteps = 4096 / 32 / kRouterWaves;  // H <= 4096
 
 MOE_DEV uint4 split_bf16_part(const float4& a, const float4& b, int part) {
@@ -658,8 +660,8 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(RouteArgs a) 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int T = a.T, E = a.E, H = a.H;
-  const int e0 = blockIdx.x * 16;
-  const int e = e0 + n;
+  const int e0 = blockIdx.x * kRouterRows;
+  const int e = n < kRouterRows ? e0 + n : E;  // B columns past the workgroup's rows stay zero
   const int NB = H / 32;
   const int spw = (NB + kRouterWaves - 1) / kRouterWaves;  // 32-input steps per wave
   const int b0 = wave * spw;
@@ -705,7 +707,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(RouteArgs a) 
   if ((int)threadIdx.x < 16 * T) {
     const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
     const int ee = e0 + c;
-    if (ee < E) {
+    if (c < kRouterRows && ee < E) {
       float sum = 0.f;
       for (int w = 0; w < kRouterWaves; ++w) {
         if constexpr (X_BF16) sum += red[w][t][c];
@@ -754,7 +756,7 @@ template <int NPER>
 static hipError_t launch_router(const RouteArgs& a, int x_dtype, int r_dtype, hipStream_t st) {
   if (r_dtype == MOE_BF16) {
     // bf16 router: matrix-core GEMV
-    const int grid = (a.E + 15) / 16;
+    const int grid = (a.E + kRouterRows - 1) / kRouterRows;
     if (x_dtype == MOE_BF16)
       return launch_timed(kTimeDecodeRoute, k_router_mfma<true, NPER>, grid, 64 * kRouterWaves, 0, st, a);
     return launch_timed(kTimeDecodeRoute, k_router_mfma<false, NPER>, grid, 64 * kRouterWaves, 0, st, a);

@@ -32,6 +32,7 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0
 
 H, F, E, K_TOP = 2048, 768, 512, 10
 X_STREAM = 1_000_000  # stream index of the benchmark's activations
+POOL_SPARES = 4  # spare pinned host buffers per slot-pool layer (victims' copies out run ahead)
 
 
 def _hip():
@@ -542,8 +543,8 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
         initial = [int(e) for e in np.argsort(ranks[0], kind="stable")[:n_slots]]
         arena = tmp[torch.as_tensor(initial, device=dev, dtype=torch.long)].contiguous()
         away = [e for e in range(E) if e not in set(initial)]
-        homes = N.HostBuffer((len(away) + 1) * stride, flags=0)
-        hv = torch.from_numpy(homes.view(np.uint8)).view(len(away) + 1, stride)
+        homes = N.HostBuffer((len(away) + POOL_SPARES) * stride, flags=0)
+        hv = torch.from_numpy(homes.view(np.uint8)).view(len(away) + POOL_SPARES, stride)
         hv[:len(away)].copy_(tmp[torch.as_tensor(away, device=dev, dtype=torch.long)])
         home_addr = [0] * E
         for i, e in enumerate(away):
@@ -556,7 +557,7 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
         ready = torch.zeros((64,), dtype=torch.int32, device=dev)
         hb = [N.HostBuffer(4 * E), N.HostBuffer(64), N.HostBuffer(4 * 8 * K_TOP)]
         pool = N.moe_pool_create(d, arena, stride, n_slots, table, initial, home_addr, homes.ptr + len(away) * stride,
-                                 hb[0].ptr, hb[1].ptr, hb[2].ptr, ready)
+                                 POOL_SPARES, hb[0].ptr, hb[1].ptr, hb[2].ptr, ready)
         layers.append(dict(arena=arena, homes=homes, shared=shared, router=router, biases=biases, table=table,
                            ready=ready, hb=hb, pool=pool, n_slots=n_slots))
     del tmp
@@ -566,7 +567,7 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
     y = torch.empty((T, H), dtype=torch.float32, device=dev)
     ws = torch.zeros(N.moe_workspace_bytes(d, T) // 4 + 64, dtype=torch.int32, device=dev)
     N.moe_workspace_init(ws)
-    compute, copy = streams
+    compute, d2h, h2d = streams
 
     def step(s):
         topic = s // topic_every
@@ -576,7 +577,7 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
             N.moe_layer_forward(d, w, L["table"], xs[layer][s:s + 1], T, y, ws, bell=bell, stream=compute)
         for i, L in enumerate(layers):
             try:
-                N.moe_pool_serve(L["pool"], ws, copy)
+                N.moe_pool_serve(L["pool"], ws, d2h, h2d_stream=h2d)
             except N.MoeError:
                 # a stream that waits on the pool cannot drain once its fill failed: report and leave
                 # without the runtime's teardown (which would wait for that stream)
@@ -593,14 +594,15 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
     for s in range(2, steps + 2):
         step(s)
     compute.synchronize()
-    copy.synchronize()
+    d2h.synchronize()
+    h2d.synchronize()
     t1 = time.perf_counter()
     assert N.moe_check_device_error(ws) == 0
     st1 = [N.moe_pool_get_stats(L["pool"]) for L in layers]
     sel = sum(b.selections - a.selections for a, b in zip(st0, st1))
     mis = sum(b.misses - a.misses for a, b in zip(st0, st1))
-    h2d = sum(b.bytes_h2d - a.bytes_h2d for a, b in zip(st0, st1))
-    d2h = sum(b.bytes_d2h - a.bytes_d2h for a, b in zip(st0, st1))
+    b_h2d = sum(b.bytes_h2d - a.bytes_h2d for a, b in zip(st0, st1))
+    b_d2h = sum(b.bytes_d2h - a.bytes_d2h for a, b in zip(st0, st1))
     # pinned host <-> HBM copy rate for one expert blob, same process (the fills' bound)
     hb = N.HostBuffer(blob * 8, flags=0)
     dbuf = torch.empty((blob * 8,), dtype=torch.uint8, device=dev)
@@ -613,8 +615,8 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
         for rep in range(8):
             dst = dbuf.data_ptr() + rep * blob if kind == 1 else hb.ptr + rep * blob
             src = hb.ptr + rep * blob if kind == 1 else dbuf.data_ptr() + rep * blob
-            hip.hipMemcpyAsync(dst, src, blob, kind, copy.cuda_stream)
-        copy.synchronize()
+            hip.hipMemcpyAsync(dst, src, blob, kind, d2h.cuda_stream)
+        d2h.synchronize()
         rates[name] = 8 * blob / (time.perf_counter() - c0) / 1e9
     hb.free()
     for L in layers:
@@ -624,15 +626,17 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
         "workload": "single-token decode through 48 layers with 5,000 HBM expert slots (240 / 92 / 60 per early / "
                     "middle / late layer) and the other 19,576 experts in pinned host memory (exclusive tiers); "
                     f"per-layer Zipf(1.1) router bias with a topic shift every {topic_every} steps; misses filled "
-                    "by the host pool service on a copy stream while the compute stream waits in-stream",
+                    "by the host pool service (victims out on one copy stream, misses in on another, "
+                    f"{POOL_SPARES} spare host buffers) while the compute stream waits in-stream",
         "tokens_per_s": steps / elapsed,
         "ms_per_token": elapsed * 1e3 / steps,
         "steps": steps,
         "hit_rate": 1.0 - mis / max(1, sel),
         "misses_per_token": mis / steps,
-        "pcie_mib_per_token": (h2d + d2h) / steps / 2**20,
+        "pcie_mib_per_token": (b_h2d + b_d2h) / steps / 2**20,
         "pcie_rate_gbs_per_blob_copy": rates,
-        "fill_time_bound_ms_per_token": (h2d / rates["h2d"] + d2h / rates["d2h"]) / 1e6 / steps,
+        "fill_time_serial_ms_per_token": (b_h2d / rates["h2d"] + b_d2h / rates["d2h"]) / 1e6 / steps,
+        "fill_time_overlapped_ms_per_token": max(b_h2d / rates["h2d"], b_d2h / rates["d2h"]) / 1e6 / steps,
     }
 
 
@@ -659,14 +663,14 @@ def main():
     def progress(msg):
         print(f"bench: {msg}", file=sys.stderr, flush=True)
 
-    # The slot pool's compute and copy streams are created first, while no other stream exists:
+    # The slot pool's compute and two copy streams are created first, while no other stream exists:
     # the runtime spreads streams over a few hardware queues, and the compute stream's in-stream
     # wait must not sit in front of the copies on a shared queue.
     pool_streams = None
     if args.pool_steps > 0:
         from mixture_experts_route_amd import native as N
 
-        pool_streams = (N.new_stream(), N.new_stream())
+        pool_streams = (N.new_stream(), N.new_stream(), N.new_stream())
     progress("single-token decode")
     res = bench_decode1(args)
     if args.copy_calibration:

@@ -247,17 +247,19 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w,
  *
  * Use per layer call: moe_pool_arm -> moe_layer_forward(..., table, &bell, ...) on the compute
  * stream -> moe_pool_serve on the host (it blocks until the call's check has run, then
- * enqueues the copies, the table update and the release of the compute stream on
- * `copy_stream`).  Several layers' calls may be enqueued before their serves; serve them in
- * the same order.  A pool is used from one host thread and one copy stream.
+ * enqueues the copies, the table update and the release of the compute stream on its copy
+ * streams).  Several layers' calls may be enqueued before their serves; serve them in the
+ * same order.  A pool is used from one host thread and one pair of copy streams (or one).
  *
  * The compute stream's wait stalls whatever the runtime has queued behind it on the same
  * hardware queue, and the runtime spreads streams over a few such queues (4 by default).
- * Create the compute and copy streams as a pair, non-blocking, before other streams (a
- * framework's stream pool, graph capture streams) exist: a copy stream that ends up behind
- * the wait never runs, and the next serve then times out.  Each serve failure is also
- * reported on stderr with its epoch and reason. */
+ * Create the compute stream and the copy streams together, non-blocking, before other
+ * streams (a framework's stream pool, graph capture streams) exist: a copy stream that ends
+ * up behind the wait never runs, and the next serve then times out.  Each serve failure is
+ * also reported on stderr with its epoch and reason. */
 typedef struct moe_pool moe_pool;
+
+#define MOE_POOL_MAX_SPARES 64
 
 typedef struct moe_pool_stats {
   int64_t calls;       /* served calls */
@@ -275,16 +277,19 @@ typedef struct moe_pool_stats {
  *                  (colder ones are evicted first); their blobs must already be in the slots;
  *   host_home      host array [E] of pinned host pointers: the blob of every expert not in
  *                  `initial`, NULL for those in it (the pool permutes these buffers);
- *   spare          one pinned host buffer of a blob's size, holding no expert;
+ *   spares, n_spares  n_spares (1..MOE_POOL_MAX_SPARES) pinned host buffers holding no
+ *                  expert, at spares + i * slot_stride; the pool permutes them with host_home
+ *                  (a miss's victim goes to the oldest, the missed expert's buffer becomes the
+ *                  newest); more spares let the copies out run ahead of the copies in;
  *   host_miss_ids  host-mapped pinned int32[E]; host_counts host-mapped pinned int32[3];
  *   host_step_ids  host-mapped pinned int32[MOE_DECODE_MAX_TOKENS * k];
  *   ready          device uint32 (set to 0 here).
  * Copies the table and the ready word synchronously.  Returns MOE_EINVAL on inconsistent
  * arguments (a slot holding an id out of range or twice, an expert with no or two homes). */
 MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_stride, int32_t n_slots,
-                            int32_t* table, const int32_t* initial, uint8_t* const* host_home, uint8_t* spare,
-                            int32_t* host_miss_ids, int32_t* host_counts, int32_t* host_step_ids,
-                            uint32_t* ready, moe_pool** pool_out);
+                            int32_t* table, const int32_t* initial, uint8_t* const* host_home, uint8_t* spares,
+                            int32_t n_spares, int32_t* host_miss_ids, int32_t* host_counts,
+                            int32_t* host_step_ids, uint32_t* ready, moe_pool** pool_out);
 
 /* Frees the pool object (not the caller's memory). */
 MOE_API int moe_pool_destroy(moe_pool* pool);
@@ -294,14 +299,19 @@ MOE_API int moe_pool_destroy(moe_pool* pool);
 MOE_API int moe_pool_arm(moe_pool* pool, moe_doorbell* bell_out);
 
 /* Serves the armed call: waits on the host until the check kernel has written the epoch
- * (polling host memory, at most timeout_us microseconds if > 0), places every miss, and on
- * copy_stream enqueues per miss a device->host copy of the victim and a host->device copy of
- * the missed expert, then the table and *ready = epoch.  fills_out (host int32[E][3] or NULL)
+ * (polling host memory, at most timeout_us microseconds if > 0), places every miss, and
+ * enqueues per miss a device->host copy of the victim into a spare buffer on d2h_stream and a
+ * host->device copy of the missed expert into the victim's slot on h2d_stream (ordered after
+ * that device->host copy by an event), then on h2d_stream the table and *ready = epoch.
+ * h2d_stream_or_null NULL puts everything on d2h_stream.  With two streams the copies of the
+ * two PCIe directions overlap; a device->host copy into a buffer waits for the host->device
+ * copy that last read it, and a serve's first one waits for the previous serve's copies in
+ * (its victims may be slots those filled).  fills_out (host int32[E][3] or NULL)
  * receives (expert, slot, evicted expert) per fill, n_fills_out their number.  On a timeout,
  * a bad doorbell or a failed copy the compute stream is still released (*ready = epoch), the
  * fill error bit is set in ws (when not NULL) and MOE_EFILL is returned. */
-MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, int32_t* fills_out,
-                           int32_t* n_fills_out, int64_t timeout_us);
+MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* d2h_stream, void* h2d_stream_or_null,
+                           int32_t* fills_out, int32_t* n_fills_out, int64_t timeout_us);
 
 /* Counters since creation. */
 MOE_API int moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* out);

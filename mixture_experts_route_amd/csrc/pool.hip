@@ -12,18 +12,23 @@
 //   moe_layer_forward -> enqueues route + check (the check kernel writes the miss list, the
 //                        step's selections and the epoch into host-mapped memory; with no miss it
 //                        also writes *ready = epoch), a stream wait on *ready >= epoch, the FFNs;
-//   moe_pool_serve    -> polls the epoch, places the misses, and on `copy_stream`: per miss one
-//                        device->host copy of the victim into the spare host buffer and one
-//                        host->device copy of the missing expert into the victim's slot, then the
-//                        updated slot table, then *ready = epoch.  The spare buffer and the filled
-//                        expert's old host buffer trade places (the exclusive swap).
+//   moe_pool_serve    -> polls the epoch, places the misses, and per miss enqueues one
+//                        device->host copy of the victim into a spare host buffer (on the d2h
+//                        stream) and one host->device copy of the missing expert into the victim's
+//                        slot (on the h2d stream, after that slot's device->host copy), then on the
+//                        h2d stream the updated slot table and *ready = epoch.  The spare buffer
+//                        and the filled expert's old host buffer trade places (the exclusive
+//                        swap); with several spares (a FIFO) and two streams the victims' copies
+//                        out and the misses' copies in overlap on the two PCIe directions.
 // The FFN kernels read the slot of a missed expert from the table when they run, after the wait.
 #include <atomic>
 #include <cstdio>
 #include <chrono>
 #include <cstring>
+#include <deque>
 #include <new>
 #include <thread>
+#include <utility>
 #include <vector>
 
 #include "kernels.hpp"
@@ -47,7 +52,14 @@ struct moe_pool {
   std::vector<int64_t> last_use;  // recency stamp of each slot
   int64_t clock = 0;
   std::vector<uint8_t*> home;     // pinned host blob of every expert not in a slot
-  uint8_t* spare = nullptr;       // pinned host blob with no expert in it
+  // pinned host blobs holding no expert, oldest first, each with the ring event (or -1) of the
+  // host->device copy that last read it (a device->host copy into it waits for that event)
+  std::deque<std::pair<uint8_t*, int>> spares;
+  std::vector<hipEvent_t> ev_ring;  // n_spares + 1 events, used round robin
+  int ev_next = 0;
+  hipEvent_t ev_d2h = nullptr;      // a miss's device->host copy (its slot's host->device copy waits)
+  hipEvent_t ev_end = nullptr;      // the h2d stream after a serve's copies (the next serve's d2h waits)
+  bool ev_end_set = false;
   int32_t* host_miss_ids = nullptr;
   int32_t* host_counts = nullptr;
   int32_t* host_step_ids = nullptr;
@@ -61,15 +73,25 @@ static bool hip_ok(hipError_t e) { return e == hipSuccess; }
 
 extern "C" {
 
+static void destroy_events(moe_pool* p) {
+  for (hipEvent_t e : p->ev_ring)
+    if (e) (void)hipEventDestroy(e);
+  p->ev_ring.clear();
+  if (p->ev_d2h) (void)hipEventDestroy(p->ev_d2h);
+  if (p->ev_end) (void)hipEventDestroy(p->ev_end);
+  p->ev_d2h = p->ev_end = nullptr;
+}
+
 MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_stride, int32_t n_slots, int32_t* table,
-                            const int32_t* initial, uint8_t* const* host_home, uint8_t* spare, int32_t* host_miss_ids,
-                            int32_t* host_counts, int32_t* host_step_ids, uint32_t* ready, moe_pool** pool_out) {
+                            const int32_t* initial, uint8_t* const* host_home, uint8_t* spares, int32_t n_spares,
+                            int32_t* host_miss_ids, int32_t* host_counts, int32_t* host_step_ids, uint32_t* ready,
+                            moe_pool** pool_out) {
   if (!pool_out) return MOE_EINVAL;
   *pool_out = nullptr;
   const size_t blob = moe_expert_blob_bytes(dims);
   if (!blob) return MOE_EINVAL;
-  if (!arena || !table || !initial || !host_home || !spare || !host_miss_ids || !host_counts || !host_step_ids ||
-      !ready)
+  if (!arena || !table || !initial || !host_home || !spares || n_spares < 1 || n_spares > MOE_POOL_MAX_SPARES ||
+      !host_miss_ids || !host_counts || !host_step_ids || !ready)
     return MOE_EINVAL;
   if (n_slots < 1 || n_slots > dims->n_experts || slot_stride < (int64_t)blob || slot_stride % 4096) return MOE_EINVAL;
   const int E = dims->n_experts;
@@ -94,12 +116,23 @@ MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_s
   p->last_use.resize(n_slots);
   for (int s = 0; s < n_slots; ++s) p->last_use[s] = -(int64_t)(s + 1);  // hottest first: colder evicted first
   p->home.assign(host_home, host_home + E);
-  p->spare = spare;
+  for (int i = 0; i < n_spares; ++i) p->spares.emplace_back(spares + (int64_t)i * slot_stride, -1);
+  p->ev_ring.assign(n_spares + 1, nullptr);
+  bool ev_ok = true;
+  for (hipEvent_t& e : p->ev_ring) ev_ok = ev_ok && hip_ok(hipEventCreateWithFlags(&e, hipEventDisableTiming));
+  ev_ok = ev_ok && hip_ok(hipEventCreateWithFlags(&p->ev_d2h, hipEventDisableTiming)) &&
+          hip_ok(hipEventCreateWithFlags(&p->ev_end, hipEventDisableTiming));
+  if (!ev_ok) {
+    destroy_events(p);
+    delete p;
+    return MOE_EHIP;
+  }
   p->host_miss_ids = host_miss_ids;
   p->host_counts = host_counts;
   p->host_step_ids = host_step_ids;
   p->ready = ready;
   if (!hip_ok(hipHostMalloc((void**)&p->table_host, sizeof(int32_t) * E, hipHostMallocDefault))) {
+    destroy_events(p);
     delete p;
     return MOE_EHIP;
   }
@@ -108,6 +141,7 @@ MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_s
   if (!hip_ok(hipMemcpy(table, p->table_host, sizeof(int32_t) * E, hipMemcpyHostToDevice)) ||
       !hip_ok(hipMemcpy(ready, &zero, sizeof(zero), hipMemcpyHostToDevice))) {
     (void)hipHostFree(p->table_host);
+    destroy_events(p);
     delete p;
     return MOE_EHIP;
   }
@@ -119,6 +153,7 @@ MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_s
 MOE_API int moe_pool_destroy(moe_pool* pool) {
   if (!pool) return MOE_EINVAL;
   (void)hipHostFree(pool->table_host);
+  destroy_events(pool);
   delete pool;
   return MOE_OK;
 }
@@ -142,15 +177,20 @@ static int release_with_error(moe_pool* p, void* ws, hipStream_t cs, const char*
   fprintf(stderr, "moe_pool_serve: epoch %u: %s (%ld, %ld)\n", p->epoch, why, v0, v1);
   if (ws) k_set_error_bits<<<1, 64, 0, cs>>>((int32_t*)ws, MOE_DERR_FILL);
   (void)hipStreamWriteValue32(cs, p->ready, p->epoch, 0);
+  // the copies already enqueued on `cs` still order the next serve's device->host copies
+  p->ev_end_set = hip_ok(hipEventRecord(p->ev_end, cs));
+  if (!p->ev_end_set) (void)hipStreamSynchronize(cs);
   p->armed = false;
   return MOE_EFILL;
 }
 
-MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, int32_t* fills_out,
-                           int32_t* n_fills_out, int64_t timeout_us) {
+MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* d2h_stream, void* h2d_stream_or_null,
+                           int32_t* fills_out, int32_t* n_fills_out, int64_t timeout_us) {
   if (!pool || !pool->armed) return MOE_EINVAL;
   moe_pool* p = pool;
-  hipStream_t cs = (hipStream_t)copy_stream;
+  hipStream_t sd = (hipStream_t)d2h_stream;
+  hipStream_t cs = h2d_stream_or_null ? (hipStream_t)h2d_stream_or_null : sd;  // h2d stream: table, release
+  const bool two = cs != sd;
   if (n_fills_out) *n_fills_out = 0;
   // wait for the check kernel's doorbell (the epoch is written after the lists)
   volatile int32_t* counts = p->host_counts;
@@ -176,6 +216,9 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, 
     selected[e] = 1;
   }
   int n_fills = 0;
+  // the victims of this serve may be slots the previous serve filled (its h2d stream ends at ev_end)
+  if (n_miss > 0 && p->ev_end_set && !hip_ok(hipStreamWaitEvent(sd, p->ev_end, 0)))
+    return release_with_error(p, ws_or_null, cs, "copy enqueue failed", -1, -1);
   for (int e : miss) {
     if (e < 0 || e >= p->E || p->table_host[e] >= 0 || !p->home[e])
       return release_with_error(p, ws_or_null, cs, "miss id not away", e, (e >= 0 && e < p->E) ? p->table_host[e] : -9);
@@ -189,16 +232,33 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, 
     if (best < 0) return release_with_error(p, ws_or_null, cs, "no victim slot", n_miss, n_sel);
     const int old = p->holder[best];
     uint8_t* slot = p->arena + (int64_t)best * p->stride;
-    // exclusive swap: the victim goes to the spare host buffer, the missing expert to the slot
-    if (!hip_ok(hipMemcpyAsync(p->spare, slot, p->blob_bytes, hipMemcpyDeviceToHost, cs)) ||
-        !hip_ok(hipMemcpyAsync(slot, p->home[e], p->blob_bytes, hipMemcpyHostToDevice, cs)))
-      return release_with_error(p, ws_or_null, cs, "copy enqueue failed", e, best);
-    p->home[old] = p->spare;
-    p->spare = p->home[e];
+    // exclusive swap: the victim goes to the oldest spare host buffer, the missing expert to the
+    // slot (after the victim's copy out); the expert's old host buffer becomes the newest spare
+    const auto [buf, buf_ev] = p->spares.front();
+    bool ok = !two || buf_ev < 0 || hip_ok(hipStreamWaitEvent(sd, p->ev_ring[buf_ev], 0));
+    ok = ok && hip_ok(hipMemcpyAsync(buf, slot, p->blob_bytes, hipMemcpyDeviceToHost, sd));
+    if (two) ok = ok && hip_ok(hipEventRecord(p->ev_d2h, sd)) && hip_ok(hipStreamWaitEvent(cs, p->ev_d2h, 0));
+    ok = ok && hip_ok(hipMemcpyAsync(slot, p->home[e], p->blob_bytes, hipMemcpyHostToDevice, cs));
+    // nothing was placed if an enqueue failed: the slot still holds the victim, the buffer stays spare
+    if (!ok) return release_with_error(p, ws_or_null, cs, "copy enqueue failed", e, best);
+    int read_ev = -1;
+    if (two) {
+      read_ev = p->ev_next;
+      p->ev_next = (p->ev_next + 1) % (int)p->ev_ring.size();
+      // without the event the buffer is guarded by draining the h2d stream
+      if (!hip_ok(hipEventRecord(p->ev_ring[read_ev], cs))) {
+        read_ev = -1;
+        ok = hip_ok(hipStreamSynchronize(cs));
+      }
+    }
+    p->spares.pop_front();
+    p->spares.emplace_back(p->home[e], read_ev);
+    p->home[old] = buf;
     p->home[e] = nullptr;
     p->table_host[old] = -1;
     p->table_host[e] = best;
     p->holder[best] = e;
+    if (!ok) return release_with_error(p, ws_or_null, cs, "event record failed", e, best);
     if (fills_out) {
       fills_out[3 * n_fills + 0] = e;
       fills_out[3 * n_fills + 1] = best;
@@ -212,6 +272,8 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* copy_stream, 
     if (!hip_ok(hipMemcpyAsync(p->table_dev, p->table_host, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, cs)) ||
         !hip_ok(hipStreamWriteValue32(cs, p->ready, p->epoch, 0)))
       return release_with_error(p, ws_or_null, cs, "table copy or release enqueue failed");
+    if (!hip_ok(hipEventRecord(p->ev_end, cs))) return release_with_error(p, ws_or_null, cs, "event record failed");
+    p->ev_end_set = true;
   }
   // recency: every selection of the step, in (token, choice) order
   for (int e : sel) p->last_use[p->table_host[e]] = ++p->clock;

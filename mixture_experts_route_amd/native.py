@@ -84,10 +84,10 @@ _sig = {
     "moe_expert_ffn_decode": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn_prefill": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward": (ctypes.c_int, [_D, _W, _P, _B, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
-    "moe_pool_create": (ctypes.c_int, [_D, _P, ctypes.c_int64, _I, _P, _P, _PP, _P, _P, _P, _P, _P, _PP]),
+    "moe_pool_create": (ctypes.c_int, [_D, _P, ctypes.c_int64, _I, _P, _P, _PP, _P, _I, _P, _P, _P, _P, _PP]),
     "moe_pool_destroy": (ctypes.c_int, [_P]),
     "moe_pool_arm": (ctypes.c_int, [_P, _B]),
-    "moe_pool_serve": (ctypes.c_int, [_P, _P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64]),
+    "moe_pool_serve": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64]),
     "moe_pool_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(moe_pool_stats)]),
     "moe_pool_get_table": (ctypes.c_int, [_P, _P]),
 }
@@ -286,15 +286,16 @@ class HostBuffer:
             self.ptr = 0
 
 
-def moe_pool_create(d: moe_dims, arena, slot_stride: int, n_slots: int, table, initial, host_home, spare,
-                    host_miss_ids: int, host_counts: int, host_step_ids: int, ready):
+def moe_pool_create(d: moe_dims, arena, slot_stride: int, n_slots: int, table, initial, host_home, spares,
+                    n_spares: int, host_miss_ids: int, host_counts: int, host_step_ids: int, ready):
     """Returns the pool handle (int).  ``initial``: sequence of n_slots expert ids; ``host_home``:
-    sequence of E addresses (0 for experts in ``initial``); other pointers as in the header."""
+    sequence of E addresses (0 for experts in ``initial``); ``spares``: n_spares pinned buffers at
+    slot_stride apart; other pointers as in the header."""
     init = (ctypes.c_int32 * n_slots)(*[int(e) for e in initial])
     homes = (ctypes.c_void_p * len(host_home))(*[int(a) if a else None for a in host_home])
     out = ctypes.c_void_p()
     _check(_lib.moe_pool_create(ctypes.byref(d), _ptr(arena), int(slot_stride), int(n_slots), _ptr(table), init,
-                                homes, _ptr(spare), host_miss_ids, host_counts, host_step_ids, _ptr(ready),
+                                homes, _ptr(spares), int(n_spares), host_miss_ids, host_counts, host_step_ids, _ptr(ready),
                                 ctypes.byref(out)), "moe_pool_create")
     return out.value
 
@@ -309,12 +310,16 @@ def moe_pool_arm(pool: int) -> moe_doorbell:
     return bell
 
 
-def moe_pool_serve(pool: int, ws=None, copy_stream=None, n_experts: int = 0, timeout_us: int = 20_000_000):
-    """Serves the armed call; returns the fills [(expert, slot, evicted)].  Raises on MOE_EFILL."""
+def moe_pool_serve(pool: int, ws=None, copy_stream=None, n_experts: int = 0, timeout_us: int = 20_000_000,
+                   h2d_stream=None):
+    """Serves the armed call; returns the fills [(expert, slot, evicted)].  Raises on MOE_EFILL.
+    ``copy_stream`` takes the device->host copies, ``h2d_stream`` (None: the same stream) the
+    host->device copies, the table and the release."""
     fills = (ctypes.c_int32 * (3 * max(1, n_experts)))()
     n = ctypes.c_int32()
-    _check(_lib.moe_pool_serve(pool, _ptr(ws), _stream(copy_stream), fills if n_experts else None, ctypes.byref(n),
-                               int(timeout_us)), "moe_pool_serve")
+    h2d = h2d_stream.cuda_stream if h2d_stream is not None else None
+    _check(_lib.moe_pool_serve(pool, _ptr(ws), _stream(copy_stream), h2d, fills if n_experts else None,
+                               ctypes.byref(n), int(timeout_us)), "moe_pool_serve")
     return [(fills[3 * i], fills[3 * i + 1], fills[3 * i + 2]) for i in range(n.value)] if n_experts else n.value
 
 

@@ -115,8 +115,10 @@ def test_pool_create_rejects_inconsistent_residency(N):
         init = (ctypes.c_int32 * len(initial))(*initial)
         hh = (ctypes.c_void_p * 512)(*[h if h else None for h in homes])
         out = ctypes.c_void_p()
-        return N.raw("moe_pool_create")(ctypes.byref(d), fake, stride, len(initial), fake, init, hh, fake, fake,
-                                        fake, fake, fake, ctypes.byref(out))
+        return N.raw("moe_pool_create")(ctypes.byref(d), fake, stride, len(initial), fake, init, hh, fake, n_spares,
+                                        fake, fake, fake, fake, ctypes.byref(out))
+
+    n_spares = 2
 
     homes = [0 if e < 4 else fake + 4096 * e for e in range(512)]
     assert create([0, 1, 2, 2], homes) == -1            # expert 2 in two slots
@@ -125,5 +127,7 @@ def test_pool_create_rejects_inconsistent_residency(N):
     both = list(homes)
     both[0] = fake
     assert create([0, 1, 2, 3], both) == -1             # expert 0 in a slot and on the host
+    for n_spares in (0, 65):                            # spare count outside 1..MOE_POOL_MAX_SPARES
+        assert create([0, 1, 2, 3], homes) == -1
     assert N.raw("moe_pool_arm")(None, None) == -1
-    assert N.raw("moe_pool_serve")(None, None, None, None, None, 0) == -1
+    assert N.raw("moe_pool_serve")(None, None, None, None, None, None, 0) == -1

@@ -36,7 +36,7 @@ class PoolLayer:
     """One model-shaped layer whose routed experts live partly in `n_slots` HBM slots and partly in
     pinned host memory, with the router bias of a popularity ranking per topic."""
 
-    def __init__(self, N, dev, layer_id, n_slots, topics=2):
+    def __init__(self, N, dev, layer_id, n_slots, topics=2, n_spares=1):
         from mixture_experts_route_amd import synth as S
 
         self.S, self.N = S, N
@@ -57,7 +57,7 @@ class PoolLayer:
         self.arena = allb[torch.as_tensor(self.initial, device=dev, dtype=torch.long)].contiguous()
         resident = set(self.initial)
         self.away = [e for e in range(E) if e not in resident]
-        self.homes = torch.empty((len(self.away) + 1, self.stride), dtype=torch.uint8, pin_memory=True)
+        self.homes = torch.empty((len(self.away) + n_spares, self.stride), dtype=torch.uint8, pin_memory=True)
         if self.away:
             self.homes[:len(self.away)].copy_(allb[torch.as_tensor(self.away, device=dev, dtype=torch.long)].cpu())
         del allb
@@ -65,7 +65,8 @@ class PoolLayer:
         self.home_addr = [0] * E
         for i, e in enumerate(self.away):
             self.home_addr[e] = self.homes[i].data_ptr()
-        self.spare = self.homes[len(self.away)]
+        self.n_spares = n_spares
+        self.spares = self.homes[len(self.away)]
         self.shared = torch.empty((self.stride,), dtype=torch.uint8, device=dev)
         S.expert_blobs_torch([S.stream_key(0, self.cfg, "shared", layer_id, 0)], self.H, self.F, self.shared.view(1, -1))
         rkey = S.stream_key(0, self.cfg, "router", layer_id, 0)
@@ -78,7 +79,7 @@ class PoolLayer:
         self.hb_counts = N.HostBuffer(64)
         self.hb_step = N.HostBuffer(4 * 8 * self.k)
         self.pool = N.moe_pool_create(self.dims(), self.arena, self.stride, n_slots, self.table, self.initial,
-                                      self.home_addr, self.spare, self.hb_ids.ptr, self.hb_counts.ptr,
+                                      self.home_addr, self.spares, n_spares, self.hb_ids.ptr, self.hb_counts.ptr,
                                       self.hb_step.ptr, self.ready)
 
     def dims(self):
@@ -110,11 +111,20 @@ def _ws(N, d, dev):
     return ws
 
 
-def test_pool_decode_steps_match_oracle_policy_and_outputs(N, dev):
-    L = PoolLayer(N, dev, layer_id=20, n_slots=60)
+@pytest.mark.parametrize("n_spares,two_streams", [(1, False), (4, True)])
+def test_pool_decode_steps_match_oracle_policy_and_outputs(N, dev, n_spares, two_streams):
+    """One copy stream and one spare buffer, or separate device->host and host->device streams
+    with four spares (the copies of the two directions overlap): same fills, tables and outputs,
+    and afterwards every evicted expert's bytes sit in the host buffer the swap rule gives it."""
+    L = PoolLayer(N, dev, layer_id=20, n_slots=60, n_spares=n_spares)
     d = L.dims()
     ws = _ws(N, d, dev)
     compute, copy = N.new_stream(), N.new_stream()
+    h2d = N.new_stream() if two_streams else None
+    # the exclusive swap replayed on the host: a victim's bytes go to the oldest spare buffer,
+    # the missed expert's buffer becomes the newest spare
+    home = list(L.home_addr)
+    spares = [L.spares.data_ptr() + i * L.stride for i in range(n_spares)]
     ref_pool = O.SlotPoolLRU(L.E, L.initial)
     ids = torch.zeros((1, L.k), dtype=torch.int32, device=dev)
     y = torch.zeros((1, L.H), dtype=torch.float32, device=dev)
@@ -127,9 +137,15 @@ def test_pool_decode_steps_match_oracle_policy_and_outputs(N, dev):
         bell = N.moe_pool_arm(L.pool)
         with torch.cuda.stream(compute):
             N.moe_layer_forward(d, L.weights(topic), L.table, x, 1, y, ws, topk_ids=ids, bell=bell, stream=compute)
-        fills = N.moe_pool_serve(L.pool, ws, copy, L.E)
+        fills = N.moe_pool_serve(L.pool, ws, copy, L.E, h2d_stream=h2d)
         compute.synchronize()
         copy.synchronize()
+        if h2d is not None:
+            h2d.synchronize()
+        for e, _, old in fills:
+            buf = spares.pop(0)
+            spares.append(home[e])
+            home[old], home[e] = buf, 0
         assert N.moe_check_device_error(ws) == 0
         got_ids = ids.cpu().numpy()
         misses, ref_fills = ref_pool.step(got_ids)
@@ -153,8 +169,18 @@ def test_pool_decode_steps_match_oracle_policy_and_outputs(N, dev):
     filled = [int(e) for e in np.nonzero(table >= 0)[0] if int(e) not in set(L.initial)]
     for e in filled[:4] + [int(e) for e in np.nonzero(table >= 0)[0][:2]]:
         assert np.array_equal(arena[table[e], :L.blob], L.blob_np(e)), e
+    # the evicted experts' bytes were copied out into the buffers the swap rule names
+    base = L.homes.data_ptr()
+    homes = L.homes.numpy()
+    evicted = [int(e) for e in L.initial if table[e] < 0]
+    assert evicted
+    for e in evicted[:6]:
+        assert home[e], e
+        assert np.array_equal(homes[(home[e] - base) // L.stride, :L.blob], L.blob_np(e)), e
     N.free_stream(compute)
     N.free_stream(copy)
+    if h2d is not None:
+        N.free_stream(h2d)
     L.close()
 
 

@@ -72,6 +72,26 @@ class KernelTimer:
             self.hip.hipEventDestroy(b)
 
 
+def hold_queue(ms: float):
+    """Enqueues about `ms` of GPU work (a clock spin) on the current stream, so that the launches
+    the host issues next queue up behind it and then run back to back, as in a graph replay,
+    instead of each starting on an idle GPU (which lengthens the first kernel of every step)."""
+    import torch
+
+    sleep = getattr(torch.cuda, "_sleep", None)
+    if sleep is None:
+        return
+    cyc = getattr(hold_queue, "cycles_per_ms", None)
+    if cyc is None:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        sleep(1_000_000)
+        b.record()
+        b.synchronize()
+        cyc = hold_queue.cycles_per_ms = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+    sleep(int(cyc * ms))
+
+
 def build_model_layer(device, seed=0, cfg=2, layer=0, bias_c=None, table_perm=True):
     """Arena of the 512 routed experts, the shared expert, bf16 router: all in HBM."""
     import numpy as np
@@ -207,13 +227,15 @@ def bench_decode1(args):
     ms_per_step = elapsed * 1e3 / args.steps
 
     # per-kernel durations of the gate/up and down launches: HIP events around the kernel itself, on
-    # the stream it runs on, over second (eager) passes of the same steps
+    # the stream it runs on, over second (eager) passes of the same steps queued behind a hold (so
+    # that they run back to back)
     n_k = min(args.steps, 200)
 
     def kernel_ms(which):
         timer = KernelTimer(n_k)
         torch.cuda.synchronize()
         with torch.cuda.stream(st):
+            hold_queue(40.0)
             for i in range(n_k):
                 s = args.warmup + i
                 N.moe_debug_kernel_events(which, timer.pairs[i][0], timer.pairs[i][1])
@@ -460,6 +482,7 @@ def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
         timer = KernelTimer(time_steps * n_layers)
         torch.cuda.synchronize()
         with torch.cuda.stream(st):
+            hold_queue(40.0)
             for i in range(time_steps):
                 for layer in range(n_layers):
                     pr = timer.pairs[i * n_layers + layer]

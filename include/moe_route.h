@@ -28,6 +28,7 @@
  *     enqueued asynchronously on it; the call returns once it is enqueued.
  *   - Every call validates its arguments on the host first and enqueues nothing when
  *     it returns an error.  Return value: MOE_OK (0) or a negative MOE_E* code.
+ *   - n_tokens >= 1 wherever a token count is taken: an empty batch is MOE_EINVAL.
  *   - `ws` is a caller-owned device workspace of `ws_bytes` bytes (256-byte aligned),
  *     at least moe_workspace_bytes(dims, n_tokens).  It must be cleared once with
  *     moe_workspace_init before its first use; calls leave it reusable.  Calls that

@@ -98,6 +98,28 @@ def test_invalid_arguments_rejected_on_host(N):
                None) == -2
 
 
+@pytest.mark.parametrize("n_tokens", [0, -1])
+def test_empty_batch_rejected_on_host(N, n_tokens):
+    """An empty (or negative) token count is refused with MOE_EINVAL by every entry point that takes
+    one, before any pointer is used (the pointers here are never dereferenced)."""
+    d = N.dims(2048, 768, 512, 10, 1)
+    fake = 1 << 20
+    w = N.moe_layer_weights(fake, 1, None, fake, 2_654_208, 512, 1 << 24)
+    wp = ctypes.byref(w)
+    calls = {
+        "moe_route": (ctypes.byref(d), fake, 1, n_tokens, fake, 1, None, fake, fake, None, fake, 1 << 30, None),
+        "moe_slot_lookup": (ctypes.byref(d), fake, 512, fake, n_tokens, fake, fake, fake, None, fake, 1 << 30, None),
+        "moe_group_tokens": (ctypes.byref(d), fake, n_tokens, fake, fake, fake, fake, 1 << 30, None),
+        "moe_expert_ffn_decode": (ctypes.byref(d), wp, None, fake, 1, n_tokens, fake, fake, fake, fake, 1 << 30, None),
+        "moe_expert_ffn_prefill": (ctypes.byref(d), wp, None, fake, 1, n_tokens, fake, fake, fake, fake, 1 << 30,
+                                   None),
+        "moe_layer_forward": (ctypes.byref(d), wp, None, None, fake, 1, n_tokens, fake, None, None, fake, 1 << 30,
+                              None),
+    }
+    for name, args in calls.items():
+        assert N.raw(name)(*args) == N.MOE_EINVAL, name
+
+
 def test_strerror(N):
     for c in range(-6, 1):
         assert isinstance(N.strerror(c), str) and N.strerror(c)

@@ -674,7 +674,7 @@ def main():
     ap.add_argument("--eager", action="store_true", help="launch decode steps one by one instead of replaying graphs")
     ap.add_argument("--prefill", default="4096,32768", help="comma-separated prefill token counts to add ('' = none)")
     ap.add_argument("--prefill-steps", type=int, default=20)
-    ap.add_argument("--decode48-steps", type=int, default=64, help="steps of the 48-layer batched decode (0 = skip)")
+    ap.add_argument("--decode48-steps", type=int, default=256, help="steps of the 48-layer batched decode (0 = skip)")
     ap.add_argument("--pool-steps", type=int, default=512, help="steps of the slot-pool decode workload (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run plain 256 MiB device copies (scale for the FETCH_SIZE / WRITE_SIZE counters)")

@@ -622,6 +622,36 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
     t1 = time.perf_counter()
     assert N.moe_check_device_error(ws) == 0
     st1 = [N.moe_pool_get_stats(L["pool"]) for L in layers]
+    # run 2: the same steps again (same tokens and topics) on the pool as run 1 left it
+    r0 = time.perf_counter()
+    for s in range(2, steps + 2):
+        step(s)
+    compute.synchronize()
+    d2h.synchronize()
+    h2d.synchronize()
+    r1 = time.perf_counter()
+    assert N.moe_check_device_error(ws) == 0
+    st2 = [N.moe_pool_get_stats(L["pool"]) for L in layers]
+    # the standalone residency check of one token's selections (two launches: slots and miss flags,
+    # then the ascending miss list), back to back on the compute stream
+    L0 = layers[0]
+    chk_ids = torch.as_tensor([[int(v) for v in range(0, 10 * 37, 37)]], dtype=torch.int32, device=dev)
+    chk_slots = torch.empty((1, K_TOP), dtype=torch.int32, device=dev)
+    chk_miss = torch.empty((E,), dtype=torch.int32, device=dev)
+    chk_count = torch.empty((1,), dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    with torch.cuda.stream(compute):
+        for rep in range(2):
+            if rep:
+                ev[0].record()
+            for _ in range(200):
+                N.moe_slot_lookup(d, L0["table"], L0["n_slots"], chk_ids, T, chk_slots, chk_miss, chk_count, ws,
+                                  stream=compute)
+        ev[1].record()
+    ev[1].synchronize()
+    check_us = ev[0].elapsed_time(ev[1]) * 1e3 / 200
+    sel2 = sum(b.selections - a.selections for a, b in zip(st1, st2))
+    mis2 = sum(b.misses - a.misses for a, b in zip(st1, st2))
     sel = sum(b.selections - a.selections for a, b in zip(st0, st1))
     mis = sum(b.misses - a.misses for a, b in zip(st0, st1))
     b_h2d = sum(b.bytes_h2d - a.bytes_h2d for a, b in zip(st0, st1))
@@ -660,6 +690,10 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
         "pcie_rate_gbs_per_blob_copy": rates,
         "fill_time_serial_ms_per_token": (b_h2d / rates["h2d"] + b_d2h / rates["d2h"]) / 1e6 / steps,
         "fill_time_overlapped_ms_per_token": max(b_h2d / rates["h2d"], b_d2h / rates["d2h"]) / 1e6 / steps,
+        "check_us_standalone": check_us,
+        "run2": {"what": "the same steps again on the pool as run 1 left it",
+                 "tokens_per_s": steps / (r1 - r0), "hit_rate": 1.0 - mis2 / max(1, sel2),
+                 "misses_per_token": mis2 / steps},
     }
 
 

@@ -269,6 +269,53 @@ __global__ __launch_bounds__(1024) void k_lookup_compact(int E, uint8_t* __restr
   }
 }
 
+// Both passes in one workgroup for a few pairs (n_pairs <= blockDim.x, E <= blockDim.x): one launch
+// instead of two.  Thread p looks up pair p and flags a miss in LDS; thread e then reads flag e, and
+// one block scan places the misses in ascending id.
+__global__ __launch_bounds__(1024) void k_lookup_small(const int32_t* __restrict__ ids, int n_pairs, int E,
+                                                       const int32_t* __restrict__ table, int n_slots,
+                                                       int32_t* __restrict__ slots, int32_t* __restrict__ miss_ids,
+                                                       int32_t* __restrict__ miss_count, int32_t* __restrict__ ctrl,
+                                                       DoorbellArgs bell) {
+  __shared__ uint32_t flag[kMaxExperts];
+  __shared__ int wave_sums[16];
+  const int t = threadIdx.x;
+  if (t < E) flag[t] = 0u;
+  __syncthreads();
+  int bad = 0;
+  if (t < n_pairs) {
+    const int e = ids[t];
+    int s = -1;
+    if (e < 0 || e >= E) {
+      bad = MOE_DERR_EXPERT_ID;
+    } else {
+      s = table ? table[e] : e;
+      if (s >= n_slots) {
+        bad = MOE_DERR_SLOT;
+        s = -1;
+      } else if (s < 0) {
+        flag[e] = 1u;  // every writer of e writes the same value
+      }
+    }
+    if (slots) slots[t] = s;
+  }
+  if (bad) set_error(ctrl, bad);
+  __syncthreads();
+  const int f = (t < E && flag[t]) ? 1 : 0;
+  int total;
+  const int pos = block_exclusive_scan(f, wave_sums, &total);
+  if (f) miss_ids[pos] = t;
+  if (t == 0) {
+    *miss_count = total;
+    ctrl[kCtrlMissCount] = total;
+  }
+  if (bell.active) {
+    __threadfence();
+    __syncthreads();
+    ring_doorbell(bell, miss_ids, total, nullptr, 0);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Decode plan (one workgroup of 256 threads, <= 8 tokens): residency check + one task per
 // distinct expert (ascending id) with the tokens that chose it, then the shared expert over all
@@ -733,6 +780,11 @@ hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, f
 hipError_t launch_lookup(const int32_t* ids, int n_pairs, int E, const int32_t* table, int n_slots,
                          int32_t* slots, uint8_t* miss_flag, int32_t* miss_ids, int32_t* miss_count,
                          int32_t* ctrl, const DoorbellArgs& bell, hipStream_t st) {
+  if (n_pairs <= 1024 && E <= kMaxExperts && E <= 1024) {
+    // a decode-sized check: one launch
+    k_lookup_small<<<1, 1024, 0, st>>>(ids, n_pairs, E, table, n_slots, slots, miss_ids, miss_count, ctrl, bell);
+    return hipGetLastError();
+  }
   if (n_pairs > 0) {
     int grid = (n_pairs + 255) / 256;
     if (grid > 1024) grid = 1024;

@@ -267,7 +267,8 @@ def test_slot_lookup_bit_exact(N, dev):
     rng = np.random.default_rng(8)
     E, k = 512, 10
     d = N.dims(2048, 768, E, k, 1)
-    for T in (1, 8, 300):
+    # one launch up to 1,024 pairs (T = 1, 8, 102), two above (T = 103, 300)
+    for T in (1, 8, 102, 103, 300):
         n_slots = 240
         table = np.full(E, -1, dtype=np.int32)
         res = rng.choice(E, n_slots, replace=False)
@@ -286,6 +287,37 @@ def test_slot_lookup_bit_exact(N, dev):
         n = int(cnt.item())
         assert n == len(m_ref)
         assert np.array_equal(miss.cpu().numpy()[:n], m_ref)
+
+
+@pytest.mark.parametrize("T", [1, 300])
+def test_slot_lookup_reports_bad_ids_and_slots(N, dev, T):
+    """An id outside [0, E) and a table entry >= n_slots set their error bits (both launch shapes);
+    the pair's slot reads -1 and the other pairs are still looked up."""
+    E, k = 512, 10
+    d = N.dims(2048, 768, E, k, 1)
+    n_slots = 100
+    table = np.arange(E, dtype=np.int32) % 128  # entries 100..127 are >= n_slots
+    table[::3] = -1
+    rng = np.random.default_rng(11)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[0, 0] = E + 5
+    ws = _ws(N, d, T, dev)
+    slots = torch.full((T, k), -9, dtype=torch.int32, device=dev)
+    miss = torch.full((E,), -9, dtype=torch.int32, device=dev)
+    cnt = torch.full((1,), -9, dtype=torch.int32, device=dev)
+    N.moe_slot_lookup(d, torch.from_numpy(table).to(dev), n_slots, torch.from_numpy(ids).to(dev), T, slots, miss, cnt,
+                      ws)
+    bits = N.moe_check_device_error(ws)
+    assert bits & N.DERR_EXPERT_ID
+    assert bits & N.DERR_SLOT
+    got = slots.cpu().numpy()
+    assert got[0, 0] == -1
+    for t in range(T):
+        for j in range(k):
+            e = int(ids[t, j])
+            if 0 <= e < E:
+                s_ref = int(table[e])
+                assert got[t, j] == (s_ref if 0 <= s_ref < n_slots else -1), (t, j)
 
 
 def test_device_errors_are_reported(N, dev, model_layer):

@@ -245,8 +245,9 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   // are issued; a lane picks its token slot's row when it reads its fragment.  fp32 rows (small
   // shapes only) are split into hi / lo bf16 rows of the task's tokens by the threads below.
   auto x_row = [&](int m) { return (const uint16_t*)a.x + (size_t)(m < a.T ? m : 0) * H; };
-  // bf16: ROWS * H / 8 chunks over 64 RG H / 512 threads is at most MAXTOK / RG per thread
-  u32x4 xv[(MAXTOK + RG - 1) / RG];
+  // bf16: ROWS * H / 8 chunks over 64 RG KS threads, KS >= H / (128 kGuQuadsPerWave) waves per row
+  // group, is at most MAXTOK kGuQuadsPerWave / (4 RG) per thread
+  u32x4 xv[(MAXTOK * kGuQuadsPerWave / 4 + RG - 1) / RG];
   if constexpr (X_BF16) stage_load(xv, ROWS, H, x_row);
   // the descriptor slot always exists (max_tasks of them): load it together with the count
   const DecodeTask tk = a.tasks[task];

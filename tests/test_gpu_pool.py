@@ -111,11 +111,12 @@ def _ws(N, d, dev):
     return ws
 
 
-@pytest.mark.parametrize("n_spares,two_streams", [(1, False), (4, True)])
+@pytest.mark.parametrize("n_spares,two_streams", [(1, False), (1, True), (4, True)])
 def test_pool_decode_steps_match_oracle_policy_and_outputs(N, dev, n_spares, two_streams):
     """One copy stream and one spare buffer, or separate device->host and host->device streams
-    with four spares (the copies of the two directions overlap): same fills, tables and outputs,
-    and afterwards every evicted expert's bytes sit in the host buffer the swap rule gives it."""
+    with one spare (every copy out waits, by event, for the copy in that last read its buffer) or
+    four (the copies of the two directions overlap): same fills, tables and outputs, and afterwards
+    every evicted expert's bytes sit in the host buffer the swap rule gives it."""
     L = PoolLayer(N, dev, layer_id=20, n_slots=60, n_spares=n_spares)
     d = L.dims()
     ws = _ws(N, d, dev)

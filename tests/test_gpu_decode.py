@@ -111,13 +111,15 @@ def _tied_router(dev, H, E):
     return torch.from_numpy(codes.view(np.int16)).to(dev)
 
 
+@pytest.mark.parametrize("E,k", [(512, 10), (1024, 10), (1024, 16)])
 @pytest.mark.parametrize("T", [1, 5, 8, 300])
-def test_topk_exact_ties_lower_id_first(N, dev, T):
+def test_topk_exact_ties_lower_id_first(N, dev, T, E, k):
     """Selection on the GPU's own fp32 logits equals the oracle's ranking (logit desc, id asc)
-    exactly when many logits are equal (decode route for T <= 8, prefill top-k above)."""
+    exactly when many logits are equal (decode route for T <= 8, prefill top-k above), at the
+    model's 512 experts (8 logits per lane) and at the largest expert count and k (16 per lane)."""
     from mixture_experts_route_amd import synth as S
 
-    H, F, E, k = 2048, 768, 512, 10
+    H, F = 2048, 768
     d = N.dims(H, F, E, k, 1)
     router = _tied_router(dev, H, E)
     x = torch.from_numpy(S.bf16_normal_np(S.stream_key(3, 2, "x", 0, T), (T, H), 1.0).view(np.int16)).to(dev)
@@ -198,6 +200,20 @@ def test_layer_tiny_decode(N, dev):
 @pytest.mark.parametrize("T", [1, 2, 5, 8])
 def test_layer_model_shape_decode(N, dev, model_layer, T):
     _layer_check(N, dev, model_layer, T, step=11 + T)
+
+
+@pytest.fixture(scope="module")
+def wide_layer(N, dev):
+    """The largest supported routing: 1,024 experts, top-16 (+ shared), model widths."""
+    return Layer(dict(MODEL, E=1024, k=16), dev, seed=0)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 40])
+def test_layer_wide_routing_1024_experts_top16(N, dev, wide_layer, T):
+    """E = 1024, k = 16 through the whole layer: 16 logits per lane in the selection, up to 129
+    decode tasks (the one-token down kernel's 17-task variant at T = 1), and the prefill path at
+    T = 40; ids and outputs against the oracle."""
+    _layer_check(N, dev, wide_layer, T, step=100 + T)
 
 
 def test_layer_batched_decode_zipf_layers(N, dev):

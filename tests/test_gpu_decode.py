@@ -216,6 +216,17 @@ def test_layer_wide_routing_1024_experts_top16(N, dev, wide_layer, T):
     _layer_check(N, dev, wide_layer, T, step=100 + T)
 
 
+@pytest.mark.parametrize("H,F,E,k", [(1024, 512, 64, 6), (4096, 1536, 64, 8)])
+@pytest.mark.parametrize("T", [1, 8, 40])
+def test_layer_other_widths(N, dev, H, F, E, k, T):
+    """Hidden and FFN widths other than the model's (the decode kernels' other chunk counts, the
+    generic prefill GEMM at T = 40), against the oracle."""
+    layer = Layer(dict(MODEL, H=H, F=F, E=E, k=k), dev, seed=0, layer=H // 256)
+    _layer_check(N, dev, layer, T, step=200 + T)
+    del layer
+    torch.cuda.empty_cache()
+
+
 def test_layer_batched_decode_zipf_layers(N, dev):
     """The 48-layer batched decode's shape: 8 tokens per step through layers with their own
     Zipf(1.1) router bias (popular experts shared by several tokens of a step), one step in each

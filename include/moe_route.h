@@ -292,7 +292,8 @@ MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_s
                             int32_t n_spares, int32_t* host_miss_ids, int32_t* host_counts,
                             int32_t* host_step_ids, uint32_t* ready, moe_pool** pool_out);
 
-/* Frees the pool object (not the caller's memory). */
+/* Frees the pool object and its events (not the caller's memory).  Synchronize the pool's copy
+ * streams first: the copies it enqueued and their event waits must have completed. */
 MOE_API int moe_pool_destroy(moe_pool* pool);
 
 /* The doorbell of the pool's next call (next epoch).  MOE_EINVAL if the previous call was

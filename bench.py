@@ -305,6 +305,34 @@ def bench_decode1(args):
     return result
 
 
+def cpu_baseline_decode48(step: int, n_layers: int, n_total: int = 48, T: int = 8, seed=0, cfg=3):
+    """The oracle timed on one 8-token step through the first `n_layers` layers of the 48-layer
+    batched decode (same router, bias, expert and token streams), scaled to all `n_total` layers."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from mixture_experts_route_amd import synth as S
+    from oracle import moe_oracle as O
+
+    work = []
+    for layer in range(n_layers):
+        Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02))
+        Wr = Wr.astype(np.float64)
+        bias = S.zipf_bias(S.rank_permutation(seed, cfg, layer, 0, E), S.ZIPF_C)
+        xall = S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), ((step + 1) * T, H), 1.0)
+        x = S.bf16_to_f32(xall[step * T:(step + 1) * T]).astype(np.float64)
+        _, _, ids, _ = O.route(x, Wr, bias, K_TOP)
+        blobs = {int(e): S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, int(e)), H, F) for e in np.unique(ids)}
+        shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
+        work.append((x, Wr, bias, blobs, shared))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for x, Wr, bias, blobs, shared in work:
+            O.moe_layer(x, Wr, bias, K_TOP, lambda e, b=blobs: b[e], shared, H, F)
+        dt = time.perf_counter() - t0
+    return T / (dt * n_total / n_layers), dt
+
+
 def cpu_baseline_prefill(T: int, n_tokens: int, seed=0, cfg=4, layer=0):
     """The oracle timed on a sample of `n_tokens` tokens of the T-token prefill batch."""
     import numpy as np
@@ -401,7 +429,7 @@ def bench_prefill(T: int, steps: int, warmup: int, cpu_sample: int | None):
     return out
 
 
-def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
+def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4, cpu_layers: int | None = None):
     """Batched decode through all 48 layers: 8 tokens per step, every layer's 512 + 1 experts resident
     in HBM (one 65 GB arena), per-layer Zipf(1.1) router bias, fresh seeded tokens per (step, layer)."""
     import numpy as np
@@ -507,7 +535,7 @@ def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
     dn_gbs = dn_bytes.sum() / dn_s.sum() / 1e9
     ffn_gbs = (gu_bytes.sum() + dn_bytes.sum()) / (gu_s.sum() + dn_s.sum()) / 1e9
     step_bytes = float(np.mean(u + 1)) * 2_654_208 * n_layers + n_layers * (E * H * 2)
-    return {
+    out = {
         "workload": "batched decode through 48 layers: 8 tokens per step, 48 x (512 routed + 1 shared) experts "
                     "resident in HBM (65.4 GB of 4-bit weights), per-layer Zipf(1.1) router bias, top-10 + shared, "
                     "hidden 2048, expert FFN 768, fresh bf16 tokens per (step, layer)",
@@ -532,6 +560,12 @@ def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4):
                         "avg_launch_us": float(dn_s.mean() * 1e6)},
         "decode_ffn_hbm_frac": ffn_gbs / HBM_PEAK_GBS,
     }
+    if cpu_layers:
+        v, dt = cpu_baseline_decode48(warmup, cpu_layers)
+        out["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"the first timed 8-token step through the first {cpu_layers} of the 48 "
+                                         f"layers, {dt:.1f} s of float64 numpy on 1 thread, scaled to 48 layers"}
+    return out
 
 
 def pool_slots(layer: int) -> int:
@@ -741,7 +775,8 @@ def main():
         res["copy_calibration_bytes"] = 256 << 20
     if args.decode48_steps > 0:
         progress("48-layer batched decode")
-        res["decode_8tok_48layers"] = bench_decode48(args.decode48_steps, 4, not args.eager)
+        res["decode_8tok_48layers"] = bench_decode48(args.decode48_steps, 4, not args.eager,
+                                                     cpu_layers=None if args.no_cpu_baseline else 4)
         import torch
 
         torch.cuda.empty_cache()

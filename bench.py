@@ -252,7 +252,8 @@ def bench_decode1(args):
     # algorithmic bytes of one gate/up launch: 11 experts (10 routed, distinct, + shared), each
     # reading its gate and up codes and scales once, plus x in and h out (bf16 hi + lo)
     per_expert = 2 * (F * H // 2 + F * (H // 32) * 2)
-    gu_bytes = 11 * per_expert + H * 2 + 11 * F * 4
+    # (+ the router's logits and the slot table, which every workgroup reads for its selection)
+    gu_bytes = 11 * per_expert + H * 2 + 11 * F * 4 + E * 4 * 2
     gu_avg_s = float(np.mean(k_ms)) * 1e-3
     achieved = gu_bytes / gu_avg_s / 1e9
     # down (one token: the weighted combine is inside the launch): the 11 experts' down codes and
@@ -280,7 +281,7 @@ def bench_decode1(args):
             "layer_bytes_per_step": 11 * 2_654_208 + E * H * 2 + H * 2 + H * 4,
         },
         "roofline": {
-            "kernel": "k_decode_gate_up (4-bit GEMV gate+up, SwiGLU fused)",
+            "kernel": "k_decode_gate_up (4-bit GEMV gate+up, SwiGLU fused; each workgroup first selects the token's top-k from the logits)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,

@@ -382,6 +382,20 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   const WsLayout L = ws_layout(dims, n_tokens);
   int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);
   float* tw = topk_w_out_or_null ? topk_w_out_or_null : at<float>(ws, L.w);
+  if (!prefill && n_tokens == 1 && !bell_or_null && x_dtype == MOE_BF16 && w->router_dtype == MOE_BF16 &&
+      decode_select1_supported(dims->hidden, dims->ffn, dims->top_k, dims->n_shared, dims->n_experts)) {
+    // one token, no doorbell: the router launch ends with its logits; the gate/up launch selects,
+    // checks residency and plans (the router launch's last-workgroup step is off the path)
+    float* logits = at<float>(ws, L.logits);
+    rc = hip_status(launch_router_logits_bf16(x, w->router, w->router_bias, dims->n_experts, dims->hidden, logits, st));
+    if (rc) return rc;
+    uint16_t* h_hi = at<uint16_t>(ws, L.h);
+    uint16_t* h_lo = h_hi + (size_t)decode_pairs(dims, 1) * dims->ffn;
+    return hip_status(launch_decode_ffn_select1(dims->hidden, dims->ffn, dims->top_k, dims->n_shared,
+                                                dims->n_experts, source_of(w, layer_table_or_null), x, logits,
+                                                at<DecodeTask>(ws, L.tasks), ids, tw, h_hi, h_lo, y, ctrl_of(ws),
+                                                st));
+  }
   if (!prefill) {
     // fused route: router GEMV, top-k, residency check, plan and doorbell in one kernel
     rc = hip_status(launch_decode_route(x, x_dtype, w->router, w->router_dtype, w->router_bias, n_tokens,

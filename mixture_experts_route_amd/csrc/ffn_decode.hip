@@ -31,6 +31,7 @@
 //     done inside the down launch by the last workgroup to finish each row tile (a counter per
 //     tile; the pair rows go through agent-scope stores and loads).
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace moe {
 
@@ -163,7 +164,98 @@ struct DecodeArgs {
   int tiles_gu;  // workgroups per task, gate/up
   int tiles_dn;  // workgroups per task, down
   int32_t* tile_done;  // per down row tile: workgroups finished (control words, zero between calls)
+  // one token, selection inside the gate/up launch: the router's logits [E], and where the plan
+  // and the routing go (tasks for the down launch, the token's ids and weights)
+  const float* sel_logits;
+  DecodeTask* sel_tasks;
+  int32_t* sel_ids;
+  int E;
 };
+
+// One token: every gate/up workgroup selects the token's top-k from the router's logits itself (one
+// wave, the router launch's algorithm), so the router launch ends with its logits.  Tasks are the k
+// selected experts in ascending id, then the shared expert; the workgroup takes task blockIdx / tiles
+// and workgroup 0 also writes the plan, the ids and the weights for the down launch and the caller.
+MOE_DEV DecodeTask select_own_task(const DecodeArgs& a, int task) {
+  __shared__ int32_t s_ids[kMaxK];
+  __shared__ float s_w[kMaxK];
+  __shared__ int32_t s_slot[8 * 64];
+  __shared__ DecodeTask s_tk;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int E = a.E, k = a.k;
+    // the slot of every expert, loaded with the logits (one wait covers both) and kept in LDS
+    int32_t tab[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int e = min(lane + 64 * i, E - 1);
+      tab[i] = a.src.table ? a.src.table[e] : e;
+    }
+    auto stage_slots = [&]() {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) s_slot[e] = tab[i];
+      }
+    };
+    select_topk_wave<8>(a.sel_logits, E, k, nullptr, nullptr, a.ctrl, s_ids, s_w, stage_slots);
+    asm volatile("" ::: "memory");  // one wave: its LDS operations take effect in issue order
+    const int my_id = lane < k ? s_ids[lane] : 0x7FFFFFFF;
+    int rank = 0;  // position of selection `lane` in ascending expert id (ids are distinct)
+#pragma unroll
+    for (int i = 0; i < kMaxK; ++i) rank += (i < k && s_ids[i] < my_id) ? 1 : 0;
+    const int my_slot = lane < k ? s_slot[my_id] : -1;
+    if (task < k) {
+      const int j = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < k && rank == task));
+      if (lane == j) {
+        DecodeTask tk;
+        tk.expert = my_id;
+        tk.slot = my_slot;
+        tk.tok_mask = 1u;
+        tk.choice = (uint32_t)j;
+        s_tk = tk;
+      }
+    } else if (lane == 0) {
+      DecodeTask tk;
+      tk.expert = -1;
+      tk.slot = -1;
+      tk.tok_mask = 1u;
+      tk.choice = 0u;
+      s_tk = tk;
+    }
+    if (blockIdx.x == 0) {
+      if (lane < k) {
+        DecodeTask tk;
+        tk.expert = my_id;
+        tk.slot = my_slot;
+        tk.tok_mask = 1u;
+        tk.choice = (uint32_t)lane;
+        a.sel_tasks[rank] = tk;
+        a.sel_ids[lane] = my_id;
+        ((float*)a.topk_w)[lane] = s_w[lane];
+      }
+      const bool bad = lane < k && my_slot >= a.src.n_slots;
+      const int n_miss = __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < k && my_slot < 0));
+      const bool any_bad = __any(bad);
+      if (lane == 0) {
+        int n_all = k;
+        if (a.n_shared) {
+          DecodeTask tk;
+          tk.expert = -1;
+          tk.slot = -1;
+          tk.tok_mask = 1u;
+          tk.choice = 0u;
+          a.sel_tasks[n_all++] = tk;
+        }
+        a.ctrl[kCtrlNTasks] = n_all;
+        a.ctrl[kCtrlMissCount] = n_miss;
+        if (any_bad) set_error(a.ctrl, MOE_DERR_SLOT);
+      }
+    }
+  }
+  __syncthreads();
+  return s_tk;
+}
 
 // ---- activation rows in LDS -----------------------------------------------------------------
 // A task's A-operand rows (bf16) are copied once per workgroup into LDS, row m at m * (K + 8)
@@ -231,7 +323,7 @@ MOE_DEV bf16x8 lds_fragment(const uint16_t* lds, int rows, int K, int m, int g, 
 // ---- gate/up: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for one task and 32 rows r ------------
 // Workgroup = RG row groups of 16 rows x KS waves splitting the H inputs in runs of 4 groups
 // (KS = H / 512).  A rows: token slot m of the task (bf16 x) or 2 m + part (fp32 x, hi / lo).
-template <int MAXTOK, bool X_BF16, int RG>
+template <int MAXTOK, bool X_BF16, int RG, bool SEL = false>
 __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   constexpr int ROWS = X_BF16 ? MAXTOK : 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;                    // live D registers per lane
@@ -249,9 +341,15 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   // group, is at most MAXTOK kGuQuadsPerWave / (4 RG) per thread
   u32x4 xv[(MAXTOK * kGuQuadsPerWave / 4 + RG - 1) / RG];
   if constexpr (X_BF16) stage_load(xv, ROWS, H, x_row);
-  // the descriptor slot always exists (max_tasks of them): load it together with the count
-  const DecodeTask tk = a.tasks[task];
-  if (task >= a.ctrl[kCtrlNTasks]) return;
+  DecodeTask tk;
+  if constexpr (SEL) {
+    static_assert(MAXTOK == 1 && X_BF16, "selection inside the launch: one bf16 token");
+    tk = select_own_task(a, task);  // every task of the grid exists (k distinct experts + shared)
+  } else {
+    // the descriptor slot always exists (max_tasks of them): load it together with the count
+    tk = a.tasks[task];
+    if (task >= a.ctrl[kCtrlNTasks]) return;
+  }
   const uint8_t* blob = task_blob(a.src, tk);
   if (!blob) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
@@ -1092,6 +1190,45 @@ hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_t
   if (T <= 2) return launch_decode_ffn_t<2>(a, max_tasks, xb, st);
   if (T <= 4) return launch_decode_ffn_t<4>(a, max_tasks, xb, st);
   return launch_decode_ffn_t<8>(a, max_tasks, xb, st);
+}
+
+bool decode_select1_supported(int H, int F, int k, int n_shared, int E) {
+  const int ks = (H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
+  return E <= 8 * 64 && F % (16 * kGuRG1) == 0 && kGuRG1 * ks <= 16 && F <= 8 * kGroupElems &&
+         k + (n_shared ? 1 : 0) <= 11 && (k + (n_shared ? 1 : 0)) * (F / kGroupElems) <= 16 * 5;
+}
+
+hipError_t launch_decode_ffn_select1(int H, int F, int k, int n_shared, int E, const ExpertSource& src,
+                                     const void* x, const float* logits, DecodeTask* tasks, int32_t* ids_out,
+                                     float* w_out, uint16_t* h_hi, uint16_t* h_lo, float* y, int32_t* ctrl,
+                                     hipStream_t st) {
+  if (!decode_select1_supported(H, F, k, n_shared, E)) return hipErrorInvalidValue;
+  DecodeArgs a{};
+  a.src = src;
+  a.tasks = tasks;
+  a.ctrl = ctrl;
+  a.x = x;
+  a.h_hi = h_hi;
+  a.h_lo = h_lo;
+  a.topk_w = w_out;
+  a.y = y;
+  a.H = H;
+  a.F = F;
+  a.T = 1;
+  a.k = k;
+  a.n_shared = n_shared;
+  a.tile_done = ctrl + kCtrlTileDone;
+  a.sel_logits = logits;
+  a.sel_tasks = tasks;
+  a.sel_ids = ids_out;
+  a.E = E;
+  const int n_tasks = k + (n_shared ? 1 : 0);
+  const int ks = (H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
+  a.tiles_gu = F / (16 * kGuRG1);
+  hipError_t err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<1, true, kGuRG1, true>, n_tasks * a.tiles_gu,
+                                64 * kGuRG1 * ks, (uint32_t)gate_up_lds_bytes(H, 1, kGuRG1 * ks), st, a);
+  if (err != hipSuccess) return err;
+  return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16>, H / 16, 1024, 0, st, a);
 }
 
 hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st) {

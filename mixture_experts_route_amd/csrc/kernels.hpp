@@ -105,6 +105,15 @@ hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r
                                DecodeTask* tasks, const DoorbellArgs& bell, hipStream_t st);
 
 // ffn_decode.hip
+// One bf16 token, the whole-layer call without a doorbell: the router launch writes only the logits
+// and the gate/up launch selects (each workgroup for itself) and plans.
+hipError_t launch_router_logits_bf16(const void* x, const void* Wr, const float* bias, int E, int H, float* logits,
+                                     hipStream_t st);
+bool decode_select1_supported(int H, int F, int k, int n_shared, int E);
+hipError_t launch_decode_ffn_select1(int H, int F, int k, int n_shared, int E, const ExpertSource& src,
+                                     const void* x, const float* logits, DecodeTask* tasks, int32_t* ids_out,
+                                     float* w_out, uint16_t* h_hi, uint16_t* h_lo, float* y, int32_t* ctrl,
+                                     hipStream_t st);
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
                              const void* x, int x_dtype, const DecodeTask* tasks, const float* topk_w,
                              uint16_t* h_hi, uint16_t* h_lo, float* y_pairs, float* y, int32_t* ctrl,

@@ -204,7 +204,7 @@ MOE_DEV DecodeTask select_own_task(const DecodeArgs& a, int task) {
     int rank = 0;  // position of selection `lane` in ascending expert id (ids are distinct)
 #pragma unroll
     for (int i = 0; i < kMaxK; ++i) rank += (i < k && s_ids[i] < my_id) ? 1 : 0;
-    const int my_slot = lane < k ? s_slot[my_id] : -1;
+    const int my_slot = lane < k ? s_slot[lane < k ? my_id : 0] : -1;  // index clamped for the other lanes
     if (task < k) {
       const int j = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < k && rank == task));
       if (lane == j) {

@@ -583,14 +583,14 @@ MOE_DEV uint4 split_bf16_part(const float4& a, const float4& b, int part) {
 }
 
 // TAIL false: the logits only (the one-token gate/up launch selects for itself).
-template <bool X_BF16, int NPER, bool TAIL = true>
+template <bool X_BF16, int NPER, bool TAIL = true, int ROWS = kRouterRows>
 __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(RouteArgs a) {
   __shared__ float red[kRouterWaves][16][16];  // [wave][A row][router row]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int T = a.T, E = a.E, H = a.H;
-  const int e0 = blockIdx.x * kRouterRows;
-  const int e = n < kRouterRows ? e0 + n : E;  // B columns past the workgroup's rows stay zero
+  const int e0 = blockIdx.x * ROWS;
+  const int e = n < ROWS ? e0 + n : E;  // B columns past the workgroup's rows stay zero
   const int NB = H / 32;
   const int spw = (NB + kRouterWaves - 1) / kRouterWaves;  // 32-input steps per wave
   const int b0 = wave * spw;
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void k_router_mfma(RouteArgs a) 
   if ((int)threadIdx.x < 16 * T) {
     const int t = threadIdx.x >> 4, c = threadIdx.x & 15;
     const int ee = e0 + c;
-    if (c < kRouterRows && ee < E) {
+    if (c < ROWS && ee < E) {
       float sum = 0.f;
       for (int w = 0; w < kRouterWaves; ++w) {
         if constexpr (X_BF16) sum += red[w][t][c];
@@ -712,8 +712,10 @@ hipError_t launch_router_logits_bf16(const void* x, const void* Wr, const float*
   a.E = E;
   a.H = H;
   a.logits = logits;
-  const int grid = (E + kRouterRows - 1) / kRouterRows;
-  return launch_timed(kTimeDecodeRoute, k_router_mfma<true, 8, false>, grid, 64 * kRouterWaves, 0, st, a);
+  // with no hand-over at the end, more and smaller workgroups: 4 router rows each
+  constexpr int kRows = 4;
+  const int grid = (E + kRows - 1) / kRows;
+  return launch_timed(kTimeDecodeRoute, k_router_mfma<true, 8, false, kRows>, grid, 64 * kRouterWaves, 0, st, a);
 }
 
 hipError_t launch_decode_route(const void* x, int x_dtype, const void* Wr, int r_dtype, const float* bias, int T,

@@ -366,3 +366,31 @@ def test_device_errors_are_reported(N, dev, model_layer):
     ids[1, 9] = 11
     N.moe_expert_ffn_decode(d, layer.native_weights(), table, x, T, ids, w, y, ws)
     assert N.moe_check_device_error(ws) & N.DERR_NOT_RESIDENT
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_layer_without_shared_expert(N, dev, T):
+    """n_shared = 0 through the whole layer (one token: the gate/up launch selects; eight: the
+    router launch plans): k tasks only, against the oracle."""
+    layer = Layer(dict(MODEL, n_shared=0), dev, seed=0, layer=7)
+    _layer_check(N, dev, layer, T, step=300 + T)
+
+
+def test_layer_forward_not_resident_is_reported(N, dev, model_layer):
+    """A selected expert the slot table marks absent (no doorbell attached) is an error of the call,
+    in the one-token path where the gate/up launch selects and in the router-planned path."""
+    layer = model_layer
+    d = layer.dims()
+    for T in (1, 8):
+        x, _ = layer.x(T, 400 + T, dev)
+        ws = _ws(N, d, T, dev)
+        y = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
+        ids = torch.zeros((T, layer.k), dtype=torch.int32, device=dev)
+        N.moe_layer_forward(d, layer.native_weights(), None, x, T, y, ws, topk_ids=ids)
+        torch.cuda.synchronize()
+        _check_no_device_error(N, ws)
+        table = torch.arange(layer.E, dtype=torch.int32, device=dev)
+        table[int(ids[0, 0].item())] = -1  # token 0's first choice is now absent
+        N.moe_layer_forward(d, layer.native_weights(), table, x, T, y, ws)
+        assert N.moe_check_device_error(ws) & N.DERR_NOT_RESIDENT, T
+        assert N.moe_check_device_error(ws) == 0

@@ -356,7 +356,10 @@ class SlotPoolLRU:
 
 
 def per_token_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
-    """max_o |y - y_ref| / max_o |y_ref| per token (normwise, the parity metric)."""
+    """max_o |y - y_ref| / max_o |y_ref| per token (normwise, the parity metric, reading R11).
+
+    A token whose reference row is all zero is measured by its absolute error max_o |y - y_ref|.
+    """
     y_gpu = np.asarray(y_gpu, np.float64)
     y_ref = np.asarray(y_ref, np.float64)
     num = np.max(np.abs(y_gpu - y_ref), axis=1)

@@ -380,3 +380,67 @@ def test_group_pairs_matches_stable_argsort():
         assert offsets[0] == 0 and offsets[-1] == n
     counts, offsets, perm = O.group_pairs(np.zeros(0, dtype=np.int64), 4)
     assert counts.sum() == 0 and perm.size == 0 and list(offsets) == [0] * 5
+
+
+# ----------------------------------------------------------------------------- comparison helpers
+
+def _frac_or_pow(s):
+    """'1/128', '2^-133', '127*2^-133', '-0' -> exact value (Fraction, or the float -0.0)."""
+    s = s.strip()
+    if s == "-0":
+        return -0.0
+    sign = -1 if s.startswith("-") else 1
+    s = s.lstrip("-")
+    if "^" in s:
+        mant, _, rest = s.rpartition("*") if "*" in s else ("1", None, s)
+        base, exp = rest.split("^")
+        return sign * Fraction(int(mant)) * Fraction(int(base)) ** int(exp)
+    return sign * Fraction(s)
+
+
+def test_bf16_codes_hand_decoded():
+    rows = list(_rows("bf16_codes.txt"))
+    codes = np.array([int(r[0], 16) for r in rows], dtype=np.uint16)
+    got = O.bf16_codes_to_f64(codes)
+    for (code, val, _), g in zip(rows, got):
+        want = _frac_or_pow(val)
+        assert g == float(want), (code, g, want)
+        assert math.copysign(1.0, g) == math.copysign(1.0, float(want)), code
+    # the same codes given as signed 16-bit patterns decode the same
+    assert np.array_equal(O.bf16_codes_to_f64(codes.view(np.int16)), got)
+    # a plausible mistake (a shift by 15 instead of 16) fails the fixture
+    wrong = (codes.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
+    assert not np.array_equal(wrong, got)
+
+
+def test_topk_gap_hand_worked():
+    rows = list(_rows("topk_gap.txt"))
+    assert len(rows) >= 8
+    for lg, k, want in rows:
+        l = np.array([[float(v) for v in lg.split()]])
+        got = O.topk_gap(l, int(k))[0]
+        assert got == float(want), (lg, k, got)
+    # the off-by-one variants differ from the fixture on at least one row each
+    def shifted(l, k, d):
+        s = -np.sort(-l, axis=1)
+        i = k - 1 + d
+        if i + 1 >= s.shape[1] or i < 0:
+            return np.full(s.shape[0], np.inf)
+        return s[:, i] - s[:, i + 1]
+    for d in (-1, 1):
+        assert any(shifted(np.array([[float(v) for v in lg.split()]]), int(k), d)[0] != float(w)
+                   for lg, k, w in rows)
+
+
+def test_parity_metric_hand_worked():
+    rows = list(_rows("parity_metric.txt"))
+    ref = np.array([[float(v) for v in r[0].split()] for r in rows])
+    y = np.array([[float(v) for v in r[1].split()] for r in rows])
+    want = np.array([float(r[2]) for r in rows])
+    got = O.per_token_rel_err(y, ref)
+    assert np.allclose(got, want, rtol=1e-15, atol=0), (got, want)
+    # a mean in place of a max, or a missing absolute value, changes at least one row
+    mean_for_max = np.abs(y - ref).mean(axis=1) / np.maximum(np.abs(ref).mean(axis=1), 1e-300)
+    no_abs_ref = np.abs(y - ref).max(axis=1) / np.where(ref.max(axis=1) > 0, ref.max(axis=1), 1.0)
+    assert not np.allclose(mean_for_max, want)
+    assert not np.allclose(no_abs_ref, want)

@@ -23,7 +23,8 @@
  *
  * Conventions for every entry point
  *   - Tensor pointers are device pointers owned by the caller (allocated by any means);
- *     the library never allocates or frees device memory and keeps no global state.
+ *     the library never allocates or frees device memory.  Its only process-wide state is
+ *     the profiling selection of moe_debug_kernel_events (off unless a caller sets it).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
  *     enqueued asynchronously on it; the call returns once it is enqueued.
  *   - Every call validates its arguments on the host first and enqueues nothing when
@@ -34,19 +35,28 @@
  *     moe_workspace_init before its first use; calls leave it reusable.  Calls that
  *     share one workspace must be ordered on one stream.
  *   - Faults the device detects (an expert id out of range, a slot index out of range,
- *     a selected expert that is not resident when its weights are needed, a NaN logit)
- *     set bits of an error word in `ws`; the outputs of that call are then invalid.
- *     moe_check_device_error reads and clears the word.
+ *     a selected expert that is not resident when its weights are needed, a NaN logit,
+ *     an expert named twice in one token's top-k list, a value outside the fp16 range on
+ *     the prefill path) set bits of an error word in `ws`; the outputs of that call are
+ *     then invalid, never silently computed (Betelgeuse article, "what bit-exact means":
+ *     a failed expert read is an error, not a zero weight).  moe_check_device_error reads
+ *     and clears the word.
  *
- * Expert blob (one routed or shared expert; H = hidden, F = ffn):
- *   [gate codes F x H/2][up codes F x H/2][down codes H x F/2]
- *   [gate scales F x H/32][up scales F x H/32][down scales H x F/32]     (bytes)
- *   Matrices are row-major: gate/up rows are the F outputs over the H inputs, down rows
- *   the H outputs over the F inputs.  Blocks of 32 consecutive elements of a row share
- *   one fp16 scale (little-endian).  A row's codes are 32-bit little-endian words; word d
- *   holds elements 8d..8d+7: element 8d+2j in bits 4j..4j+3 and element 8d+2j+1 in bits
- *   16+4j..16+4j+3 (j = 0..3).  A code u (0..15) stands for q = u - 8, and the weight is
- *   q * scale.  Model shape (H 2048, F 768): 2,654,208 bytes = 648 x 4 KiB.
+ * Expert blob (one routed or shared expert; H = hidden, F = ffn), six sections in this order:
+ *   [gate codes F*H/2][up codes F*H/2][down codes H*F/2]
+ *   [gate scales F*H/16][up scales F*H/16][down scales H*F/16]          (bytes)
+ * Gate and up have R = F rows over K = H inputs, down R = H rows over K = F inputs.  A code
+ * u (0..15) stands for q = u - 8; blocks of 32 consecutive inputs of a row share one fp16
+ * scale (little-endian), and the weight is q * scale (halogen README, "Bring your own GGUF":
+ * a small set of values times a per-block scale, moved losslessly into the kernels' layout).
+ * Each row is cut into K/128 groups of 128 inputs (four blocks), stored group-major:
+ *   - codes of group c of row r: the 64-byte record at byte 64 * (c * R + r) of the section,
+ *     sixteen little-endian 32-bit words.  Word 4g + i (g, i = 0..3) holds slice g of block i,
+ *     that is inputs 128c + 32i + 8g .. 128c + 32i + 8g + 7: input 128c + 32i + 8g + 2j in bits
+ *     4j..4j+3 and input 128c + 32i + 8g + 2j + 1 in bits 16+4j..16+4j+3 (j = 0..3);
+ *   - scales of group c of row r: four fp16 values (blocks 4c .. 4c+3 of the row) at byte
+ *     8 * (c * R + r) of the scale section.
+ * Model shape (H 2048, F 768): 2,654,208 bytes = 648 x 4 KiB.
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H
@@ -78,7 +88,10 @@ enum moe_device_error {
   MOE_DERR_SLOT = 2,          /* a slot-table entry >= n_slots */
   MOE_DERR_NOT_RESIDENT = 4,  /* an expert needed by an FFN call has no slot (-1) */
   MOE_DERR_NAN = 8,           /* a NaN logit reached the selection */
-  MOE_DERR_FILL = 16          /* the slot-pool service reported a failed fill */
+  MOE_DERR_FILL = 16,         /* the slot-pool service reported a failed fill */
+  MOE_DERR_DUP_ID = 32,       /* a token's top-k list names one expert twice */
+  MOE_DERR_RANGE = 64         /* prefill: an activation, SwiGLU output or weighted expert row
+                                 beyond the fp16 range (|v| > 65504) or not finite */
 };
 
 /* Largest token count the decode entry points take (the pages' concurrent streams: Basalt
@@ -88,10 +101,10 @@ enum moe_device_error {
 /* Layer dimensions.  hidden = H, ffn = F (expert FFN width, shared expert too),
  * n_experts = E routed experts, top_k = k, n_shared = 0 or 1, block = 32 (the only
  * supported quantization block; anything else is MOE_EUNSUPPORTED).
- * Supported: H and F multiples of 32 in [128, 4096] (H/32 and F/32 either <= 64 or exactly
- * 128); 1 <= k <= 16; k <= E;
- * E <= 1024.  The prefill path (more than MOE_DECODE_MAX_TOKENS tokens) further needs
- * H % 256 == 0, F % 128 == 0 and bf16 activations and router. */
+ * Supported: H and F multiples of 128 (whole groups of the code layout; else MOE_EINVAL)
+ * and at most 4096; 1 <= k <= 16; k <= E <= 1024 (beyond: MOE_EUNSUPPORTED).  The prefill
+ * path (more than MOE_DECODE_MAX_TOKENS tokens) further needs H % 256 == 0 and bf16
+ * activations and router. */
 typedef struct moe_dims {
   int32_t hidden;
   int32_t ffn;
@@ -193,7 +206,10 @@ MOE_API int moe_route(const moe_dims* dims, const void* x, int32_t x_dtype, int3
  *   topk_ids    [n_tokens][k].
  *   slots       [n_tokens][k] int32 out: layer_table[id] (-1 for a miss).
  *   miss_ids    [E] int32 out: the distinct missing ids, ascending; miss_count [1] out.
- *   bell        optional doorbell (see moe_doorbell), or NULL.
+ *   bell        optional doorbell (see moe_doorbell), or NULL.  With a doorbell the call also
+ *               publishes the selections to bell->host_step_ids (when not NULL), so a pool
+ *               knows the step's hits; it then takes at most MOE_DECODE_MAX_TOKENS tokens
+ *               (more: MOE_EUNSUPPORTED).
  * Entries >= n_slots set MOE_DERR_SLOT; ids outside [0, E) set MOE_DERR_EXPERT_ID. */
 MOE_API int moe_slot_lookup(const moe_dims* dims, const int32_t* layer_table, int32_t n_slots,
                             const int32_t* topk_ids, int32_t n_tokens, int32_t* slots,
@@ -203,35 +219,50 @@ MOE_API int moe_slot_lookup(const moe_dims* dims, const int32_t* layer_table, in
 /* Grouping of the (token, choice) pairs p = t*k + j by expert: a stable counting sort.
  *   counts [E] out, offsets [E+1] out (exclusive prefix sums), perm [n_tokens*k] out:
  *   pair indices in (expert, p) order.  (halogen README, "Measured": the ordering step
- *   of the tokens moves prefill speed.) */
+ *   of the tokens moves prefill speed.)  A token's k ids must be distinct (as moe_route
+ *   writes them); a repeated id sets MOE_DERR_DUP_ID and the outputs are invalid. */
 MOE_API int moe_group_tokens(const moe_dims* dims, const int32_t* topk_ids, int32_t n_tokens,
                              int32_t* counts, int32_t* offsets, int32_t* perm,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs + combine for a small batch (1..MOE_DECODE_MAX_TOKENS tokens): 4-bit GEMV,
- * dequantized in registers, fp32 accumulation, bandwidth-bound.
+/* Expert FFNs + combine for a small batch (1..MOE_DECODE_MAX_TOKENS tokens).  Betelgeuse
+ * article, "mechanism": every token runs its 10 routed experts and the shared expert, all of
+ * them, none dropped; halogen README, "Bring your own GGUF": decode pays per byte of weights
+ * read.  So each distinct selected expert's blob is streamed once per call, whatever the
+ * number of tokens that chose it: 4-bit GEMVs, codes entering the matrix cores exactly,
+ * fp32 accumulation, bandwidth-bound.
  *   layer_table [E] or NULL (NULL: expert e sits in slot e, all resident).
  *   x [n_tokens][H] (MOE_F32 or MOE_BF16); topk_ids / topk_w [n_tokens][k] (as moe_route
- *   writes them); y [n_tokens][H] fp32 out.
+ *   writes them: a token's ids distinct, else MOE_DERR_DUP_ID); y [n_tokens][H] fp32 out.
  * Every expert a token selected must be resident (else MOE_DERR_NOT_RESIDENT). */
 MOE_API int moe_expert_ffn_decode(const moe_dims* dims, const moe_layer_weights* w,
                                   const int32_t* layer_table_or_null, const void* x, int32_t x_dtype,
                                   int32_t n_tokens, const int32_t* topk_ids, const float* topk_w,
                                   float* y, void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs + combine for a long batch (prefill): tokens grouped by expert, grouped GEMM
- * on MFMA with dequantized fp16 tiles and fp32 accumulation, SwiGLU fused into the gate/up
- * epilogue.  x must be MOE_BF16.  Arguments as moe_expert_ffn_decode, any n_tokens >= 1. */
+/* Expert FFNs + combine for a long batch (prefill).  halogen README, "Measured": prefill is
+ * compute-bound and the ordering of tokens moves its speed; Basalt README, "Prompt chunks":
+ * a chunk's cost per token keeps falling up to a few thousand tokens.  Tokens are grouped by
+ * expert (a stable counting sort), and each expert's rows run as a grouped GEMM on MFMA with
+ * dequantized fp16 tiles and fp32 accumulation, SwiGLU fused into the gate/up epilogue.
+ * x must be MOE_BF16.  Arguments as moe_expert_ffn_decode, any n_tokens >= 1.  The fp16
+ * operands and intermediates hold |v| <= 65504: a bf16 activation, a SwiGLU output or a
+ * router-weighted expert row beyond that sets MOE_DERR_RANGE (the output is then invalid). */
 MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights* w,
                                    const int32_t* layer_table_or_null, const void* x, int32_t x_dtype,
                                    int32_t n_tokens, const int32_t* topk_ids, const float* topk_w,
                                    float* y, void* ws, size_t ws_bytes, void* stream);
 
-/* The whole layer: route -> residency check -> (wait for fills) -> expert FFNs -> combine.
+/* The whole layer (Betelgeuse article, "mechanism": router and shared expert resident, 10
+ * routed experts of 512 per token, the residency check in the stream and the host rung only
+ * on a miss): route -> residency check -> (wait for fills) -> expert FFNs -> combine.
  * Uses the decode kernels for n_tokens <= MOE_DECODE_MAX_TOKENS and the prefill kernels
  * above.  With a layer_table and a doorbell, misses are reported to the host and the FFNs
  * run after *bell->ready >= bell->epoch (the host fills the slots and updates the table
- * meanwhile).  topk_ids_out / topk_w_out [n_tokens][k] receive the routing if not NULL. */
+ * meanwhile); a doorbell is taken only by a decode-sized call (n_tokens <=
+ * MOE_DECODE_MAX_TOKENS; more: MOE_EUNSUPPORTED), since the host's recency policy needs the
+ * step's selections.  topk_ids_out / topk_w_out [n_tokens][k] receive the routing if not
+ * NULL. */
 MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w,
                               const int32_t* layer_table_or_null, const moe_doorbell* bell_or_null,
                               const void* x, int32_t x_dtype, int32_t n_tokens, float* y,

@@ -312,6 +312,9 @@ MOE_API int moe_slot_lookup(const moe_dims* dims, const int32_t* layer_table, in
   if (!layer_table || !topk_ids || !slots || !miss_ids || !miss_count || n_tokens < 1 || n_slots < 1)
     return MOE_EINVAL;
   if ((rc = check_bell(bell_or_null))) return rc;
+  // a doorbell publishes the step's selections too (the pool's recency policy needs the hits):
+  // decode-sized calls only
+  if (bell_or_null && n_tokens > kMaxDecodeTok) return MOE_EUNSUPPORTED;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
   const WsLayout L = ws_layout(dims, n_tokens);
   return hip_status(launch_lookup(topk_ids, n_tokens * dims->top_k, dims->n_experts, layer_table, n_slots, slots,
@@ -372,6 +375,8 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   if (!w->router || (rc = check_dtype(w->router_dtype))) return rc ? rc : MOE_EINVAL;
   if ((rc = check_bell(bell_or_null))) return rc;
   if (bell_or_null && !layer_table_or_null) return MOE_EINVAL;
+  // a doorbell goes with a decode-sized call, whose plan publishes the step's selections
+  if (bell_or_null && n_tokens > kMaxDecodeTok) return MOE_EUNSUPPORTED;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
   const bool prefill = n_tokens > kMaxDecodeTok;
   if (prefill) {
@@ -409,15 +414,11 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   rc = do_route(dims, x, x_dtype, n_tokens, w->router, w->router_dtype, w->router_bias, ids, tw, nullptr, ws, st);
   if (rc) return rc;
   if (layer_table_or_null) {
-    // residency check over all pairs; the doorbell is rung from the compaction kernel
+    // residency check over all pairs (no doorbell at this size: a missing expert is an error)
     rc = hip_status(launch_lookup(ids, n_tokens * dims->top_k, dims->n_experts, layer_table_or_null, w->n_slots,
                                   at<int32_t>(ws, L.slots), at<uint8_t>(ws, L.miss_flag), at<int32_t>(ws, L.miss_ids),
-                                  ctrl_of(ws) + kCtrlMissCount, ctrl_of(ws), bell_args(bell_or_null), st));
+                                  ctrl_of(ws) + kCtrlMissCount, ctrl_of(ws), DoorbellArgs{}, st));
     if (rc) return rc;
-    if (bell_or_null &&
-        hipStreamWaitValue32(st, bell_or_null->ready, bell_or_null->epoch, hipStreamWaitValueGte, 0xFFFFFFFFu) !=
-            hipSuccess)
-      return MOE_EHIP;
   }
   return do_prefill_ffn(dims, w, layer_table_or_null, x, n_tokens, ids, tw, y, ws, st);
 }

@@ -116,6 +116,13 @@ MOE_DEV uint32_t word_of(const uint4& c, int d) { return d == 0 ? c.x : d == 1 ?
 
 MOE_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// fp16 operands and intermediates hold |v| <= 65504: a value beyond (or not finite) would be
+// stored as an infinity, so it is reported instead (MOE_DERR_RANGE), once per wave.
+MOE_DEV bool f16_out_of_range(float v) { return !(fabsf(v) <= 65504.0f); }
+MOE_DEV void report_range(bool bad, int32_t* ctrl) {
+  if (__any(bad) && (threadIdx.x & 63) == 0) set_error(ctrl, MOE_DERR_RANGE);
+}
+
 // RROWS: rows of a router work (the router's weights are read once per work: longer calls take
 // taller works)
 template <int MODE, int RROWS = kRouterTileRows>
@@ -305,6 +312,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   }
 
   // ---- epilogue: lane holds D[16i + 4g + r][16s + n] -----------------------------------------
+  bool range_bad = false;
 #pragma unroll
   for (int i = 0; i < MSUB; ++i) {
     if (i >= ms) continue;
@@ -317,14 +325,18 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
         for (int s = 0; s < 2; ++s) {
           const float gv = acc[i][s][r], uv = acc[i][s + 2][r];
           const int col = ntile * (kNTileW / 2) + wave * 32 + 16 * s + n;
-          a.h_out[(size_t)(it.row0 + row) * F + col] = (_Float16)(silu(gv) * uv);
+          const float hv = silu(gv) * uv;
+          range_bad |= f16_out_of_range(hv);
+          a.h_out[(size_t)(it.row0 + row) * F + col] = (_Float16)hv;
         }
       } else if constexpr (MODE == kDown) {
         const float wv = a.row_w[it.row0 + row];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int col = ntile * kNTileW + wave * 64 + 16 * s + n;
-          a.y16_out[(size_t)(it.row0 + row) * H + col] = (_Float16)(acc[i][s][r] * wv);
+          const float yv = acc[i][s][r] * wv;
+          range_bad |= f16_out_of_range(yv);
+          a.y16_out[(size_t)(it.row0 + row) * H + col] = (_Float16)yv;
         }
       } else {
 #pragma unroll
@@ -336,6 +348,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
       }
     }
   }
+  if constexpr (MODE != kRouter) report_range(range_bad, a.ctrl);
 }
 
 // ---- pipelined variant (the model's K: NK chunks of 128) ----------------------------------------
@@ -501,6 +514,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   });
 
   // ---- epilogue: lane holds D[16i + 4g + r][16s + n] -----------------------------------------
+  bool range_bad = false;
 #pragma unroll
   for (int i = 0; i < kMSub; ++i) {
     if (i >= ms) continue;
@@ -513,26 +527,37 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
         for (int s = 0; s < 2; ++s) {
           const float gv = acc[i][s][r], uv = acc[i][s + 2][r];
           const int col = ntile * (kPNTile / 2) + wave * 32 + 16 * s + n;
-          a.h_out[(size_t)(it.row0 + row) * F + col] = (_Float16)(silu(gv) * uv);
+          const float hv = silu(gv) * uv;
+          range_bad |= f16_out_of_range(hv);
+          a.h_out[(size_t)(it.row0 + row) * F + col] = (_Float16)hv;
         }
       } else {
         const float wv = a.row_w[it.row0 + row];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
           const int col = ntile * kPNTile + wave * 64 + 16 * s + n;
-          a.y16_out[(size_t)(it.row0 + row) * H + col] = (_Float16)(acc[i][s][r] * wv);
+          const float yv = acc[i][s][r] * wv;
+          range_bad |= f16_out_of_range(yv);
+          a.y16_out[(size_t)(it.row0 + row) * H + col] = (_Float16)yv;
         }
       }
     }
   }
+  report_range(range_bad, a.ctrl);
   (void)K;
 }
 
-// x (bf16) -> fp16, exact for values inside the fp16 normal range.
+// x (bf16) -> fp16, exact for values inside the fp16 normal range; a value beyond the fp16 range
+// is reported (MOE_DERR_RANGE).
 __global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* __restrict__ x, _Float16* __restrict__ y,
-                                                     size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
-    y[i] = (_Float16)__uint_as_float((uint32_t)x[i] << 16);
+                                                     size_t n, int32_t* __restrict__ ctrl) {
+  bool bad = false;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const float v = __uint_as_float((uint32_t)x[i] << 16);
+    bad |= f16_out_of_range(v);
+    y[i] = (_Float16)v;
+  }
+  report_range(bad, ctrl);
 }
 
 // y[t] = sum_{j<k} y_rows[inv[t*k+j]] + y_rows[inv[T*k+t]] (rows already weighted, fp16), fixed
@@ -577,7 +602,7 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   const size_t nx = (size_t)T * H;
   int grid = (int)((nx + 255) / 256);
   if (grid > 4096) grid = 4096;
-  k_bf16_to_f16<<<grid, 256, 0, st>>>((const uint16_t*)x_bf16, b.x16, nx);
+  k_bf16_to_f16<<<grid, 256, 0, st>>>((const uint16_t*)x_bf16, b.x16, nx, ctrl);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
   const int max_items = prefill_max_items(T, k, E, n_shared);

@@ -6,7 +6,8 @@
 //
 // Stable and deterministic without a sort: each expert e keeps a bitmap over tokens (bit t set
 // when token t chose e; a token chooses an expert at most once, so the pairs of bucket e in pair
-// order are its tokens in increasing order).  Setting bits with atomicOr is order-independent.
+// order are its tokens in increasing order; a second choice of the same expert finds its bit set
+// and is reported as MOE_DERR_DUP_ID).  Setting bits with atomicOr is order-independent.
 // The rank of (t, e) inside bucket e is the popcount of the bits below t: a per-bucket prefix of
 // word popcounts plus a popcount of the masked word.  The shared expert is bucket E and holds
 // every token in order.
@@ -21,11 +22,13 @@ __global__ __launch_bounds__(256) void k_group_setbits(const int32_t* __restrict
   for (int p = blockIdx.x * blockDim.x + threadIdx.x; p < n; p += gridDim.x * blockDim.x) {
     const int e = ids[p];
     if (e < 0 || e >= E) {
-      bad = MOE_DERR_EXPERT_ID;
+      bad |= MOE_DERR_EXPERT_ID;
       continue;
     }
     const int t = p / k;
-    atomicOr(&bits[(size_t)e * W + (t >> 5)], 1u << (t & 31));
+    const uint32_t bit = 1u << (t & 31);
+    // a bit already set: the token named expert e twice (its pairs would share one sorted row)
+    if (atomicOr(&bits[(size_t)e * W + (t >> 5)], bit) & bit) bad |= MOE_DERR_DUP_ID;
   }
   if (bad) set_error(ctrl, bad);
 }

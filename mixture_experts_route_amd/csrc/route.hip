@@ -191,9 +191,11 @@ __global__ __launch_bounds__(1024) void k_lookup_small(const int32_t* __restrict
     ctrl[kCtrlMissCount] = total;
   }
   if (bell.active) {
+    // the selections go with the miss list (a pool's recency policy needs the hits); a doorbell
+    // comes only with a decode-sized call (n_pairs <= kMaxDecodeTok * kMaxK, checked on the host)
     __threadfence();
     __syncthreads();
-    ring_doorbell(bell, miss_ids, total, nullptr, 0);
+    ring_doorbell(bell, miss_ids, total, ids, n_pairs);
   }
 }
 
@@ -227,8 +229,9 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     if (e < 0 || e >= E) {
       atomicOr(&sh.bad, MOE_DERR_EXPERT_ID);
     } else {
-      atomicOr(&sh.tok_mask[e], 1u << t);
-      atomicOr(&sh.choice[e], (uint32_t)j << (4 * t));
+      // a token naming e twice: reported, and only its first choice keeps a pair row
+      if (atomicOr(&sh.tok_mask[e], 1u << t) & (1u << t)) atomicOr(&sh.bad, MOE_DERR_DUP_ID);
+      else atomicOr(&sh.choice[e], (uint32_t)j << (4 * t));
       const int s = slots_staged ? sh.slot_of[e] : table ? table[e] : e;
       if (!slots_staged) sh.slot_of[e] = s;  // every writer of e writes the same value
       if (s >= n_slots) atomicOr(&sh.bad, MOE_DERR_SLOT);
@@ -340,11 +343,16 @@ MOE_DEV void plan_wave(const RouteArgs& a, PlanShared& sh, const int32_t* s_ids,
   }
   asm volatile("" ::: "memory");  // keep the LDS phases in program order
   const int n_pairs = a.T * a.k;
+  bool dup = false;
   for (int p = lane; p < n_pairs; p += 64) {
     const int e = s_ids[p];
     const int t = p / a.k, j = p - t * a.k;
-    __hip_atomic_fetch_or(&sh.tok_mask[e], 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_or(&sh.choice[e], (uint32_t)j << (4 * t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // (the selection's ids are distinct; a repeat would be reported, its choice dropped)
+    const uint32_t old =
+        __hip_atomic_fetch_or(&sh.tok_mask[e], 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    dup |= (old >> t) & 1u;
+    if (!((old >> t) & 1u))
+      __hip_atomic_fetch_or(&sh.choice[e], (uint32_t)j << (4 * t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   asm volatile("" ::: "memory");
   uint32_t m[NPER], c[NPER];
@@ -398,6 +406,7 @@ MOE_DEV void plan_wave(const RouteArgs& a, PlanShared& sh, const int32_t* s_ids,
     }
   }
   const bool any_bad = __any(bad);
+  const bool any_dup = __any(dup);
   if (lane == 0) {
     int n_all = n_tasks;
     if (a.n_shared) {
@@ -410,7 +419,7 @@ MOE_DEV void plan_wave(const RouteArgs& a, PlanShared& sh, const int32_t* s_ids,
     }
     a.ctrl[kCtrlNTasks] = n_all;
     a.ctrl[kCtrlMissCount] = n_miss;
-    if (any_bad) set_error(a.ctrl, MOE_DERR_SLOT);
+    if (any_bad || any_dup) set_error(a.ctrl, (any_bad ? MOE_DERR_SLOT : 0) | (any_dup ? MOE_DERR_DUP_ID : 0));
     *s_nmiss = n_miss;
   }
 }

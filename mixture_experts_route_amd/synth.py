@@ -23,10 +23,12 @@ CPU only, by numpy's PCG64 seeded from the same key.
 Storage formats (the ones the layer's C interface reads):
 
 * bf16: uint16 codes, little-endian.
-* expert blob: six sections, in order ``gate codes [F][H/2]``, ``up codes
-  [F][H/2]``, ``down codes [H][F/2]``, then the fp16 scales ``gate [F][H/32]``,
-  ``up [F][H/32]``, ``down [H][F/32]``.  Codes are uniform random bytes, so every
-  4-bit code is uniform over 0..15; scales are fp16(|N(0, 0.02)|).
+* expert blob: six sections, in order the gate, up and down codes (F*H/2 bytes
+  each) and then their fp16 block scales (F*H/16 bytes each), in the group-major
+  record layout the library's header states (64 code bytes and 8 scale bytes per
+  row and group of 128 inputs).  This module only fills the sections with random
+  bytes: codes are uniform random bytes, so every 4-bit code is uniform over
+  0..15 wherever it sits; scales are fp16(|N(0, 0.02)|), one per 2-byte slot.
 """
 
 from __future__ import annotations

@@ -153,3 +153,75 @@ def test_pool_create_rejects_inconsistent_residency(N):
         assert create([0, 1, 2, 3], homes) == -1
     assert N.raw("moe_pool_arm")(None, None) == -1
     assert N.raw("moe_pool_serve")(None, None, None, None, None, None, 0) == -1
+
+
+def test_header_blob_layout_packs_what_the_oracle_reads():
+    """One expert blob packed by following the header's text alone (written here from the sentences
+    it states, not from the oracle), then read by the oracle: every code and scale lands where the
+    header says.  The header must still state the rule this packer follows."""
+    import numpy as np
+
+    from oracle import moe_oracle as O
+
+    text = " ".join(" ".join(re.sub(r"^\s*\*", "", ln) for ln in open(HEADER).read().splitlines()).split())
+    for phrase in ("the 64-byte record at byte 64 * (c * R + r) of the section",
+                   "Word 4g + i (g, i = 0..3) holds slice g of block i",
+                   "input 128c + 32i + 8g + 2j in bits 4j..4j+3",
+                   "input 128c + 32i + 8g + 2j + 1 in bits 16+4j..16+4j+3",
+                   "at byte 8 * (c * R + r) of the scale section",
+                   "[gate codes F*H/2][up codes F*H/2][down codes H*F/2]",
+                   "[gate scales F*H/16][up scales F*H/16][down scales H*F/16]"):
+        assert phrase in text, phrase
+
+    H, F = 256, 128
+    rng = np.random.default_rng(11)
+    u = {m: rng.integers(0, 16, size=(R, K)) for m, (R, K) in {"gate": (F, H), "up": (F, H), "down": (H, F)}.items()}
+    sc = {m: rng.integers(0x0400, 0x3C00, size=(R, K // 32)).astype(np.uint16) for m, (R, K) in
+          {"gate": (F, H), "up": (F, H), "down": (H, F)}.items()}
+
+    def pack_codes(codes):
+        R, K = codes.shape
+        out = bytearray(R * K // 2)
+        for c in range(K // 128):
+            for r in range(R):
+                rec = 64 * (c * R + r)
+                for g in range(4):
+                    for i in range(4):
+                        word = 0
+                        for j in range(4):
+                            word |= int(codes[r, 128 * c + 32 * i + 8 * g + 2 * j]) << (4 * j)
+                            word |= int(codes[r, 128 * c + 32 * i + 8 * g + 2 * j + 1]) << (16 + 4 * j)
+                        out[rec + 4 * (4 * g + i): rec + 4 * (4 * g + i) + 4] = word.to_bytes(4, "little")
+        return bytes(out)
+
+    def pack_scales(s):
+        R, nb = s.shape
+        out = bytearray(R * nb * 2)
+        for c in range(nb // 4):
+            for r in range(R):
+                for i in range(4):
+                    out[8 * (c * R + r) + 2 * i: 8 * (c * R + r) + 2 * i + 2] = int(s[r, 4 * c + i]).to_bytes(2, "little")
+        return bytes(out)
+
+    blob = b"".join([pack_codes(u["gate"]), pack_codes(u["up"]), pack_codes(u["down"]),
+                     pack_scales(sc["gate"]), pack_scales(sc["up"]), pack_scales(sc["down"])])
+    assert len(blob) == O.blob_layout(H, F)["total"][1]
+    Wg, Wu, Wd = O.expert_weights(np.frombuffer(blob, np.uint8), H, F)
+    for m, W in (("gate", Wg), ("up", Wu), ("down", Wd)):
+        s = sc[m].view(np.float16).astype(np.float64)
+        want = (u[m] - 8).astype(np.float64) * np.repeat(s, 32, axis=1)
+        assert np.array_equal(W, want), m
+
+
+def test_doorbell_only_with_decode_sized_calls(N):
+    """A doorbell publishes the step's selections for the pool's recency policy: the calls refuse it
+    (MOE_EUNSUPPORTED, nothing enqueued) above MOE_DECODE_MAX_TOKENS tokens."""
+    d = N.dims(2048, 768, 512, 10, 1)
+    fake = 1 << 20
+    bell = N.moe_doorbell(fake, fake, fake, 1, fake)
+    w = N.moe_layer_weights(fake, 1, None, fake, 2_654_208, 512, 1 << 24)
+    T = N.MOE_DECODE_MAX_TOKENS + 1
+    assert N.raw("moe_slot_lookup")(ctypes.byref(d), fake, 512, fake, T, fake, fake, fake, ctypes.byref(bell), fake,
+                                    1 << 30, None) == N.MOE_EUNSUPPORTED
+    assert N.raw("moe_layer_forward")(ctypes.byref(d), ctypes.byref(w), fake, ctypes.byref(bell), fake, 1, T, fake,
+                                      None, None, fake, 1 << 30, None) == N.MOE_EUNSUPPORTED

@@ -191,3 +191,66 @@ def test_prefill_not_resident_is_an_error(N, dev, model_layer):
     y = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
     N.moe_expert_ffn_prefill(d, layer.native_weights(), table, x, T, ids, w, y, ws)
     assert N.moe_check_device_error(ws) & N.DERR_NOT_RESIDENT
+
+
+def _dup_ids(T, k, E, seed):
+    """Distinct ids per token, except token T // 2 whose choice 3 repeats its choice 1."""
+    rng = np.random.default_rng(seed)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[T // 2, 3] = ids[T // 2, 1]
+    return ids
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 40])
+def test_duplicate_ids_are_reported(N, dev, model_layer, T):
+    """A token whose top-k list names one expert twice is an error (MOE_DERR_DUP_ID), never a silent
+    result, through the grouping, the decode FFNs (up to 8 tokens) and the prefill FFNs; the
+    workspace stays usable for the next call."""
+    layer = model_layer
+    d = layer.dims()
+    E, k = layer.E, layer.k
+    ids_np = _dup_ids(T, k, E, seed=T)
+    ids = torch.from_numpy(ids_np).to(dev)
+    w = torch.full((T, k), 1.0 / k, dtype=torch.float32, device=dev)
+    x, _ = layer.x(T, 3, dev)
+    ws = _ws(N, d, T, dev)
+    counts = torch.zeros((E,), dtype=torch.int32, device=dev)
+    offsets = torch.zeros((E + 1,), dtype=torch.int32, device=dev)
+    perm = torch.zeros((T * k,), dtype=torch.int32, device=dev)
+    N.moe_group_tokens(d, ids, T, counts, offsets, perm, ws)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) & N.DERR_DUP_ID
+    y = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
+    if T <= N.MOE_DECODE_MAX_TOKENS:
+        N.moe_expert_ffn_decode(d, layer.native_weights(), None, x, T, ids, w, y, ws)
+        torch.cuda.synchronize()
+        assert N.moe_check_device_error(ws) & N.DERR_DUP_ID
+    N.moe_expert_ffn_prefill(d, layer.native_weights(), None, x, T, ids, w, y, ws)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) & N.DERR_DUP_ID
+    # the same workspace then serves a valid call with no error
+    _prefill_check(N, dev, layer, 40, step=41)
+
+
+def test_prefill_fp16_range_is_reported(N, dev, model_layer):
+    """The prefill path holds activations, the SwiGLU intermediate and the weighted expert rows in
+    fp16: a token whose values leave the fp16 range sets MOE_DERR_RANGE instead of turning into
+    infinities.  Large activations (x 100) overflow the SwiGLU output; a bf16 activation beyond
+    65504 overflows the conversion itself."""
+    layer = model_layer
+    d = layer.dims()
+    T = 24
+    x, _ = layer.x(T, 9, dev)
+    ws = _ws(N, d, T, dev)
+    y = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
+    big = (x.view(torch.bfloat16).float() * 100.0).to(torch.bfloat16).view(torch.int16)
+    N.moe_layer_forward(d, layer.native_weights(), None, big, T, y, ws)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) & N.DERR_RANGE
+    huge = x.clone()
+    huge[5, 17] = 0x4780  # bf16 65536.0
+    N.moe_layer_forward(d, layer.native_weights(), None, huge, T, y, ws)
+    torch.cuda.synchronize()
+    assert N.moe_check_device_error(ws) & N.DERR_RANGE
+    # the unscaled batch passes (and the flag is not left set)
+    _prefill_check(N, dev, layer, T, step=9)

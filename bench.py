@@ -92,6 +92,29 @@ def hold_queue(ms: float):
     sleep(int(cyc * ms))
 
 
+def host_cpu():
+    """(CPU model name, logical CPUs) of this host."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def cpu_baseline_record(units: float, dt1: float, dtn: float, n: int, unit: str, sample: str, scale: float = 1.0):
+    """The cpu_baseline object: `units` of work (tokens) in the timed sample, `scale` the factor from
+    the sample to the reported unit (e.g. 4 of 48 layers -> 1/12)."""
+    model, ncpu = host_cpu()
+    return {"value": units * scale / dtn, "unit": unit, "cores": n, "kind": "oracle", "sample": sample,
+            "value_1_thread": units * scale / dt1, "seconds_1_thread": dt1, "seconds_all_threads": dtn,
+            "host_cpus": ncpu, "cpu_model": model,
+            "oracle": "float64 numpy (library matmul steps threaded by its BLAS; the rest single-threaded)"}
+
+
 def build_model_layer(device, seed=0, cfg=2, layer=0, bias_c=None, table_perm=True):
     """Arena of the 512 routed experts, the shared expert, bf16 router: all in HBM."""
     import numpy as np
@@ -120,31 +143,143 @@ def build_model_layer(device, seed=0, cfg=2, layer=0, bias_c=None, table_perm=Tr
                 slot_of=slot_of, seed=seed, cfg=cfg, layer=layer)
 
 
-def cpu_baseline_decode(n_tokens: int, seed=0, cfg=2, layer=0):
-    """The oracle (as it stands) timed on host cores for `n_tokens` single-token steps."""
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the oracle (as it stands) on the host, on 1 thread and on all cores
+# ---------------------------------------------------------------------------------------------
+def _oracle_job(kind: str, share):
+    """Builds (untimed) the oracle's inputs for one share of a bounded sample and returns the timed
+    part as a closure.  Shares: single-token decode steps, layers of one 8-token decode step, or
+    tokens of a prefill batch; the same streams as the GPU run."""
     import numpy as np
-    from threadpoolctl import threadpool_limits
 
     from mixture_experts_route_amd import synth as S
     from oracle import moe_oracle as O
 
-    Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02)).astype(np.float64)
-    shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
-    # the first n_tokens steps' tokens of the GPU run (same stream, same rows)
-    xall = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), (n_tokens, H), 1.0))
-    xs = [xall[s:s + 1].astype(np.float64) for s in range(n_tokens)]
-    # the expert bytes are generated before the clock starts (data generation is not timed)
-    need = set()
-    for x in xs:
-        _, _, ids, _ = O.route(x, Wr, None, K_TOP)
-        need.update(int(e) for e in ids.ravel())
-    blobs = {e: S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, e), H, F) for e in need}
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
+    if kind == "decode1":
+        seed, cfg, layer = 0, 2, 0
+        steps = list(share)
+        Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02))
+        Wr = Wr.astype(np.float64)
+        shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
+        xall = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), (max(steps) + 1, H), 1.0))
+        xs = [xall[s:s + 1].astype(np.float64) for s in steps]
+        need = set()
         for x in xs:
-            O.moe_layer(x, Wr, None, K_TOP, lambda e: blobs[e], shared, H, F)
-        dt = time.perf_counter() - t0
-    return n_tokens / dt, dt
+            need.update(int(e) for e in O.route(x, Wr, None, K_TOP)[2].ravel())
+        blobs = {e: S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, e), H, F) for e in need}
+
+        def run():
+            for x in xs:
+                O.moe_layer(x, Wr, None, K_TOP, lambda e: blobs[e], shared, H, F)
+        return run
+    if kind == "decode48":
+        step, layers, T, seed, cfg = share[0], share[1], 8, 0, 3
+        work = []
+        for layer in layers:
+            Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02))
+            Wr = Wr.astype(np.float64)
+            bias = S.zipf_bias(S.rank_permutation(seed, cfg, layer, 0, E), S.ZIPF_C)
+            xall = S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), ((step + 1) * T, H), 1.0)
+            x = S.bf16_to_f32(xall[step * T:(step + 1) * T]).astype(np.float64)
+            ids = O.route(x, Wr, bias, K_TOP)[2]
+            blobs = {int(e): S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, int(e)), H, F)
+                     for e in np.unique(ids)}
+            shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
+            work.append((x, Wr, bias, blobs, shared))
+
+        def run():
+            for x, Wr, bias, blobs, shared in work:
+                O.moe_layer(x, Wr, bias, K_TOP, lambda e, b=blobs: b[e], shared, H, F)
+        return run
+    if kind == "prefill":
+        T, lo, hi = share
+        seed, cfg, layer = 0, 4, 0
+        Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02))
+        Wr = Wr.astype(np.float64)
+        bias = S.zipf_bias(S.rank_permutation(seed, cfg, layer, 0, E), S.ZIPF_C)
+        shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
+        x = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), (hi, H), 1.0))[lo:hi]
+        x = x.astype(np.float64)
+        ids = O.route(x, Wr, bias, K_TOP)[2]
+        blobs = {int(e): S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, int(e)), H, F) for e in np.unique(ids)}
+
+        def run():
+            O.moe_layer(x, Wr, bias, K_TOP, lambda e: blobs[e], shared, H, F)
+        return run
+    raise ValueError(kind)
+
+
+def _oracle_worker(kind, share, barrier, out):
+    """One process of the all-cores run: inputs built before the barrier, one numerical thread."""
+    from threadpoolctl import threadpool_limits
+
+    run = _oracle_job(kind, share)
+    with threadpool_limits(1):
+        barrier.wait()
+        t0 = time.monotonic()
+        run()
+        out.put((t0, time.monotonic()))
+
+
+def time_oracle(kind: str, whole, shares):
+    """Seconds for the sample `whole` on 1 thread in this process, and for the same sample split in
+    `shares` over as many worker processes (spawned: fresh interpreters that never touch the GPU),
+    wall time from the common start to the last finish.  Returns (t_1, t_all, processes)."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+
+    run = _oracle_job(kind, whole)
+    with threadpool_limits(1):
+        t0 = time.monotonic()
+        run()
+        dt1 = time.monotonic() - t0
+    ctx = mp.get_context("spawn")
+    barrier, out = ctx.Barrier(len(shares)), ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(kind, sh, barrier, out)) for sh in shares]
+    for p in procs:
+        p.start()
+    spans = [out.get(timeout=600) for _ in procs]
+    for p in procs:
+        p.join()
+    return dt1, max(b for _, b in spans) - min(a for a, _ in spans), len(procs)
+
+
+def _split(items, n):
+    n = max(1, min(n, len(items)))
+    return [items[i::n] for i in range(n)]
+
+
+def cpu_baselines(workers: int, decode_steps: int = 24, prefill_tokens: int = 48, decode48_layers: int = 4):
+    """The oracle timed on bounded samples of the benchmark's workloads (data generation excluded),
+    on 1 thread and on `workers` processes; one record per workload."""
+    out = {}
+    steps = list(range(50, 50 + decode_steps))  # the bench's first timed steps (after 50 warmup)
+    dt1, dtn, n = time_oracle("decode1", steps, [sorted(sh) for sh in _split(steps, workers)])
+    out["decode1"] = cpu_baseline_record(
+        decode_steps, dt1, dtn, n, "tokens/s",
+        f"{decode_steps} single-token steps of the same layer and token stream: {dt1:.1f} s on 1 thread, "
+        f"{dtn:.1f} s on {n} processes (steps split between them)")
+    layers = list(range(max(decode48_layers, workers)))
+    dt1, dtn, n = time_oracle("decode48", (4, layers[:decode48_layers]),
+                              [(4, sorted(sh)) for sh in _split(layers, workers)])
+    # 1 thread: `decode48_layers` layers; all cores: len(layers) layers; both scaled to 48 layers
+    rec = cpu_baseline_record(8, dtn, dtn, n, "tokens/s",
+                              f"one 8-token step through {len(layers)} of the 48 layers on {n} processes (a layer "
+                              f"each) in {dtn:.1f} s, and through {decode48_layers} layers on 1 thread in {dt1:.1f} s; "
+                              f"both scaled to 48 layers", scale=len(layers) / 48)
+    rec["value_1_thread"] = 8 * decode48_layers / 48 / dt1
+    rec["seconds_1_thread"] = dt1
+    out["decode48"] = rec
+    toks = list(range(prefill_tokens))
+    chunks = [(4096, c[0], c[-1] + 1) for c in
+              [toks[i:i + max(1, prefill_tokens // workers)] for i in range(0, prefill_tokens, max(1, prefill_tokens // workers))]]
+    dt1, dtn, n = time_oracle("prefill", (4096, 0, prefill_tokens), chunks)
+    out["prefill"] = cpu_baseline_record(
+        prefill_tokens, dt1, dtn, n, "tokens/s",
+        f"first {prefill_tokens} tokens of the 4096-token batch: {dt1:.1f} s on 1 thread in one oracle call, "
+        f"{dtn:.1f} s on {n} processes (consecutive token runs)")
+    return out
 
 
 def measured_traffic(path="profiles/decode1_gate_up_traffic.txt"):
@@ -297,66 +432,12 @@ def bench_decode1(args):
         "decode_ffn_hbm_frac": (gu_bytes + dn_bytes) / (gu_avg_s + dn_avg_s) / 1e9 / HBM_PEAK_GBS,
         "timed_region": "eager launches" if args.eager else "HIP graph replay of the timed steps",
     }
-    if not args.no_cpu_baseline:
-        n = args.cpu_sample
-        v, dt = cpu_baseline_decode(n)
-        result["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                                  "sample": f"first {n} single-token steps of the same layer (seed 0), "
-                                            f"{dt:.1f} s of float64 numpy on 1 thread"}
+    if args.cpu:
+        result["cpu_baseline"] = args.cpu["decode1"]
     return result
 
 
-def cpu_baseline_decode48(step: int, n_layers: int, n_total: int = 48, T: int = 8, seed=0, cfg=3):
-    """The oracle timed on one 8-token step through the first `n_layers` layers of the 48-layer
-    batched decode (same router, bias, expert and token streams), scaled to all `n_total` layers."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    from mixture_experts_route_amd import synth as S
-    from oracle import moe_oracle as O
-
-    work = []
-    for layer in range(n_layers):
-        Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02))
-        Wr = Wr.astype(np.float64)
-        bias = S.zipf_bias(S.rank_permutation(seed, cfg, layer, 0, E), S.ZIPF_C)
-        xall = S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), ((step + 1) * T, H), 1.0)
-        x = S.bf16_to_f32(xall[step * T:(step + 1) * T]).astype(np.float64)
-        _, _, ids, _ = O.route(x, Wr, bias, K_TOP)
-        blobs = {int(e): S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, int(e)), H, F) for e in np.unique(ids)}
-        shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
-        work.append((x, Wr, bias, blobs, shared))
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for x, Wr, bias, blobs, shared in work:
-            O.moe_layer(x, Wr, bias, K_TOP, lambda e, b=blobs: b[e], shared, H, F)
-        dt = time.perf_counter() - t0
-    return T / (dt * n_total / n_layers), dt
-
-
-def cpu_baseline_prefill(T: int, n_tokens: int, seed=0, cfg=4, layer=0):
-    """The oracle timed on a sample of `n_tokens` tokens of the T-token prefill batch."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
-
-    from mixture_experts_route_amd import synth as S
-    from oracle import moe_oracle as O
-
-    Wr = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "router", layer, 0), (E, H), 0.02)).astype(np.float64)
-    bias = S.zipf_bias(S.rank_permutation(seed, cfg, layer, 0, E), S.ZIPF_C)
-    shared = S.expert_blob_np(S.stream_key(seed, cfg, "shared", layer, 0), H, F)
-    x = S.bf16_to_f32(S.bf16_normal_np(S.stream_key(seed, cfg, "x", layer, X_STREAM), (n_tokens, H), 1.0))
-    x = x.astype(np.float64)
-    _, _, ids, _ = O.route(x, Wr, bias, K_TOP)
-    blobs = {int(e): S.expert_blob_np(S.stream_key(seed, cfg, "blob", layer, int(e)), H, F) for e in np.unique(ids)}
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        O.moe_layer(x, Wr, bias, K_TOP, lambda e: blobs[e], shared, H, F)
-        dt = time.perf_counter() - t0
-    return n_tokens / dt, dt
-
-
-def bench_prefill(T: int, steps: int, warmup: int, cpu_sample: int | None):
+def bench_prefill(T: int, steps: int, warmup: int, cpu_baseline: dict | None):
     """T-token prefill through one model-shaped layer with Zipf(1.1)-skewed routing."""
     import numpy as np
     import torch
@@ -422,15 +503,12 @@ def bench_prefill(T: int, steps: int, warmup: int, cpu_sample: int | None):
                       "frac": dn_flop / dn_s / 1e12 / FP16_MFMA_PEAK_TFLOPS},
         "both_gemms_mfma_frac": (gu_flop + dn_flop) / (gu_s + dn_s) / 1e12 / FP16_MFMA_PEAK_TFLOPS,
     }
-    if cpu_sample:
-        v, dt = cpu_baseline_prefill(T, cpu_sample)
-        out["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"first {cpu_sample} tokens of the batch in one oracle call, "
-                                         f"{dt:.1f} s of float64 numpy on 1 thread"}
+    if cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline
     return out
 
 
-def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4, cpu_layers: int | None = None):
+def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4, cpu_baseline: dict | None = None):
     """Batched decode through all 48 layers: 8 tokens per step, every layer's 512 + 1 experts resident
     in HBM (one 65 GB arena), per-layer Zipf(1.1) router bias, fresh seeded tokens per (step, layer)."""
     import numpy as np
@@ -561,11 +639,8 @@ def bench_decode48(steps: int, warmup: int, graph: bool, time_steps: int = 4, cp
                         "avg_launch_us": float(dn_s.mean() * 1e6)},
         "decode_ffn_hbm_frac": ffn_gbs / HBM_PEAK_GBS,
     }
-    if cpu_layers:
-        v, dt = cpu_baseline_decode48(warmup, cpu_layers)
-        out["cpu_baseline"] = {"value": v, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-                               "sample": f"the first timed 8-token step through the first {cpu_layers} of the 48 "
-                                         f"layers, {dt:.1f} s of float64 numpy on 1 thread, scaled to 48 layers"}
+    if cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline
     return out
 
 
@@ -738,7 +813,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="decode1", choices=["decode1"])
-    ap.add_argument("--cpu-sample", type=int, default=40)
+    ap.add_argument("--cpu-sample", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="launch decode steps one by one instead of replaying graphs")
     ap.add_argument("--prefill", default="4096,32768", help="comma-separated prefill token counts to add ('' = none)")
@@ -754,6 +829,13 @@ def main():
         sys.exit(2)
     def progress(msg):
         print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+    # the CPU baseline first, before this process touches the GPU (its workers are spawned
+    # interpreters that never do)
+    args.cpu = {}
+    if not args.no_cpu_baseline:
+        progress("CPU baseline (oracle)")
+        args.cpu = cpu_baselines(min(16, os.cpu_count() or 1), decode_steps=args.cpu_sample)
 
     # The slot pool's compute and two copy streams are created first, while no other stream exists:
     # the runtime spreads streams over a few hardware queues, and the compute stream's in-stream
@@ -777,7 +859,7 @@ def main():
     if args.decode48_steps > 0:
         progress("48-layer batched decode")
         res["decode_8tok_48layers"] = bench_decode48(args.decode48_steps, 4, not args.eager,
-                                                     cpu_layers=None if args.no_cpu_baseline else 4)
+                                                     cpu_baseline=args.cpu.get("decode48"))
         import torch
 
         torch.cuda.empty_cache()
@@ -786,9 +868,15 @@ def main():
         res["decode_slot_pool_48layers"] = bench_pool(args.pool_steps, pool_streams)
     for T in [int(v) for v in args.prefill.split(",") if v.strip()]:
         steps = args.prefill_steps if T <= 8192 else max(4, args.prefill_steps // 4)
-        sample = None if args.no_cpu_baseline else (48 if T == 4096 else None)
         progress(f"{T}-token prefill")
-        res[f"prefill_{T}"] = bench_prefill(T, steps, max(2, steps // 5), sample)
+        base = args.cpu.get("prefill")
+        if base and T != 4096:
+            # the oracle's time is linear in the tokens (each token's experts, one after another): a
+            # batch of T tokens runs at the sampled rate and takes T / 4096 times as long as 4096
+            base = dict(base, sample=f"extrapolated from the 4096-token batch's sample ({base['sample']}): the "
+                                     f"oracle's time is linear in the tokens, so {T} tokens take {T / 4096:g}x the "
+                                     f"time of 4096")
+        res[f"prefill_{T}"] = bench_prefill(T, steps, max(2, steps // 5), base)
     print(json.dumps(res), flush=True)
 
 

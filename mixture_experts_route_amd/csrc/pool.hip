@@ -199,7 +199,11 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* d2h_stream, v
     if (timeout_us > 0 &&
         std::chrono::duration_cast<std::chrono::microseconds>(std::chrono::steady_clock::now() - t0).count() >
             timeout_us)
-      return release_with_error(p, ws_or_null, cs, "no doorbell before the timeout", (long)counts[1], (long)p->epoch);
+      return release_with_error(p, ws_or_null, cs,
+                                "no doorbell before the timeout (precondition: the compute and copy streams were "
+                                "created together before other streams, so no copy stream shares a hardware queue "
+                                "with the compute stream's wait)",
+                                (long)counts[1], (long)p->epoch);
     std::this_thread::yield();
   }
   std::atomic_thread_fence(std::memory_order_acquire);

@@ -269,6 +269,27 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w,
                               int32_t* topk_ids_out_or_null, float* topk_w_out_or_null,
                               void* ws, size_t ws_bytes, void* stream);
 
+/* The whole layer without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments and results as moe_layer_forward, with two differences:
+ *   - the workspace is a library-owned static device array of MOE_STATIC_SCRATCH_BYTES per GPU
+ *     (held from the first call on that GPU until the process ends); a call whose workspace
+ *     would exceed it (moe_workspace_bytes(dims, n_tokens) > MOE_STATIC_SCRATCH_BYTES; the
+ *     model shape fits up to about 100 tokens) returns MOE_EWORKSPACE, enqueueing nothing;
+ *   - device_error_out (device int32[1], required) receives the call's device error bits
+ *     (0 = none; the moe_device_error bits otherwise), copied from the array and cleared there
+ *     by the call's last kernel.
+ * It calls no hipMalloc, hipFree or allocating routine.  Every call on one GPU shares that GPU's
+ * array: calls that may overlap on one GPU (different streams, or other threads) race and must be
+ * ordered by the caller.  The first call on a GPU looks the array up and clears its control words
+ * on `stream`. */
+#define MOE_STATIC_SCRATCH_BYTES (8u << 20)
+MOE_API int moe_layer_forward_static(const moe_dims* dims, const moe_layer_weights* w,
+                                     const int32_t* layer_table_or_null, const moe_doorbell* bell_or_null,
+                                     const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
+                                     int32_t* topk_ids_out_or_null, float* topk_w_out_or_null,
+                                     int32_t* device_error_out, void* stream);
+
 /* ---- Host service of a per-layer expert-slot pool (decode calls) ----------------------------
  * Betelgeuse news article, section "mechanism: VRAM expert-slot pool, in-stream doorbell and
  * victim cache": a layer keeps a fixed number of HBM slots, the in-stream check rings the host

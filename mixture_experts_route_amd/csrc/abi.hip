@@ -1,5 +1,7 @@
 // The C interface (include/moe_route.h): host-side validation, workspace carving and launches.
 // Nothing here allocates device memory; every error is reported before anything is enqueued.
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace moe {
@@ -225,6 +227,26 @@ static int do_prefill_ffn(const moe_dims* d, const moe_layer_weights* w, const i
                                        x, g, b, y, ctrl, st));
 }
 
+// Host-side validation of a whole-layer call (everything but the workspace).
+static int check_layer_args(const moe_dims* dims, const moe_layer_weights* w, const int32_t* table,
+                            const moe_doorbell* bell, const void* x, int x_dtype, int n_tokens, const float* y) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!x || !y || n_tokens < 1) return MOE_EINVAL;
+  if ((rc = check_dtype(x_dtype))) return rc;
+  if ((rc = check_weights(dims, w, table))) return rc;
+  if (!w->router || (rc = check_dtype(w->router_dtype))) return rc ? rc : MOE_EINVAL;
+  if ((rc = check_bell(bell))) return rc;
+  if (bell && !table) return MOE_EINVAL;
+  // a doorbell goes with a decode-sized call, whose plan publishes the step's selections
+  if (bell && n_tokens > kMaxDecodeTok) return MOE_EUNSUPPORTED;
+  if (n_tokens > kMaxDecodeTok) {
+    if (x_dtype != MOE_BF16 || w->router_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
+    if ((rc = prefill_shape_ok(dims))) return rc;
+  }
+  return MOE_OK;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -367,22 +389,10 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
                               const moe_doorbell* bell_or_null, const void* x, int32_t x_dtype, int32_t n_tokens,
                               float* y, int32_t* topk_ids_out_or_null, float* topk_w_out_or_null, void* ws,
                               size_t ws_bytes, void* stream) {
-  int rc = check_dims(dims);
+  int rc = check_layer_args(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, y);
   if (rc) return rc;
-  if (!x || !y || n_tokens < 1) return MOE_EINVAL;
-  if ((rc = check_dtype(x_dtype))) return rc;
-  if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
-  if (!w->router || (rc = check_dtype(w->router_dtype))) return rc ? rc : MOE_EINVAL;
-  if ((rc = check_bell(bell_or_null))) return rc;
-  if (bell_or_null && !layer_table_or_null) return MOE_EINVAL;
-  // a doorbell goes with a decode-sized call, whose plan publishes the step's selections
-  if (bell_or_null && n_tokens > kMaxDecodeTok) return MOE_EUNSUPPORTED;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
   const bool prefill = n_tokens > kMaxDecodeTok;
-  if (prefill) {
-    if (x_dtype != MOE_BF16 || w->router_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-    if ((rc = prefill_shape_ok(dims))) return rc;
-  }
   hipStream_t st = (hipStream_t)stream;
   const WsLayout L = ws_layout(dims, n_tokens);
   int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);
@@ -424,3 +434,62 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
 }
 
 }  // extern "C"
+
+// ---- the layer without a caller workspace (moe_layer_forward_static) ----------------------------
+// Its workspace is a file-scope device array, one per GPU, of kScratchBytes.  Host code never uses
+// the array's name as an address: on the first call on a device (with that device current) its
+// device address is looked up once with hipGetSymbolAddress and kept per device.
+namespace moe {
+
+constexpr size_t kScratchBytes = (size_t)MOE_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Copies the call's device error word out to the caller and clears it (one thread).
+__global__ void k_take_error(int32_t* ctrl, int32_t* out) {
+  if (threadIdx.x == 0) {
+    out[0] = ctrl[kCtrlError];
+    ctrl[kCtrlError] = 0;
+  }
+}
+
+// The current device's scratch address; the first call on a device looks it up and clears the
+// control area on `st` (a fill kernel), so the counters and the error word start at zero.
+static int scratch_for_current_device(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_EHIP;
+    if (launch_fill_zero(p, kCtrlBytes, st) != hipSuccess) return MOE_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace moe
+
+extern "C" MOE_API int moe_layer_forward_static(const moe_dims* dims, const moe_layer_weights* w,
+                                                const int32_t* layer_table_or_null, const moe_doorbell* bell_or_null,
+                                                const void* x, int32_t x_dtype, int32_t n_tokens, float* y,
+                                                int32_t* topk_ids_out_or_null, float* topk_w_out_or_null,
+                                                int32_t* device_error_out, void* stream) {
+  int rc = check_layer_args(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, y);
+  if (rc) return rc;
+  if (!device_error_out) return MOE_EINVAL;
+  if (ws_layout(dims, n_tokens).total > kScratchBytes) return MOE_EWORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(st, &ws))) return rc;
+  rc = moe_layer_forward(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, y, topk_ids_out_or_null,
+                         topk_w_out_or_null, ws, kScratchBytes, stream);
+  if (rc) return rc;
+  k_take_error<<<1, 64, 0, st>>>(ctrl_of(ws), device_error_out);
+  return hip_status(hipGetLastError());
+}

@@ -29,7 +29,7 @@ DERR_EXPERT_ID, DERR_SLOT, DERR_NOT_RESIDENT, DERR_NAN, DERR_FILL, DERR_DUP_ID, 
 EXPORTS = [
     "moe_expert_blob_bytes", "moe_workspace_bytes", "moe_strerror", "moe_workspace_init",
     "moe_check_device_error", "moe_debug_kernel_events", "moe_debug_dequant", "moe_route", "moe_slot_lookup", "moe_group_tokens",
-    "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "moe_layer_forward",
+    "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "moe_layer_forward", "moe_layer_forward_static",
     "moe_pool_create", "moe_pool_destroy", "moe_pool_arm", "moe_pool_serve", "moe_pool_get_stats",
     "moe_pool_get_table",
 ]
@@ -84,6 +84,7 @@ _sig = {
     "moe_expert_ffn_decode": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_expert_ffn_prefill": (ctypes.c_int, [_D, _W, _P, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_layer_forward": (ctypes.c_int, [_D, _W, _P, _B, _P, _I, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_layer_forward_static": (ctypes.c_int, [_D, _W, _P, _B, _P, _I, _I, _P, _P, _P, _P, _P]),
     "moe_pool_create": (ctypes.c_int, [_D, _P, ctypes.c_int64, _I, _P, _P, _PP, _P, _I, _P, _P, _P, _P, _PP]),
     "moe_pool_destroy": (ctypes.c_int, [_P]),
     "moe_pool_arm": (ctypes.c_int, [_P, _B]),
@@ -218,6 +219,20 @@ def moe_layer_forward(d: moe_dims, w: moe_layer_weights, table, x, n_tokens: int
     _check(_lib.moe_layer_forward(ctypes.byref(d), ctypes.byref(w), _ptr(table), ctypes.byref(bell) if bell else None,
                                   _ptr(x), xd, n_tokens, _ptr(y), _ptr(topk_ids), _ptr(topk_w), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream)), "moe_layer_forward")
+
+
+MOE_STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def moe_layer_forward_static(d: moe_dims, w: moe_layer_weights, table, x, n_tokens: int, y, device_error,
+                             topk_ids=None, topk_w=None, bell: moe_doorbell | None = None, stream=None, x_dtype=None):
+    """moe_layer_forward on the library's static per-GPU workspace; ``device_error`` is a device
+    int32[1] tensor that receives the call's device error bits."""
+    xd = dtype_code(x) if x_dtype is None else x_dtype
+    _check(_lib.moe_layer_forward_static(ctypes.byref(d), ctypes.byref(w), _ptr(table),
+                                         ctypes.byref(bell) if bell else None, _ptr(x), xd, n_tokens, _ptr(y),
+                                         _ptr(topk_ids), _ptr(topk_w), _ptr(device_error), _stream(stream)),
+           "moe_layer_forward_static")
 
 
 def raw(name: str):

@@ -688,7 +688,7 @@ def bench_pool(steps: int, streams, topic_every: int = 128, n_layers: int = 48):
         biases = [torch.from_numpy(S.zipf_bias(r, S.ZIPF_C)).to(dev) for r in ranks]
         table = torch.full((E,), -1, dtype=torch.int32, device=dev)
         ready = torch.zeros((64,), dtype=torch.int32, device=dev)
-        hb = [N.HostBuffer(4 * E), N.HostBuffer(64), N.HostBuffer(4 * 8 * K_TOP)]
+        hb = [N.HostBuffer(4 * E), N.HostBuffer(64), N.HostBuffer(4 * N.MOE_DECODE_MAX_TOKENS * K_TOP)]
         pool = N.moe_pool_create(d, arena, stride, n_slots, table, initial, home_addr, homes.ptr + len(away) * stride,
                                  POOL_SPARES, hb[0].ptr, hb[1].ptr, hb[2].ptr, ready)
         layers.append(dict(arena=arena, homes=homes, shared=shared, router=router, biases=biases, table=table,

@@ -94,9 +94,18 @@ enum moe_device_error {
                                  beyond the fp16 range (|v| > 65504) or not finite */
 };
 
-/* Largest token count the decode entry points take (the pages' concurrent streams: Basalt
- * README "Concurrent requests: --parallel N", N = 1..8). */
-#define MOE_DECODE_MAX_TOKENS 8
+/* Largest token count of a decode call.  The pages' decode batches: concurrent streams (Basalt
+ * README, "Concurrent requests: --parallel N", N = 1..8) and speculative verify batches, whose
+ * tokens must come out byte-identical to the same request decoded alone and serially (halogen
+ * README, "Quality: what is measured, and what is not", identity properties).  On the decode
+ * path a token's output is bitwise the same at every batch size up to the limit:
+ *   MOE_DECODE_MAX_TOKENS (16) with bf16 activations (and a bf16 router, for the calls that
+ *   route) and F <= 2048;
+ *   MOE_DECODE_MAX_TOKENS_NARROW (8) otherwise: an fp32 token takes two matrix-core rows, and 16
+ *   tokens' SwiGLU rows of a wider F do not fit a workgroup's LDS.
+ * Above the limit moe_layer_forward takes the prefill kernels. */
+#define MOE_DECODE_MAX_TOKENS 16
+#define MOE_DECODE_MAX_TOKENS_NARROW 8
 
 /* Layer dimensions.  hidden = H, ffn = F (expert FFN width, shared expert too),
  * n_experts = E routed experts, top_k = k, n_shared = 0 or 1, block = 32 (the only
@@ -194,7 +203,7 @@ MOE_API int moe_debug_dequant(const moe_dims* dims, const uint8_t* blob, int32_t
  *   topk_w   [n_tokens][k] fp32 out: softmax over the k selected logits.
  *   logits   [n_tokens][E] fp32 out (x . router_e + bias_e), or NULL.
  * Logits accumulate in fp32 (bf16 x bf16 products are exact).  With more than
- * MOE_DECODE_MAX_TOKENS tokens both x and router must be bf16. */
+ * MOE_DECODE_MAX_TOKENS_NARROW tokens both x and router must be bf16. */
 MOE_API int moe_route(const moe_dims* dims, const void* x, int32_t x_dtype, int32_t n_tokens,
                       const void* router, int32_t router_dtype, const float* bias,
                       int32_t* topk_ids, float* topk_w, float* logits_or_null,
@@ -225,7 +234,8 @@ MOE_API int moe_group_tokens(const moe_dims* dims, const int32_t* topk_ids, int3
                              int32_t* counts, int32_t* offsets, int32_t* perm,
                              void* ws, size_t ws_bytes, void* stream);
 
-/* Expert FFNs + combine for a small batch (1..MOE_DECODE_MAX_TOKENS tokens).  Betelgeuse
+/* Expert FFNs + combine for a small batch (1..MOE_DECODE_MAX_TOKENS tokens with bf16 x and
+ * F <= 2048, else 1..MOE_DECODE_MAX_TOKENS_NARROW; more: MOE_EINVAL).  Betelgeuse
  * article, "mechanism": every token runs its 10 routed experts and the shared expert, all of
  * them, none dropped; halogen README, "Bring your own GGUF": decode pays per byte of weights
  * read.  So each distinct selected expert's blob is streamed once per call, whatever the
@@ -256,11 +266,11 @@ MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights
 /* The whole layer (Betelgeuse article, "mechanism": router and shared expert resident, 10
  * routed experts of 512 per token, the residency check in the stream and the host rung only
  * on a miss): route -> residency check -> (wait for fills) -> expert FFNs -> combine.
- * Uses the decode kernels for n_tokens <= MOE_DECODE_MAX_TOKENS and the prefill kernels
- * above.  With a layer_table and a doorbell, misses are reported to the host and the FFNs
+ * Uses the decode kernels up to the decode limit (MOE_DECODE_MAX_TOKENS for bf16 x and router
+ * and F <= 2048, else MOE_DECODE_MAX_TOKENS_NARROW) and the prefill kernels above.  With a layer_table and a doorbell, misses are reported to the host and the FFNs
  * run after *bell->ready >= bell->epoch (the host fills the slots and updates the table
- * meanwhile); a doorbell is taken only by a decode-sized call (n_tokens <=
- * MOE_DECODE_MAX_TOKENS; more: MOE_EUNSUPPORTED), since the host's recency policy needs the
+ * meanwhile); a doorbell is taken only by a decode-sized call (n_tokens within the decode
+ * limit; more: MOE_EUNSUPPORTED), since the host's recency policy needs the
  * step's selections.  topk_ids_out / topk_w_out [n_tokens][k] receive the routing if not
  * NULL. */
 MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w,

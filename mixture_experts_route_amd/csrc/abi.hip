@@ -78,6 +78,22 @@ static WsLayout ws_layout(const moe_dims* d, int T) {
   return L;
 }
 
+// Largest decode batch of the FFN kernels for these activations: 16 bf16 tokens when F <= 2048
+// (the down launch stages every token's h rows, hi and lo, in LDS), else 8 (an fp32 token takes
+// two matrix-core rows).
+static int decode_limit(const moe_dims* d, int x_dtype) {
+  return (x_dtype == MOE_BF16 && d->ffn <= kMaxDecodeF16Tok) ? kMaxDecodeTok : kMaxDecodeTokNarrow;
+}
+// ... and of the routing launch (the router GEMV's rows: one per bf16 token, two per fp32 token;
+// an fp32 router stages the tokens in LDS as fp32).
+static int route_decode_limit(int x_dtype, int r_dtype) {
+  return (x_dtype == MOE_BF16 && r_dtype == MOE_BF16) ? kMaxDecodeTok : kMaxDecodeTokNarrow;
+}
+static int layer_decode_limit(const moe_dims* d, int x_dtype, int r_dtype) {
+  const int a = decode_limit(d, x_dtype), b = route_decode_limit(x_dtype, r_dtype);
+  return a < b ? a : b;
+}
+
 static int check_dims(const moe_dims* d) {
   if (!d) return MOE_EINVAL;
   if (d->hidden <= 0 || d->ffn <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
@@ -144,7 +160,7 @@ static int do_route(const moe_dims* d, const void* x, int x_dtype, int T, const 
   const WsLayout L = ws_layout(d, T);
   float* lg = logits ? logits : at<float>(ws, L.logits);
   int rc;
-  if (T > kMaxDecodeTok) {
+  if (T > route_decode_limit(x_dtype, r_dtype)) {
     // long batches: router GEMM on MFMA (bf16 x bf16, fp32 accumulation)
     if (x_dtype != MOE_BF16 || r_dtype != MOE_BF16 || d->hidden % 128) return MOE_EUNSUPPORTED;
     rc = hip_status(launch_router_gemm(x, router, bias, T, d->n_experts, d->hidden, lg, st));
@@ -239,8 +255,9 @@ static int check_layer_args(const moe_dims* dims, const moe_layer_weights* w, co
   if ((rc = check_bell(bell))) return rc;
   if (bell && !table) return MOE_EINVAL;
   // a doorbell goes with a decode-sized call, whose plan publishes the step's selections
-  if (bell && n_tokens > kMaxDecodeTok) return MOE_EUNSUPPORTED;
-  if (n_tokens > kMaxDecodeTok) {
+  const int limit = layer_decode_limit(dims, x_dtype, w->router_dtype);
+  if (bell && n_tokens > limit) return MOE_EUNSUPPORTED;
+  if (n_tokens > limit) {
     if (x_dtype != MOE_BF16 || w->router_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
     if ((rc = prefill_shape_ok(dims))) return rc;
   }
@@ -363,8 +380,8 @@ MOE_API int moe_expert_ffn_decode(const moe_dims* dims, const moe_layer_weights*
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!x || !topk_ids || !topk_w || !y) return MOE_EINVAL;
-  if (n_tokens < 1 || n_tokens > kMaxDecodeTok) return MOE_EINVAL;
   if ((rc = check_dtype(x_dtype))) return rc;
+  if (n_tokens < 1 || n_tokens > decode_limit(dims, x_dtype)) return MOE_EINVAL;
   if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
   return do_decode_ffn(dims, w, layer_table_or_null, nullptr, x, x_dtype, n_tokens, topk_ids, topk_w, y, ws,
@@ -392,7 +409,7 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   int rc = check_layer_args(dims, w, layer_table_or_null, bell_or_null, x, x_dtype, n_tokens, y);
   if (rc) return rc;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
-  const bool prefill = n_tokens > kMaxDecodeTok;
+  const bool prefill = n_tokens > layer_decode_limit(dims, x_dtype, w->router_dtype);
   hipStream_t st = (hipStream_t)stream;
   const WsLayout L = ws_layout(dims, n_tokens);
   int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);

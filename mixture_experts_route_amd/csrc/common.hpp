@@ -16,6 +16,8 @@ namespace moe {
 constexpr int kBlock = 32;        // weights per quantization block
 constexpr int kWave = 64;         // CDNA wavefront
 constexpr int kMaxDecodeTok = MOE_DECODE_MAX_TOKENS;
+constexpr int kMaxDecodeTokNarrow = MOE_DECODE_MAX_TOKENS_NARROW;
+constexpr int kMaxDecodeF16Tok = 2048;  // largest F with 16 decode tokens (their h rows staged in LDS)
 constexpr int kMaxK = 16;
 constexpr int kMaxExperts = 1024;
 constexpr int kCtrlBytes = 4096;  // control area at the start of the workspace

@@ -122,7 +122,7 @@ MOE_DEV int task_token(uint32_t mask, int m) {
 
 // FFN output row (pair) of token t in a task.
 MOE_DEV int task_pair(const DecodeTask& tk, int t, int T, int k) {
-  return tk.expert < 0 ? T * k + t : t * k + (int)((tk.choice >> (4 * t)) & 15u);
+  return tk.expert < 0 ? T * k + t : t * k + task_choice(tk, t);
 }
 
 // Keeps every load above it ahead of the code below it: the loads of a wave's whole tile go out
@@ -207,30 +207,13 @@ MOE_DEV DecodeTask select_own_task(const DecodeArgs& a, int task) {
     const int my_slot = lane < k ? s_slot[lane < k ? my_id : 0] : -1;  // index clamped for the other lanes
     if (task < k) {
       const int j = __builtin_ctzll(__builtin_amdgcn_ballot_w64(lane < k && rank == task));
-      if (lane == j) {
-        DecodeTask tk;
-        tk.expert = my_id;
-        tk.slot = my_slot;
-        tk.tok_mask = 1u;
-        tk.choice = (uint32_t)j;
-        s_tk = tk;
-      }
+      if (lane == j) s_tk = make_task(my_id, my_slot, 1u, (uint32_t)j, 0u);
     } else if (lane == 0) {
-      DecodeTask tk;
-      tk.expert = -1;
-      tk.slot = -1;
-      tk.tok_mask = 1u;
-      tk.choice = 0u;
-      s_tk = tk;
+      s_tk = shared_task(1);
     }
     if (blockIdx.x == 0) {
       if (lane < k) {
-        DecodeTask tk;
-        tk.expert = my_id;
-        tk.slot = my_slot;
-        tk.tok_mask = 1u;
-        tk.choice = (uint32_t)lane;
-        a.sel_tasks[rank] = tk;
+        a.sel_tasks[rank] = make_task(my_id, my_slot, 1u, (uint32_t)lane, 0u);
         a.sel_ids[lane] = my_id;
         ((float*)a.topk_w)[lane] = s_w[lane];
       }
@@ -239,14 +222,7 @@ MOE_DEV DecodeTask select_own_task(const DecodeArgs& a, int task) {
       const bool any_bad = __any(bad);
       if (lane == 0) {
         int n_all = k;
-        if (a.n_shared) {
-          DecodeTask tk;
-          tk.expert = -1;
-          tk.slot = -1;
-          tk.tok_mask = 1u;
-          tk.choice = 0u;
-          a.sel_tasks[n_all++] = tk;
-        }
+        if (a.n_shared) a.sel_tasks[n_all++] = shared_task(1);
         a.ctrl[kCtrlNTasks] = n_all;
         a.ctrl[kCtrlMissCount] = n_miss;
         if (any_bad) set_error(a.ctrl, MOE_DERR_SLOT);
@@ -529,6 +505,7 @@ template <int MAXTOK, int RGW>
 MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) {
   constexpr int ROWS = 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
+  constexpr int MB = (ROWS + 15) / 16;  // 16-row A blocks: a second one holds token slots 8..15
   const DecodeTask tk = a.tasks[task];
   const uint8_t* blob = task_blob(a.src, tk);
   if (!blob) {
@@ -565,11 +542,13 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
   }
   const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
-  float acc[RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
+  float acc[MB][RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
 #pragma unroll
-  for (int r = 0; r < RGW; ++r)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NR / 2; ++j) acc[r][j] = 0.f;
+    for (int r = 0; r < RGW; ++r)
+#pragma unroll
+      for (int j = 0; j < NR / 2; ++j) acc[mb][r][j] = 0.f;
   // one batch of kDnQuadsPerPass groups: every load issued, then the MFMA steps group by group
   auto batch = [&](int q0, bool first) {
     const int nq = min(kDnQuadsPerPass, NQ - q0);
@@ -590,40 +569,57 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
 #pragma unroll
     for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
       if (qi >= nq) continue;
-      float part[RGW][NR];
+      float part[MB][RGW][NR];
 #pragma unroll
-      for (int r = 0; r < RGW; ++r)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < NR; ++j) part[r][j] = 0.f;
+        for (int r = 0; r < RGW; ++r)
+#pragma unroll
+          for (int j = 0; j < NR; ++j) part[mb][r][j] = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 A = lds_fragment(smem, ROWS, F, n, g, (q0 + qi) * kGroupElems + 32 * i);
-        const float4v O = mfma_bf16(A, neg, zero);
+        bf16x8 A[MB];
+        float4v O[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          A[mb] = lds_fragment(smem, ROWS, F, 16 * mb + n, g, (q0 + qi) * kGroupElems + 32 * i);
+          O[mb] = mfma_bf16(A[mb], neg, zero);
+        }
 #pragma unroll
         for (int r = 0; r < RGW; ++r) {
-          const float4v D = mfma_bf16(A, codes_q136(word_at(cd[r][qi], i)), O);
+          const bf16x8 B = codes_q136(word_at(cd[r][qi], i));
           const float s = scale_at(sd[r][qi], i);
 #pragma unroll
-          for (int j = 0; j < NR; ++j) part[r][j] = fmaf(s, D[j], part[r][j]);
+          for (int mb = 0; mb < MB; ++mb) {
+            const float4v D = mfma_bf16(A[mb], B, O[mb]);
+#pragma unroll
+            for (int j = 0; j < NR; ++j) part[mb][r][j] = fmaf(s, D[j], part[mb][r][j]);
+          }
         }
       }
 #pragma unroll
-      for (int r = 0; r < RGW; ++r)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < NR / 2; ++j) acc[r][j] += part[r][2 * j] + part[r][2 * j + 1];
+        for (int r = 0; r < RGW; ++r)
+#pragma unroll
+          for (int j = 0; j < NR / 2; ++j) acc[mb][r][j] += part[mb][r][2 * j] + part[mb][r][2 * j + 1];
     }
   };
   batch(0, true);  // peeled: a loop head would wait for every outstanding load, the staging too
   for (int q0 = kDnQuadsPerPass; q0 < NQ; q0 += kDnQuadsPerPass) batch(q0, false);
-  // lane (g, n) holds rows 4g + j: token slots 2g (j = 0, 1) and 2g + 1 (j = 2, 3)
+  // lane (g, n) holds rows 4g + j of each A block: token slots 8 mb + 2g (j = 0, 1) and
+  // 8 mb + 2g + 1 (j = 2, 3)
 #pragma unroll
-  for (int r = 0; r < RGW; ++r) {
+  for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int s2 = 0; s2 < NR / 2; ++s2) {
-      const int slot = 2 * g + s2;
-      if (rg_live[r] && slot < n_tok)
-        store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
-                   acc[r][s2]);
+    for (int r = 0; r < RGW; ++r) {
+#pragma unroll
+      for (int s2 = 0; s2 < NR / 2; ++s2) {
+        const int slot = 8 * mb + 2 * g + s2;
+        if (rg_live[r] && slot < n_tok)
+          store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
+                     acc[mb][r][s2]);
+      }
     }
   }
 }
@@ -798,10 +794,13 @@ constexpr int kPipeDnRGW = 2;     // down: row groups per wave (at most 2: one o
 static_assert(kPipeDnRGW >= 1 && kPipeDnRGW <= 2, "down row groups per wave");
 constexpr int kPipeDnGroups = 3;  // down: groups of 128 inputs per chunk
 constexpr int kPipeDnBufs = 2;    // down: chunks in flight
+// Waves per SIMD the pipelined kernels are compiled for: 4 (128 registers each) up to 8 tokens;
+// 2 (256 registers) at 16, whose staged activation rows would not fit beside the weight ring.
+constexpr int pipe_waves_per_eu(int maxtok) { return maxtok > 8 ? 2 : 4; }
 
 // gate/up: H = 128 kPipeGuGroups UNITS; A rows = token slots of the task (bf16 x).
 template <int MAXTOK, int UNITS>
-__global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_gate_up_pipe(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu(MAXTOK)))) void k_decode_gate_up_pipe(DecodeArgs a) {
   constexpr int ROWS = MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
   constexpr int QG = kPipeGuGroups;
@@ -928,6 +927,7 @@ template <int MAXTOK, int UNITS>
 MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) {
   constexpr int ROWS = 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
+  constexpr int MB = (ROWS + 15) / 16;  // 16-row A blocks: a second one holds token slots 8..15
   constexpr int QG = kPipeDnGroups;
   constexpr int RGW = kPipeDnRGW;
   const DecodeTask tk = a.tasks[task];
@@ -988,37 +988,52 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
 
   const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
-  float acc[RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
+  float acc[MB][RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
 #pragma unroll
-  for (int r = 0; r < RGW; ++r)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NR / 2; ++j) acc[r][j] = 0.f;
+    for (int r = 0; r < RGW; ++r)
+#pragma unroll
+      for (int j = 0; j < NR / 2; ++j) acc[mb][r][j] = 0.f;
   static_for<UNITS>([&](auto uc) {
     constexpr int u = decltype(uc)::value;
     constexpr int b = u % kPipeDnBufs;
 #pragma unroll
     for (int qi = 0; qi < QG; ++qi) {
-      float part[RGW][NR];
+      float part[MB][RGW][NR];
 #pragma unroll
-      for (int r = 0; r < RGW; ++r)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < NR; ++j) part[r][j] = 0.f;
+        for (int r = 0; r < RGW; ++r)
+#pragma unroll
+          for (int j = 0; j < NR; ++j) part[mb][r][j] = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bf16x8 A = lds_fragment(smem, ROWS, F, n, g, (u * QG + qi) * kGroupElems + 32 * i);
-        const float4v O = mfma_bf16(A, neg, zero);
+        bf16x8 A[MB];
+        float4v O[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          A[mb] = lds_fragment(smem, ROWS, F, 16 * mb + n, g, (u * QG + qi) * kGroupElems + 32 * i);
+          O[mb] = mfma_bf16(A[mb], neg, zero);
+        }
 #pragma unroll
         for (int r = 0; r < RGW; ++r) {
-          const float4v D = mfma_bf16(A, codes_q136(word_at(cd[b][r][qi], i), uk), O);
+          const bf16x8 B = codes_q136(word_at(cd[b][r][qi], i), uk);
           const float s = scale_at(sd[b][r][qi], i);
 #pragma unroll
-          for (int j = 0; j < NR; ++j) part[r][j] = fmaf(s, D[j], part[r][j]);
+          for (int mb = 0; mb < MB; ++mb) {
+            const float4v D = mfma_bf16(A[mb], B, O[mb]);
+#pragma unroll
+            for (int j = 0; j < NR; ++j) part[mb][r][j] = fmaf(s, D[j], part[mb][r][j]);
+          }
         }
       }
 #pragma unroll
-      for (int r = 0; r < RGW; ++r)
+      for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < NR / 2; ++j) acc[r][j] += part[r][2 * j] + part[r][2 * j + 1];
+        for (int r = 0; r < RGW; ++r)
+#pragma unroll
+          for (int j = 0; j < NR / 2; ++j) acc[mb][r][j] += part[mb][r][2 * j] + part[mb][r][2 * j + 1];
       __builtin_amdgcn_sched_barrier(0);  // one group at a time
     }
     if constexpr (u + kPipeDnBufs < UNITS) {
@@ -1028,24 +1043,30 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
   });
   // final accumulators (kept from being sunk into the conditional stores)
 #pragma unroll
-  for (int r = 0; r < RGW; ++r)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int j = 0; j < NR / 2; ++j) asm volatile("" : "+v"(acc[r][j]));
-  // lane (g, n) holds rows 4g + j: token slots 2g (j = 0, 1) and 2g + 1 (j = 2, 3)
+    for (int r = 0; r < RGW; ++r)
 #pragma unroll
-  for (int r = 0; r < RGW; ++r) {
+      for (int j = 0; j < NR / 2; ++j) asm volatile("" : "+v"(acc[mb][r][j]));
+  // lane (g, n) holds rows 4g + j of each A block: token slots 8 mb + 2g (j = 0, 1) and
+  // 8 mb + 2g + 1 (j = 2, 3)
 #pragma unroll
-    for (int s2 = 0; s2 < NR / 2; ++s2) {
-      const int slot = 2 * g + s2;
-      if (rg_live[r] && slot < n_tok)
-        store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
-                   acc[r][s2]);
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int r = 0; r < RGW; ++r) {
+#pragma unroll
+      for (int s2 = 0; s2 < NR / 2; ++s2) {
+        const int slot = 8 * mb + 2 * g + s2;
+        if (rg_live[r] && slot < n_tok)
+          store_pair(a.y_pairs + (size_t)task_pair(tk, task_token(tk.tok_mask, slot), a.T, a.k) * H + rows[r],
+                     acc[mb][r][s2]);
+      }
     }
   }
 }
 
 template <int MAXTOK, int UNITS>
-__global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_down_pipe(DecodeArgs a) {
+__global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu(MAXTOK)))) void k_decode_down_pipe(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   const int task = blockIdx.x / a.tiles_dn;
   const int tile = blockIdx.x - task * a.tiles_dn;
@@ -1135,8 +1156,11 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
       if (xb)
         return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true, RG>, grid_gu, gu_threads,
                             (uint32_t)gate_up_lds_bytes(a.H, MAXTOK, RG * ks), st, a);
-      return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false, RG>, grid_gu, gu_threads,
-                          (uint32_t)gate_up_lds_bytes(a.H, 2 * MAXTOK, RG * ks), st, a);
+      // fp32 tokens are two A rows (hi, lo) each: 8 of them fill the MFMA's 16 rows
+      if constexpr (MAXTOK <= 8)
+        return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false, RG>, grid_gu, gu_threads,
+                            (uint32_t)gate_up_lds_bytes(a.H, 2 * MAXTOK, RG * ks), st, a);
+      return hipErrorInvalidValue;
     };
     if (MAXTOK == 1 && a.F % (16 * kGuRG1) == 0 && kGuRG1 * ks <= 16)
       err = launch_rg(std::integral_constant<int, kGuRG1>{});
@@ -1189,7 +1213,9 @@ hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_t
   if (T <= 1) return launch_decode_ffn_t<1>(a, max_tasks, xb, st);
   if (T <= 2) return launch_decode_ffn_t<2>(a, max_tasks, xb, st);
   if (T <= 4) return launch_decode_ffn_t<4>(a, max_tasks, xb, st);
-  return launch_decode_ffn_t<8>(a, max_tasks, xb, st);
+  if (T <= 8) return launch_decode_ffn_t<8>(a, max_tasks, xb, st);
+  if (!xb) return hipErrorInvalidValue;  // fp32 tokens take two A rows each: at most 8 (host-checked)
+  return launch_decode_ffn_t<16>(a, max_tasks, xb, st);
 }
 
 bool decode_select1_supported(int H, int F, int k, int n_shared, int E) {

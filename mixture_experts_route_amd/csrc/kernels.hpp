@@ -32,12 +32,36 @@ hipError_t launch_timed(int which, K kernel, dim3 grid, dim3 block, uint32_t lds
 // Token t of a routed task owns FFN output row (pair) t*k + j; of the shared task, T*k + t.
 constexpr int kTaskTok = kMaxDecodeTok;
 
-struct DecodeTask {
-  int32_t expert;     // routed expert id, or -1 for the shared expert
-  int32_t slot;       // slot resolved by the plan, or -1: look the table up when the FFN runs (a miss)
-  uint32_t tok_mask;  // bit t: token t chose the expert
-  uint32_t choice;    // bits 4t..4t+3: j of token t (routed tasks)
+struct alignas(16) DecodeTask {
+  int32_t expert;      // routed expert id, or -1 for the shared expert
+  int32_t slot;        // slot resolved by the plan, or -1: look the table up when the FFN runs (a miss)
+  uint32_t tok_mask;   // bit t: token t chose the expert
+  uint32_t choice;     // bits 4t..4t+3: j of token t < 8 (routed tasks)
+  uint32_t choice_hi;  // bits 4(t-8)..4(t-8)+3: j of token t >= 8
+  uint32_t pad[3];
 };
+
+__host__ __device__ inline DecodeTask make_task(int32_t expert, int32_t slot, uint32_t tok_mask, uint32_t choice,
+                                                uint32_t choice_hi) {
+  DecodeTask t;
+  t.expert = expert;
+  t.slot = slot;
+  t.tok_mask = tok_mask;
+  t.choice = choice;
+  t.choice_hi = choice_hi;
+  t.pad[0] = t.pad[1] = t.pad[2] = 0u;
+  return t;
+}
+
+// The shared expert's task over T tokens.
+__host__ __device__ inline DecodeTask shared_task(int T) {
+  return make_task(-1, -1, T >= 32 ? 0xFFFFFFFFu : ((1u << T) - 1u), 0u, 0u);
+}
+
+// Position j of token t in a routed task's expert list.
+__host__ __device__ inline int task_choice(const DecodeTask& tk, int t) {
+  return (int)(((t < 8 ? tk.choice : tk.choice_hi) >> (4 * (t & 7))) & 15u);
+}
 
 // Upper bound on decode tasks for T tokens: every routed task holds >= 1 pair, plus one task
 // for the shared expert.

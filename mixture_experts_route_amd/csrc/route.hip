@@ -208,7 +208,8 @@ __global__ __launch_bounds__(1024) void k_lookup_small(const int32_t* __restrict
 struct alignas(16) PlanShared {
   uint32_t tok_mask[kMaxExperts];
   int32_t slot_of[kMaxExperts];
-  uint32_t choice[kMaxExperts];  // 4 bits per token: position j of the expert in its top-k
+  uint32_t choice[kMaxExperts];     // 4 bits per token t < 8: position j of the expert in its top-k
+  uint32_t choice_hi[kMaxExperts];  // tokens 8..15
   int wave_sums[16];
   int bad;
 };
@@ -219,7 +220,7 @@ struct alignas(16) PlanShared {
 MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, const int32_t* table, int n_slots,
                         int32_t* miss_ids, DecodeTask* tasks, int32_t* ctrl, const DoorbellArgs& bell,
                         PlanShared& sh, bool slots_staged = false) {
-  for (int e = threadIdx.x; e < E; e += blockDim.x) sh.tok_mask[e] = sh.choice[e] = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) sh.tok_mask[e] = sh.choice[e] = sh.choice_hi[e] = 0;
   if (threadIdx.x == 0) sh.bad = 0;
   __syncthreads();
   const int n_pairs = T * k;
@@ -231,7 +232,7 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     } else {
       // a token naming e twice: reported, and only its first choice keeps a pair row
       if (atomicOr(&sh.tok_mask[e], 1u << t) & (1u << t)) atomicOr(&sh.bad, MOE_DERR_DUP_ID);
-      else atomicOr(&sh.choice[e], (uint32_t)j << (4 * t));
+      else atomicOr(t < 8 ? &sh.choice[e] : &sh.choice_hi[e], (uint32_t)j << (4 * (t & 7)));
       const int s = slots_staged ? sh.slot_of[e] : table ? table[e] : e;
       if (!slots_staged) sh.slot_of[e] = s;  // every writer of e writes the same value
       if (s >= n_slots) atomicOr(&sh.bad, MOE_DERR_SLOT);
@@ -261,24 +262,11 @@ MOE_DEV void build_plan(const int32_t* ids, int T, int k, int E, int n_shared, c
     if (!m) continue;
     const int s = sh.slot_of[e];
     if (s < 0) miss_ids[mpos++] = e;
-    const uint32_t choice = sh.choice[e];
-    DecodeTask tk;
-    tk.expert = e;
-    tk.slot = s;
-    tk.tok_mask = m;
-    tk.choice = choice;
-    tasks[tpos++] = tk;
+    tasks[tpos++] = make_task(e, s, m, sh.choice[e], sh.choice_hi[e]);
   }
   if (threadIdx.x == 0) {
     int n_all = n_tasks;
-    if (n_shared) {
-      DecodeTask tk;
-      tk.expert = -1;
-      tk.slot = -1;
-      tk.tok_mask = (T >= 32) ? 0xFFFFFFFFu : ((1u << T) - 1u);
-      tk.choice = 0;
-      tasks[n_all++] = tk;
-    }
+    if (n_shared) tasks[n_all++] = shared_task(T);
     ctrl[kCtrlNTasks] = n_all;
     ctrl[kCtrlMissCount] = n_miss;
     if (sh.bad) set_error(ctrl, sh.bad);
@@ -340,6 +328,7 @@ MOE_DEV void plan_wave(const RouteArgs& a, PlanShared& sh, const int32_t* s_ids,
   for (int i = 0; i < NPER; i += 4) {
     *(uint4*)&sh.tok_mask[e0 + i] = make_uint4(0u, 0u, 0u, 0u);
     *(uint4*)&sh.choice[e0 + i] = make_uint4(0u, 0u, 0u, 0u);
+    *(uint4*)&sh.choice_hi[e0 + i] = make_uint4(0u, 0u, 0u, 0u);
   }
   asm volatile("" ::: "memory");  // keep the LDS phases in program order
   const int n_pairs = a.T * a.k;
@@ -352,18 +341,21 @@ MOE_DEV void plan_wave(const RouteArgs& a, PlanShared& sh, const int32_t* s_ids,
         __hip_atomic_fetch_or(&sh.tok_mask[e], 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     dup |= (old >> t) & 1u;
     if (!((old >> t) & 1u))
-      __hip_atomic_fetch_or(&sh.choice[e], (uint32_t)j << (4 * t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      __hip_atomic_fetch_or(t < 8 ? &sh.choice[e] : &sh.choice_hi[e], (uint32_t)j << (4 * (t & 7)), __ATOMIC_RELAXED,
+                            __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   asm volatile("" ::: "memory");
-  uint32_t m[NPER], c[NPER];
+  uint32_t m[NPER], c[NPER], ch[NPER];
   int32_t sl[NPER];
 #pragma unroll
   for (int i = 0; i < NPER; i += 4) {
     const uint4 mv = *(const uint4*)&sh.tok_mask[e0 + i];
     const uint4 cv = *(const uint4*)&sh.choice[e0 + i];
+    const uint4 hv = *(const uint4*)&sh.choice_hi[e0 + i];
     const int4 sv = *(const int4*)&sh.slot_of[e0 + i];
     m[i] = mv.x, m[i + 1] = mv.y, m[i + 2] = mv.z, m[i + 3] = mv.w;
     c[i] = cv.x, c[i + 1] = cv.y, c[i + 2] = cv.z, c[i + 3] = cv.w;
+    ch[i] = hv.x, ch[i + 1] = hv.y, ch[i + 2] = hv.z, ch[i + 3] = hv.w;
     sl[i] = sv.x, sl[i + 1] = sv.y, sl[i + 2] = sv.z, sl[i + 3] = sv.w;
   }
   int n_sub = 0, n_mis = 0;
@@ -397,26 +389,14 @@ MOE_DEV void plan_wave(const RouteArgs& a, PlanShared& sh, const int32_t* s_ids,
         s_miss[mpos] = e;
         ++mpos;
       }
-      DecodeTask tk;
-      tk.expert = e;
-      tk.slot = sl[i];
-      tk.tok_mask = m[i];
-      tk.choice = c[i];
-      a.tasks[tpos++] = tk;
+      a.tasks[tpos++] = make_task(e, sl[i], m[i], c[i], ch[i]);
     }
   }
   const bool any_bad = __any(bad);
   const bool any_dup = __any(dup);
   if (lane == 0) {
     int n_all = n_tasks;
-    if (a.n_shared) {
-      DecodeTask tk;
-      tk.expert = -1;
-      tk.slot = -1;
-      tk.tok_mask = (a.T >= 32) ? 0xFFFFFFFFu : ((1u << a.T) - 1u);
-      tk.choice = 0;
-      a.tasks[n_all++] = tk;
-    }
+    if (a.n_shared) a.tasks[n_all++] = shared_task(a.T);
     a.ctrl[kCtrlNTasks] = n_all;
     a.ctrl[kCtrlMissCount] = n_miss;
     if (any_bad || any_dup) set_error(a.ctrl, (any_bad ? MOE_DERR_SLOT : 0) | (any_dup ? MOE_DERR_DUP_ID : 0));

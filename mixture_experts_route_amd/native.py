@@ -23,7 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP, MOE_EDEVICE, MOE_EFILL = 0, -1, -2, -3, -4, -5, -6
 MOE_F32, MOE_BF16 = 0, 1
-MOE_DECODE_MAX_TOKENS = 8
+MOE_DECODE_MAX_TOKENS, MOE_DECODE_MAX_TOKENS_NARROW = 16, 8
 DERR_EXPERT_ID, DERR_SLOT, DERR_NOT_RESIDENT, DERR_NAN, DERR_FILL, DERR_DUP_ID, DERR_RANGE = 1, 2, 4, 8, 16, 32, 64
 
 EXPORTS = [

@@ -79,11 +79,19 @@ def test_invalid_arguments_rejected_on_host(N):
     assert route(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, (1 << 20) + 8, 1 << 30,
                  None) == -3
     assert route(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, 1 << 20, 64, None) == -3
-    # decode refuses more than MOE_DECODE_MAX_TOKENS tokens
+    # decode refuses more than MOE_DECODE_MAX_TOKENS bf16 tokens, and more than
+    # MOE_DECODE_MAX_TOKENS_NARROW fp32 tokens or bf16 tokens with F > 2048
     dec = N.raw("moe_expert_ffn_decode")
     w = N.moe_layer_weights(1 << 20, 1, None, 1 << 20, 2_654_208, 512, 1 << 24)
-    assert dec(ctypes.byref(d), ctypes.byref(w), None, 1 << 20, 1, 9, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 30,
+    assert dec(ctypes.byref(d), ctypes.byref(w), None, 1 << 20, 1, 17, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 30,
                None) == -1
+    assert dec(ctypes.byref(d), ctypes.byref(w), None, 1 << 20, 0, 9, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 30,
+               None) == -1
+    d_wide = N.dims(2048, 2304, 512, 10, 1)
+    w_wide = N.moe_layer_weights(1 << 20, 1, None, 1 << 20, N.moe_expert_blob_bytes(d_wide) + 4096 -
+                                 N.moe_expert_blob_bytes(d_wide) % 4096, 512, 1 << 24)
+    assert dec(ctypes.byref(d_wide), ctypes.byref(w_wide), None, 1 << 20, 1, 9, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+               1 << 30, None) == -1
     # slot stride must hold a blob and be 4 KiB aligned
     w_bad = N.moe_layer_weights(1 << 20, 1, None, 1 << 20, 2_654_208 + 512, 512, 1 << 24)
     assert dec(ctypes.byref(d), ctypes.byref(w_bad), None, 1 << 20, 1, 1, 1 << 20, 1 << 20, 1 << 20, 1 << 20,

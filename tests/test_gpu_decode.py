@@ -94,7 +94,7 @@ def test_route_tiny(N, dev):
         _route_check(N, dev, layer, 4, step)
 
 
-@pytest.mark.parametrize("T", [1, 3, 8])
+@pytest.mark.parametrize("T", [1, 3, 8, 16])
 def test_route_model_shape(N, dev, model_layer, T):
     ties = sum(_route_check(N, dev, model_layer, T, step) for step in range(3))
     assert ties <= T  # near ties are rare at this logit spread
@@ -112,7 +112,7 @@ def _tied_router(dev, H, E):
 
 
 @pytest.mark.parametrize("E,k", [(512, 10), (1024, 10), (1024, 16)])
-@pytest.mark.parametrize("T", [1, 5, 8, 300])
+@pytest.mark.parametrize("T", [1, 5, 8, 16, 300])
 def test_topk_exact_ties_lower_id_first(N, dev, T, E, k):
     """Selection on the GPU's own fp32 logits equals the oracle's ranking (logit desc, id asc)
     exactly when many logits are equal (decode route for T <= 8, prefill top-k above), at the
@@ -141,7 +141,7 @@ def test_topk_exact_ties_lower_id_first(N, dev, T, E, k):
     assert tied >= T
 
 
-@pytest.mark.parametrize("T", [1, 8])
+@pytest.mark.parametrize("T", [1, 8, 16])
 def test_layer_forward_exact_ties(N, dev, model_layer, T):
     """The decode plan path (router launch with selection and plan) ranks exact ties as moe_route."""
     layer = model_layer
@@ -197,7 +197,7 @@ def test_layer_tiny_decode(N, dev):
         assert err.max() < 1e-5  # fp32 activations ride as bf16 hi+lo; everything else fp32
 
 
-@pytest.mark.parametrize("T", [1, 2, 5, 8])
+@pytest.mark.parametrize("T", [1, 2, 5, 8, 9, 12, 16])
 def test_layer_model_shape_decode(N, dev, model_layer, T):
     _layer_check(N, dev, model_layer, T, step=11 + T)
 
@@ -208,7 +208,7 @@ def wide_layer(N, dev):
     return Layer(dict(MODEL, E=1024, k=16), dev, seed=0)
 
 
-@pytest.mark.parametrize("T", [1, 3, 8, 40])
+@pytest.mark.parametrize("T", [1, 3, 8, 16, 40])
 def test_layer_wide_routing_1024_experts_top16(N, dev, wide_layer, T):
     """E = 1024, k = 16 through the whole layer: 16 logits per lane in the selection, up to 129
     decode tasks (the one-token down kernel's 17-task variant at T = 1), and the prefill path at
@@ -217,7 +217,7 @@ def test_layer_wide_routing_1024_experts_top16(N, dev, wide_layer, T):
 
 
 @pytest.mark.parametrize("H,F,E,k", [(1024, 512, 64, 6), (4096, 1536, 64, 8)])
-@pytest.mark.parametrize("T", [1, 8, 40])
+@pytest.mark.parametrize("T", [1, 8, 16, 40])
 def test_layer_other_widths(N, dev, H, F, E, k, T):
     """Hidden and FFN widths other than the model's (the decode kernels' other chunk counts, the
     generic prefill GEMM at T = 40), against the oracle."""
@@ -245,14 +245,34 @@ def test_layer_batched_decode_zipf_layers(N, dev):
         torch.cuda.empty_cache()
 
 
-def test_ffn_decode_entry_point(N, dev, model_layer):
-    _layer_check(N, dev, model_layer, 3, step=2, via_layer=False)
+@pytest.mark.parametrize("T", [3, 16])
+def test_ffn_decode_entry_point(N, dev, model_layer, T):
+    _layer_check(N, dev, model_layer, T, step=2 + T, via_layer=False)
+
+
+def test_layer_batched_decode_16_tokens_zipf(N, dev):
+    """A 16-token verify batch through a Zipf(1.1)-biased layer: popular experts are chosen by
+    tokens on both sides of the 8-token boundary (tasks whose token slots fill both 16-row A
+    blocks of the down kernels)."""
+    from mixture_experts_route_amd import synth as S
+
+    layer = Layer(dict(MODEL, cfg=3), dev, seed=0, layer=5, bias_c=S.ZIPF_C)
+    x, x64 = layer.x(16, 3, dev)
+    ids = layer.oracle(x64)["ids"]
+    both = [e for e in np.unique(ids) if (ids[:8] == e).any() and (ids[8:] == e).any()]
+    assert both, "no expert shared across the two halves"
+    _layer_check(N, dev, layer, 16, 3)
+    del layer
+    torch.cuda.empty_cache()
 
 
 def test_decode_bitwise_deterministic_and_batch_invariant(N, dev, model_layer):
+    """A token's decode output is bitwise the same alone, in a batch of 8 and in a verify batch of
+    16 at any position (halogen README, "Quality: what is measured, and what is not": a request
+    batched with others emits the same bytes as alone; speculative verify = serial)."""
     layer = model_layer
     d = layer.dims()
-    T = 8
+    T = 16
     x, _ = layer.x(T, 99, dev)
     ws = _ws(N, d, T, dev)
     wts = layer.native_weights()
@@ -262,10 +282,22 @@ def test_decode_bitwise_deterministic_and_batch_invariant(N, dev, model_layer):
         N.moe_layer_forward(d, wts, None, x, T, y, ws)
         ys.append(y.clone())
     assert torch.equal(ys[0], ys[1])
-    for t in (0, 5):
+    # the first 8 tokens as a batch of 8, and every 4th token alone; the batch of 16 reversed
+    y8 = torch.zeros((8, layer.H), dtype=torch.float32, device=dev)
+    N.moe_layer_forward(d, wts, None, x[:8].contiguous(), 8, y8, ws)
+    assert torch.equal(y8, ys[0][:8]), "tokens 0..7 differ in a batch of 8 vs 16"
+    for t in (0, 5, 8, 15):
         y1 = torch.zeros((1, layer.H), dtype=torch.float32, device=dev)
         N.moe_layer_forward(d, wts, None, x[t:t + 1].contiguous(), 1, y1, ws)
         assert torch.equal(y1[0], ys[0][t]), f"token {t} differs alone vs in a batch of {T}"
+    yr = torch.zeros((T, layer.H), dtype=torch.float32, device=dev)
+    N.moe_layer_forward(d, wts, None, x.flip(0).contiguous(), T, yr, ws)
+    assert torch.equal(yr.flip(0), ys[0]), "a token's output depends on its position in the batch"
+    # 9..15 tokens (the other kernel variants' batch sizes) agree too
+    for T2 in (3, 11):
+        y2 = torch.zeros((T2, layer.H), dtype=torch.float32, device=dev)
+        N.moe_layer_forward(d, wts, None, x[:T2].contiguous(), T2, y2, ws)
+        assert torch.equal(y2, ys[0][:T2]), f"batch of {T2}"
     _check_no_device_error(N, ws)
 
 

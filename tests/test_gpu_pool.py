@@ -77,7 +77,7 @@ class PoolLayer:
         self.ready = torch.zeros((64,), dtype=torch.int32, device=dev)
         self.hb_ids = N.HostBuffer(4 * E)
         self.hb_counts = N.HostBuffer(64)
-        self.hb_step = N.HostBuffer(4 * 8 * self.k)
+        self.hb_step = N.HostBuffer(4 * N.MOE_DECODE_MAX_TOKENS * self.k)
         self.pool = N.moe_pool_create(self.dims(), self.arena, self.stride, n_slots, self.table, self.initial,
                                       self.home_addr, self.spares, n_spares, self.hb_ids.ptr, self.hb_counts.ptr,
                                       self.hb_step.ptr, self.ready)

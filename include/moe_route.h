@@ -383,6 +383,36 @@ MOE_API int moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* out);
 /* The pool's current slot table (host int32[E]). */
 MOE_API int moe_pool_get_table(const moe_pool* pool, int32_t* table_out);
 
+/* Hot-expert profile (Betelgeuse article, "limits and licence": a profile file only seeds the
+ * cache with hot experts; "mechanism": the package carries a hot-expert profile).
+ * moe_pool_get_profile: host int64[E], the selections of every expert the pool has served
+ * (hits and misses) since creation.
+ * moe_profile_seed: from such counts, the initial residency of a pool of n_slots slots: the
+ * n_slots experts with the most selections, hottest first (ties: lower id first), as
+ * moe_pool_create's `initial` takes it (host int32[n_slots] out).  1 <= n_slots <= n_experts. */
+MOE_API int moe_pool_get_profile(const moe_pool* pool, int64_t* counts_out);
+MOE_API int moe_profile_seed(const int64_t* counts, int32_t n_experts, int32_t n_slots, int32_t* initial_out);
+
+/* Slot lending (Basalt README, "Prompt chunks: --prefill": a prompt chunk's buffers are carved
+ * from the expert cache's last slots for the length of the prompt, and the experts in those slots
+ * are copied back afterwards).  moe_pool_lend lends the pool's last n slots (n_slots - n ..
+ * n_slots - 1, one contiguous region of n * slot_stride bytes at *region_out, e.g. another call's
+ * workspace): on `stream` it copies their experts out to host_bufs (caller's pinned host memory,
+ * n * slot_stride bytes, which holds them meanwhile: the tiers stay exclusive) and marks them not
+ * resident in the table.  Use the region only after those copies (same stream, or an event).
+ * moe_pool_unlend copies the experts back on `stream` (after the caller's last use of the region
+ * in that stream's order) and restores the table; the recency policy is as if nothing had been
+ * lent.  Neither may be called while a call is armed; moe_pool_arm refuses while slots are lent
+ * (MOE_EINVAL).  A failed copy enqueue returns MOE_EFILL with the lend state unchanged. */
+MOE_API int moe_pool_lend(moe_pool* pool, int32_t n, uint8_t* host_bufs, void* stream, uint8_t** region_out);
+MOE_API int moe_pool_unlend(moe_pool* pool, void* stream);
+
+/* Test hook for the failure path: after `after_n` more successful copy enqueues, the pool treats
+ * the next one as failed (the copy is not enqueued), as a failed hipMemcpyAsync would be: serve
+ * then releases the compute stream with MOE_DERR_FILL set and returns MOE_EFILL (Betelgeuse article,
+ * "what bit-exact means": a failed expert read is an error, never zero weights).  -1 = off. */
+MOE_API int moe_pool_debug_fail_copies(moe_pool* pool, int32_t after_n);
+
 #ifdef __cplusplus
 }
 #endif

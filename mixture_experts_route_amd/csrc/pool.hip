@@ -21,6 +21,7 @@
 //                        swap); with several spares (a FIFO) and two streams the victims' copies
 //                        out and the misses' copies in overlap on the two PCIe directions.
 // The FFN kernels read the slot of a missed expert from the table when they run, after the wait.
+#include <algorithm>
 #include <atomic>
 #include <cstdio>
 #include <chrono>
@@ -67,7 +68,18 @@ struct moe_pool {
   uint32_t epoch = 0;
   bool armed = false;
   moe_pool_stats stats{};
+  std::vector<int64_t> profile;   // selections seen per expert (hits and misses)
+  int lent = 0;                   // slots n_slots - lent .. n_slots - 1 are lent out
+  uint8_t* lent_bufs = nullptr;   // their experts' host copies while lent
+  int fail_after = -1;            // test hook: copy enqueues that succeed before one is failed
 };
+
+// A copy enqueue of the pool, or the failure the test hook injects in its place.
+static hipError_t pool_copy(moe_pool* p, void* dst, const void* src, size_t n, hipMemcpyKind kind, hipStream_t s) {
+  if (p->fail_after == 0) return hipErrorInvalidValue;
+  if (p->fail_after > 0) --p->fail_after;
+  return hipMemcpyAsync(dst, src, n, kind, s);
+}
 
 static bool hip_ok(hipError_t e) { return e == hipSuccess; }
 
@@ -116,6 +128,7 @@ MOE_API int moe_pool_create(const moe_dims* dims, uint8_t* arena, int64_t slot_s
   p->last_use.resize(n_slots);
   for (int s = 0; s < n_slots; ++s) p->last_use[s] = -(int64_t)(s + 1);  // hottest first: colder evicted first
   p->home.assign(host_home, host_home + E);
+  p->profile.assign(E, 0);
   for (int i = 0; i < n_spares; ++i) p->spares.emplace_back(spares + (int64_t)i * slot_stride, -1);
   p->ev_ring.assign(n_spares + 1, nullptr);
   bool ev_ok = true;
@@ -161,6 +174,7 @@ MOE_API int moe_pool_destroy(moe_pool* pool) {
 MOE_API int moe_pool_arm(moe_pool* pool, moe_doorbell* bell_out) {
   if (!pool || !bell_out) return MOE_EINVAL;
   if (pool->armed) return MOE_EINVAL;  // the previous call was not served
+  if (pool->lent) return MOE_EINVAL;   // slots are lent out: return them first
   pool->epoch += 1;
   pool->armed = true;
   bell_out->host_miss_ids = pool->host_miss_ids;
@@ -240,9 +254,9 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* d2h_stream, v
     // slot (after the victim's copy out); the expert's old host buffer becomes the newest spare
     const auto [buf, buf_ev] = p->spares.front();
     bool ok = !two || buf_ev < 0 || hip_ok(hipStreamWaitEvent(sd, p->ev_ring[buf_ev], 0));
-    ok = ok && hip_ok(hipMemcpyAsync(buf, slot, p->blob_bytes, hipMemcpyDeviceToHost, sd));
+    ok = ok && hip_ok(pool_copy(p, buf, slot, p->blob_bytes, hipMemcpyDeviceToHost, sd));
     if (two) ok = ok && hip_ok(hipEventRecord(p->ev_d2h, sd)) && hip_ok(hipStreamWaitEvent(cs, p->ev_d2h, 0));
-    ok = ok && hip_ok(hipMemcpyAsync(slot, p->home[e], p->blob_bytes, hipMemcpyHostToDevice, cs));
+    ok = ok && hip_ok(pool_copy(p, slot, p->home[e], p->blob_bytes, hipMemcpyHostToDevice, cs));
     // nothing was placed if an enqueue failed: the slot still holds the victim, the buffer stays spare
     if (!ok) return release_with_error(p, ws_or_null, cs, "copy enqueue failed", e, best);
     int read_ev = -1;
@@ -279,8 +293,11 @@ MOE_API int moe_pool_serve(moe_pool* pool, void* ws_or_null, void* d2h_stream, v
     if (!hip_ok(hipEventRecord(p->ev_end, cs))) return release_with_error(p, ws_or_null, cs, "event record failed");
     p->ev_end_set = true;
   }
-  // recency: every selection of the step, in (token, choice) order
-  for (int e : sel) p->last_use[p->table_host[e]] = ++p->clock;
+  // recency: every selection of the step, in (token, choice) order; the profile counts them
+  for (int e : sel) {
+    p->last_use[p->table_host[e]] = ++p->clock;
+    ++p->profile[e];
+  }
   if (n_sel == 0)
     for (int i = 0; i < n_miss; ++i) p->last_use[p->table_host[miss[i]]] = ++p->clock;
   p->stats.calls += 1;
@@ -300,6 +317,83 @@ MOE_API int moe_pool_get_stats(const moe_pool* pool, moe_pool_stats* out) {
 MOE_API int moe_pool_get_table(const moe_pool* pool, int32_t* table_out) {
   if (!pool || !table_out) return MOE_EINVAL;
   std::memcpy(table_out, pool->table_host, sizeof(int32_t) * pool->E);
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_get_profile(const moe_pool* pool, int64_t* counts_out) {
+  if (!pool || !counts_out) return MOE_EINVAL;
+  std::memcpy(counts_out, pool->profile.data(), sizeof(int64_t) * pool->E);
+  return MOE_OK;
+}
+
+MOE_API int moe_profile_seed(const int64_t* counts, int32_t n_experts, int32_t n_slots, int32_t* initial_out) {
+  if (!counts || !initial_out || n_experts < 1 || n_slots < 1 || n_slots > n_experts) return MOE_EINVAL;
+  std::vector<int32_t> order(n_experts);
+  for (int e = 0; e < n_experts; ++e) order[e] = e;
+  // hottest first: more selections first, the lower id first among equal counts
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return counts[a] > counts[b]; });
+  std::memcpy(initial_out, order.data(), sizeof(int32_t) * n_slots);
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_lend(moe_pool* pool, int32_t n, uint8_t* host_bufs, void* stream, uint8_t** region_out) {
+  if (!pool || !host_bufs || !region_out || n < 1 || n > pool->n_slots) return MOE_EINVAL;
+  moe_pool* p = pool;
+  if (p->armed || p->lent) return MOE_EINVAL;
+  hipStream_t st = (hipStream_t)stream;
+  const int first = p->n_slots - n;
+  // the last serve's copies into these slots come first
+  if (p->ev_end_set && !hip_ok(hipStreamWaitEvent(st, p->ev_end, 0))) return MOE_EHIP;
+  for (int i = 0; i < n; ++i) {
+    const int s = first + i;
+    if (!hip_ok(pool_copy(p, host_bufs + (int64_t)i * p->stride, p->arena + (int64_t)s * p->stride, p->blob_bytes,
+                          hipMemcpyDeviceToHost, st))) {
+      (void)hipStreamSynchronize(st);  // nothing changed hands: the slots keep their experts
+      return MOE_EFILL;
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    const int e = p->holder[first + i];
+    p->table_host[e] = -1;
+    p->home[e] = host_bufs + (int64_t)i * p->stride;
+  }
+  if (!hip_ok(hipMemcpyAsync(p->table_dev, p->table_host, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, st)))
+    return MOE_EHIP;
+  p->lent = n;
+  p->lent_bufs = host_bufs;
+  *region_out = p->arena + (int64_t)first * p->stride;
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_unlend(moe_pool* pool, void* stream) {
+  if (!pool || !pool->lent) return MOE_EINVAL;
+  moe_pool* p = pool;
+  hipStream_t st = (hipStream_t)stream;
+  const int n = p->lent, first = p->n_slots - n;
+  for (int i = 0; i < n; ++i) {
+    const int s = first + i;
+    if (!hip_ok(pool_copy(p, p->arena + (int64_t)s * p->stride, p->lent_bufs + (int64_t)i * p->stride, p->blob_bytes,
+                          hipMemcpyHostToDevice, st)))
+      return MOE_EFILL;  // still lent: the call can be repeated
+  }
+  for (int i = 0; i < n; ++i) {
+    const int e = p->holder[first + i];
+    p->table_host[e] = first + i;
+    p->home[e] = nullptr;
+  }
+  if (!hip_ok(hipMemcpyAsync(p->table_dev, p->table_host, sizeof(int32_t) * p->E, hipMemcpyHostToDevice, st)))
+    return MOE_EHIP;
+  // the next serve's copies out of these slots wait for the restore
+  p->ev_end_set = hip_ok(hipEventRecord(p->ev_end, st));
+  if (!p->ev_end_set) (void)hipStreamSynchronize(st);
+  p->lent = 0;
+  p->lent_bufs = nullptr;
+  return MOE_OK;
+}
+
+MOE_API int moe_pool_debug_fail_copies(moe_pool* pool, int32_t after_n) {
+  if (!pool) return MOE_EINVAL;
+  pool->fail_after = after_n < 0 ? -1 : after_n;
   return MOE_OK;
 }
 

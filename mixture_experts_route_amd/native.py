@@ -31,7 +31,8 @@ EXPORTS = [
     "moe_check_device_error", "moe_debug_kernel_events", "moe_debug_dequant", "moe_route", "moe_slot_lookup", "moe_group_tokens",
     "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "moe_layer_forward", "moe_layer_forward_static",
     "moe_pool_create", "moe_pool_destroy", "moe_pool_arm", "moe_pool_serve", "moe_pool_get_stats",
-    "moe_pool_get_table",
+    "moe_pool_get_table", "moe_pool_get_profile", "moe_profile_seed", "moe_pool_lend", "moe_pool_unlend",
+    "moe_pool_debug_fail_copies",
 ]
 
 
@@ -91,6 +92,11 @@ _sig = {
     "moe_pool_serve": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(ctypes.c_int32), ctypes.c_int64]),
     "moe_pool_get_stats": (ctypes.c_int, [_P, ctypes.POINTER(moe_pool_stats)]),
     "moe_pool_get_table": (ctypes.c_int, [_P, _P]),
+    "moe_pool_get_profile": (ctypes.c_int, [_P, _P]),
+    "moe_profile_seed": (ctypes.c_int, [_P, _I, _I, _P]),
+    "moe_pool_lend": (ctypes.c_int, [_P, _I, _P, _P, _PP]),
+    "moe_pool_unlend": (ctypes.c_int, [_P, _P]),
+    "moe_pool_debug_fail_copies": (ctypes.c_int, [_P, _I]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -350,3 +356,36 @@ def moe_pool_get_table(pool: int, n_experts: int):
     out = np.zeros(n_experts, dtype=np.int32)
     _check(_lib.moe_pool_get_table(pool, out.ctypes.data), "moe_pool_get_table")
     return out
+
+
+def moe_pool_get_profile(pool: int, n_experts: int):
+    import numpy as np
+
+    out = np.zeros(n_experts, dtype=np.int64)
+    _check(_lib.moe_pool_get_profile(pool, out.ctypes.data), "moe_pool_get_profile")
+    return out
+
+
+def moe_profile_seed(counts, n_slots: int):
+    """Initial residency (hottest first) of a pool of ``n_slots`` slots from per-expert counts."""
+    import numpy as np
+
+    c = np.ascontiguousarray(counts, dtype=np.int64)
+    out = np.zeros(n_slots, dtype=np.int32)
+    _check(_lib.moe_profile_seed(c.ctypes.data, len(c), n_slots, out.ctypes.data), "moe_profile_seed")
+    return out
+
+
+def moe_pool_lend(pool: int, n: int, host_bufs: int, stream=None) -> int:
+    """Lends the pool's last ``n`` slots; returns the region's device address."""
+    region = ctypes.c_void_p()
+    _check(_lib.moe_pool_lend(pool, n, host_bufs, _stream(stream), ctypes.byref(region)), "moe_pool_lend")
+    return region.value
+
+
+def moe_pool_unlend(pool: int, stream=None):
+    _check(_lib.moe_pool_unlend(pool, _stream(stream)), "moe_pool_unlend")
+
+
+def moe_pool_debug_fail_copies(pool: int, after_n: int):
+    _check(_lib.moe_pool_debug_fail_copies(pool, after_n), "moe_pool_debug_fail_copies")

@@ -355,6 +355,15 @@ class SlotPoolLRU:
         return misses, fills
 
 
+def profile_seed(counts, n_slots: int) -> np.ndarray:
+    """Initial residency from a hot-expert profile ([BG] "limits and licence": the profile only
+    seeds the cache with hot experts): the n_slots experts with the most selections, hottest
+    first; equal counts keep the lower id first (a stable sort as a step)."""
+    counts = np.asarray(counts, dtype=np.int64)
+    order = np.argsort(-counts, kind="stable")
+    return order[:n_slots].astype(np.int32)
+
+
 def per_token_rel_err(y_gpu: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
     """max_o |y - y_ref| / max_o |y_ref| per token (normwise, the parity metric, reading R11).
 

@@ -233,3 +233,20 @@ def test_doorbell_only_with_decode_sized_calls(N):
                                     1 << 30, None) == N.MOE_EUNSUPPORTED
     assert N.raw("moe_layer_forward")(ctypes.byref(d), ctypes.byref(w), fake, ctypes.byref(bell), fake, 1, T, fake,
                                       None, None, fake, 1 << 30, None) == N.MOE_EUNSUPPORTED
+
+
+def test_profile_seed_matches_the_oracle(N):
+    """moe_profile_seed (host code of the library) against the oracle's rule, ties included; bad
+    sizes refused."""
+    import numpy as np
+
+    from oracle import moe_oracle as O
+
+    rng = np.random.default_rng(3)
+    for E, n in ((512, 60), (512, 240), (64, 64), (8, 1)):
+        counts = rng.integers(0, 6, size=E).astype(np.int64)  # many equal counts
+        assert np.array_equal(N.moe_profile_seed(counts, n), O.profile_seed(counts, n))
+    f = N.raw("moe_profile_seed")
+    c = (ctypes.c_int64 * 4)(1, 2, 3, 4)
+    out = (ctypes.c_int32 * 8)()
+    assert f(c, 4, 5, out) == N.MOE_EINVAL and f(c, 4, 0, out) == N.MOE_EINVAL and f(None, 4, 2, out) == N.MOE_EINVAL

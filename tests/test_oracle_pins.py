@@ -444,3 +444,27 @@ def test_parity_metric_hand_worked():
     no_abs_ref = np.abs(y - ref).max(axis=1) / np.where(ref.max(axis=1) > 0, ref.max(axis=1), 1.0)
     assert not np.allclose(mean_for_max, want)
     assert not np.allclose(no_abs_ref, want)
+
+
+def test_profile_seed_hand_worked():
+    rows = list(_rows("profile_seed.txt"))
+    assert len(rows) >= 5
+    for counts, n, want in rows:
+        c = [int(v) for v in counts.split()]
+        got = O.profile_seed(c, int(n))
+        assert list(got) == [int(v) for v in want.split()], (counts, n, list(got))
+
+
+def test_profile_seed_brute_force():
+    """The seeded list is the unique order in which every expert beats every later one by count,
+    or by id on equal counts, and the n listed experts beat every unlisted one."""
+    rng = np.random.default_rng(21)
+    for _ in range(40):
+        E = int(rng.integers(1, 12))
+        n = int(rng.integers(1, E + 1))
+        c = rng.integers(0, 4, size=E)
+        got = [int(e) for e in O.profile_seed(c, n)]
+        assert len(set(got)) == n
+        beats = lambda a, b: c[a] > c[b] or (c[a] == c[b] and a < b)  # noqa: E731
+        assert all(beats(got[i], got[i + 1]) for i in range(n - 1))
+        assert all(beats(a, b) for a in got for b in range(E) if b not in got)

@@ -51,6 +51,14 @@ The readings taken here:
 * R9 miss list: unique expert ids, ascending;
 * R10 slot pool policy: per-layer LRU with an exclusive swap (see
   :class:`SlotPoolLRU`).
+* R15 codebook format ([HG] "Bring your own GGUF": the IQ4_NL / IQ4_XS family
+  is a small set of values times a per-block scale): a 4-bit code u selects
+  value u of the layer's codebook of 16 signed 8-bit integers, and the weight is
+  codebook[u] * scale; codes and scales sit where the default format has them.
+* R16 affine format ([HG] same section: Q4_K / Q5_K / Q5_1 read as exact affine
+  planes): weight = u * scale - min with u in 0..15 and one fp16 scale and one
+  fp16 min per block of 32; the min plane follows the scale planes in the blob,
+  in the scales' record layout.
 """
 
 from __future__ import annotations
@@ -58,6 +66,9 @@ from __future__ import annotations
 import numpy as np
 
 BLOCK = 32
+
+# weight formats: (u - 8) * scale; codebook[u] * scale; u * scale - min
+FMT_Q4_0, FMT_CB4, FMT_AFFINE4 = 0, 1, 2
 
 
 # ----------------------------------------------------------------------------
@@ -75,20 +86,24 @@ def fp16_codes_to_f64(codes) -> np.ndarray:
     return np.asarray(codes).astype(np.uint16).view(np.float16).astype(np.float64)
 
 
-def blob_layout(H: int, F: int) -> dict:
-    """Byte offsets of the six sections of one expert blob.
+def blob_layout(H: int, F: int, fmt: int = FMT_Q4_0) -> dict:
+    """Byte offsets of the sections of one expert blob.
 
     Order: gate codes (F rows of H), up codes (F rows of H), down codes (H rows
     of F), each F*H/2 bytes, then the fp16 scales of gate, up and down, F*H/32 * 2
-    bytes each; codes and scales group-major (:func:`decode_codes`,
-    :func:`decode_scales`).  (Layout is ours: [HG] "Bring your own GGUF" repacks
-    a file's values into the kernels' layout.)
+    bytes each, and with the affine format (R16) the fp16 mins of gate, up and
+    down, laid out like the scales; codes, scales and mins group-major
+    (:func:`decode_codes`, :func:`decode_scales`).  (Layout is ours: [HG] "Bring
+    your own GGUF" repacks a file's values into the kernels' layout.)
     """
     sizes = [
         ("gate_codes", F * H // 2), ("up_codes", F * H // 2), ("down_codes", H * F // 2),
         ("gate_scales", F * (H // BLOCK) * 2), ("up_scales", F * (H // BLOCK) * 2),
         ("down_scales", H * (F // BLOCK) * 2),
     ]
+    if fmt == FMT_AFFINE4:
+        sizes += [("gate_mins", F * (H // BLOCK) * 2), ("up_mins", F * (H // BLOCK) * 2),
+                  ("down_mins", H * (F // BLOCK) * 2)]
     out, off = {}, 0
     for name, sz in sizes:
         out[name] = (off, sz)
@@ -135,25 +150,43 @@ def decode_scales(scale_bytes, rows: int, cols: int) -> np.ndarray:
     return s.transpose(1, 0, 2).reshape(rows, cols // BLOCK)
 
 
-def dequant(code_bytes, scale_bytes, rows: int, cols: int) -> np.ndarray:
-    """w[r][c] = (u[r][c] - 8) * scale[r][c // 32]  ([HG]: small set x block scale)."""
+def dequant(code_bytes, scale_bytes, rows: int, cols: int, fmt: int = FMT_Q4_0, codebook=None,
+            min_bytes=None) -> np.ndarray:
+    """The weights w[r][c] of a [rows][cols] matrix, with s = scale[r][c // 32]:
+
+    * FMT_Q4_0 (R3): (u - 8) * s ([HG]: small set x block scale);
+    * FMT_CB4 (R15): codebook[u] * s;
+    * FMT_AFFINE4 (R16): u * s - min[r][c // 32].
+    """
     u = decode_codes(code_bytes, rows, cols)
-    s = decode_scales(scale_bytes, rows, cols)
-    return (u - 8).astype(np.float64) * np.repeat(s, BLOCK, axis=1)
+    s = np.repeat(decode_scales(scale_bytes, rows, cols), BLOCK, axis=1)
+    if fmt == FMT_Q4_0:
+        return (u - 8).astype(np.float64) * s
+    if fmt == FMT_CB4:
+        cb = np.asarray(codebook, dtype=np.int64)
+        assert cb.shape == (16,)
+        return cb[u].astype(np.float64) * s
+    if fmt == FMT_AFFINE4:
+        m = np.repeat(decode_scales(min_bytes, rows, cols), BLOCK, axis=1)
+        return u.astype(np.float64) * s - m
+    raise ValueError(fmt)
 
 
-def expert_weights(blob: np.ndarray, H: int, F: int):
+def expert_weights(blob: np.ndarray, H: int, F: int, fmt: int = FMT_Q4_0, codebook=None):
     """Dequantized (Wg [F][H], Wu [F][H], Wd [H][F]) of one expert blob."""
-    lay = blob_layout(H, F)
+    lay = blob_layout(H, F, fmt)
     blob = np.asarray(blob, dtype=np.uint8)
 
     def sec(name):
         off, sz = lay[name]
         return blob[off:off + sz]
 
-    Wg = dequant(sec("gate_codes"), sec("gate_scales"), F, H)
-    Wu = dequant(sec("up_codes"), sec("up_scales"), F, H)
-    Wd = dequant(sec("down_codes"), sec("down_scales"), H, F)
+    def mins(name):
+        return sec(name) if fmt == FMT_AFFINE4 else None
+
+    Wg = dequant(sec("gate_codes"), sec("gate_scales"), F, H, fmt, codebook, mins("gate_mins"))
+    Wu = dequant(sec("up_codes"), sec("up_scales"), F, H, fmt, codebook, mins("up_mins"))
+    Wd = dequant(sec("down_codes"), sec("down_scales"), H, F, fmt, codebook, mins("down_mins"))
     return Wg, Wu, Wd
 
 
@@ -233,24 +266,26 @@ def combine(w: np.ndarray, y_routed: np.ndarray, y_shared) -> np.ndarray:
     return y
 
 
-def moe_layer(x, Wr, bias, k: int, expert_blob, shared_blob, H: int, F: int):
+def moe_layer(x, Wr, bias, k: int, expert_blob, shared_blob, H: int, F: int, fmt: int = FMT_Q4_0,
+              codebook=None):
     """The whole routed MoE layer on activations x [T][H] (exact values).
 
     ``expert_blob(e)`` returns routed expert e's blob; ``shared_blob`` is the
-    shared expert's blob or None.  Returns a dict with y [T][H] (float64) and the
-    routing (logits64, logits32, ids, w).
+    shared expert's blob or None; ``fmt`` / ``codebook`` the weight format.
+    Returns a dict with y [T][H] (float64) and the routing (logits64, logits32,
+    ids, w).
     """
     x = np.asarray(x, np.float64)
     T = x.shape[0]
     l64, l32, ids, w = route(x, Wr, bias, k)
     y_routed = np.zeros((T, k, H), dtype=np.float64)
     for e in np.unique(ids):
-        Wg, Wu, Wd = expert_weights(expert_blob(int(e)), H, F)
+        Wg, Wu, Wd = expert_weights(expert_blob(int(e)), H, F, fmt, codebook)
         rows = np.nonzero(ids == e)
         y_routed[rows[0], rows[1], :] = swiglu_ffn(Wg, Wu, Wd, x[rows[0]])
     y_shared = None
     if shared_blob is not None:
-        Wg, Wu, Wd = expert_weights(shared_blob, H, F)
+        Wg, Wu, Wd = expert_weights(shared_blob, H, F, fmt, codebook)
         y_shared = swiglu_ffn(Wg, Wu, Wd, x)
     y = combine(w, y_routed, y_shared)
     return {"y": y, "logits64": l64, "logits32": l32, "ids": ids, "w": w}

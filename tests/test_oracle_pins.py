@@ -468,3 +468,76 @@ def test_profile_seed_brute_force():
         beats = lambda a, b: c[a] > c[b] or (c[a] == c[b] and a < b)  # noqa: E731
         assert all(beats(got[i], got[i + 1]) for i in range(n - 1))
         assert all(beats(a, b) for a in got for b in range(E) if b not in got)
+
+
+def test_codebook_and_affine_formats_hand_encoded():
+    """The codebook and affine formats on a hand-encoded group: every listed element's weight is
+    the hand-worked value (a wrong table index, a missing or doubled min, a sign error or a wrong
+    block fails)."""
+    fx = list(_rows("format_groups.txt"))
+    cb = [int(v) for v in [r for r in fx if r[0] == "codebook"][0][1].split()]
+    sbits = [int(h, 16) for h in [r for r in fx if r[0] == "scales"][0][1].split()]
+    mbits = [int(h, 16) for h in [r for r in fx if r[0] == "mins"][0][1].split()]
+    ramp = [r for r in _rows("dequant_groups.txt") if r[0] == "ramp_one"][0]
+    code_bytes = np.array([int(b, 16) for b in ramp[1].split()], dtype=np.uint8)
+    sb = np.array(sbits, dtype=np.uint16).view(np.uint8)
+    mb = np.array(mbits, dtype=np.uint16).view(np.uint8)
+    w_cb = O.dequant(code_bytes, sb, 1, 128, O.FMT_CB4, codebook=cb)[0]
+    w_af = O.dequant(code_bytes, sb, 1, 128, O.FMT_AFFINE4, min_bytes=mb)[0]
+    n = 0
+    for fmt, e, val in [r for r in fx if r[0] in ("cb", "aff")]:
+        got = (w_cb if fmt == "cb" else w_af)[int(e)]
+        assert got == float(Fraction(val)), (fmt, e, got, val)
+        n += 1
+    assert n >= 20
+    # the default format on the same bytes is unchanged
+    assert O.dequant(code_bytes, sb, 1, 128)[0][15] == 7.0
+
+
+def test_affine_blob_layout_appends_min_planes():
+    q = O.blob_layout(2048, 768)
+    a = O.blob_layout(2048, 768, O.FMT_AFFINE4)
+    for name in ("gate_codes", "up_codes", "down_codes", "gate_scales", "up_scales", "down_scales"):
+        assert q[name] == a[name]
+    assert a["gate_mins"][0] == q["total"][1] and a["total"][1] == 2_654_208 + 3 * 98_304
+    assert O.blob_layout(2048, 768, O.FMT_CB4) == q
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_layer_formats_match_fp64_dense_brute_force(fmt):
+    """The tiny layer in the codebook and affine formats: the oracle's layer equals a dense fp64
+    mixture computed from the dequantized matrices of every expert."""
+    rng = np.random.default_rng(40 + fmt)
+    T, E, H, F, k = 4, 8, 256, 128, 2
+    cb = np.sort(rng.choice(np.arange(-127, 128), 16, replace=False))
+    nbytes = O.blob_layout(H, F, fmt)["total"][1]
+    lay = O.blob_layout(H, F, fmt)
+
+    def blob():
+        b = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+        for sec in ("gate_scales", "up_scales", "down_scales", "gate_mins", "up_mins", "down_mins"):
+            if sec in lay:
+                off, sz = lay[sec]
+                v = (np.abs(rng.standard_normal(sz // 2)) * (0.02 if "scales" in sec else 0.1)).astype(np.float16)
+                b[off:off + sz] = v.view(np.uint8)
+        return b
+
+    blobs = [blob() for _ in range(E)]
+    shared = blob()
+    x = rng.standard_normal((T, H))
+    Wr = rng.standard_normal((E, H)) * 0.1
+    out = O.moe_layer(x, Wr, None, k, lambda e: blobs[e], shared, H, F, fmt, cb)
+    l = (x @ Wr.T).astype(np.float32).astype(np.float64)  # selection and weights on fp32 logits (R8)
+    y = np.zeros((T, H))
+    for t in range(T):
+        sel = np.argsort(-l[t], kind="stable")[:k]
+        w = np.exp(l[t, sel] - l[t, sel].max())
+        w /= w.sum()
+        for j, e in enumerate(sel):
+            Wg, Wu, Wd = O.expert_weights(blobs[e], H, F, fmt, cb)
+            g, u = Wg @ x[t], Wu @ x[t]
+            y[t] += w[j] * (Wd @ (g / (1 + np.exp(-g)) * u))
+        Wg, Wu, Wd = O.expert_weights(shared, H, F, fmt, cb)
+        g, u = Wg @ x[t], Wu @ x[t]
+        y[t] += Wd @ (g / (1 + np.exp(-g)) * u)
+    assert np.allclose(out["y"], y, rtol=1e-12, atol=1e-12)

@@ -56,7 +56,8 @@
  *     4j..4j+3 and input 128c + 32i + 8g + 2j + 1 in bits 16+4j..16+4j+3 (j = 0..3);
  *   - scales of group c of row r: four fp16 values (blocks 4c .. 4c+3 of the row) at byte
  *     8 * (c * R + r) of the scale section.
- * Model shape (H 2048, F 768): 2,654,208 bytes = 648 x 4 KiB.
+ * With MOE_FMT_AFFINE4 three more sections follow, [gate mins][up mins][down mins], laid out
+ * as the scales.  Model shape (H 2048, F 768): 2,654,208 bytes = 648 x 4 KiB (affine: 2,949,120).
  */
 #ifndef MOE_ROUTE_H
 #define MOE_ROUTE_H
@@ -121,7 +122,19 @@ typedef struct moe_dims {
   int32_t top_k;
   int32_t n_shared;
   int32_t block;
+  int32_t format;        /* weight format (moe_format); 0 = MOE_FMT_Q4_0, so a zeroed tail is the default */
+  int8_t codebook[16];   /* MOE_FMT_CB4: the 16 values a code stands for (times the block scale) */
 } moe_dims;
+
+/* Weight formats (halogen README, "Bring your own GGUF": the engine reads the IQ4_NL / IQ4_XS /
+ * IQ3_S / Q4_0 family as a small set of values times a per-block scale, and Q4_K / Q5_K / Q5_1
+ * as exact affine planes; other block layouts are refused by name).  With a block scale s (fp16):
+ *   MOE_FMT_Q4_0     w = (u - 8) * s;
+ *   MOE_FMT_CB4      w = codebook[u] * s, codebook = dims.codebook (16 signed 8-bit values);
+ *   MOE_FMT_AFFINE4  w = u * s - m, with a second fp16 plane m per block (the blob's mins).
+ * Any other value of dims.format is MOE_EUNSUPPORTED.  Q4_0 runs on every kernel; the other two
+ * run on the general (non-pipelined) decode and prefill kernels. */
+enum moe_format { MOE_FMT_Q4_0 = 0, MOE_FMT_CB4 = 1, MOE_FMT_AFFINE4 = 2 };
 
 /* One layer's weights (all device pointers).
  *   router       [E][H], dtype router_dtype (MOE_F32 or MOE_BF16); row e scores expert e.

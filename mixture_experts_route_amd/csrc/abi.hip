@@ -100,6 +100,7 @@ static int check_dims(const moe_dims* d) {
   if (d->n_shared != 0 && d->n_shared != 1) return MOE_EINVAL;
   if (d->top_k > d->n_experts) return MOE_EINVAL;
   if (d->block != kBlock) return MOE_EUNSUPPORTED;
+  if (d->format != MOE_FMT_Q4_0 && d->format != MOE_FMT_CB4 && d->format != MOE_FMT_AFFINE4) return MOE_EUNSUPPORTED;
   // rows are whole groups of 4 blocks (the interleaved code layout)
   if (d->hidden % kGroupElems || d->ffn % kGroupElems) return MOE_EINVAL;
   if (d->hidden > 4096 || d->ffn > 4096) return MOE_EUNSUPPORTED;
@@ -116,7 +117,7 @@ static int check_ws(const moe_dims* d, int T, const void* ws, size_t ws_bytes) {
 static int check_weights(const moe_dims* d, const moe_layer_weights* w, const int32_t* table) {
   if (!w || !w->arena) return MOE_EINVAL;
   if (w->n_slots <= 0) return MOE_EINVAL;
-  if (w->slot_stride < blob_layout(d->hidden, d->ffn).total || (w->slot_stride % 4096)) return MOE_EINVAL;
+  if (w->slot_stride < blob_layout(d->hidden, d->ffn, d->format).total || (w->slot_stride % 4096)) return MOE_EINVAL;
   if (((uintptr_t)w->arena & 255)) return MOE_EINVAL;
   if (d->n_shared == 1 && (!w->shared_blob || ((uintptr_t)w->shared_blob & 15))) return MOE_EINVAL;
   if (d->n_shared == 0 && w->shared_blob) return MOE_EINVAL;
@@ -173,13 +174,23 @@ static int do_route(const moe_dims* d, const void* x, int x_dtype, int T, const 
                                         DoorbellArgs{}, st));
 }
 
-static ExpertSource source_of(const moe_layer_weights* w, const int32_t* table) {
+static Codebook codebook_of(const moe_dims* d) {
+  Codebook cb;
+  for (int i = 0; i < 4; ++i)
+    cb.w[i] = (uint32_t)(uint8_t)d->codebook[4 * i] | ((uint32_t)(uint8_t)d->codebook[4 * i + 1] << 8) |
+              ((uint32_t)(uint8_t)d->codebook[4 * i + 2] << 16) | ((uint32_t)(uint8_t)d->codebook[4 * i + 3] << 24);
+  return cb;
+}
+
+static ExpertSource source_of(const moe_dims* d, const moe_layer_weights* w, const int32_t* table) {
   ExpertSource s;
   s.arena = w->arena;
   s.slot_stride = w->slot_stride;
   s.n_slots = w->n_slots;
   s.table = table;
   s.shared_blob = w->shared_blob;
+  s.fmt = d->format;
+  s.cb = codebook_of(d);
   return s;
 }
 
@@ -205,7 +216,7 @@ static int do_decode_ffn(const moe_dims* d, const moe_layer_weights* w, const in
   uint16_t* h_hi = at<uint16_t>(ws, L.h);
   uint16_t* h_lo = h_hi + (size_t)decode_pairs(d, T) * d->ffn;
   return hip_status(launch_decode_ffn(d->hidden, d->ffn, d->top_k, d->n_shared, T,
-                                      decode_max_tasks(T, d->top_k, d->n_shared), source_of(w, table), x, x_dtype,
+                                      decode_max_tasks(T, d->top_k, d->n_shared), source_of(d, w, table), x, x_dtype,
                                       tasks, topk_w, h_hi, h_lo, at<float>(ws, L.y_pairs), y, ctrl, st));
 }
 
@@ -239,7 +250,7 @@ static int do_prefill_ffn(const moe_dims* d, const moe_layer_weights* w, const i
   b.x16 = at<_Float16>(ws, L.x16);
   b.h16 = at<_Float16>(ws, L.h16);
   b.y_rows = at<_Float16>(ws, L.y_rows);
-  return hip_status(launch_prefill_ffn(d->hidden, d->ffn, d->top_k, d->n_experts, d->n_shared, T, source_of(w, table),
+  return hip_status(launch_prefill_ffn(d->hidden, d->ffn, d->top_k, d->n_experts, d->n_shared, T, source_of(d, w, table),
                                        x, g, b, y, ctrl, st));
 }
 
@@ -272,7 +283,7 @@ extern "C" {
 
 MOE_API size_t moe_expert_blob_bytes(const moe_dims* dims) {
   if (check_dims(dims) != MOE_OK) return 0;
-  return (size_t)blob_layout(dims->hidden, dims->ffn).total;
+  return (size_t)blob_layout(dims->hidden, dims->ffn, dims->format).total;
 }
 
 MOE_API size_t moe_workspace_bytes(const moe_dims* dims, int32_t max_tokens) {
@@ -327,7 +338,8 @@ MOE_API int moe_debug_dequant(const moe_dims* dims, const uint8_t* blob, int32_t
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!blob || !out || matrix < 0 || matrix > 2 || ((uintptr_t)blob & 3)) return MOE_EINVAL;
-  return hip_status(launch_debug_dequant(dims->hidden, dims->ffn, blob, matrix, out, (hipStream_t)stream));
+  return hip_status(launch_debug_dequant(dims->hidden, dims->ffn, dims->format, codebook_of(dims), blob, matrix, out,
+                                         (hipStream_t)stream));
 }
 
 MOE_API int moe_route(const moe_dims* dims, const void* x, int32_t x_dtype, int32_t n_tokens, const void* router,
@@ -415,6 +427,7 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);
   float* tw = topk_w_out_or_null ? topk_w_out_or_null : at<float>(ws, L.w);
   if (!prefill && n_tokens == 1 && !bell_or_null && x_dtype == MOE_BF16 && w->router_dtype == MOE_BF16 &&
+      dims->format == MOE_FMT_Q4_0 &&
       decode_select1_supported(dims->hidden, dims->ffn, dims->top_k, dims->n_shared, dims->n_experts)) {
     // one token, no doorbell: the router launch ends with its logits; the gate/up launch selects,
     // checks residency and plans (the router launch's last-workgroup step is off the path)
@@ -424,7 +437,7 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
     uint16_t* h_hi = at<uint16_t>(ws, L.h);
     uint16_t* h_lo = h_hi + (size_t)decode_pairs(dims, 1) * dims->ffn;
     return hip_status(launch_decode_ffn_select1(dims->hidden, dims->ffn, dims->top_k, dims->n_shared,
-                                                dims->n_experts, source_of(w, layer_table_or_null), x, logits,
+                                                dims->n_experts, source_of(dims, w, layer_table_or_null), x, logits,
                                                 at<DecodeTask>(ws, L.tasks), ids, tw, h_hi, h_lo, y, ctrl_of(ws),
                                                 st));
   }

@@ -37,10 +37,12 @@ enum CtrlWord {
 // Expert blob layout (see moe_route.h)
 // ---------------------------------------------------------------------------------------
 struct BlobLayout {
-  int64_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales, total;
+  int64_t gate_codes, up_codes, down_codes, gate_scales, up_scales, down_scales;
+  int64_t gate_mins, up_mins, down_mins;  // affine format only (else equal to total)
+  int64_t total;
 };
 
-__host__ __device__ inline BlobLayout blob_layout(int H, int F) {
+__host__ __device__ inline BlobLayout blob_layout(int H, int F, int fmt = MOE_FMT_Q4_0) {
   BlobLayout L;
   const int64_t gu = (int64_t)F * H / 2, d = (int64_t)H * F / 2;
   const int64_t sgu = (int64_t)F * (H / kBlock) * 2, sd = (int64_t)H * (F / kBlock) * 2;
@@ -50,8 +52,27 @@ __host__ __device__ inline BlobLayout blob_layout(int H, int F) {
   L.gate_scales = 2 * gu + d;
   L.up_scales = L.gate_scales + sgu;
   L.down_scales = L.up_scales + sgu;
-  L.total = L.down_scales + sd;
+  L.gate_mins = L.down_scales + sd;
+  L.up_mins = L.gate_mins + sgu;
+  L.down_mins = L.up_mins + sgu;
+  L.total = fmt == MOE_FMT_AFFINE4 ? L.down_mins + sd : L.gate_mins;
+  if (fmt != MOE_FMT_AFFINE4) L.up_mins = L.down_mins = L.gate_mins;
   return L;
+}
+
+// ---------------------------------------------------------------------------------------
+// Weight formats (moe_format).  The codebook's 16 signed bytes travel to the kernels as four
+// words; a workgroup expands them into a 256-entry LDS table indexed by a code pair (the two
+// codes of a word's pair j: bits 4j and 16 + 4j), each entry the pair's two values as 16-bit
+// floats, so one LDS read gives a ready operand register.
+// ---------------------------------------------------------------------------------------
+struct Codebook {
+  uint32_t w[4];  // value u in byte u % 4 of word u / 4
+};
+MOE_DEV int codebook_value(const Codebook& cb, int u) { return (int)(int8_t)(cb.w[u >> 2] >> (8 * (u & 3))); }
+// Index of pair j of a code word in the 256-entry table: code 2j in bits 0..3, code 2j+1 in 4..7.
+MOE_DEV uint32_t code_pair_index(uint32_t w, int j) {
+  return ((w >> (4 * j)) & 0xFu) | ((w >> (12 + 4 * j)) & 0xF0u);
 }
 
 // ---------------------------------------------------------------------------------------

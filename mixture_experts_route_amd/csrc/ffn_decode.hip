@@ -98,6 +98,46 @@ MOE_DEV bf16x8 const_neg136() {
   return __builtin_bit_cast(bf16x8, p);
 }
 
+// ---- weight formats on the matrix cores -------------------------------------------------------
+// One block of 32 inputs is one MFMA D = A B + C, and the block's scale s then multiplies D:
+//   MOE_FMT_Q4_0:    B = 128 + u (= q + 136), C = -136 sum_k A  ->  D = sum A q;  acc += s D
+//   MOE_FMT_AFFINE4: B = 128 + u,             C = -128 sum_k A  ->  D = sum A u;  acc += s D, and
+//                    the block's -m sum_k A is (m / 128) C:      acc += (m / 128) C
+//   MOE_FMT_CB4:     B = codebook[u] (8-bit integers are exact bf16), C = 0 ->  D = sum A cb[u]
+// Products are exact in every format; the sums are fp32.
+template <int FMT>
+MOE_DEV bf16x8 fmt_offset() {
+  constexpr uint32_t p = FMT == MOE_FMT_AFFINE4 ? 0xC300C300u : kNeg136Pair;  // bf16 pair -128 / -136
+  return __builtin_bit_cast(bf16x8, make_uint4(p, p, p, p));
+}
+template <int FMT>
+MOE_DEV float4v fmt_c(const bf16x8& A, const float4v& zero) {
+  if constexpr (FMT == MOE_FMT_CB4) return zero;
+  else return __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, fmt_offset<FMT>(), zero, 0, 0, 0);
+}
+// The B operand of one code word: 8 values, pair j (codes in bits 4j, 16 + 4j) in register j.
+template <int FMT>
+MOE_DEV bf16x8 fmt_b(uint32_t w, const uint32_t* cbt) {
+  if constexpr (FMT == MOE_FMT_CB4) {
+    uint4 p;
+    p.x = cbt[code_pair_index(w, 0)];
+    p.y = cbt[code_pair_index(w, 1)];
+    p.z = cbt[code_pair_index(w, 2)];
+    p.w = cbt[code_pair_index(w, 3)];
+    return __builtin_bit_cast(bf16x8, p);
+  } else {
+    return codes_q136(w);
+  }
+}
+// The 256-entry LDS table of the codebook format: entry (c1 << 4 | c0) = (bf16 cb[c0], bf16 cb[c1]).
+MOE_DEV void fill_codebook_bf16(const Codebook& cb, uint32_t* cbt) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    const uint32_t lo = f32_to_bf16_rne((float)codebook_value(cb, i & 15));
+    const uint32_t hi = f32_to_bf16_rne((float)codebook_value(cb, i >> 4));
+    cbt[i] = lo | (hi << 16);
+  }
+}
+
 MOE_DEV uint32_t word_at(const uint4& c, int i) { return i == 0 ? c.x : i == 1 ? c.y : i == 2 ? c.z : c.w; }
 MOE_DEV uint32_t word_at(const u32x4& c, int i) { return c[i]; }
 
@@ -299,11 +339,13 @@ MOE_DEV bf16x8 lds_fragment(const uint16_t* lds, int rows, int K, int m, int g, 
 // ---- gate/up: h[pair][r] = silu(Wg[r] . x) * (Wu[r] . x) for one task and 32 rows r ------------
 // Workgroup = RG row groups of 16 rows x KS waves splitting the H inputs in runs of 4 groups
 // (KS = H / 512).  A rows: token slot m of the task (bf16 x) or 2 m + part (fp32 x, hi / lo).
-template <int MAXTOK, bool X_BF16, int RG, bool SEL = false>
+template <int MAXTOK, bool X_BF16, int RG, bool SEL = false, int FMT = MOE_FMT_Q4_0>
 __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   constexpr int ROWS = X_BF16 ? MAXTOK : 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;                    // live D registers per lane
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  __shared__ uint32_t cbt[FMT == MOE_FMT_CB4 ? 256 : 1];
+  static_assert(FMT == MOE_FMT_Q4_0 || !SEL, "the selecting launch runs the default format");
 
   const int task = blockIdx.x / a.tiles_gu;
   const int tile = blockIdx.x - task * a.tiles_gu;
@@ -331,11 +373,12 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
     if (threadIdx.x == 0) set_error(a.ctrl, MOE_DERR_NOT_RESIDENT);
     return;
   }
-  const BlobLayout lay = blob_layout(H, F);
+  const BlobLayout lay = blob_layout(H, F, FMT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int NQ = H / kGroupElems;
   const int KS = (NQ + kGuQuadsPerWave - 1) / kGuQuadsPerWave;  // waves per row group
+  if constexpr (FMT == MOE_FMT_CB4) fill_codebook_bf16(a.src.cb, cbt);  // visible after the barrier below
   const int rg = wave / KS, kq = wave - rg * KS;
   const int row = (tile * RG + rg) * 16 + n;
   const int q0 = kq * kGuQuadsPerWave;
@@ -362,6 +405,7 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   const uint8_t* uscale = blob + lay.up_scales + (size_t)row * kGroupScaleBytes;
   uint4 cg[kGuQuadsPerWave], cu[kGuQuadsPerWave];
   uint2 sg[kGuQuadsPerWave], su[kGuQuadsPerWave];
+  uint2 mg[kGuQuadsPerWave], mu[kGuQuadsPerWave];  // affine format: the records' mins
 #pragma unroll
   for (int qi = 0; qi < kGuQuadsPerWave; ++qi) {
     const int qq = min(q0 + qi, NQ - 1);  // record (qq, row) at 64 (qq F + row)
@@ -369,6 +413,10 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
     cu[qi] = *(const uint4*)(ucode + (size_t)qq * F * kGroupBytes);
     sg[qi] = *(const uint2*)(gscale + (size_t)qq * F * kGroupScaleBytes);
     su[qi] = *(const uint2*)(uscale + (size_t)qq * F * kGroupScaleBytes);
+    if constexpr (FMT == MOE_FMT_AFFINE4) {
+      mg[qi] = *(const uint2*)(gscale - lay.gate_scales + lay.gate_mins + (size_t)qq * F * kGroupScaleBytes);
+      mu[qi] = *(const uint2*)(uscale - lay.up_scales + lay.up_mins + (size_t)qq * F * kGroupScaleBytes);
+    }
     __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
   }
   issue_fence();
@@ -378,7 +426,6 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
     __syncthreads();
   }
 
-  const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   float accg[NR], accu[NR];
 #pragma unroll
@@ -389,14 +436,22 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bf16x8 A = lds_fragment(smem, ROWS, H, arow, g, (q0 + qi) * kGroupElems + 32 * i);
-      const float4v O = mfma_bf16(A, neg, zero);
-      const float4v Dg = mfma_bf16(A, codes_q136(word_at(cg[qi], i)), O);
-      const float4v Du = mfma_bf16(A, codes_q136(word_at(cu[qi], i)), O);
+      const float4v O = fmt_c<FMT>(A, zero);
+      const float4v Dg = mfma_bf16(A, fmt_b<FMT>(word_at(cg[qi], i), cbt), O);
+      const float4v Du = mfma_bf16(A, fmt_b<FMT>(word_at(cu[qi], i), cbt), O);
       const float s_g = scale_at(sg[qi], i), s_u = scale_at(su[qi], i);
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         accg[r] = fmaf(s_g, Dg[r], accg[r]);
         accu[r] = fmaf(s_u, Du[r], accu[r]);
+      }
+      if constexpr (FMT == MOE_FMT_AFFINE4) {
+        const float m_g = scale_at(mg[qi], i) * 0.0078125f, m_u = scale_at(mu[qi], i) * 0.0078125f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          accg[r] = fmaf(m_g, O[r], accg[r]);
+          accu[r] = fmaf(m_u, O[r], accu[r]);
+        }
       }
     }
   }
@@ -501,8 +556,8 @@ MOE_DEV void combine_tile_if_last(const DecodeArgs& a, int tile, int tile_rows, 
 
 // ---- down: y_e[pair][o] = Wd[o] . h[pair] for one task; RGW row groups of 16 per wave ----------
 // A rows 2 s + part: token slot s, part 0 = h_hi, 1 = h_lo, staged in LDS once per workgroup.
-template <int MAXTOK, int RGW>
-MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) {
+template <int MAXTOK, int RGW, int FMT = MOE_FMT_Q4_0>
+MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem, uint32_t* cbt) {
   constexpr int ROWS = 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
   constexpr int MB = (ROWS + 15) / 16;  // 16-row A blocks: a second one holds token slots 8..15
@@ -513,11 +568,12 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
     return;
   }
   const int H = a.H, F = a.F;
-  const BlobLayout lay = blob_layout(H, F);
+  const BlobLayout lay = blob_layout(H, F, FMT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int NQ = F / kGroupElems;
   const int n_tok = __builtin_popcount(tk.tok_mask);
+  if constexpr (FMT == MOE_FMT_CB4) fill_codebook_bf16(a.src.cb, cbt);  // visible after the staging barrier
 
   auto h_row = [&](int m) {
     const int slot = m >> 1;
@@ -540,7 +596,6 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
     dcode[r] = blob + lay.down_codes + (size_t)rows[r] * kGroupBytes + 16 * g;
     dscale[r] = blob + lay.down_scales + (size_t)rows[r] * kGroupScaleBytes;
   }
-  const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   float acc[MB][RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
 #pragma unroll
@@ -554,6 +609,7 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
     const int nq = min(kDnQuadsPerPass, NQ - q0);
     uint4 cd[RGW][kDnQuadsPerPass];
     uint2 sd[RGW][kDnQuadsPerPass];
+    uint2 md[RGW][kDnQuadsPerPass];  // affine format: the records' mins
 #pragma unroll
     for (int qi = 0; qi < kDnQuadsPerPass; ++qi) {
       const int qq = min(q0 + qi, NQ - 1);
@@ -561,6 +617,8 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
       for (int r = 0; r < RGW; ++r) {
         cd[r][qi] = *(const uint4*)(dcode[r] + (size_t)qq * H * kGroupBytes);
         sd[r][qi] = *(const uint2*)(dscale[r] + (size_t)qq * H * kGroupScaleBytes);
+        if constexpr (FMT == MOE_FMT_AFFINE4)
+          md[r][qi] = *(const uint2*)(dscale[r] - lay.down_scales + lay.down_mins + (size_t)qq * H * kGroupScaleBytes);
       }
       __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
     }
@@ -583,17 +641,22 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           A[mb] = lds_fragment(smem, ROWS, F, 16 * mb + n, g, (q0 + qi) * kGroupElems + 32 * i);
-          O[mb] = mfma_bf16(A[mb], neg, zero);
+          O[mb] = fmt_c<FMT>(A[mb], zero);
         }
 #pragma unroll
         for (int r = 0; r < RGW; ++r) {
-          const bf16x8 B = codes_q136(word_at(cd[r][qi], i));
+          const bf16x8 B = fmt_b<FMT>(word_at(cd[r][qi], i), cbt);
           const float s = scale_at(sd[r][qi], i);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             const float4v D = mfma_bf16(A[mb], B, O[mb]);
 #pragma unroll
             for (int j = 0; j < NR; ++j) part[mb][r][j] = fmaf(s, D[j], part[mb][r][j]);
+            if constexpr (FMT == MOE_FMT_AFFINE4) {
+              const float m = scale_at(md[r][qi], i) * 0.0078125f;
+#pragma unroll
+              for (int j = 0; j < NR; ++j) part[mb][r][j] = fmaf(m, O[mb][j], part[mb][r][j]);
+            }
           }
         }
       }
@@ -624,14 +687,15 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) 
   }
 }
 
-template <int MAXTOK, int RGW>
+template <int MAXTOK, int RGW, int FMT = MOE_FMT_Q4_0>
 __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  __shared__ uint32_t cbt[FMT == MOE_FMT_CB4 ? 256 : 1];
   const int task = blockIdx.x / a.tiles_dn;
   const int tile = blockIdx.x - task * a.tiles_dn;
   const int n_tasks = a.ctrl[kCtrlNTasks];
   if (task >= n_tasks) return;  // task slots past the step's count neither compute nor count
-  down_body<MAXTOK, RGW>(a, task, tile, smem);
+  down_body<MAXTOK, RGW, FMT>(a, task, tile, smem, cbt);
   combine_tile_if_last(a, tile, 16 * kDnWaves * RGW, n_tasks);
 }
 
@@ -1076,13 +1140,21 @@ __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_
   combine_tile_if_last(a, tile, 16 * kPipeDnWaves * kPipeDnRGW, n_tasks);
 }
 
-// ---- dequantization check: one thread per code word, the same unpacking as the FFN kernels --
-__global__ __launch_bounds__(256) void k_debug_dequant(int H, int F, const uint8_t* __restrict__ blob,
-                                                        int matrix, float* __restrict__ out) {
-  const BlobLayout lay = blob_layout(H, F);
+// ---- dequantization check: one thread per code word, the same operands as the FFN kernels ------
+// The default and affine formats decode the word as the MFMA operand 128 + u; the codebook format
+// through the same 256-entry pair table.  Q4_0: (128 + u - 136) s; CB4: cb[u] s (both exact in
+// fp32); AFFINE4: fma(u, s, -m), the exact u s - m rounded once.
+__global__ __launch_bounds__(256) void k_debug_dequant(int H, int F, int fmt, Codebook cb,
+                                                        const uint8_t* __restrict__ blob, int matrix,
+                                                        float* __restrict__ out) {
+  __shared__ uint32_t cbt[256];
+  fill_codebook_bf16(cb, cbt);
+  __syncthreads();
+  const BlobLayout lay = blob_layout(H, F, fmt);
   const int rows = matrix == 2 ? H : F, cols = matrix == 2 ? F : H;
   const int64_t codes = matrix == 0 ? lay.gate_codes : matrix == 1 ? lay.up_codes : lay.down_codes;
   const int64_t scales = matrix == 0 ? lay.gate_scales : matrix == 1 ? lay.up_scales : lay.down_scales;
+  const int64_t mins = matrix == 0 ? lay.gate_mins : matrix == 1 ? lay.up_mins : lay.down_mins;
   const int n_words = rows * cols / 8;
   for (int wi = blockIdx.x * blockDim.x + threadIdx.x; wi < n_words; wi += gridDim.x * blockDim.x) {
     const int rec = wi >> 4, p = wi & 15, g = p >> 2, i = p & 3;  // word 4g + i of record rec
@@ -1091,12 +1163,28 @@ __global__ __launch_bounds__(256) void k_debug_dequant(int H, int F, const uint8
     const int c0 = blk * kBlock + 8 * g;
     const uint32_t w = *(const uint32_t*)(blob + codes + (size_t)wi * 4);
     const float s = fp16_bits_to_f32(*(const uint16_t*)(blob + scales + (size_t)rec * kGroupScaleBytes + 2 * i));
-    const uint4 q = __builtin_bit_cast(uint4, codes_q136(w));
+    const float m = fmt == MOE_FMT_AFFINE4
+                        ? fp16_bits_to_f32(*(const uint16_t*)(blob + mins + (size_t)rec * kGroupScaleBytes + 2 * i))
+                        : 0.f;
+    const uint4 q = fmt == MOE_FMT_CB4 ? __builtin_bit_cast(uint4, fmt_b<MOE_FMT_CB4>(w, cbt))
+                                       : __builtin_bit_cast(uint4, codes_q136(w));
     const uint32_t pr[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      out[(size_t)r * cols + c0 + 2 * j] = (bf16_lo(pr[j]) - 136.f) * s;
-      out[(size_t)r * cols + c0 + 2 * j + 1] = (bf16_hi(pr[j]) - 136.f) * s;
+      const float v0 = bf16_lo(pr[j]), v1 = bf16_hi(pr[j]);
+      float w0, w1;
+      if (fmt == MOE_FMT_CB4) {
+        w0 = v0 * s;
+        w1 = v1 * s;
+      } else if (fmt == MOE_FMT_AFFINE4) {
+        w0 = fmaf(v0 - 128.f, s, -m);
+        w1 = fmaf(v1 - 128.f, s, -m);
+      } else {
+        w0 = (v0 - 136.f) * s;
+        w1 = (v1 - 136.f) * s;
+      }
+      out[(size_t)r * cols + c0 + 2 * j] = w0;
+      out[(size_t)r * cols + c0 + 2 * j + 1] = w1;
     }
   }
 }
@@ -1139,13 +1227,16 @@ static hipError_t launch_down_pipe(DecodeArgs a, int max_tasks, int units, hipSt
   return launch_timed(kTimeDecodeDown, k_decode_down_pipe<MAXTOK, 4>, grid, threads, lds, st, a);
 }
 
-template <int MAXTOK>
+template <int MAXTOK, int FMT>
 static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipStream_t st) {
+  // the pipelined kernels and the one-token down kernel run the default format; the codebook and
+  // affine formats take the general kernels at every token count
+  constexpr bool kQ = FMT == MOE_FMT_Q4_0;
   hipError_t err = hipSuccess;
   // tasks of more than 2 tokens (bf16 x) at the covered shapes: the pipelined kernels
-  const int gu_units = (MAXTOK >= 4 && xb) ? gate_up_pipe_units(a.H) : 0;
+  const int gu_units = (kQ && MAXTOK >= 4 && xb) ? gate_up_pipe_units(a.H) : 0;
   if (gu_units) {
-    if constexpr (MAXTOK >= 4) err = launch_gate_up_pipe<MAXTOK>(a, max_tasks, gu_units, st);
+    if constexpr (kQ && MAXTOK >= 4) err = launch_gate_up_pipe<MAXTOK>(a, max_tasks, gu_units, st);
   } else {
     const int ks = (a.H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
     auto launch_rg = [&](auto rgc) {
@@ -1154,11 +1245,11 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
       a.tiles_gu = a.F / (16 * RG);
       const int grid_gu = max_tasks * a.tiles_gu;
       if (xb)
-        return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true, RG>, grid_gu, gu_threads,
+        return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, true, RG, false, FMT>, grid_gu, gu_threads,
                             (uint32_t)gate_up_lds_bytes(a.H, MAXTOK, RG * ks), st, a);
       // fp32 tokens are two A rows (hi, lo) each: 8 of them fill the MFMA's 16 rows
       if constexpr (MAXTOK <= 8)
-        return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false, RG>, grid_gu, gu_threads,
+        return launch_timed(kTimeDecodeGateUp, k_decode_gate_up<MAXTOK, false, RG, false, FMT>, grid_gu, gu_threads,
                             (uint32_t)gate_up_lds_bytes(a.H, 2 * MAXTOK, RG * ks), st, a);
       return hipErrorInvalidValue;
     };
@@ -1168,8 +1259,8 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
       err = launch_rg(std::integral_constant<int, kGuRG>{});
   }
   if (err != hipSuccess) return err;
-  const int dn_units = MAXTOK >= 4 ? down_pipe_units(a.F) : 0;
-  if (MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
+  const int dn_units = (kQ && MAXTOK >= 4) ? down_pipe_units(a.F) : 0;
+  if (kQ && MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
     // one token: output rows outermost, (task, group) items spread over the waves, no pair rows
     const int items = max_tasks * (a.F / kGroupElems);
     if (max_tasks <= 11 && items <= 16 * 5)
@@ -1177,15 +1268,25 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
     return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16, 8>, a.H / 16, 512, 0, st, a);
   }
   if (dn_units) {
-    if constexpr (MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);
+    if constexpr (kQ && MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);
   } else {
     const int dn_rows = 16 * kDnWaves * kDnRGW<MAXTOK>;
     a.tiles_dn = (a.H + dn_rows - 1) / dn_rows;
     const uint32_t dn_lds = (uint32_t)(2 * MAXTOK * (a.F + 8) * 2);
-    err = launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, kDnRGW<MAXTOK>>, max_tasks * a.tiles_dn, 64 * kDnWaves,
-                       dn_lds, st, a);
+    err = launch_timed(kTimeDecodeDown, k_decode_down<MAXTOK, kDnRGW<MAXTOK>, FMT>, max_tasks * a.tiles_dn,
+                       64 * kDnWaves, dn_lds, st, a);
   }
   return err;
+}
+
+template <int FMT>
+static hipError_t launch_decode_ffn_fmt(DecodeArgs a, int T, int max_tasks, bool xb, hipStream_t st) {
+  if (T <= 1) return launch_decode_ffn_t<1, FMT>(a, max_tasks, xb, st);
+  if (T <= 2) return launch_decode_ffn_t<2, FMT>(a, max_tasks, xb, st);
+  if (T <= 4) return launch_decode_ffn_t<4, FMT>(a, max_tasks, xb, st);
+  if (T <= 8) return launch_decode_ffn_t<8, FMT>(a, max_tasks, xb, st);
+  if (!xb) return hipErrorInvalidValue;  // fp32 tokens take two A rows each: at most 8 (host-checked)
+  return launch_decode_ffn_t<16, FMT>(a, max_tasks, xb, st);
 }
 
 hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_tasks, const ExpertSource& src,
@@ -1210,12 +1311,9 @@ hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_t
   a.tile_done = ctrl + kCtrlTileDone;
   const bool xb = x_dtype == MOE_BF16;
   static_assert(kTaskTok == kMaxDecodeTok, "a decode task holds every token of the step that chose its expert");
-  if (T <= 1) return launch_decode_ffn_t<1>(a, max_tasks, xb, st);
-  if (T <= 2) return launch_decode_ffn_t<2>(a, max_tasks, xb, st);
-  if (T <= 4) return launch_decode_ffn_t<4>(a, max_tasks, xb, st);
-  if (T <= 8) return launch_decode_ffn_t<8>(a, max_tasks, xb, st);
-  if (!xb) return hipErrorInvalidValue;  // fp32 tokens take two A rows each: at most 8 (host-checked)
-  return launch_decode_ffn_t<16>(a, max_tasks, xb, st);
+  if (src.fmt == MOE_FMT_CB4) return launch_decode_ffn_fmt<MOE_FMT_CB4>(a, T, max_tasks, xb, st);
+  if (src.fmt == MOE_FMT_AFFINE4) return launch_decode_ffn_fmt<MOE_FMT_AFFINE4>(a, T, max_tasks, xb, st);
+  return launch_decode_ffn_fmt<MOE_FMT_Q4_0>(a, T, max_tasks, xb, st);
 }
 
 bool decode_select1_supported(int H, int F, int k, int n_shared, int E) {
@@ -1257,11 +1355,12 @@ hipError_t launch_decode_ffn_select1(int H, int F, int k, int n_shared, int E, c
   return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16>, H / 16, 1024, 0, st, a);
 }
 
-hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st) {
+hipError_t launch_debug_dequant(int H, int F, int fmt, const Codebook& cb, const uint8_t* blob, int matrix, float* out,
+                                hipStream_t st) {
   const int n_words = H * F / 8;
   int grid = (n_words + 255) / 256;
   if (grid > 2048) grid = 2048;
-  k_debug_dequant<<<grid, 256, 0, st>>>(H, F, blob, matrix, out);
+  k_debug_dequant<<<grid, 256, 0, st>>>(H, F, fmt, cb, blob, matrix, out);
   return hipGetLastError();
 }
 

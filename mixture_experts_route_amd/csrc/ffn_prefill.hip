@@ -113,6 +113,41 @@ MOE_DEV half8 dequant_word_k(uint32_t w, half2v s2, const DequantConsts& c) {
 
 MOE_DEV uint32_t word_of(const uint4& c, int d) { return d == 0 ? c.x : d == 1 ? c.y : d == 2 ? c.z : c.w; }
 
+// The other weight formats, one rounding to fp16 each:
+//   affine:   fp16(u * s - m) by one fp16 fma on the exact u (fp16 1024 + u minus 1024);
+//   codebook: fp16(cb[u] * s), cb[u] exact in fp16, from a 256-entry table of fp16 pairs indexed by
+//             a code pair (the pair j of a word: codes in bits 4j and 16 + 4j).
+MOE_DEV half8 dequant_word_affine(uint32_t w, half2v s2, half2v nm2) {
+  const half2v k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  half8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t = ((w >> (4 * j)) & 0x000F000Fu) | 0x64006400u;  // fp16 (1024 + u) pair
+    const half2v u = __builtin_bit_cast(half2v, t) - k1024;           // u, exact
+    const half2v v = __builtin_elementwise_fma(u, s2, nm2);           // fp16(u * s - m)
+    r[2 * j] = v.x;
+    r[2 * j + 1] = v.y;
+  }
+  return r;
+}
+MOE_DEV half8 dequant_word_cb(uint32_t w, half2v s2, const uint32_t* cbt16) {
+  half8 r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half2v v = __builtin_bit_cast(half2v, cbt16[code_pair_index(w, j)]) * s2;
+    r[2 * j] = v.x;
+    r[2 * j + 1] = v.y;
+  }
+  return r;
+}
+// The fp16 pair table of the codebook: entry (c1 << 4 | c0) = (fp16 cb[c0], fp16 cb[c1]).
+MOE_DEV void fill_codebook_f16(const Codebook& cb, uint32_t* cbt16) {
+  for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+    const _Float16 lo = (_Float16)(float)codebook_value(cb, i & 15), hi = (_Float16)(float)codebook_value(cb, i >> 4);
+    cbt16[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+  }
+}
+
 
 MOE_DEV void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -125,8 +160,9 @@ MOE_DEV void report_range(bool bad, int32_t* ctrl) {
 
 // RROWS: rows of a router work (the router's weights are read once per work: longer calls take
 // taller works)
-template <int MODE, int RROWS = kRouterTileRows>
+template <int MODE, int RROWS = kRouterTileRows, int FMT = MOE_FMT_Q4_0>
 __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
+  __shared__ uint32_t cbt16[FMT == MOE_FMT_CB4 ? 256 : 1];
   // 16-row subtiles per work: a 128-row item, or a router work
   constexpr int MSUB = MODE == kRouter ? RROWS / 16 : kMSub;
   // A tile: 128 rows x 128 16-bit elements per stage, two stages.  16-byte chunk c of row r is
@@ -184,7 +220,7 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
       soff[s] = 0;
     }
   } else {
-    const BlobLayout lay = blob_layout(H, F);
+    const BlobLayout lay = blob_layout(H, F, FMT);
     bbase = blob;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -231,6 +267,13 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   constexpr int kBW = MODE == kRouter ? 4 : 1;  // 16-byte loads per subtile per chunk
   uint4 braw[4][kBW];
   uint2 bsc[4];  // the four block scales (fp16) of the chunk
+  uint2 bmn[4];  // affine format: the four block mins
+  // distance from a scale record to its min record (the min planes follow the scale planes)
+  int64_t min_from_scale = 0;
+  if constexpr (MODE != kRouter && FMT == MOE_FMT_AFFINE4) {
+    const BlobLayout lay = blob_layout(H, F, FMT);
+    min_from_scale = MODE == kDown ? lay.down_mins - lay.down_scales : lay.gate_mins - lay.gate_scales;
+  }
   auto load_b = [&](int kc) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -243,9 +286,12 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
       } else {
         braw[s][0] = *(const uint4*)(bbase + coff[s] + (size_t)kc * wrows * kGroupBytes + 16 * g);
         bsc[s] = *(const uint2*)(bbase + soff[s] + (size_t)kc * wrows * kGroupScaleBytes);
+        if constexpr (FMT == MOE_FMT_AFFINE4)
+          bmn[s] = *(const uint2*)(bbase + soff[s] + min_from_scale + (size_t)kc * wrows * kGroupScaleBytes);
       }
     }
   };
+  if constexpr (MODE != kRouter && FMT == MOE_FMT_CB4) fill_codebook_f16(a.src.cb, cbt16);  // before the barrier
 
   float4v acc[MSUB][4];
 #pragma unroll
@@ -261,12 +307,13 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
   for (int kc = 0; kc < nk; ++kc) {
     uint16_t* Ab = (kc & 1) ? As1 : As0;
     uint4 bcur[4][kBW];
-    uint2 scur[4];
+    uint2 scur[4], mcur[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int d = 0; d < kBW; ++d) bcur[s][d] = braw[s][d];
       scur[s] = bsc[s];
+      if constexpr (FMT == MOE_FMT_AFFINE4) mcur[s] = bmn[s];
     }
     if (kc + 1 < nk) {
       issue_a(kc + 1, (kc & 1) ? As0 : As1);
@@ -294,7 +341,15 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
         for (int s = 0; s < 4; ++s) {
           const uint32_t sw = d < 2 ? scur[s].x : scur[s].y;
           const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)((d & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-          bf[s] = dequant_word(word_of(bcur[s][0], d), (half2v){sv, sv});
+          if constexpr (FMT == MOE_FMT_AFFINE4) {
+            const uint32_t mw = d < 2 ? mcur[s].x : mcur[s].y;
+            const _Float16 mv = __builtin_bit_cast(_Float16, (uint16_t)((d & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
+            bf[s] = dequant_word_affine(word_of(bcur[s][0], d), (half2v){sv, sv}, (half2v){-mv, -mv});
+          } else if constexpr (FMT == MOE_FMT_CB4) {
+            bf[s] = dequant_word_cb(word_of(bcur[s][0], d), (half2v){sv, sv}, cbt16);
+          } else {
+            bf[s] = dequant_word(word_of(bcur[s][0], d), (half2v){sv, sv});
+          }
         }
 #pragma unroll
         for (int i = 0; i < MSUB; ++i) {
@@ -385,7 +440,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   const int H = a.H, F = a.F;
   constexpr int K = NK * kKC;
   const int wrows = MODE == kDown ? H : F;
-  const BlobLayout lay = blob_layout(H, F);
+  const BlobLayout lay = blob_layout(H, F);  // (the default format: the codes and scales its kernels read)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int ms = (it.rows + 15) >> 4;
@@ -620,14 +675,25 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   a.a16 = (const uint16_t*)b.x16;
   a.row_tok = g.row_tok;
   a.h_out = b.h16;
-  if (H == 16 * kKC && F % (kPNTile / 2) == 0) {
+  // (the codebook and affine formats run on the general kernel)
+  const bool q4 = src.fmt == MOE_FMT_Q4_0;
+  auto general = [&](auto mode_c) {
+    constexpr int M = decltype(mode_c)::value;
+    const int timed = M == kGateUp ? kTimePrefillGateUp : kTimePrefillDown;
+    if (src.fmt == MOE_FMT_CB4)
+      return launch_timed(timed, k_expert_gemm<M, kRouterTileRows, MOE_FMT_CB4>, round8(a.n_works), 256, 0, st, a);
+    if (src.fmt == MOE_FMT_AFFINE4)
+      return launch_timed(timed, k_expert_gemm<M, kRouterTileRows, MOE_FMT_AFFINE4>, round8(a.n_works), 256, 0, st, a);
+    return launch_timed(timed, k_expert_gemm<M>, round8(a.n_works), 256, 0, st, a);
+  };
+  if (q4 && H == 16 * kKC && F % (kPNTile / 2) == 0) {
     a.n_ntiles = F / (kPNTile / 2);
     a.n_works = max_items * a.n_ntiles;
     err = launch_timed(kTimePrefillGateUp, k_expert_gemm_pipe<kGateUp, 16>, round8(a.n_works), 64 * kPWaves, 0, st, a);
   } else {
     a.n_ntiles = F / (kNTileW / 2);
     a.n_works = max_items * a.n_ntiles;
-    err = launch_timed(kTimePrefillGateUp, k_expert_gemm<kGateUp>, round8(a.n_works), 256, 0, st, a);
+    err = general(std::integral_constant<int, kGateUp>{});
   }
   if (err != hipSuccess) return err;
 
@@ -635,14 +701,14 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   a.a16 = (const uint16_t*)b.h16;
   a.row_w = g.row_w;
   a.y16_out = b.y_rows;
-  if (F == 6 * kKC && H % kPNTile == 0) {
+  if (q4 && F == 6 * kKC && H % kPNTile == 0) {
     a.n_ntiles = H / kPNTile;
     a.n_works = max_items * a.n_ntiles;
     err = launch_timed(kTimePrefillDown, k_expert_gemm_pipe<kDown, 6>, round8(a.n_works), 64 * kPWaves, 0, st, a);
   } else {
     a.n_ntiles = H / kNTileW;
     a.n_works = max_items * a.n_ntiles;
-    err = launch_timed(kTimePrefillDown, k_expert_gemm<kDown>, round8(a.n_works), 256, 0, st, a);
+    err = general(std::integral_constant<int, kDown>{});
   }
   if (err != hipSuccess) return err;
 

@@ -83,6 +83,8 @@ struct ExpertSource {
   int32_t n_slots;
   const int32_t* table;  // may be null
   const uint8_t* shared_blob;
+  int32_t fmt;           // moe_format
+  Codebook cb;           // MOE_FMT_CB4
 };
 
 // Prefill: one grouped-GEMM work item = up to kTileRows consecutive rows of one bucket
@@ -159,7 +161,8 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
 hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const float* bias, int T, int E, int H,
                               float* logits, hipStream_t st);
 
-hipError_t launch_debug_dequant(int H, int F, const uint8_t* blob, int matrix, float* out, hipStream_t st);
+hipError_t launch_debug_dequant(int H, int F, int fmt, const Codebook& cb, const uint8_t* blob, int matrix, float* out,
+                                hipStream_t st);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 
 }  // namespace moe

@@ -38,7 +38,11 @@ EXPORTS = [
 
 class moe_dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("ffn", ctypes.c_int32), ("n_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("block", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("n_shared", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("format", ctypes.c_int32), ("codebook", ctypes.c_int8 * 16)]
+
+
+MOE_FMT_Q4_0, MOE_FMT_CB4, MOE_FMT_AFFINE4 = 0, 1, 2
 
 
 class moe_layer_weights(ctypes.Structure):
@@ -127,8 +131,10 @@ def _stream(stream=None):
     return stream.cuda_stream
 
 
-def dims(hidden: int, ffn: int, n_experts: int, top_k: int, n_shared: int = 1, block: int = 32) -> moe_dims:
-    return moe_dims(hidden, ffn, n_experts, top_k, n_shared, block)
+def dims(hidden: int, ffn: int, n_experts: int, top_k: int, n_shared: int = 1, block: int = 32, format: int = 0,
+         codebook=None) -> moe_dims:
+    cb = (ctypes.c_int8 * 16)(*([int(v) for v in codebook] if codebook is not None else [0] * 16))
+    return moe_dims(hidden, ffn, n_experts, top_k, n_shared, block, format, cb)
 
 
 def dtype_code(t) -> int:

@@ -53,6 +53,25 @@ KINDS = {
 
 BLOCK = 32
 
+# weight formats of the library (identifiers only; the values they stand for are the library's
+# and the oracle's business): 0 = 4-bit codes with a block scale, 1 = codes into a 16-entry
+# codebook with a block scale, 2 = codes with a block scale and a block min
+FMT_Q4_0, FMT_CB4, FMT_AFFINE4 = 0, 1, 2
+# scale and min laws per format, so that the weights of every format have magnitudes like the
+# first one's (its codes stand for -8..7; a codebook entry is up to 127; affine codes are 0..15
+# less a min): the layer's outputs then stay in the same range
+SCALE_SIGMA = {FMT_Q4_0: 0.02, FMT_CB4: 0.00125, FMT_AFFINE4: 0.02}
+MIN_SIGMA = 0.15
+
+
+def synthetic_codebook():
+    """16 signed 8-bit values, ascending and unevenly spaced: 127 * z_i / z_15 rounded, with z_i
+    the normal quantile at (i + 0.5) / 16 (a small set of values, denser near zero)."""
+    from statistics import NormalDist
+
+    z = [NormalDist().inv_cdf((i + 0.5) / 16) for i in range(16)]
+    return [int(round(127 * v / z[15])) for v in z]
+
 
 # ----------------------------------------------------------------------------
 # keys and the SplitMix64 stream
@@ -217,9 +236,9 @@ def blob_sections(H: int, F: int):
     return out
 
 
-def blob_bytes(H: int, F: int) -> int:
+def blob_bytes(H: int, F: int, fmt: int = FMT_Q4_0) -> int:
     name, off, sz = blob_sections(H, F)[-1]
-    return off + sz
+    return off + sz + (3 * F * H // BLOCK * 2 if fmt == FMT_AFFINE4 else 0)
 
 
 def _blob_counts(H: int, F: int):
@@ -229,33 +248,43 @@ def _blob_counts(H: int, F: int):
     return n_code_bytes, n_scales
 
 
-def expert_blob_np(key: int, H: int, F: int, scale_sigma: float = 0.02) -> np.ndarray:
-    """One expert blob (uint8) from stream ``key``."""
+def expert_blob_np(key: int, H: int, F: int, scale_sigma: float | None = None, fmt: int = FMT_Q4_0) -> np.ndarray:
+    """One expert blob (uint8) from stream ``key``: codes, scales and (affine format) mins."""
     nb, ns = _blob_counts(H, F)
+    sigma = SCALE_SIGMA[fmt] if scale_sigma is None else scale_sigma
     w = words_np(key, 0, nb // 8)
     codes = w.view(np.uint8)  # little-endian bytes of each word
     u = _u32_np(key, nb // 8, ns)
-    scales = _lookup_np(_halfnormal_fp16_table(float(scale_sigma)), u).astype(np.uint16)
-    return np.concatenate([codes, scales.view(np.uint8)])
+    scales = _lookup_np(_halfnormal_fp16_table(float(sigma)), u).astype(np.uint16)
+    parts = [codes, scales.view(np.uint8)]
+    if fmt == FMT_AFFINE4:
+        um = _u32_np(key, nb // 8 + (ns + 1) // 2, ns)
+        parts.append(_lookup_np(_halfnormal_fp16_table(MIN_SIGMA), um).astype(np.uint16).view(np.uint8))
+    return np.concatenate(parts)
 
 
-def expert_blobs_torch(keys, H: int, F: int, out, scale_sigma: float = 0.02):
+def expert_blobs_torch(keys, H: int, F: int, out, scale_sigma: float | None = None, fmt: int = FMT_Q4_0):
     """Write blob ``keys[i]`` into row ``i`` of the uint8 device tensor ``out``.
 
-    ``out`` is ``[len(keys)][stride]`` with ``stride >= blob_bytes(H, F)``; bytes
+    ``out`` is ``[len(keys)][stride]`` with ``stride >= blob_bytes(H, F, fmt)``; bytes
     past the blob are left as they are.  Bit-identical to :func:`expert_blob_np`.
     """
     import torch
 
     nb, ns = _blob_counts(H, F)
+    sigma = SCALE_SIGMA[fmt] if scale_sigma is None else scale_sigma
     dev = out.device
+
+    def fp16_draws(key, start, sig):
+        c = _lookup_torch(_halfnormal_fp16_table(float(sig)), _u32_torch(key, start, ns, dev))
+        return torch.where(c >= 0x8000, c - 0x10000, c).to(torch.int16).view(torch.uint8)
+
     for i, key in enumerate(keys):
         w = words_torch(key, 0, nb // 8, dev)
         out[i, :nb].copy_(w.view(torch.uint8))
-        u = _u32_torch(key, nb // 8, ns, dev)
-        sc = _lookup_torch(_halfnormal_fp16_table(float(scale_sigma)), u)
-        sc = torch.where(sc >= 0x8000, sc - 0x10000, sc).to(torch.int16)
-        out[i, nb:nb + 2 * ns].copy_(sc.view(torch.uint8))
+        out[i, nb:nb + 2 * ns].copy_(fp16_draws(key, nb // 8, sigma))
+        if fmt == FMT_AFFINE4:
+            out[i, nb + 2 * ns:nb + 4 * ns].copy_(fp16_draws(key, nb // 8 + (ns + 1) // 2, MIN_SIGMA))
     return out
 
 

@@ -14,8 +14,8 @@ TINY = dict(H=256, F=128, E=8, k=2, n_shared=1, cfg=1, x_sigma=1.0, r_sigma=0.1,
 MODEL = dict(H=2048, F=768, E=512, k=10, n_shared=1, cfg=2, x_sigma=1.0, r_sigma=0.02, x_f32=False, r_f32=False)
 
 
-def slot_stride(H, F):
-    b = S.blob_bytes(H, F)
+def slot_stride(H, F, fmt=0):
+    b = S.blob_bytes(H, F, fmt)
     return (b + 4095) // 4096 * 4096
 
 
@@ -32,7 +32,9 @@ class Layer:
         H, F, E = spec["H"], spec["F"], spec["E"]
         self.H, self.F, self.E, self.k, self.n_shared = H, F, E, spec["k"], spec["n_shared"]
         self.seed, self.cfg, self.layer = seed, spec["cfg"], layer
-        self.stride = slot_stride(H, F)
+        self.fmt = spec.get("fmt", S.FMT_Q4_0)
+        self.codebook = S.synthetic_codebook() if self.fmt == S.FMT_CB4 else None
+        self.stride = slot_stride(H, F, self.fmt)
         self.n_slots = n_slots if n_slots is not None else E
         # slot_of[e] = slot of expert e (-1 = not resident); default identity
         self.slot_of = np.arange(E) if slot_of is None else np.asarray(slot_of)
@@ -40,14 +42,15 @@ class Layer:
         experts = [e for e in range(E) if self.slot_of[e] >= 0]
         keys = [self.key(e) for e in experts]
         tmp = torch.empty((len(keys), self.stride), dtype=torch.uint8, device=device)
-        S.expert_blobs_torch(keys, H, F, tmp)
+        S.expert_blobs_torch(keys, H, F, tmp, fmt=self.fmt)
         idx = torch.as_tensor([int(self.slot_of[e]) for e in experts], device=device, dtype=torch.long)
         self.arena[idx] = tmp
         del tmp
         self.shared = None
         if self.n_shared:
             self.shared = torch.zeros((self.stride,), dtype=torch.uint8, device=device)
-            S.expert_blobs_torch([S.stream_key(seed, self.cfg, "shared", layer, 0)], H, F, self.shared.view(1, -1))
+            S.expert_blobs_torch([S.stream_key(seed, self.cfg, "shared", layer, 0)], H, F, self.shared.view(1, -1),
+                                 fmt=self.fmt)
         rkey = S.stream_key(seed, self.cfg, "router", layer, 0)
         if spec["r_f32"]:
             self.router_np = S.f32_normal_np(rkey, (E, H), spec["r_sigma"])
@@ -67,12 +70,13 @@ class Layer:
         return S.stream_key(self.seed, self.cfg, "blob", self.layer, e)
 
     def blob_np(self, e):
-        return S.expert_blob_np(self.key(e), self.H, self.F)
+        return S.expert_blob_np(self.key(e), self.H, self.F, fmt=self.fmt)
 
     def shared_np(self):
         if not self.n_shared:
             return None
-        return S.expert_blob_np(S.stream_key(self.seed, self.cfg, "shared", self.layer, 0), self.H, self.F)
+        return S.expert_blob_np(S.stream_key(self.seed, self.cfg, "shared", self.layer, 0), self.H, self.F,
+                                fmt=self.fmt)
 
     def table_tensor(self, device):
         import torch
@@ -92,7 +96,7 @@ class Layer:
 
     def oracle(self, x64):
         return O.moe_layer(x64, self.router_np.astype(np.float64), self.bias_np, self.k, self.blob_np,
-                           self.shared_np(), self.H, self.F)
+                           self.shared_np(), self.H, self.F, self.fmt, self.codebook)
 
     def native_weights(self):
         from mixture_experts_route_amd import native as N
@@ -102,7 +106,7 @@ class Layer:
     def dims(self):
         from mixture_experts_route_amd import native as N
 
-        return N.dims(self.H, self.F, self.E, self.k, self.n_shared)
+        return N.dims(self.H, self.F, self.E, self.k, self.n_shared, format=self.fmt, codebook=self.codebook)
 
 
 def near_tie_tokens(logits64: np.ndarray, k: int, gap: float = 1e-4) -> np.ndarray:

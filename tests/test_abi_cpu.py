@@ -250,3 +250,15 @@ def test_profile_seed_matches_the_oracle(N):
     c = (ctypes.c_int64 * 4)(1, 2, 3, 4)
     out = (ctypes.c_int32 * 8)()
     assert f(c, 4, 5, out) == N.MOE_EINVAL and f(c, 4, 0, out) == N.MOE_EINVAL and f(None, 4, 2, out) == N.MOE_EINVAL
+
+
+def test_format_sizes_and_refusal(N):
+    """Blob sizes per weight format (the affine format adds three fp16 min planes); an unknown
+    format is refused by name (MOE_EUNSUPPORTED) before anything else."""
+    assert N.moe_expert_blob_bytes(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_CB4)) == 2_654_208
+    assert N.moe_expert_blob_bytes(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_AFFINE4)) == 2_654_208 + 3 * 98_304
+    d = N.dims(2048, 768, 512, 10, 1, format=3)
+    assert N.moe_expert_blob_bytes(d) == 0
+    f = N.raw("moe_route")
+    assert f(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, 1 << 20, 1 << 30, None) == \
+        N.MOE_EUNSUPPORTED

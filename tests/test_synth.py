@@ -91,3 +91,25 @@ def test_batched_torch_blobs_equal_single():
     S.expert_blobs_torch_batch(keys, H, F, b, batch=2)
     assert torch.equal(a, b)
     assert np.array_equal(b[3, :S.blob_bytes(H, F)].numpy(), S.expert_blob_np(keys[3], H, F))
+
+
+def test_format_blobs_numpy_equals_torch():
+    """The codebook and affine formats' blobs: the numpy and torch generators give the same bytes;
+    the affine blob's min planes follow the scales and draw the min law."""
+    import numpy as np
+    import torch
+
+    for fmt in (S.FMT_CB4, S.FMT_AFFINE4):
+        keys = [S.stream_key(0, 1, "blob", 0, e) for e in range(3)]
+        n = S.blob_bytes(256, 128, fmt)
+        out = torch.zeros((3, n + 64), dtype=torch.uint8)
+        S.expert_blobs_torch(keys, 256, 128, out, fmt=fmt)
+        for i, k in enumerate(keys):
+            assert np.array_equal(out[i, :n].numpy(), S.expert_blob_np(k, 256, 128, fmt=fmt))
+        assert (out[:, n:] == 0).all()
+    b = S.expert_blob_np(S.stream_key(0, 1, "blob", 0, 9), 2048, 768, fmt=S.FMT_AFFINE4)
+    assert len(b) == 2_654_208 + 3 * 98_304
+    mins = b[2_654_208:].view(np.float16).astype(np.float64)
+    assert (mins >= 0).all() and abs(mins.mean() / (S.MIN_SIGMA * np.sqrt(2 / np.pi)) - 1) < 0.02
+    cb = S.synthetic_codebook()
+    assert len(cb) == 16 and cb == sorted(cb) and len(set(cb)) == 16 and max(map(abs, cb)) == 127

@@ -201,6 +201,32 @@ MOE_API int moe_check_device_error(void* ws, void* stream, int32_t* bits_out);
  * not for concurrent use from several threads. */
 MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop_event);
 
+/* Prefill plan (halogen README, "Measured": the engine's GEMM plan carries choices measured on
+ * the hardware).  How a prefill call of n_tokens runs: the rows per grouped-GEMM work item (64 or
+ * 128), the grouped-GEMM kernel of the gate/up and of the down projection, and the router GEMM's
+ * rows per work (32 or 64).  The library takes the plan from a table measured on MI355X per shape
+ * and token range (tune.py in the package writes it), else a default.  Kernels:
+ *   MOE_GEMM_PIPE128      8 waves x 512 weight rows, up to 128-row items, weights 1 chunk ahead;
+ *   MOE_GEMM_PIPE64_DEEP  the same with up to 64-row items and weights 3 chunks ahead;
+ *   MOE_GEMM_GENERAL      4 waves x 256 weight rows, every width and weight format.
+ * The pipelined kernels exist for the default format at the model's reduction widths (gate/up over
+ * H = 2048, down over F = 768); elsewhere the general kernel runs whatever the plan says. */
+enum moe_gemm_kernel { MOE_GEMM_PIPE128 = 0, MOE_GEMM_PIPE64_DEEP = 1, MOE_GEMM_GENERAL = 2 };
+typedef struct moe_prefill_plan {
+  int32_t item_rows;
+  int32_t gate_up_kernel;
+  int32_t down_kernel;
+  int32_t router_rows;
+} moe_prefill_plan;
+
+/* The plan a prefill call of n_tokens with these dims runs (the kernels as they will run). */
+MOE_API int moe_prefill_plan_get(const moe_dims* dims, int32_t n_tokens, moe_prefill_plan* out);
+
+/* Tuning aid: every prefill call of the process runs `plan` (validated: item_rows 64 or 128,
+ * MOE_GEMM_PIPE64_DEEP only with 64, router_rows 32 or 64; else MOE_EINVAL) until the next call;
+ * NULL returns to the table.  Process-wide, not for concurrent use from several threads. */
+MOE_API int moe_debug_force_prefill_plan(const moe_prefill_plan* plan_or_null);
+
 /* Test entry point: dequantizes matrix `matrix` (0 = gate [F][H], 1 = up [F][H],
  * 2 = down [H][F]) of the expert blob at `blob` into fp32 `out` (row-major), exactly
  * (q * scale is exact in fp32).  Follows halogen README "Bring your own GGUF" (a small

@@ -94,6 +94,51 @@ static int layer_decode_limit(const moe_dims* d, int x_dtype, int r_dtype) {
   return a < b ? a : b;
 }
 
+// ---- prefill plans: the tuned table, a default, and a process-wide override for the tuner -------
+struct TunedPlanRow {
+  int H, F, E, k, fmt, t_lo, t_hi;
+  PrefillPlan plan;
+};
+static const TunedPlanRow kTunedPlans[] = {
+#include "tuned_plans.inc"
+    {0, 0, 0, 0, 0, 0, 0, {0, 0, 0, 0}}  // end marker
+};
+
+static PrefillPlan g_forced_plan;
+static bool g_plan_forced = false;
+
+// Without a table row: 128-row items, the pipelined kernels where they are built, the router GEMM
+// with 32-row works up to 16K tokens and 64-row works above (half the router-weight re-reads,
+// still thousands of works).
+static PrefillPlan default_plan(int T) {
+  PrefillPlan p;
+  p.item_rows = 128;
+  p.gate_up = p.down = kGemmPipe128;
+  p.router_rows = T > 16384 ? 64 : 32;
+  return p;
+}
+
+static PrefillPlan plan_for(const moe_dims* d, int T) {
+  if (g_plan_forced) return g_forced_plan;
+  for (const TunedPlanRow& r : kTunedPlans) {
+    if (r.H == 0) break;
+    if (r.H == d->hidden && r.F == d->ffn && r.E == d->n_experts && r.k == d->top_k && r.fmt == d->format &&
+        T >= r.t_lo && T <= r.t_hi)
+      return r.plan;
+  }
+  return default_plan(T);
+}
+
+static int check_plan(const moe_prefill_plan* p) {
+  if (p->item_rows != 64 && p->item_rows != 128) return MOE_EINVAL;
+  if (p->router_rows != 32 && p->router_rows != 64) return MOE_EINVAL;
+  for (int k : {p->gate_up_kernel, p->down_kernel}) {
+    if (k < kGemmPipe128 || k > kGemmGeneral) return MOE_EINVAL;
+    if (k == kGemmPipe64Deep && p->item_rows != 64) return MOE_EINVAL;
+  }
+  return MOE_OK;
+}
+
 static int check_dims(const moe_dims* d) {
   if (!d) return MOE_EINVAL;
   if (d->hidden <= 0 || d->ffn <= 0 || d->n_experts <= 0 || d->top_k <= 0) return MOE_EINVAL;
@@ -164,7 +209,7 @@ static int do_route(const moe_dims* d, const void* x, int x_dtype, int T, const 
   if (T > route_decode_limit(x_dtype, r_dtype)) {
     // long batches: router GEMM on MFMA (bf16 x bf16, fp32 accumulation)
     if (x_dtype != MOE_BF16 || r_dtype != MOE_BF16 || d->hidden % 128) return MOE_EUNSUPPORTED;
-    rc = hip_status(launch_router_gemm(x, router, bias, T, d->n_experts, d->hidden, lg, st));
+    rc = hip_status(launch_router_gemm(x, router, bias, T, d->n_experts, d->hidden, lg, plan_for(d, T).router_rows, st));
     if (rc) return rc;
     return hip_status(launch_topk(lg, T, d->n_experts, d->top_k, ids, w, ctrl_of(ws), st));
   }
@@ -244,14 +289,16 @@ static int do_prefill_ffn(const moe_dims* d, const moe_layer_weights* w, const i
   const WsLayout L = ws_layout(d, T);
   int32_t* ctrl = ctrl_of(ws);
   const GroupBuffers g = group_buffers(L, ws);
-  int rc = hip_status(launch_group(ids, topk_w, T, d->top_k, d->n_experts, d->n_shared, g, ctrl, nullptr, nullptr, st));
+  const PrefillPlan plan = plan_for(d, T);
+  int rc = hip_status(
+      launch_group(ids, topk_w, T, d->top_k, d->n_experts, d->n_shared, g, ctrl, nullptr, nullptr, st, plan.item_rows));
   if (rc) return rc;
   PrefillBuffers b;
   b.x16 = at<_Float16>(ws, L.x16);
   b.h16 = at<_Float16>(ws, L.h16);
   b.y_rows = at<_Float16>(ws, L.y_rows);
   return hip_status(launch_prefill_ffn(d->hidden, d->ffn, d->top_k, d->n_experts, d->n_shared, T, source_of(d, w, table),
-                                       x, g, b, y, ctrl, st));
+                                       x, g, b, y, ctrl, plan, st));
 }
 
 // Host-side validation of a whole-layer call (everything but the workspace).
@@ -330,6 +377,35 @@ MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop
   g_kernel_events.which = which;
   g_kernel_events.start = (hipEvent_t)start_event;
   g_kernel_events.stop = (hipEvent_t)stop_event;
+  return MOE_OK;
+}
+
+MOE_API int moe_prefill_plan_get(const moe_dims* dims, int32_t n_tokens, moe_prefill_plan* out) {
+  int rc = check_dims(dims);
+  if (rc) return rc;
+  if (!out || n_tokens < 1) return MOE_EINVAL;
+  const PrefillPlan p = plan_for(dims, n_tokens);
+  out->item_rows = p.item_rows;
+  out->gate_up_kernel =
+      prefill_kernel_fits(p.gate_up, 0, dims->hidden, dims->ffn, dims->format, p.item_rows) ? p.gate_up : kGemmGeneral;
+  out->down_kernel =
+      prefill_kernel_fits(p.down, 1, dims->hidden, dims->ffn, dims->format, p.item_rows) ? p.down : kGemmGeneral;
+  out->router_rows = p.router_rows;
+  return MOE_OK;
+}
+
+MOE_API int moe_debug_force_prefill_plan(const moe_prefill_plan* plan_or_null) {
+  if (!plan_or_null) {
+    g_plan_forced = false;
+    return MOE_OK;
+  }
+  const int rc = check_plan(plan_or_null);
+  if (rc) return rc;
+  g_forced_plan.item_rows = plan_or_null->item_rows;
+  g_forced_plan.gate_up = plan_or_null->gate_up_kernel;
+  g_forced_plan.down = plan_or_null->down_kernel;
+  g_forced_plan.router_rows = plan_or_null->router_rows;
+  g_plan_forced = true;
   return MOE_OK;
 }
 

@@ -413,16 +413,21 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
 // its MFMA work (written to LDS one chunk after its loads were issued, so the wait is for those
 // loads alone); weights go through a 3-slot register ring, 2 chunks ahead.  One barrier per chunk
 // and no wait for all loads: the weight stream never drains inside a work.
+// Two shapes of it (a tuning choice, see the plan table): items of up to 128 rows with the weights
+// 1 chunk ahead (MSUB 8, BD 2), or items of up to 64 rows, whose accumulators take half the registers,
+// with the weights 3 chunks ahead (MSUB 4, BD 4): three times the weight bytes in flight per CU for
+// the short items of a skewed routing, at the price of twice the weight reads of long groups.
 constexpr int kPWaves = 8;
 constexpr int kPNTile = 64 * kPWaves;                       // weight rows per workgroup
-constexpr int kPAPer = kTileRows * (kKC / 8) / (64 * kPWaves);  // A 16-byte pieces per thread per chunk
-static_assert(kPAPer * 64 * kPWaves == kTileRows * (kKC / 8), "A pieces split evenly");
 
-template <int MODE, int NK>
+template <int MODE, int NK, int MSUB = kMSub, int BD = 2>
 __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a) {
   static_assert(MODE == kGateUp || MODE == kDown, "expert GEMMs only");
-  static_assert(NK >= 3, "pipeline depth");
-  __shared__ __attribute__((aligned(1024))) uint16_t As[3][kTileRows * kKC];
+  static_assert(NK >= 3 && NK >= BD, "pipeline depth");
+  static_assert(BD >= 2 && MSUB >= 1 && MSUB <= kMSub, "tile shape");
+  constexpr int kPAPer = MSUB * 16 * (kKC / 8) / (64 * kPWaves);  // A 16-byte pieces per thread per chunk
+  static_assert(kPAPer >= 1 && kPAPer * 64 * kPWaves == MSUB * 16 * (kKC / 8), "A pieces split evenly");
+  __shared__ __attribute__((aligned(1024))) uint16_t As[3][MSUB * 16 * kKC];
 
   const int n_works = min(*a.n_items * a.n_ntiles, a.n_works);
   const int per_xcd = (n_works + 7) >> 3;
@@ -465,8 +470,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   }
   // record (kc, row): codes at 64 (kc R + row), scales at 8 (kc R + row)
   const int voff_c = row0 * kGroupBytes + 16 * g, voff_s = row0 * kGroupScaleBytes;
-  u32x4 bc[2][4];
-  u32x2 bs[2][4];
+  u32x4 bc[BD][4];
+  u32x2 bs[BD][4];
   auto load_b = [&](auto slot_c, int kc) {
     constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
@@ -507,19 +512,19 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
     asm volatile("" ::: "memory");
   };
 
-  float4v acc[kMSub][4];
+  float4v acc[MSUB][4];
 #pragma unroll
-  for (int i = 0; i < kMSub; ++i)
+  for (int i = 0; i < MSUB; ++i)
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[i][s] = (float4v){0.f, 0.f, 0.f, 0.f};
 
-  // ---- prologue: A(0), A(1) in LDS, A(2) and B(0) in flight -------------------------------------
+  // ---- prologue: A(0), A(1) in LDS, A(2) and B(0 .. BD-2) in flight -------------------------------
   u32x4 av[kPAPer];
   {
     u32x4 a0[kPAPer];
     load_a(a0, 0);
     load_a(av, 1);
-    load_b(std::integral_constant<int, 0>{}, 0);
+    static_for<BD - 1>([&](auto bc_c) { load_b(bc_c, decltype(bc_c)::value); });
     store_a(a0, As[0]);
     store_a(av, As[1]);
     load_a(av, 2);
@@ -528,8 +533,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
 
   static_for<NK>([&](auto kc_c) {
     constexpr int kc = decltype(kc_c)::value;
-    constexpr int sl = kc % 2;
-    if constexpr (kc + 1 < NK) load_b(std::integral_constant<int, (kc + 1) % 2>{}, kc + 1);
+    constexpr int sl = kc % BD;
+    if constexpr (kc + BD - 1 < NK) load_b(std::integral_constant<int, (kc + BD - 1) % BD>{}, kc + BD - 1);
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* Ab = As[kc % 3];
 #pragma unroll
@@ -548,9 +553,9 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
       // last one is clamped and not used), so the LDS latency is not paid once per subtile
       half8 af = *(const half8*)(Ab + n * kKC + pcol);
 #pragma unroll
-      for (int i = 0; i < kMSub; ++i) {
+      for (int i = 0; i < MSUB; ++i) {
         if (i < ms) {
-          const int inext = i + 1 < kMSub ? i + 1 : i;
+          const int inext = i + 1 < MSUB ? i + 1 : i;
           half8 af_next = *(const half8*)(Ab + (16 * inext + n) * kKC + pcol);
 #pragma unroll
           for (int s = 0; s < 4; ++s)
@@ -571,7 +576,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   // ---- epilogue: lane holds D[16i + 4g + r][16s + n] -----------------------------------------
   bool range_bad = false;
 #pragma unroll
-  for (int i = 0; i < kMSub; ++i) {
+  for (int i = 0; i < MSUB; ++i) {
     if (i >= ms) continue;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -650,9 +655,17 @@ __global__ __launch_bounds__(256) void k_prefill_combine(const _Float16* __restr
 
 static int round8(int v) { return (v + 7) & ~7; }
 
+bool prefill_kernel_fits(int kernel, int mode_down, int H, int F, int fmt, int item_rows) {
+  if (kernel == kGemmGeneral) return true;
+  if (fmt != MOE_FMT_Q4_0) return false;  // the pipelined kernels read the default format
+  if (kernel == kGemmPipe64Deep && item_rows > 64) return false;
+  // built for the model's reduction widths: gate/up over H = 2048 (16 chunks), down over F = 768 (6)
+  return mode_down ? (F == 6 * kKC && H % kPNTile == 0) : (H == 16 * kKC && F % (kPNTile / 2) == 0);
+}
+
 hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, const ExpertSource& src,
                               const void* x_bf16, const GroupBuffers& g, const PrefillBuffers& b, float* y,
-                              int32_t* ctrl, hipStream_t st) {
+                              int32_t* ctrl, const PrefillPlan& plan, hipStream_t st) {
   hipError_t err;
   const size_t nx = (size_t)T * H;
   int grid = (int)((nx + 255) / 256);
@@ -660,7 +673,7 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   k_bf16_to_f16<<<grid, 256, 0, st>>>((const uint16_t*)x_bf16, b.x16, nx, ctrl);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
-  const int max_items = prefill_max_items(T, k, E, n_shared);
+  const int max_items = prefill_max_items(T, k, E, n_shared, plan.item_rows);
   GemmArgs a{};
   a.src = src;
   a.items = g.items;
@@ -671,46 +684,40 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   a.F = F;
   a.T = T;
 
-  // gate/up + SwiGLU: h16[row][F]; the pipelined kernel at H = 2048 (16 chunks), F % 256 == 0
+  // the plan's kernel for one projection: a pipelined shape where it is built for the widths and the
+  // format, else the general kernel (which also runs the codebook and affine formats)
+  auto run = [&](auto mode_c, int kernel) {
+    constexpr int M = decltype(mode_c)::value;
+    constexpr int timed = M == kGateUp ? kTimePrefillGateUp : kTimePrefillDown;
+    constexpr int NK = M == kGateUp ? 16 : 6;
+    const int pipe_cols = M == kGateUp ? kPNTile / 2 : kPNTile;  // output columns per pipelined workgroup
+    const int gen_cols = M == kGateUp ? kNTileW / 2 : kNTileW;
+    if (!prefill_kernel_fits(kernel, M == kDown, H, F, src.fmt, plan.item_rows)) kernel = kGemmGeneral;
+    a.n_ntiles = (M == kGateUp ? F : H) / (kernel == kGemmGeneral ? gen_cols : pipe_cols);
+    a.n_works = max_items * a.n_ntiles;
+    const int blocks = round8(a.n_works);
+    if (kernel == kGemmPipe128)
+      return launch_timed(timed, k_expert_gemm_pipe<M, NK>, blocks, 64 * kPWaves, 0, st, a);
+    if (kernel == kGemmPipe64Deep)
+      return launch_timed(timed, k_expert_gemm_pipe<M, NK, 4, 4>, blocks, 64 * kPWaves, 0, st, a);
+    if (src.fmt == MOE_FMT_CB4)
+      return launch_timed(timed, k_expert_gemm<M, kRouterTileRows, MOE_FMT_CB4>, blocks, 256, 0, st, a);
+    if (src.fmt == MOE_FMT_AFFINE4)
+      return launch_timed(timed, k_expert_gemm<M, kRouterTileRows, MOE_FMT_AFFINE4>, blocks, 256, 0, st, a);
+    return launch_timed(timed, k_expert_gemm<M>, blocks, 256, 0, st, a);
+  };
+
+  // gate/up + SwiGLU: h16[row][F]
   a.a16 = (const uint16_t*)b.x16;
   a.row_tok = g.row_tok;
   a.h_out = b.h16;
-  // (the codebook and affine formats run on the general kernel)
-  const bool q4 = src.fmt == MOE_FMT_Q4_0;
-  auto general = [&](auto mode_c) {
-    constexpr int M = decltype(mode_c)::value;
-    const int timed = M == kGateUp ? kTimePrefillGateUp : kTimePrefillDown;
-    if (src.fmt == MOE_FMT_CB4)
-      return launch_timed(timed, k_expert_gemm<M, kRouterTileRows, MOE_FMT_CB4>, round8(a.n_works), 256, 0, st, a);
-    if (src.fmt == MOE_FMT_AFFINE4)
-      return launch_timed(timed, k_expert_gemm<M, kRouterTileRows, MOE_FMT_AFFINE4>, round8(a.n_works), 256, 0, st, a);
-    return launch_timed(timed, k_expert_gemm<M>, round8(a.n_works), 256, 0, st, a);
-  };
-  if (q4 && H == 16 * kKC && F % (kPNTile / 2) == 0) {
-    a.n_ntiles = F / (kPNTile / 2);
-    a.n_works = max_items * a.n_ntiles;
-    err = launch_timed(kTimePrefillGateUp, k_expert_gemm_pipe<kGateUp, 16>, round8(a.n_works), 64 * kPWaves, 0, st, a);
-  } else {
-    a.n_ntiles = F / (kNTileW / 2);
-    a.n_works = max_items * a.n_ntiles;
-    err = general(std::integral_constant<int, kGateUp>{});
-  }
-  if (err != hipSuccess) return err;
+  if ((err = run(std::integral_constant<int, kGateUp>{}, plan.gate_up)) != hipSuccess) return err;
 
-  // down: y_rows[row][H] = w_row * (Wd h); the pipelined kernel at F = 768 (6 chunks), H % 512 == 0
+  // down: y_rows[row][H] = w_row * (Wd h)
   a.a16 = (const uint16_t*)b.h16;
   a.row_w = g.row_w;
   a.y16_out = b.y_rows;
-  if (q4 && F == 6 * kKC && H % kPNTile == 0) {
-    a.n_ntiles = H / kPNTile;
-    a.n_works = max_items * a.n_ntiles;
-    err = launch_timed(kTimePrefillDown, k_expert_gemm_pipe<kDown, 6>, round8(a.n_works), 64 * kPWaves, 0, st, a);
-  } else {
-    a.n_ntiles = H / kNTileW;
-    a.n_works = max_items * a.n_ntiles;
-    err = general(std::integral_constant<int, kDown>{});
-  }
-  if (err != hipSuccess) return err;
+  if ((err = run(std::integral_constant<int, kDown>{}, plan.down)) != hipSuccess) return err;
 
   const size_t nc = (size_t)T * (H / 4);
   grid = (int)((nc + 255) / 256);
@@ -720,7 +727,7 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
 }
 
 hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const float* bias, int T, int E, int H,
-                              float* logits, hipStream_t st) {
+                              float* logits, int rows_per_work, hipStream_t st) {
   GemmArgs a{};
   a.E = E;
   a.H = H;
@@ -730,7 +737,7 @@ hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const flo
   a.bias = bias;
   a.y_out = logits;
   a.n_ntiles = (E + kNTileW - 1) / kNTileW;
-  if (T > kRouterTallFrom) {
+  if (rows_per_work == kRouterTallRows) {
     a.n_works = ((T + kRouterTallRows - 1) / kRouterTallRows) * a.n_ntiles;
     k_expert_gemm<kRouter, kRouterTallRows><<<round8(a.n_works), 256, 0, st>>>(a);
   } else {

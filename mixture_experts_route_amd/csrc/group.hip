@@ -75,13 +75,14 @@ __global__ __launch_bounds__(256) void k_group_bucket_scan(const uint32_t* __res
 
 // One workgroup (1024 threads): bucket offsets, the GEMM tile list, the public counts/offsets.
 __global__ __launch_bounds__(1024) void k_group_offsets(const int32_t* __restrict__ count, int E, int n_shared, int T,
-                                                         int32_t* __restrict__ offsets, TileItem* __restrict__ items,
-                                                         int32_t* __restrict__ ctrl, int32_t* __restrict__ counts_out,
+                                                         int item_rows, int32_t* __restrict__ offsets,
+                                                         TileItem* __restrict__ items, int32_t* __restrict__ ctrl,
+                                                         int32_t* __restrict__ counts_out,
                                                          int32_t* __restrict__ offsets_out) {
   __shared__ int wave_sums[16];
   const int e = threadIdx.x;
   const int c = e < E ? count[e] : 0;
-  const int n_it = (c + kTileRows - 1) / kTileRows;
+  const int n_it = (c + item_rows - 1) / item_rows;
   int total_rows, total_items;
   // block-wide exclusive scans (blockDim.x == 1024 >= E)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -112,8 +113,8 @@ __global__ __launch_bounds__(1024) void k_group_offsets(const int32_t* __restric
     for (int i = 0; i < n_it; ++i) {
       TileItem it;
       it.bucket = e;
-      it.row0 = off + i * kTileRows;
-      it.rows = min(kTileRows, c - i * kTileRows);
+      it.row0 = off + i * item_rows;
+      it.rows = min(item_rows, c - i * item_rows);
       it.pad = 0;
       items[ipos + i] = it;
     }
@@ -124,11 +125,11 @@ __global__ __launch_bounds__(1024) void k_group_offsets(const int32_t* __restric
     int n_all = total_items;
     if (n_shared) {
       offsets[E + 1] = total_rows + T;
-      for (int r0 = 0; r0 < T; r0 += kTileRows) {
+      for (int r0 = 0; r0 < T; r0 += item_rows) {
         TileItem it;
         it.bucket = E;
         it.row0 = total_rows + r0;
-        it.rows = min(kTileRows, T - r0);
+        it.rows = min(item_rows, T - r0);
         it.pad = 0;
         items[n_all++] = it;
       }
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) void k_group_scatter(const int32_t* __restrict
 
 hipError_t launch_group(const int32_t* ids, const float* topk_w, int T, int k, int E, int n_shared,
                         const GroupBuffers& g, int32_t* ctrl, int32_t* counts_out, int32_t* offsets_out,
-                        hipStream_t st) {
+                        hipStream_t st, int item_rows) {
   const int W = (T + 31) / 32;
   hipError_t err = launch_fill_zero(g.bits, sizeof(uint32_t) * (size_t)E * W, st);
   if (err != hipSuccess) return err;
@@ -189,7 +190,8 @@ hipError_t launch_group(const int32_t* ids, const float* topk_w, int T, int k, i
   if ((err = hipGetLastError()) != hipSuccess) return err;
   k_group_bucket_scan<<<E, 256, 0, st>>>(g.bits, W, g.prefix, g.count);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  k_group_offsets<<<1, 1024, 0, st>>>(g.count, E, n_shared, T, g.offsets, g.items, ctrl, counts_out, offsets_out);
+  k_group_offsets<<<1, 1024, 0, st>>>(g.count, E, n_shared, T, item_rows, g.offsets, g.items, ctrl, counts_out,
+                                      offsets_out);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   const int np = n + (n_shared ? T : 0);
   grid = (np + 255) / 256;

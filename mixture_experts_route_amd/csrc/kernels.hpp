@@ -87,9 +87,10 @@ struct ExpertSource {
   Codebook cb;           // MOE_FMT_CB4
 };
 
-// Prefill: one grouped-GEMM work item = up to kTileRows consecutive rows of one bucket
-// (bucket E = the shared expert) in bucket-sorted order.
-constexpr int kTileRows = 128;
+// Prefill: one grouped-GEMM work item = up to item_rows (64 or 128, the plan's choice) consecutive
+// rows of one bucket (bucket E = the shared expert) in bucket-sorted order.
+constexpr int kTileRows = 128;    // the largest item
+constexpr int kMinItemRows = 64;  // the smallest item a plan takes
 
 struct TileItem {
   int32_t bucket;
@@ -98,11 +99,21 @@ struct TileItem {
   int32_t pad;
 };
 
-// Upper bound on work items: sum over non-empty buckets of ceil(c / kTileRows).
-inline int prefill_max_items(int T, int k, int E, int n_shared) {
+// Upper bound on work items: sum over non-empty buckets of ceil(c / item_rows).
+inline int prefill_max_items(int T, int k, int E, int n_shared, int item_rows = kMinItemRows) {
   const long long rows = (long long)T * (k + n_shared);
-  return (int)((rows + kTileRows - 1) / kTileRows) + E + 1;
+  return (int)((rows + item_rows - 1) / item_rows) + E + 1;
 }
+
+// How a prefill call runs (moe_prefill_plan): the item size, the grouped-GEMM kernel of each
+// projection and the router GEMM's rows per work.
+enum GemmKernel { kGemmPipe128 = 0, kGemmPipe64Deep = 1, kGemmGeneral = 2 };
+struct PrefillPlan {
+  int item_rows;
+  int gate_up;
+  int down;
+  int router_rows;
+};
 
 struct GroupBuffers {
   uint32_t* bits;    // [E][W] token bitmaps, W = ceil(T / 32)
@@ -147,7 +158,7 @@ hipError_t launch_decode_ffn(int H, int F, int k, int n_shared, int T, int max_t
 // group.hip
 hipError_t launch_group(const int32_t* ids, const float* topk_w, int T, int k, int E, int n_shared,
                         const GroupBuffers& g, int32_t* ctrl, int32_t* counts_out, int32_t* offsets_out,
-                        hipStream_t st);
+                        hipStream_t st, int item_rows = kTileRows);
 
 // ffn_prefill.hip
 struct PrefillBuffers {
@@ -157,9 +168,11 @@ struct PrefillBuffers {
 };
 hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, const ExpertSource& src,
                               const void* x_bf16, const GroupBuffers& g, const PrefillBuffers& b, float* y,
-                              int32_t* ctrl, hipStream_t st);
+                              int32_t* ctrl, const PrefillPlan& plan, hipStream_t st);
 hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const float* bias, int T, int E, int H,
-                              float* logits, hipStream_t st);
+                              float* logits, int rows_per_work, hipStream_t st);
+// Whether a grouped-GEMM kernel is built for these widths and this format.
+bool prefill_kernel_fits(int kernel, int mode_down, int H, int F, int fmt, int item_rows);
 
 hipError_t launch_debug_dequant(int H, int F, int fmt, const Codebook& cb, const uint8_t* blob, int matrix, float* out,
                                 hipStream_t st);

@@ -32,7 +32,7 @@ EXPORTS = [
     "moe_expert_ffn_decode", "moe_expert_ffn_prefill", "moe_layer_forward", "moe_layer_forward_static",
     "moe_pool_create", "moe_pool_destroy", "moe_pool_arm", "moe_pool_serve", "moe_pool_get_stats",
     "moe_pool_get_table", "moe_pool_get_profile", "moe_profile_seed", "moe_pool_lend", "moe_pool_unlend",
-    "moe_pool_debug_fail_copies",
+    "moe_pool_debug_fail_copies", "moe_prefill_plan_get", "moe_debug_force_prefill_plan",
 ]
 
 
@@ -54,6 +54,14 @@ class moe_layer_weights(ctypes.Structure):
 class moe_doorbell(ctypes.Structure):
     _fields_ = [("host_miss_ids", ctypes.c_void_p), ("host_miss_count", ctypes.c_void_p),
                 ("ready", ctypes.c_void_p), ("epoch", ctypes.c_uint32), ("host_step_ids", ctypes.c_void_p)]
+
+
+class moe_prefill_plan(ctypes.Structure):
+    _fields_ = [("item_rows", ctypes.c_int32), ("gate_up_kernel", ctypes.c_int32), ("down_kernel", ctypes.c_int32),
+                ("router_rows", ctypes.c_int32)]
+
+
+MOE_GEMM_PIPE128, MOE_GEMM_PIPE64_DEEP, MOE_GEMM_GENERAL = 0, 1, 2
 
 
 class moe_pool_stats(ctypes.Structure):
@@ -101,6 +109,8 @@ _sig = {
     "moe_pool_lend": (ctypes.c_int, [_P, _I, _P, _P, _PP]),
     "moe_pool_unlend": (ctypes.c_int, [_P, _P]),
     "moe_pool_debug_fail_copies": (ctypes.c_int, [_P, _I]),
+    "moe_prefill_plan_get": (ctypes.c_int, [_D, _I, ctypes.POINTER(moe_prefill_plan)]),
+    "moe_debug_force_prefill_plan": (ctypes.c_int, [ctypes.POINTER(moe_prefill_plan)]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -395,3 +405,14 @@ def moe_pool_unlend(pool: int, stream=None):
 
 def moe_pool_debug_fail_copies(pool: int, after_n: int):
     _check(_lib.moe_pool_debug_fail_copies(pool, after_n), "moe_pool_debug_fail_copies")
+
+
+def moe_prefill_plan_get(d: moe_dims, n_tokens: int) -> moe_prefill_plan:
+    p = moe_prefill_plan()
+    _check(_lib.moe_prefill_plan_get(ctypes.byref(d), n_tokens, ctypes.byref(p)), "moe_prefill_plan_get")
+    return p
+
+
+def moe_debug_force_prefill_plan(plan: moe_prefill_plan | None):
+    _check(_lib.moe_debug_force_prefill_plan(ctypes.byref(plan) if plan is not None else None),
+           "moe_debug_force_prefill_plan")

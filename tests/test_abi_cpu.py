@@ -262,3 +262,26 @@ def test_format_sizes_and_refusal(N):
     f = N.raw("moe_route")
     assert f(ctypes.byref(d), 1 << 20, 1, 1, 1 << 20, 1, None, 1 << 20, 1 << 20, None, 1 << 20, 1 << 30, None) == \
         N.MOE_EUNSUPPORTED
+
+
+def test_prefill_plan_get_and_force(N):
+    """The plan of a prefill call: the table (or default) plan, pipelined kernels only where they are
+    built (the model's widths, default format); a forced plan overrides it until cleared; invalid
+    plans are refused."""
+    d = N.dims(2048, 768, 512, 10, 1)
+    p = N.moe_prefill_plan_get(d, 4096)
+    assert p.item_rows in (64, 128) and p.router_rows in (32, 64)
+    wide = N.moe_prefill_plan_get(N.dims(4096, 1536, 64, 8, 1), 4096)
+    assert wide.gate_up_kernel == N.MOE_GEMM_GENERAL and wide.down_kernel == N.MOE_GEMM_GENERAL
+    cb = N.moe_prefill_plan_get(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_CB4), 4096)
+    assert cb.gate_up_kernel == N.MOE_GEMM_GENERAL and cb.down_kernel == N.MOE_GEMM_GENERAL
+    N.moe_debug_force_prefill_plan(N.moe_prefill_plan(64, 1, 2, 64))
+    try:
+        f = N.moe_prefill_plan_get(d, 100)
+        assert (f.item_rows, f.gate_up_kernel, f.down_kernel, f.router_rows) == (64, 1, 2, 64)
+    finally:
+        N.moe_debug_force_prefill_plan(None)
+    assert N.moe_prefill_plan_get(d, 4096).item_rows == p.item_rows
+    for bad in ((96, 0, 0, 32), (128, 1, 0, 32), (64, 3, 0, 32), (64, 0, 0, 48)):
+        with pytest.raises(N.MoeError):
+            N.moe_debug_force_prefill_plan(N.moe_prefill_plan(*bad))

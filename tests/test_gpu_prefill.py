@@ -257,3 +257,28 @@ def test_prefill_fp16_range_is_reported(N, dev, model_layer):
     assert N.moe_check_device_error(ws) & N.DERR_RANGE
     # the unscaled batch passes (and the flag is not left set)
     _prefill_check(N, dev, layer, T, step=9)
+
+
+@pytest.mark.parametrize("plan", [(128, 0, 0, 32), (64, 1, 1, 32), (64, 0, 2, 64), (128, 2, 2, 64), (64, 2, 1, 32)])
+@pytest.mark.parametrize("T", [300, 4096])
+def test_prefill_plans_parity(N, dev, model_layer, plan, T):
+    """Every grouped-GEMM kernel and item size a plan can choose (forced), against the oracle: in full
+    at 300 tokens, on sampled rows at 4096."""
+    N.moe_debug_force_prefill_plan(N.moe_prefill_plan(*plan))
+    try:
+        got = N.moe_prefill_plan_get(model_layer.dims(), T)
+        assert (got.item_rows, got.gate_up_kernel, got.down_kernel, got.router_rows) == plan
+        sample = None if T <= 300 else np.r_[0:3, 2047:2050, T - 3:T]
+        _prefill_check(N, dev, model_layer, T, step=T + plan[1] * 10 + plan[2], sample=sample)
+    finally:
+        N.moe_debug_force_prefill_plan(None)
+
+
+def test_prefill_deep_plan_zipf_routing(N, dev):
+    """The 64-row deep-prefetch kernels under Zipf(1.1)-skewed routing (long and short groups)."""
+    layer = Layer(dict(MODEL, cfg=4), dev, seed=0, layer=2, bias_c=S.ZIPF_C)
+    N.moe_debug_force_prefill_plan(N.moe_prefill_plan(64, 1, 1, 32))
+    try:
+        _prefill_check(N, dev, layer, 700, step=1)
+    finally:
+        N.moe_debug_force_prefill_plan(None)

@@ -550,7 +550,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
         bf[s] = dequant_word_k(bc[sl][s][d], __builtin_bit_cast(half2v, sv | (sv << 16)), uk);
       }
       // each subtile's MFMAs run while the next subtile's fragment is read (the read of the
-      // last one is clamped and not used), so the LDS latency is not paid once per subtile
+      // last one is clamped and not used), so the LDS latency is not paid once per subtile: the
+      // read is scheduled before the four MFMAs, and the wait for it falls before the next ones
       half8 af = *(const half8*)(Ab + n * kKC + pcol);
 #pragma unroll
       for (int i = 0; i < MSUB; ++i) {
@@ -560,7 +561,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
 #pragma unroll
           for (int s = 0; s < 4; ++s)
             acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[s], acc[i][s], 0, 0, 0);
-          asm volatile("" : "+v"(af_next));  // read inside this subtile's block, not sunk into the next
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // the DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
           af = af_next;
         }
       }

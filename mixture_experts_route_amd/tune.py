@@ -23,8 +23,11 @@ import time
 H, F, E, K_TOP = 2048, 768, 512, 10
 
 
-def candidates():
-    """(item_rows, gate_up kernel, down kernel) triples the library accepts."""
+def candidates(only: str = ""):
+    """(item_rows, gate_up kernel, down kernel) triples the library accepts (or those of `only`,
+    a comma-separated list of rows:gate_up:down)."""
+    if only:
+        return [tuple(int(v) for v in c.split(":")) for c in only.split(",")]
     out = []
     for rows, gu, dn in itertools.product((128, 64), (0, 1, 2), (0, 1, 2)):
         if rows == 128 and (gu == 1 or dn == 1):
@@ -44,6 +47,7 @@ def main():
     ap.add_argument("--out", required=True)
     ap.add_argument("--tokens", default="17,64,256,1024,2048,4096,8192,16384,32768")
     ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--only", default="", help="candidate plans rows:gate_up:down,... (default: all)")
     args = ap.parse_args()
     dev = torch.device("cuda:0")
     cfg = 4
@@ -83,7 +87,7 @@ def main():
         t0 = time.perf_counter()
         default_router = 64 if T > 16384 else 32
         res = {}
-        for rows_, gu, dn in candidates():
+        for rows_, gu, dn in candidates(args.only):
             res[(rows_, gu, dn)] = time_plan(T, N.moe_prefill_plan(rows_, gu, dn, default_router))
         best = min(res, key=res.get)
         r_res = {r: time_plan(T, N.moe_prefill_plan(*best, r)) for r in (32, 64)}
@@ -100,7 +104,7 @@ def main():
              "// (kernels: 0 pipelined, 128-row items, weights 1 chunk ahead; 1 pipelined, 64-row items, weights",
              "// 3 chunks ahead; 2 general).  Shapes or token counts with no row take the default plan.",
              f"// Command: python -m mixture_experts_route_amd.tune --out PATH --tokens {args.tokens} "
-             f"--reps {args.reps}",
+             f"--reps {args.reps}" + (f" --only {args.only}" if args.only else ""),
              "// Layer: hidden 2048, expert FFN 768, 512 experts top-10 + 1 shared, default format, Zipf(1.1)",
              "// routing; median microseconds per moe_layer_forward call, candidate (item_rows, gate_up, down)."]
     for i, (T, best, best_r, res, r_res) in enumerate(rows):

@@ -504,6 +504,10 @@ static size_t gate_up_lds_bytes(int H, int rows, int waves) {
 // finished) combines the tile's rows after an agent-scope acquire:
 // y[t][o] = sum_j w[t][j] * y_pair[t k + j][o], then + y_pair[T k + t][o], in that order.
 // No workgroup waits on another.
+// Invariant this rests on: every pair-row write the combining workgroup reads is such an
+// agent-scope store, completed (s_waitcnt vmcnt(0)) before the relaxed counter increment.  There
+// is no release fence: a plain store added to the pair rows would stay in its XCD's L2, and the
+// combine could read stale rows.
 MOE_DEV void store_pair(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 // n_tasks: the step's task count (one counting workgroup per task for this tile; the slots past

@@ -464,6 +464,9 @@ MOE_DEV void select_and_plan(const RouteArgs& a) {
 // coherence point the XCDs share); it waits for them and counts itself; the workgroup that
 // completes the count (every router row is then written) acquires at agent scope and runs the
 // selection and the plan.  No workgroup waits on another.
+// Invariant this rests on: every logit the selecting workgroup reads is written by such an
+// agent-scope store (store_logit), completed before the relaxed counter increment.  There is no
+// release fence: a plain store to the logits would stay in its XCD's L2, unseen by the selection.
 MOE_DEV void store_logit(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
 template <int NPER>

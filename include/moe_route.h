@@ -209,8 +209,9 @@ MOE_API int moe_debug_kernel_events(int32_t which, void* start_event, void* stop
  *   MOE_GEMM_PIPE128      8 waves x 512 weight rows, up to 128-row items, weights 1 chunk ahead;
  *   MOE_GEMM_PIPE64_DEEP  the same with up to 64-row items and weights 3 chunks ahead;
  *   MOE_GEMM_GENERAL      4 waves x 256 weight rows, every width and weight format.
- * The pipelined kernels exist for the default format at the model's reduction widths (gate/up over
- * H = 2048, down over F = 768); elsewhere the general kernel runs whatever the plan says. */
+ * The pipelined kernels exist at the model's reduction widths (gate/up over H = 2048, down over
+ * F = 768), for every weight format except the affine one on MOE_GEMM_PIPE128; elsewhere the
+ * general kernel runs whatever the plan says. */
 enum moe_gemm_kernel { MOE_GEMM_PIPE128 = 0, MOE_GEMM_PIPE64_DEEP = 1, MOE_GEMM_GENERAL = 2 };
 typedef struct moe_prefill_plan {
   int32_t item_rows;

@@ -503,7 +503,6 @@ MOE_API int moe_layer_forward(const moe_dims* dims, const moe_layer_weights* w, 
   int32_t* ids = topk_ids_out_or_null ? topk_ids_out_or_null : at<int32_t>(ws, L.ids);
   float* tw = topk_w_out_or_null ? topk_w_out_or_null : at<float>(ws, L.w);
   if (!prefill && n_tokens == 1 && !bell_or_null && x_dtype == MOE_BF16 && w->router_dtype == MOE_BF16 &&
-      dims->format == MOE_FMT_Q4_0 &&
       decode_select1_supported(dims->hidden, dims->ffn, dims->top_k, dims->n_shared, dims->n_experts)) {
     // one token, no doorbell: the router launch ends with its logits; the gate/up launch selects,
     // checks residency and plans (the router launch's last-workgroup step is off the path)

@@ -129,6 +129,12 @@ MOE_DEV bf16x8 fmt_b(uint32_t w, const uint32_t* cbt) {
     return codes_q136(w);
   }
 }
+// The same operand with the unpacking constants in registers (the pipelined kernels).
+template <int FMT>
+MOE_DEV bf16x8 pipe_b(uint32_t w, const Unpack& uk, const uint32_t* cbt) {
+  if constexpr (FMT == MOE_FMT_CB4) return fmt_b<FMT>(w, cbt);
+  else return codes_q136(w, uk);
+}
 // The 256-entry LDS table of the codebook format: entry (c1 << 4 | c0) = (bf16 cb[c0], bf16 cb[c1]).
 MOE_DEV void fill_codebook_bf16(const Codebook& cb, uint32_t* cbt) {
   for (int i = threadIdx.x; i < 256; i += blockDim.x) {
@@ -345,7 +351,6 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
   constexpr int NR = ROWS < 4 ? ROWS : 4;                    // live D registers per lane
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
   __shared__ uint32_t cbt[FMT == MOE_FMT_CB4 ? 256 : 1];
-  static_assert(FMT == MOE_FMT_Q4_0 || !SEL, "the selecting launch runs the default format");
 
   const int task = blockIdx.x / a.tiles_gu;
   const int tile = blockIdx.x - task * a.tiles_gu;
@@ -712,21 +717,28 @@ __global__ __launch_bounds__(64 * kDnWaves) void k_decode_down(DecodeArgs a) {
 // the group partial of its task's pair value; the workgroup then forms every pair value and the
 // combine in the same order as the per-pair rows and the combine of the other decode kernels, and
 // stores y directly: no per-pair rows and no cross-workgroup combine.
-template <int MAXT, int MAXI, int RT, int NWV>
+template <int MAXT, int MAXI, int RT, int NWV, int FMT = MOE_FMT_Q4_0>
 __global__ __launch_bounds__(64 * NWV) void k_decode_down_rows1(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t hs[NWV][MAXI][2][kGroupElems];  // [wave][item][part][input]
   __shared__ float red[8][MAXT + 1][16];  // [group][task][row]: group partials (task MAXT: unused items)
   __shared__ float pv[MAXT][16];      // [task][row]: pair values
   __shared__ int s_inv[kMaxK];        // task of each top-k position j
+  __shared__ uint32_t cbt[FMT == MOE_FMT_CB4 ? 256 : 1];
+  constexpr bool kAff = FMT == MOE_FMT_AFFINE4;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int H = a.H, F = a.F;
+  if constexpr (FMT == MOE_FMT_CB4) {
+    // the codebook's pair table, before any load is in flight (the barrier would wait for them)
+    fill_codebook_bf16(a.src.cb, cbt);
+    __syncthreads();
+  }
   const int NW = F / kGroupElems;  // groups of F inputs (<= 8)
   // RT output rows per workgroup; with RT = 8 lanes n and n + 8 load the same row (the upper
   // half of D is not used)
   const int row = blockIdx.x * RT + (n & (RT - 1));
-  const BlobLayout lay = blob_layout(H, F);
+  const BlobLayout lay = blob_layout(H, F, FMT);
   // task descriptors: lane t loads task t (the task list always has room for MAXT entries), so one
   // vector load brings them all; the per-task values are then read from those lanes
   const int n_tasks = min(a.ctrl[kCtrlNTasks], MAXT);
@@ -780,10 +792,12 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_down_rows1(DecodeArgs a) {
   // weights of every item: record (q, row) of the down matrix
   u32x4 cd[MAXI];
   u32x2 sd[MAXI];
+  u32x2 md[kAff ? MAXI : 1];  // affine format: the records' mins
   static_for<MAXI>([&](auto c) {
     constexpr int m = c.value;
     cd[m] = *(const u32x4*)(blob[m] + lay.down_codes + ((size_t)it_q[m] * H + row) * kGroupBytes + 16 * g);
     sd[m] = *(const u32x2*)(blob[m] + lay.down_scales + ((size_t)it_q[m] * H + row) * kGroupScaleBytes);
+    if constexpr (kAff) md[m] = *(const u32x2*)(blob[m] + lay.down_mins + ((size_t)it_q[m] * H + row) * kGroupScaleBytes);
   });
   issue_fence();
   static_for<HC>([&](auto c) {
@@ -794,7 +808,6 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_down_rows1(DecodeArgs a) {
   asm volatile("" ::: "memory");  // the wave reads back only its own slices: LDS order suffices
   if (wave == 0 && lane < n_tasks && l_expert >= 0) s_inv[tv[3] & 15u] = lane;
   const Unpack uk = make_unpack();
-  const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   // every item is computed (one basic block, so the MFMA chains of different items interleave);
   // unused items write their result to the spare task row
@@ -806,11 +819,16 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_down_rows1(DecodeArgs a) {
       uint4 av = *(const uint4*)&hs[wave][m][n & 1][32 * i + 8 * g];
       if (n >= 2) av = make_uint4(0u, 0u, 0u, 0u);
       const bf16x8 A = __builtin_bit_cast(bf16x8, av);
-      const float4v O = mfma_bf16(A, neg, zero);
-      const float4v D = mfma_bf16(A, codes_q136(word_at(cd[m], i), uk), O);
+      const float4v O = fmt_c<FMT>(A, zero);
+      const float4v D = mfma_bf16(A, pipe_b<FMT>(word_at(cd[m], i), uk, cbt), O);
       const float sc = scale_at(sd[m], i);
       acc0 = fmaf(sc, D[0], acc0);
       acc1 = fmaf(sc, D[1], acc1);
+      if constexpr (kAff) {
+        const float mn = scale_at(md[m], i) * 0.0078125f;
+        acc0 = fmaf(mn, O[0], acc0);
+        acc1 = fmaf(mn, O[1], acc1);
+      }
     }
     // lanes 0..15 hold rows 0 and 1 of D (the token's hi and lo parts) for output row n
     if (lane < RT) red[use[m] ? it_q[m] : 0][use[m] ? it_t[m] : MAXT][n] = acc0 + acc1;
@@ -866,13 +884,16 @@ constexpr int kPipeDnBufs = 2;    // down: chunks in flight
 // 2 (256 registers) at 16, whose staged activation rows would not fit beside the weight ring.
 constexpr int pipe_waves_per_eu(int maxtok) { return maxtok > 8 ? 2 : 4; }
 
-// gate/up: H = 128 kPipeGuGroups UNITS; A rows = token slots of the task (bf16 x).
-template <int MAXTOK, int UNITS>
+// gate/up: H = 128 kPipeGuGroups UNITS; A rows = token slots of the task (bf16 x).  Every weight
+// format, with the operands, the C term and the affine min term of the general kernel.
+template <int MAXTOK, int UNITS, int FMT = MOE_FMT_Q4_0>
 __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu(MAXTOK)))) void k_decode_gate_up_pipe(DecodeArgs a) {
   constexpr int ROWS = MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
   constexpr int QG = kPipeGuGroups;
+  constexpr bool kAff = FMT == MOE_FMT_AFFINE4;
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  __shared__ uint32_t cbt[FMT == MOE_FMT_CB4 ? 256 : 1];
   const int task = blockIdx.x / a.tiles_gu;
   const int tile = blockIdx.x - task * a.tiles_gu;
   constexpr int H = 128 * QG * UNITS;
@@ -881,8 +902,9 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   // ROWS * H / 8 chunks over 64 kPipeGuWaves threads
   constexpr int XC = (ROWS * (H / 8) + 64 * kPipeGuWaves - 1) / (64 * kPipeGuWaves);
   u32x4 xv[XC];
-  // chunks in flight (fewer when the staged rows need many registers)
-  constexpr int NBUF = XC > 8 ? 2 : kPipeGuBufs;
+  // chunks in flight (fewer when the staged rows, or the affine format's min records, need many
+  // registers)
+  constexpr int NBUF = (XC > 8 || kAff) ? 2 : kPipeGuBufs;
   stage_load(xv, ROWS, H, x_row);
   const DecodeTask tk = a.tasks[task];
   if (task >= a.ctrl[kCtrlNTasks]) return;
@@ -892,19 +914,22 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
     return;
   }
   const int F = a.F;
-  const BlobLayout lay = blob_layout(H, F);
+  const BlobLayout lay = blob_layout(H, F, FMT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int row = (tile * kPipeGuWaves + wave) * 16 + n;
   const int n_tok = __builtin_popcount(tk.tok_mask);
   const int arow = n < n_tok ? task_token(tk.tok_mask, n) : ROWS;  // LDS row of this lane's slot
   const Unpack uk = make_unpack();
+  if constexpr (FMT == MOE_FMT_CB4) fill_codebook_bf16(a.src.cb, cbt);  // visible after the staging barrier
 
   const __amdgpu_buffer_rsrc_t rs = blob_rsrc(blob, lay.total);
   const int voff_c = row * kGroupBytes + 16 * g, voff_s = row * kGroupScaleBytes;
   u32x4 cg[NBUF][QG], cu[NBUF][QG];
   u32x2 sg[NBUF][QG], su[NBUF][QG];
-  // chunk u into buffer b: record (q, row) at 64 (q F + row), its scales at 8 (q F + row)
+  u32x2 mg[kAff ? NBUF : 1][QG], mu[kAff ? NBUF : 1][QG];  // affine format: the records' mins
+  // chunk u into buffer b: record (q, row) at 64 (q F + row), its scales at 8 (q F + row) (and
+  // its mins likewise in the min planes)
   auto load_chunk = [&](auto bc, int u) {
     constexpr int b = decltype(bc)::value;
 #pragma unroll
@@ -914,6 +939,10 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
       cu[b][qi] = buf_load16(rs, voff_c, (int)lay.up_codes + q * kGroupBytes);
       sg[b][qi] = buf_load8(rs, voff_s, (int)lay.gate_scales + q * kGroupScaleBytes);
       su[b][qi] = buf_load8(rs, voff_s, (int)lay.up_scales + q * kGroupScaleBytes);
+      if constexpr (kAff) {
+        mg[b][qi] = buf_load8(rs, voff_s, (int)lay.gate_mins + q * kGroupScaleBytes);
+        mu[b][qi] = buf_load8(rs, voff_s, (int)lay.up_mins + q * kGroupScaleBytes);
+      }
       __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
     }
   };
@@ -923,7 +952,6 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   issue_fence();
   stage_store_sync<false>(xv, smem, ROWS, H, x_row);
 
-  const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   // Summation order of the split kernel above (a partial sum per range of kGuQuadsPerWave groups,
   // the partials added in range order), so a token's h is bitwise the same whichever kernel the
@@ -945,14 +973,22 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bf16x8 A = lds_fragment(smem, ROWS, H, arow, g, (u * QG + qi) * kGroupElems + 32 * i);
-        const float4v O = mfma_bf16(A, neg, zero);
-        const float4v Dg = mfma_bf16(A, codes_q136(word_at(cg[b][qi], i), uk), O);
-        const float4v Du = mfma_bf16(A, codes_q136(word_at(cu[b][qi], i), uk), O);
+        const float4v O = fmt_c<FMT>(A, zero);
+        const float4v Dg = mfma_bf16(A, pipe_b<FMT>(word_at(cg[b][qi], i), uk, cbt), O);
+        const float4v Du = mfma_bf16(A, pipe_b<FMT>(word_at(cu[b][qi], i), uk, cbt), O);
         const float s_g = scale_at(sg[b][qi], i), s_u = scale_at(su[b][qi], i);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           accg[r] = fmaf(s_g, Dg[r], accg[r]);
           accu[r] = fmaf(s_u, Du[r], accu[r]);
+        }
+        if constexpr (kAff) {
+          const float m_g = scale_at(mg[b][qi], i) * 0.0078125f, m_u = scale_at(mu[b][qi], i) * 0.0078125f;
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            accg[r] = fmaf(m_g, O[r], accg[r]);
+            accu[r] = fmaf(m_u, O[r], accu[r]);
+          }
         }
       }
       // one group at a time: an unbounded schedule hoists every MFMA and spills their results
@@ -990,9 +1026,11 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   }
 }
 
-// down: F = 128 kPipeDnGroups UNITS; A rows 2 s + part (token slot s, h hi / lo).
-template <int MAXTOK, int UNITS>
-MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* smem) {
+// down: F = 128 kPipeDnGroups UNITS; A rows 2 s + part (token slot s, h hi / lo).  Every weight
+// format, as in the general down kernel.
+template <int MAXTOK, int UNITS, int FMT = MOE_FMT_Q4_0>
+MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* smem, const uint32_t* cbt) {
+  constexpr bool kAff = FMT == MOE_FMT_AFFINE4;
   constexpr int ROWS = 2 * MAXTOK;
   constexpr int NR = ROWS < 4 ? ROWS : 4;
   constexpr int MB = (ROWS + 15) / 16;  // 16-row A blocks: a second one holds token slots 8..15
@@ -1006,7 +1044,7 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
   }
   constexpr int F = 128 * QG * UNITS;
   const int H = a.H;
-  const BlobLayout lay = blob_layout(H, F);
+  const BlobLayout lay = blob_layout(H, F, FMT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int n_tok = __builtin_popcount(tk.tok_mask);
@@ -1035,6 +1073,7 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
   const int voff_c1 = rows[RGW - 1] * kGroupBytes + 16 * g, voff_s1 = rows[RGW - 1] * kGroupScaleBytes;
   u32x4 cd[kPipeDnBufs][RGW][QG];
   u32x2 sd[kPipeDnBufs][RGW][QG];
+  u32x2 md[kAff ? kPipeDnBufs : 1][RGW][QG];  // affine format: the records' mins
   auto load_chunk = [&](auto bc, int u) {
     constexpr int b = decltype(bc)::value;
 #pragma unroll
@@ -1044,6 +1083,8 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
       for (int r = 0; r < RGW; ++r) {
         cd[b][r][qi] = buf_load16(rs, r == 0 ? voff_c0 : voff_c1, (int)lay.down_codes + q * kGroupBytes);
         sd[b][r][qi] = buf_load8(rs, r == 0 ? voff_s0 : voff_s1, (int)lay.down_scales + q * kGroupScaleBytes);
+        if constexpr (kAff)
+          md[b][r][qi] = buf_load8(rs, r == 0 ? voff_s0 : voff_s1, (int)lay.down_mins + q * kGroupScaleBytes);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1054,7 +1095,6 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
   issue_fence();
   stage_store_sync<false>(hv, smem, ROWS, F, h_row);
 
-  const bf16x8 neg = const_neg136();
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   float acc[MB][RGW][NR / 2];  // per token slot: sum over groups of (hi + lo) group partials
 #pragma unroll
@@ -1082,17 +1122,22 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
           A[mb] = lds_fragment(smem, ROWS, F, 16 * mb + n, g, (u * QG + qi) * kGroupElems + 32 * i);
-          O[mb] = mfma_bf16(A[mb], neg, zero);
+          O[mb] = fmt_c<FMT>(A[mb], zero);
         }
 #pragma unroll
         for (int r = 0; r < RGW; ++r) {
-          const bf16x8 B = codes_q136(word_at(cd[b][r][qi], i), uk);
+          const bf16x8 B = pipe_b<FMT>(word_at(cd[b][r][qi], i), uk, cbt);
           const float s = scale_at(sd[b][r][qi], i);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
             const float4v D = mfma_bf16(A[mb], B, O[mb]);
 #pragma unroll
             for (int j = 0; j < NR; ++j) part[mb][r][j] = fmaf(s, D[j], part[mb][r][j]);
+            if constexpr (kAff) {
+              const float m = scale_at(md[b][r][qi], i) * 0.0078125f;
+#pragma unroll
+              for (int j = 0; j < NR; ++j) part[mb][r][j] = fmaf(m, O[mb][j], part[mb][r][j]);
+            }
           }
         }
       }
@@ -1133,14 +1178,16 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
   }
 }
 
-template <int MAXTOK, int UNITS>
+template <int MAXTOK, int UNITS, int FMT = MOE_FMT_Q4_0>
 __global__ __launch_bounds__(64 * kPipeDnWaves) __attribute__((amdgpu_waves_per_eu(pipe_waves_per_eu(MAXTOK)))) void k_decode_down_pipe(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint16_t smem[];
+  __shared__ uint32_t cbt[FMT == MOE_FMT_CB4 ? 256 : 1];
   const int task = blockIdx.x / a.tiles_dn;
   const int tile = blockIdx.x - task * a.tiles_dn;
   const int n_tasks = a.ctrl[kCtrlNTasks];
   if (task >= n_tasks) return;  // task slots past the step's count neither compute nor count
-  down_pipe_body<MAXTOK, UNITS>(a, task, tile, smem);
+  if constexpr (FMT == MOE_FMT_CB4) fill_codebook_bf16(a.src.cb, cbt);  // visible after the staging barrier
+  down_pipe_body<MAXTOK, UNITS, FMT>(a, task, tile, smem, cbt);
   combine_tile_if_last(a, tile, 16 * kPipeDnWaves * kPipeDnRGW, n_tasks);
 }
 
@@ -1211,36 +1258,35 @@ static int down_pipe_units(int F) {
   return F % (kGroupElems * kPipeDnGroups) == 0 && (u == 2 || u == 4) ? u : 0;
 }
 
-template <int MAXTOK>
+template <int MAXTOK, int FMT>
 static hipError_t launch_gate_up_pipe(DecodeArgs a, int max_tasks, int units, hipStream_t st) {
   a.tiles_gu = a.F / (16 * kPipeGuWaves);
   const int grid = max_tasks * a.tiles_gu, threads = 64 * kPipeGuWaves;
   const uint32_t lds = (uint32_t)(MAXTOK * (a.H + 8) * 2);
-  if (units == 4) return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 4>, grid, threads, lds, st, a);
-  if (units == 8) return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 8>, grid, threads, lds, st, a);
-  return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 16>, grid, threads, lds, st, a);
+  if (units == 4)
+    return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 4, FMT>, grid, threads, lds, st, a);
+  if (units == 8)
+    return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 8, FMT>, grid, threads, lds, st, a);
+  return launch_timed(kTimeDecodeGateUp, k_decode_gate_up_pipe<MAXTOK, 16, FMT>, grid, threads, lds, st, a);
 }
 
-template <int MAXTOK>
+template <int MAXTOK, int FMT>
 static hipError_t launch_down_pipe(DecodeArgs a, int max_tasks, int units, hipStream_t st) {
   const int rows = 16 * kPipeDnWaves * kPipeDnRGW;
   a.tiles_dn = (a.H + rows - 1) / rows;
   const int grid = max_tasks * a.tiles_dn, threads = 64 * kPipeDnWaves;
   const uint32_t lds = (uint32_t)(2 * MAXTOK * (a.F + 8) * 2);
-  if (units == 2) return launch_timed(kTimeDecodeDown, k_decode_down_pipe<MAXTOK, 2>, grid, threads, lds, st, a);
-  return launch_timed(kTimeDecodeDown, k_decode_down_pipe<MAXTOK, 4>, grid, threads, lds, st, a);
+  if (units == 2) return launch_timed(kTimeDecodeDown, k_decode_down_pipe<MAXTOK, 2, FMT>, grid, threads, lds, st, a);
+  return launch_timed(kTimeDecodeDown, k_decode_down_pipe<MAXTOK, 4, FMT>, grid, threads, lds, st, a);
 }
 
 template <int MAXTOK, int FMT>
 static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipStream_t st) {
-  // the pipelined kernels and the one-token down kernel run the default format; the codebook and
-  // affine formats take the general kernels at every token count
-  constexpr bool kQ = FMT == MOE_FMT_Q4_0;
   hipError_t err = hipSuccess;
   // tasks of more than 2 tokens (bf16 x) at the covered shapes: the pipelined kernels
-  const int gu_units = (kQ && MAXTOK >= 4 && xb) ? gate_up_pipe_units(a.H) : 0;
+  const int gu_units = (MAXTOK >= 4 && xb) ? gate_up_pipe_units(a.H) : 0;
   if (gu_units) {
-    if constexpr (kQ && MAXTOK >= 4) err = launch_gate_up_pipe<MAXTOK>(a, max_tasks, gu_units, st);
+    if constexpr (MAXTOK >= 4) err = launch_gate_up_pipe<MAXTOK, FMT>(a, max_tasks, gu_units, st);
   } else {
     const int ks = (a.H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
     auto launch_rg = [&](auto rgc) {
@@ -1263,16 +1309,17 @@ static hipError_t launch_decode_ffn_t(DecodeArgs a, int max_tasks, bool xb, hipS
       err = launch_rg(std::integral_constant<int, kGuRG>{});
   }
   if (err != hipSuccess) return err;
-  const int dn_units = (kQ && MAXTOK >= 4) ? down_pipe_units(a.F) : 0;
-  if (kQ && MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
+  const int dn_units = MAXTOK >= 4 ? down_pipe_units(a.F) : 0;
+  if (MAXTOK == 1 && a.F <= 8 * kGroupElems && max_tasks <= kMaxK + 1) {
     // one token: output rows outermost, (task, group) items spread over the waves, no pair rows
     const int items = max_tasks * (a.F / kGroupElems);
     if (max_tasks <= 11 && items <= 16 * 5)
-      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16>, a.H / 16, 1024, 0, st, a);
-    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16, 8>, a.H / 16, 512, 0, st, a);
+      return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16, FMT>, a.H / 16, 1024, 0, st, a);
+    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<kMaxK + 1, kMaxK + 1, 16, 8, FMT>, a.H / 16, 512, 0, st,
+                        a);
   }
   if (dn_units) {
-    if constexpr (kQ && MAXTOK >= 4) err = launch_down_pipe<MAXTOK>(a, max_tasks, dn_units, st);
+    if constexpr (MAXTOK >= 4) err = launch_down_pipe<MAXTOK, FMT>(a, max_tasks, dn_units, st);
   } else {
     const int dn_rows = 16 * kDnWaves * kDnRGW<MAXTOK>;
     a.tiles_dn = (a.H + dn_rows - 1) / dn_rows;
@@ -1353,10 +1400,17 @@ hipError_t launch_decode_ffn_select1(int H, int F, int k, int n_shared, int E, c
   const int n_tasks = k + (n_shared ? 1 : 0);
   const int ks = (H / kGroupElems + kGuQuadsPerWave - 1) / kGuQuadsPerWave;
   a.tiles_gu = F / (16 * kGuRG1);
-  hipError_t err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<1, true, kGuRG1, true>, n_tasks * a.tiles_gu,
-                                64 * kGuRG1 * ks, (uint32_t)gate_up_lds_bytes(H, 1, kGuRG1 * ks), st, a);
-  if (err != hipSuccess) return err;
-  return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16>, H / 16, 1024, 0, st, a);
+  auto run = [&](auto fmt_c) -> hipError_t {
+    constexpr int FMT = decltype(fmt_c)::value;
+    hipError_t err = launch_timed(kTimeDecodeGateUp, k_decode_gate_up<1, true, kGuRG1, true, FMT>,
+                                  n_tasks * a.tiles_gu, 64 * kGuRG1 * ks,
+                                  (uint32_t)gate_up_lds_bytes(H, 1, kGuRG1 * ks), st, a);
+    if (err != hipSuccess) return err;
+    return launch_timed(kTimeDecodeDown, k_decode_down_rows1<11, 5, 16, 16, FMT>, H / 16, 1024, 0, st, a);
+  };
+  if (src.fmt == MOE_FMT_CB4) return run(std::integral_constant<int, MOE_FMT_CB4>{});
+  if (src.fmt == MOE_FMT_AFFINE4) return run(std::integral_constant<int, MOE_FMT_AFFINE4>{});
+  return run(std::integral_constant<int, MOE_FMT_Q4_0>{});
 }
 
 hipError_t launch_debug_dequant(int H, int F, int fmt, const Codebook& cb, const uint8_t* blob, int matrix, float* out,

@@ -420,9 +420,11 @@ __global__ __launch_bounds__(256, 2) void k_expert_gemm(GemmArgs a) {
 constexpr int kPWaves = 8;
 constexpr int kPNTile = 64 * kPWaves;                       // weight rows per workgroup
 
-template <int MODE, int NK, int MSUB = kMSub, int BD = 2>
+template <int MODE, int NK, int MSUB = kMSub, int BD = 2, int FMT = MOE_FMT_Q4_0>
 __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a) {
   static_assert(MODE == kGateUp || MODE == kDown, "expert GEMMs only");
+  constexpr bool kAff = FMT == MOE_FMT_AFFINE4;
+  __shared__ uint32_t cbt16[FMT == MOE_FMT_CB4 ? 256 : 1];
   static_assert(NK >= 3 && NK >= BD, "pipeline depth");
   static_assert(BD >= 2 && MSUB >= 1 && MSUB <= kMSub, "tile shape");
   constexpr int kPAPer = MSUB * 16 * (kKC / 8) / (64 * kPWaves);  // A 16-byte pieces per thread per chunk
@@ -445,7 +447,7 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   const int H = a.H, F = a.F;
   constexpr int K = NK * kKC;
   const int wrows = MODE == kDown ? H : F;
-  const BlobLayout lay = blob_layout(H, F);  // (the default format: the codes and scales its kernels read)
+  const BlobLayout lay = blob_layout(H, F, FMT);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lane & 15, g = lane >> 4;
   const int ms = (it.rows + 15) >> 4;
@@ -456,22 +458,25 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   // subtile s = rows row0 + 16 s (down) or gate rows row0 + 16 (s & 1), up rows likewise (gate/up):
   // one per-lane offset per stream, the rest is uniform (scalar offset) or an immediate
   int row0;
-  int32_t cb0, sb0, cb_up = 0, sb_up = 0;
+  int32_t cb0, sb0, mb0 = 0, cb_up = 0, sb_up = 0;
   if constexpr (MODE == kGateUp) {
     row0 = ntile * (kPNTile / 2) + wave * 32 + n;
     cb0 = (int32_t)lay.gate_codes;
     sb0 = (int32_t)lay.gate_scales;
     cb_up = (int32_t)(lay.up_codes - lay.gate_codes);
-    sb_up = (int32_t)(lay.up_scales - lay.gate_scales);
+    sb_up = (int32_t)(lay.up_scales - lay.gate_scales);  // the min planes are spaced as the scale planes
+    if constexpr (kAff) mb0 = (int32_t)lay.gate_mins;
   } else {
     row0 = ntile * kPNTile + wave * 64 + n;
     cb0 = (int32_t)lay.down_codes;
     sb0 = (int32_t)lay.down_scales;
+    if constexpr (kAff) mb0 = (int32_t)lay.down_mins;
   }
-  // record (kc, row): codes at 64 (kc R + row), scales at 8 (kc R + row)
+  // record (kc, row): codes at 64 (kc R + row), scales at 8 (kc R + row), mins likewise
   const int voff_c = row0 * kGroupBytes + 16 * g, voff_s = row0 * kGroupScaleBytes;
   u32x4 bc[BD][4];
   u32x2 bs[BD][4];
+  u32x2 bm[kAff ? BD : 1][4];  // affine format: the records' mins
   auto load_b = [&](auto slot_c, int kc) {
     constexpr int sl = decltype(slot_c)::value;
 #pragma unroll
@@ -480,6 +485,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
       const bool up = MODE == kGateUp && s >= 2;
       bc[sl][s] = buf_load16(rs, voff_c + rsub * kGroupBytes, cb0 + (up ? cb_up : 0) + kc * wrows * kGroupBytes);
       bs[sl][s] = buf_load8(rs, voff_s + rsub * kGroupScaleBytes, sb0 + (up ? sb_up : 0) + kc * wrows * kGroupScaleBytes);
+      if constexpr (kAff)
+        bm[sl][s] = buf_load8(rs, voff_s + rsub * kGroupScaleBytes, mb0 + (up ? sb_up : 0) + kc * wrows * kGroupScaleBytes);
     }
   };
 
@@ -518,6 +525,8 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
 #pragma unroll
     for (int s = 0; s < 4; ++s) acc[i][s] = (float4v){0.f, 0.f, 0.f, 0.f};
 
+  if constexpr (FMT == MOE_FMT_CB4) fill_codebook_f16(a.src.cb, cbt16);  // visible after the prologue's barrier
+
   // ---- prologue: A(0), A(1) in LDS, A(2) and B(0 .. BD-2) in flight -------------------------------
   u32x4 av[kPAPer];
   {
@@ -547,7 +556,16 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
       for (int s = 0; s < 4; ++s) {
         const uint32_t sw = bs[sl][s][d >> 1];
         const uint32_t sv = (d & 1) ? (sw >> 16) : (sw & 0xFFFFu);
-        bf[s] = dequant_word_k(bc[sl][s][d], __builtin_bit_cast(half2v, sv | (sv << 16)), uk);
+        const half2v s2 = __builtin_bit_cast(half2v, sv | (sv << 16));
+        if constexpr (kAff) {
+          const uint32_t mw = bm[sl][s][d >> 1];
+          const _Float16 mv = __builtin_bit_cast(_Float16, (uint16_t)((d & 1) ? (mw >> 16) : (mw & 0xFFFFu)));
+          bf[s] = dequant_word_affine(bc[sl][s][d], s2, (half2v){-mv, -mv});
+        } else if constexpr (FMT == MOE_FMT_CB4) {
+          bf[s] = dequant_word_cb(bc[sl][s][d], s2, cbt16);
+        } else {
+          bf[s] = dequant_word_k(bc[sl][s][d], s2, uk);
+        }
       }
       // each subtile's MFMAs run while the next subtile's fragment is read (the read of the
       // last one is clamped and not used), so the LDS latency is not paid once per subtile: the
@@ -659,8 +677,9 @@ static int round8(int v) { return (v + 7) & ~7; }
 
 bool prefill_kernel_fits(int kernel, int mode_down, int H, int F, int fmt, int item_rows) {
   if (kernel == kGemmGeneral) return true;
-  if (fmt != MOE_FMT_Q4_0) return false;  // the pipelined kernels read the default format
   if (kernel == kGemmPipe64Deep && item_rows > 64) return false;
+  // the affine format's min records do not fit the 128-row kernel's registers beside its ring
+  if (kernel == kGemmPipe128 && fmt == MOE_FMT_AFFINE4) return false;
   // built for the model's reduction widths: gate/up over H = 2048 (16 chunks), down over F = 768 (6)
   return mode_down ? (F == 6 * kKC && H % kPNTile == 0) : (H == 16 * kKC && F % (kPNTile / 2) == 0);
 }
@@ -698,10 +717,18 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
     a.n_ntiles = (M == kGateUp ? F : H) / (kernel == kGemmGeneral ? gen_cols : pipe_cols);
     a.n_works = max_items * a.n_ntiles;
     const int blocks = round8(a.n_works);
-    if (kernel == kGemmPipe128)
-      return launch_timed(timed, k_expert_gemm_pipe<M, NK>, blocks, 64 * kPWaves, 0, st, a);
-    if (kernel == kGemmPipe64Deep)
-      return launch_timed(timed, k_expert_gemm_pipe<M, NK, 4, 4>, blocks, 64 * kPWaves, 0, st, a);
+    auto pipe = [&](auto fmt_c) -> hipError_t {
+      constexpr int FMT = decltype(fmt_c)::value;
+      if constexpr (FMT != MOE_FMT_AFFINE4)
+        if (kernel == kGemmPipe128)
+          return launch_timed(timed, k_expert_gemm_pipe<M, NK, kMSub, 2, FMT>, blocks, 64 * kPWaves, 0, st, a);
+      return launch_timed(timed, k_expert_gemm_pipe<M, NK, 4, 4, FMT>, blocks, 64 * kPWaves, 0, st, a);
+    };
+    if (kernel == kGemmPipe128 || kernel == kGemmPipe64Deep) {
+      if (src.fmt == MOE_FMT_CB4) return pipe(std::integral_constant<int, MOE_FMT_CB4>{});
+      if (src.fmt == MOE_FMT_AFFINE4) return pipe(std::integral_constant<int, MOE_FMT_AFFINE4>{});
+      return pipe(std::integral_constant<int, MOE_FMT_Q4_0>{});
+    }
     if (src.fmt == MOE_FMT_CB4)
       return launch_timed(timed, k_expert_gemm<M, kRouterTileRows, MOE_FMT_CB4>, blocks, 256, 0, st, a);
     if (src.fmt == MOE_FMT_AFFINE4)

@@ -266,15 +266,19 @@ def test_format_sizes_and_refusal(N):
 
 def test_prefill_plan_get_and_force(N):
     """The plan of a prefill call: the table (or default) plan, pipelined kernels only where they are
-    built (the model's widths, default format); a forced plan overrides it until cleared; invalid
-    plans are refused."""
+    built (the model's widths; the affine format not on the 128-row kernel); a forced plan overrides
+    it until cleared; invalid plans are refused."""
     d = N.dims(2048, 768, 512, 10, 1)
     p = N.moe_prefill_plan_get(d, 4096)
     assert p.item_rows in (64, 128) and p.router_rows in (32, 64)
     wide = N.moe_prefill_plan_get(N.dims(4096, 1536, 64, 8, 1), 4096)
     assert wide.gate_up_kernel == N.MOE_GEMM_GENERAL and wide.down_kernel == N.MOE_GEMM_GENERAL
+    # the codebook format runs the pipelined kernels; the affine format's min records do not fit the
+    # 128-row kernel, which then falls back to the general one
     cb = N.moe_prefill_plan_get(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_CB4), 4096)
-    assert cb.gate_up_kernel == N.MOE_GEMM_GENERAL and cb.down_kernel == N.MOE_GEMM_GENERAL
+    assert cb.gate_up_kernel == N.MOE_GEMM_PIPE128 and cb.down_kernel == N.MOE_GEMM_PIPE128
+    af = N.moe_prefill_plan_get(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_AFFINE4), 4096)
+    assert af.gate_up_kernel == N.MOE_GEMM_GENERAL and af.down_kernel == N.MOE_GEMM_GENERAL
     N.moe_debug_force_prefill_plan(N.moe_prefill_plan(64, 1, 2, 64))
     try:
         f = N.moe_prefill_plan_get(d, 100)

@@ -121,3 +121,20 @@ def test_formats_decode_batch_invariant(N, dev, model_layer):
         assert torch.equal(y1[0], y[t]), t
     torch.cuda.synchronize()
     assert N.moe_check_device_error(ws) == 0
+
+
+@pytest.mark.parametrize("plan", [(128, 0, 0, 32), (64, 1, 1, 32), (128, 2, 2, 32)])
+def test_model_shape_formats_prefill_plans(N, dev, model_layer, plan):
+    """Each grouped-GEMM kernel a plan can name, forced, on the codebook and affine formats: the
+    pipelined kernels dequantize both formats (the affine format's 128-row plan falls back to the
+    general kernel, which the plan query reports)."""
+    N.moe_debug_force_prefill_plan(N.moe_prefill_plan(*plan))
+    try:
+        got = N.moe_prefill_plan_get(model_layer.dims(), 300)
+        want_gu = plan[1]
+        if model_layer.fmt == S.FMT_AFFINE4 and plan[1] == N.MOE_GEMM_PIPE128:
+            want_gu = N.MOE_GEMM_GENERAL
+        assert got.gate_up_kernel == want_gu
+        _check(N, dev, model_layer, 300, step=300 + plan[1])
+    finally:
+        N.moe_debug_force_prefill_plan(None)

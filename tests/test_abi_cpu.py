@@ -273,12 +273,15 @@ def test_prefill_plan_get_and_force(N):
     assert p.item_rows in (64, 128) and p.router_rows in (32, 64)
     wide = N.moe_prefill_plan_get(N.dims(4096, 1536, 64, 8, 1), 4096)
     assert wide.gate_up_kernel == N.MOE_GEMM_GENERAL and wide.down_kernel == N.MOE_GEMM_GENERAL
-    # the codebook format runs the pipelined kernels; the affine format's min records do not fit the
-    # 128-row kernel, which then falls back to the general one
-    cb = N.moe_prefill_plan_get(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_CB4), 4096)
+    # (256 experts: no table row, so the default plan, the 128-row pipelined kernel) the codebook
+    # format runs it; the affine format's min records do not fit it, and the general kernel runs
+    cb = N.moe_prefill_plan_get(N.dims(2048, 768, 256, 10, 1, format=N.MOE_FMT_CB4), 4096)
     assert cb.gate_up_kernel == N.MOE_GEMM_PIPE128 and cb.down_kernel == N.MOE_GEMM_PIPE128
-    af = N.moe_prefill_plan_get(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_AFFINE4), 4096)
+    af = N.moe_prefill_plan_get(N.dims(2048, 768, 256, 10, 1, format=N.MOE_FMT_AFFINE4), 4096)
     assert af.gate_up_kernel == N.MOE_GEMM_GENERAL and af.down_kernel == N.MOE_GEMM_GENERAL
+    # a measured row of the table for the affine format names a kernel it runs
+    af_t = N.moe_prefill_plan_get(N.dims(2048, 768, 512, 10, 1, format=N.MOE_FMT_AFFINE4), 4096)
+    assert af_t.gate_up_kernel != N.MOE_GEMM_PIPE128 and af_t.down_kernel != N.MOE_GEMM_PIPE128
     N.moe_debug_force_prefill_plan(N.moe_prefill_plan(64, 1, 2, 64))
     try:
         f = N.moe_prefill_plan_get(d, 100)

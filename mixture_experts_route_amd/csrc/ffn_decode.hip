@@ -414,13 +414,13 @@ __global__ __launch_bounds__(1024) void k_decode_gate_up(DecodeArgs a) {
 #pragma unroll
   for (int qi = 0; qi < kGuQuadsPerWave; ++qi) {
     const int qq = min(q0 + qi, NQ - 1);  // record (qq, row) at 64 (qq F + row)
-    cg[qi] = *(const uint4*)(gcode + (size_t)qq * F * kGroupBytes);
-    cu[qi] = *(const uint4*)(ucode + (size_t)qq * F * kGroupBytes);
-    sg[qi] = *(const uint2*)(gscale + (size_t)qq * F * kGroupScaleBytes);
-    su[qi] = *(const uint2*)(uscale + (size_t)qq * F * kGroupScaleBytes);
+    cg[qi] = ld16_nt_u4(gcode + (size_t)qq * F * kGroupBytes);
+    cu[qi] = ld16_nt_u4(ucode + (size_t)qq * F * kGroupBytes);
+    sg[qi] = ld8_nt_u2(gscale + (size_t)qq * F * kGroupScaleBytes);
+    su[qi] = ld8_nt_u2(uscale + (size_t)qq * F * kGroupScaleBytes);
     if constexpr (FMT == MOE_FMT_AFFINE4) {
-      mg[qi] = *(const uint2*)(gscale - lay.gate_scales + lay.gate_mins + (size_t)qq * F * kGroupScaleBytes);
-      mu[qi] = *(const uint2*)(uscale - lay.up_scales + lay.up_mins + (size_t)qq * F * kGroupScaleBytes);
+      mg[qi] = ld8_nt_u2(gscale - lay.gate_scales + lay.gate_mins + (size_t)qq * F * kGroupScaleBytes);
+      mu[qi] = ld8_nt_u2(uscale - lay.up_scales + lay.up_mins + (size_t)qq * F * kGroupScaleBytes);
     }
     __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
   }
@@ -624,10 +624,10 @@ MOE_DEV void down_body(const DecodeArgs& a, int task, int tile, uint16_t* smem, 
       const int qq = min(q0 + qi, NQ - 1);
 #pragma unroll
       for (int r = 0; r < RGW; ++r) {
-        cd[r][qi] = *(const uint4*)(dcode[r] + (size_t)qq * H * kGroupBytes);
-        sd[r][qi] = *(const uint2*)(dscale[r] + (size_t)qq * H * kGroupScaleBytes);
+        cd[r][qi] = ld16_nt_u4(dcode[r] + (size_t)qq * H * kGroupBytes);
+        sd[r][qi] = ld8_nt_u2(dscale[r] + (size_t)qq * H * kGroupScaleBytes);
         if constexpr (FMT == MOE_FMT_AFFINE4)
-          md[r][qi] = *(const uint2*)(dscale[r] - lay.down_scales + lay.down_mins + (size_t)qq * H * kGroupScaleBytes);
+          md[r][qi] = ld8_nt_u2(dscale[r] - lay.down_scales + lay.down_mins + (size_t)qq * H * kGroupScaleBytes);
       }
       __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
     }
@@ -795,9 +795,9 @@ __global__ __launch_bounds__(64 * NWV) void k_decode_down_rows1(DecodeArgs a) {
   u32x2 md[kAff ? MAXI : 1];  // affine format: the records' mins
   static_for<MAXI>([&](auto c) {
     constexpr int m = c.value;
-    cd[m] = *(const u32x4*)(blob[m] + lay.down_codes + ((size_t)it_q[m] * H + row) * kGroupBytes + 16 * g);
-    sd[m] = *(const u32x2*)(blob[m] + lay.down_scales + ((size_t)it_q[m] * H + row) * kGroupScaleBytes);
-    if constexpr (kAff) md[m] = *(const u32x2*)(blob[m] + lay.down_mins + ((size_t)it_q[m] * H + row) * kGroupScaleBytes);
+    cd[m] = ld16_nt(blob[m] + lay.down_codes + ((size_t)it_q[m] * H + row) * kGroupBytes + 16 * g);
+    sd[m] = ld8_nt(blob[m] + lay.down_scales + ((size_t)it_q[m] * H + row) * kGroupScaleBytes);
+    if constexpr (kAff) md[m] = ld8_nt(blob[m] + lay.down_mins + ((size_t)it_q[m] * H + row) * kGroupScaleBytes);
   });
   issue_fence();
   static_for<HC>([&](auto c) {
@@ -897,15 +897,13 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   const int task = blockIdx.x / a.tiles_gu;
   const int tile = blockIdx.x - task * a.tiles_gu;
   constexpr int H = 128 * QG * UNITS;
-  // the rows of every token of the step (row t = token t), loaded before the task is known
-  auto x_row = [&](int m) { return (const uint16_t*)a.x + (size_t)(m < a.T ? m : 0) * H; };
-  // ROWS * H / 8 chunks over 64 kPipeGuWaves threads
-  constexpr int XC = (ROWS * (H / 8) + 64 * kPipeGuWaves - 1) / (64 * kPipeGuWaves);
+  constexpr int NT = 64 * kPipeGuWaves;  // threads
+  // up to ROWS * H / 8 chunks of 16 bytes over the threads
+  constexpr int XC = (ROWS * (H / 8) + NT - 1) / NT;
   u32x4 xv[XC];
   // chunks in flight (fewer when the staged rows, or the affine format's min records, need many
   // registers)
   constexpr int NBUF = (XC > 8 || kAff) ? 2 : kPipeGuBufs;
-  stage_load(xv, ROWS, H, x_row);
   const DecodeTask tk = a.tasks[task];
   if (task >= a.ctrl[kCtrlNTasks]) return;
   const uint8_t* blob = task_blob(a.src, tk);
@@ -919,7 +917,20 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   const int n = lane & 15, g = lane >> 4;
   const int row = (tile * kPipeGuWaves + wave) * 16 + n;
   const int n_tok = __builtin_popcount(tk.tok_mask);
-  const int arow = n < n_tok ? task_token(tk.tok_mask, n) : ROWS;  // LDS row of this lane's slot
+  const int arow = n < n_tok ? n : ROWS;  // LDS row of this lane's token slot (ROWS: a zero row)
+  // Only the task's own token rows are staged, in slot order (most tasks of a step carry one
+  // token): n_tok H / 8 chunks; a round of chunks is loaded only if some thread has one (the
+  // condition is uniform across the workgroup, so no load sits under a per-lane branch).
+  auto x_row = [&](int m) { return (const uint16_t*)a.x + (size_t)task_token(tk.tok_mask, m < n_tok ? m : 0) * H; };
+  const int n_chunks = n_tok * (H / 8);
+  static_for<XC>([&](auto c) {
+    if (c.value * NT < n_chunks) {
+      int m, col;
+      chunk_pos(min((int)threadIdx.x + c.value * NT, n_chunks - 1), H, m, col);
+      xv[c.value] = *(const u32x4*)(x_row(m) + col);
+    }
+  });
+  __builtin_amdgcn_sched_barrier(0);  // these loads go out before the weight loads
   const Unpack uk = make_unpack();
   if constexpr (FMT == MOE_FMT_CB4) fill_codebook_bf16(a.src.cb, cbt);  // visible after the staging barrier
 
@@ -935,13 +946,13 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
 #pragma unroll
     for (int qi = 0; qi < QG; ++qi) {
       const int q = (u * QG + qi) * F;
-      cg[b][qi] = buf_load16(rs, voff_c, (int)lay.gate_codes + q * kGroupBytes);
-      cu[b][qi] = buf_load16(rs, voff_c, (int)lay.up_codes + q * kGroupBytes);
-      sg[b][qi] = buf_load8(rs, voff_s, (int)lay.gate_scales + q * kGroupScaleBytes);
-      su[b][qi] = buf_load8(rs, voff_s, (int)lay.up_scales + q * kGroupScaleBytes);
+      cg[b][qi] = buf_load16_nt(rs, voff_c, (int)lay.gate_codes + q * kGroupBytes);
+      cu[b][qi] = buf_load16_nt(rs, voff_c, (int)lay.up_codes + q * kGroupBytes);
+      sg[b][qi] = buf_load8_nt(rs, voff_s, (int)lay.gate_scales + q * kGroupScaleBytes);
+      su[b][qi] = buf_load8_nt(rs, voff_s, (int)lay.up_scales + q * kGroupScaleBytes);
       if constexpr (kAff) {
-        mg[b][qi] = buf_load8(rs, voff_s, (int)lay.gate_mins + q * kGroupScaleBytes);
-        mu[b][qi] = buf_load8(rs, voff_s, (int)lay.up_mins + q * kGroupScaleBytes);
+        mg[b][qi] = buf_load8_nt(rs, voff_s, (int)lay.gate_mins + q * kGroupScaleBytes);
+        mu[b][qi] = buf_load8_nt(rs, voff_s, (int)lay.up_mins + q * kGroupScaleBytes);
       }
       __builtin_amdgcn_sched_barrier(0);  // group order kept: the waits below are per group
     }
@@ -950,7 +961,7 @@ __global__ __launch_bounds__(64 * kPipeGuWaves) __attribute__((amdgpu_waves_per_
   // loads only, issued first)
   static_for<(NBUF < UNITS ? NBUF : UNITS)>([&](auto uc) { load_chunk(uc, decltype(uc)::value); });
   issue_fence();
-  stage_store_sync<false>(xv, smem, ROWS, H, x_row);
+  stage_store_sync<false>(xv, smem, n_tok, H, x_row);
 
   const float4v zero = {0.f, 0.f, 0.f, 0.f};
   // Summation order of the split kernel above (a partial sum per range of kGuQuadsPerWave groups,
@@ -1081,10 +1092,10 @@ MOE_DEV void down_pipe_body(const DecodeArgs& a, int task, int tile, uint16_t* s
       const int q = (u * QG + qi) * H;  // record (q, row) of the down matrix (H rows)
 #pragma unroll
       for (int r = 0; r < RGW; ++r) {
-        cd[b][r][qi] = buf_load16(rs, r == 0 ? voff_c0 : voff_c1, (int)lay.down_codes + q * kGroupBytes);
-        sd[b][r][qi] = buf_load8(rs, r == 0 ? voff_s0 : voff_s1, (int)lay.down_scales + q * kGroupScaleBytes);
+        cd[b][r][qi] = buf_load16_nt(rs, r == 0 ? voff_c0 : voff_c1, (int)lay.down_codes + q * kGroupBytes);
+        sd[b][r][qi] = buf_load8_nt(rs, r == 0 ? voff_s0 : voff_s1, (int)lay.down_scales + q * kGroupScaleBytes);
         if constexpr (kAff)
-          md[b][r][qi] = buf_load8(rs, r == 0 ? voff_s0 : voff_s1, (int)lay.down_mins + q * kGroupScaleBytes);
+          md[b][r][qi] = buf_load8_nt(rs, r == 0 ? voff_s0 : voff_s1, (int)lay.down_mins + q * kGroupScaleBytes);
       }
       __builtin_amdgcn_sched_barrier(0);
     }

@@ -4,7 +4,7 @@
 // per block, used as stored).  The layer: Betelgeuse news article, "mechanism" (10 routed + 1
 // shared expert per token).  Decode pays per byte of weights read (halogen README, "Bring your
 // own GGUF": an 8-bit trunk costs 2 GB more per token at 240 GB/s), so each selected expert's blob
-// is streamed once from HBM per step, whatever the number of tokens (1..8) that chose it.
+// is streamed once from HBM per step, whatever the number of tokens (1 to 16) that chose it.
 //
 // Design (gfx950).  A VALU GEMV over 4-bit weights spends ~2 vector instructions per weight
 // (unpack, dot, scale) and at one token that is as long as the weight stream itself.  Here the
@@ -21,12 +21,16 @@
 // What is left on the VALU is ~7 instructions per 8 weights of a lane plus the scale FMAs.
 //
 // Kernels of a step; no workgroup waits on another:
-//   gate/up: one workgroup per (task, 16-row tile of the F rows).  Its waves split the H inputs
-//     in runs of 4 groups (512 inputs), reduce through LDS, apply SwiGLU and store h = silu(g) * u
-//     of the task's tokens as bf16 hi + lo, ready to be the down projection's A operand.
-//   down: one wave per (task, 16 output rows) over all F inputs.  A rows are the (hi, lo) row
-//     pairs of the task's tokens (<= 8 tokens -> <= 16 rows), so one MFMA per block covers both
-//     parts.  Writes each pair's output row y_e.
+//   gate/up: the general kernel takes one workgroup per (task, 16-row tile of the F rows); its
+//     waves split the H inputs in runs of 4 groups (512 inputs) and reduce through LDS.  The
+//     pipelined kernel (4 to 16 bf16 tokens) gives each wave a whole 16-row tile over all H inputs,
+//     its weight loads one or two chunks ahead; the single-token kernel also selects the token's
+//     top-k from the logits itself.  Each applies SwiGLU and stores h = silu(g) * u of the task's
+//     tokens as bf16 hi + lo, ready to be the down projection's A operand.
+//   down: 16 output rows of a task per wave over all F inputs (general and pipelined kernels), or,
+//     for one token, the output rows outermost with the combine in the same workgroup.  A rows are
+//     the (hi, lo) row pairs of the task's tokens (a 16-row A block per 8 tokens), so one MFMA per
+//     block covers both parts.  Writes each pair's output row y_e.
 //   combine: y[t] = sum_j w[t][j] * y_{e_j}[t] (j = 0..k-1), then + y_shared[t]: fixed order,
 //     done inside the down launch by the last workgroup to finish each row tile (a counter per
 //     tile; the pair rows go through agent-scope stores and loads).

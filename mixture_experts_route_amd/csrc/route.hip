@@ -200,7 +200,7 @@ __global__ __launch_bounds__(1024) void k_lookup_small(const int32_t* __restrict
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode plan (one workgroup of 256 threads, <= 8 tokens): residency check + one task per
+// Decode plan (one workgroup of 256 threads, <= 16 tokens): residency check + one task per
 // distinct expert (ascending id) with the tokens that chose it, then the shared expert over all
 // tokens.  A task whose expert missed keeps slot -1 and the FFN kernels read the table entry when
 // they run, so slots filled after this check (doorbell path) are seen.
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void k_decode_plan(const int32_t* __restrict__
 }
 
 // ------------------------------------------------------------------------------------------
-// Decode route (<= 8 tokens): a router GEMV over all workgroups (each wave's first router row
+// Decode route (<= 16 tokens): a router GEMV over all workgroups (each wave's first router row
 // is loaded before the activations are staged); the last workgroup to finish then selects and
 // plans, in the same launch.  The logits cross the XCDs through agent-scope stores and an
 // agent-scope acquire in that workgroup (a release fence in every workgroup would write back each

@@ -755,6 +755,136 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   return hipGetLastError();
 }
 
+// ---- router logits for prefill, pipelined ------------------------------------------------------
+// logits[t][e] = bias[e] + sum_k x[t][k] Wr[e][k] over a work of RM tokens x 64 NS router rows:
+// four waves of 16 NS router rows each, every wave over all RM tokens.  The token tile goes through a
+// 3-stage LDS ring loaded through registers 3 chunks ahead (as in the expert GEMM above); the
+// router rows through a 3-slot register ring 2 chunks ahead.  Each logit takes the same sequence of
+// MFMA steps (128-input chunks, then 32-input steps, in ascending order) as the general kernel's
+// router mode, so both give the same bits.  XCD-aware: an XCD runs consecutive works, and the
+// router-row tiles of one token tile are consecutive, so they share that tile in the XCD's L2.
+template <int NK, int RM, int NS>
+__global__ __launch_bounds__(256, 2) void k_router_gemm_pipe(GemmArgs a) {
+  constexpr int kCols = 64 * NS;              // router rows per work: 4 waves x NS subtiles of 16
+  constexpr int MS = RM / 16;                 // 16-token subtiles
+  constexpr int kAPer = RM * (kKC / 8) / 256;  // A 16-byte pieces per thread per chunk
+  static_assert(kAPer >= 1 && kAPer * 256 == RM * (kKC / 8), "A pieces split evenly");
+  constexpr int BD = 3;                       // B slots (2 chunks ahead)
+  __shared__ __attribute__((aligned(1024))) uint16_t As[3][RM * kKC];
+
+  const int n_works = a.n_works;
+  const int per_xcd = (n_works + 7) >> 3;
+  const int local = (int)(blockIdx.x >> 3);
+  const int work = (int)(blockIdx.x & 7) * per_xcd + local;
+  if (local >= per_xcd || work >= n_works) return;
+  const int mtile = work / a.n_ntiles;
+  const int ntile = work - mtile * a.n_ntiles;
+  const int row0 = mtile * RM;
+  const int rows = min(RM, a.T - row0);
+  const int H = a.H, E = a.E;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  const int ms = (rows + 15) >> 4;
+
+  // B: lane (g, n) of subtile s takes router row e_s, inputs 32 d + 8 g .. +7 of each 32-input step d
+  const int e0 = ntile * kCols + wave * 16 * NS + n;  // e_s = e0 + 16 s < E: E % kCols == 0
+  const uint16_t* wr = a.wr + (size_t)e0 * H + 8 * g;
+  u32x4 b[BD][NS][4];
+  auto load_b = [&](auto slot_c, int kc) {
+    constexpr int sl = decltype(slot_c)::value;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int d = 0; d < 4; ++d) b[sl][s][d] = *(const u32x4*)(wr + (size_t)16 * s * H + kc * kKC + 32 * d);
+  };
+
+  // A: piece j of this thread = token row r_j = (tid >> 4) + 16 j, logical 16-byte chunk tid & 15,
+  // stored at chunk lc ^ (r & 15) of its LDS row
+  const int lc = threadIdx.x & 15;
+  const int a_dst0 = (threadIdx.x >> 4) * kKC + ((lc ^ ((threadIdx.x >> 4) & 15)) * 8);
+  int a_src[kAPer];
+#pragma unroll
+  for (int j = 0; j < kAPer; ++j) {
+    const int r = (threadIdx.x >> 4) + 16 * j;
+    a_src[j] = (row0 + (r < rows ? r : 0)) * H + lc * 8;  // padding rows copy row 0 (outputs dropped)
+  }
+  auto load_a = [&](u32x4 (&v)[kAPer], int kc) {
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) v[j] = *(const u32x4*)(a.a16 + a_src[j] + kc * kKC);
+  };
+  auto store_a = [&](const u32x4 (&v)[kAPer], uint16_t* buf) {
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) *(u32x4*)(buf + a_dst0 + 16 * kKC * j) = v[j];
+  };
+  auto barrier = [&]() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  float4v acc[MS][NS];
+#pragma unroll
+  for (int i = 0; i < MS; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[i][s] = (float4v){0.f, 0.f, 0.f, 0.f};
+
+  // prologue: A(0), A(1) in LDS, A(2) and B(0), B(1) in flight
+  u32x4 av[kAPer];
+  {
+    u32x4 a0[kAPer];
+    load_a(a0, 0);
+    load_a(av, 1);
+    load_b(std::integral_constant<int, 0>{}, 0);
+    if constexpr (NK > 1) load_b(std::integral_constant<int, 1>{}, 1);
+    store_a(a0, As[0]);
+    if constexpr (NK > 1) store_a(av, As[1]);
+    if constexpr (NK > 2) load_a(av, 2);
+    barrier();
+  }
+  static_for<NK>([&](auto kc_c) {
+    constexpr int kc = decltype(kc_c)::value;
+    constexpr int sl = kc % BD;
+    if constexpr (kc + BD - 1 < NK) load_b(std::integral_constant<int, (kc + BD - 1) % BD>{}, kc + BD - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* Ab = As[kc % 3];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int pcol = ((4 * d + g) ^ n) * 8;
+#pragma unroll
+      for (int i = 0; i < MS; ++i) {
+        if (i < ms) {
+          const bf16x8 af = *(const bf16x8*)(Ab + (16 * i + n) * kKC + pcol);
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, __builtin_bit_cast(bf16x8, b[sl][s][d]), acc[i][s], 0, 0, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (kc + 2 < NK) {
+      store_a(av, As[(kc + 2) % 3]);  // its stage was last read in chunk kc - 1
+      if constexpr (kc + 3 < NK) load_a(av, kc + 3);
+    }
+    if constexpr (kc + 1 < NK) barrier();
+  });
+
+  // epilogue: lane holds D[16 i + 4 g + r][16 s + n]
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int e = e0 + 16 * s;
+    const float bv = a.bias ? a.bias[e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+      if (i >= ms) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * i + 4 * g + r;
+        if (row < rows) a.y_out[(size_t)(row0 + row) * E + e] = acc[i][s][r] + bv;
+      }
+    }
+  }
+}
+
 hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const float* bias, int T, int E, int H,
                               float* logits, int rows_per_work, hipStream_t st) {
   GemmArgs a{};
@@ -765,6 +895,23 @@ hipError_t launch_router_gemm(const void* x_bf16, const void* Wr_bf16, const flo
   a.wr = (const uint16_t*)Wr_bf16;
   a.bias = bias;
   a.y_out = logits;
+  // the pipelined kernel at the covered widths (the plan's token rows per work, 128 router rows)
+  const int nk = H / kKC;
+  constexpr int kRgNS = 2;  // 128 router rows per work (measured: 4K 40 -> 39 us, 32K 189 -> 168 us against 64)
+  if (E % (64 * kRgNS) == 0 && H % kKC == 0 && (nk == 8 || nk == 16 || nk == 32)) {
+    const int rm = rows_per_work == kRouterTallRows ? 64 : 32;
+    a.n_ntiles = E / (64 * kRgNS);
+    a.n_works = ((T + rm - 1) / rm) * a.n_ntiles;
+    auto go = [&](auto kern) { kern<<<round8(a.n_works), 256, 0, st>>>(a); return hipGetLastError(); };
+    if (rm == 64) {
+      if (nk == 8) return go(k_router_gemm_pipe<8, 64, kRgNS>);
+      if (nk == 16) return go(k_router_gemm_pipe<16, 64, kRgNS>);
+      return go(k_router_gemm_pipe<32, 64, kRgNS>);
+    }
+    if (nk == 8) return go(k_router_gemm_pipe<8, 32, kRgNS>);
+    if (nk == 16) return go(k_router_gemm_pipe<16, 32, kRgNS>);
+    return go(k_router_gemm_pipe<32, 32, kRgNS>);
+  }
   a.n_ntiles = (E + kNTileW - 1) / kNTileW;
   if (rows_per_work == kRouterTallRows) {
     a.n_works = ((T + kRouterTallRows - 1) / kRouterTallRows) * a.n_ntiles;

@@ -107,14 +107,17 @@ static const TunedPlanRow kTunedPlans[] = {
 static PrefillPlan g_forced_plan;
 static bool g_plan_forced = false;
 
-// Without a table row: 128-row items, the pipelined kernels where they are built, the router GEMM
-// with 32-row works up to 16K tokens and 64-row works above (half the router-weight re-reads,
-// still thousands of works).
-static PrefillPlan default_plan(int T) {
+// Without a table row: 128-row items, the pipelined kernels where they are built, and the router
+// GEMM's token rows per work where each router kernel was measured faster: 64-row works from 3,072
+// tokens with the pipelined router kernel (E a multiple of 128, H / 128 = 8, 16 or 32), from 16K
+// tokens with the general one (half the router-weight re-reads, still thousands of works).
+static PrefillPlan default_plan(const moe_dims* d, int T) {
   PrefillPlan p;
   p.item_rows = 128;
   p.gate_up = p.down = kGemmPipe128;
-  p.router_rows = T > 16384 ? 64 : 32;
+  const int nk = d->hidden / 128;
+  const bool pipe_router = d->n_experts % 128 == 0 && d->hidden % 128 == 0 && (nk == 8 || nk == 16 || nk == 32);
+  p.router_rows = T >= (pipe_router ? 3072 : 16385) ? 64 : 32;
   return p;
 }
 
@@ -126,7 +129,7 @@ static PrefillPlan plan_for(const moe_dims* d, int T) {
         T >= r.t_lo && T <= r.t_hi)
       return r.plan;
   }
-  return default_plan(T);
+  return default_plan(d, T);
 }
 
 static int check_plan(const moe_prefill_plan* p) {

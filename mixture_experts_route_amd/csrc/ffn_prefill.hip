@@ -35,12 +35,12 @@ constexpr int kMSub = kTileRows / 16;     // 16-row subtiles per item
 constexpr int kNTileW = 256;              // weight rows per workgroup (4 waves x 64)
 
 enum GemmMode { kGateUp = 0, kDown = 1, kRouter = 2 };
-// Router GEMM rows per work: 32 (not a full 128-row tile), so that a 4K-token call has 256 works
-// (x 2 router tiles) instead of 64 and the router streams through every CU; above kRouterTallFrom
-// tokens there are works enough with kRouterTallRows rows, which read the router weights fewer times.
+// Router GEMM token rows per work (the plan's choice): 32 or 64.  In the general kernel's router
+// mode, 32-row works give a 4K-token call works enough to stream the router through every CU; the
+// pipelined router kernel below (128 router rows per work) is faster with 64-row works from ~3K
+// tokens (the default plan's thresholds follow these measurements).
 constexpr int kRouterTileRows = 32;
 constexpr int kRouterTallRows = 64;
-constexpr int kRouterTallFrom = 16384;
 
 struct GemmArgs {
   ExpertSource src;

@@ -629,10 +629,27 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
 
 // x (bf16) -> fp16, exact for values inside the fp16 normal range; a value beyond the fp16 range
 // is reported (MOE_DERR_RANGE).
+// Eight values per thread and step (16-byte loads and stores), then a tail of single values.
 __global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* __restrict__ x, _Float16* __restrict__ y,
                                                      size_t n, int32_t* __restrict__ ctrl) {
+  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
   bool bad = false;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t n8 = n / 8;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 w = ((const uint4*)x)[i];
+    const uint32_t word[4] = {w.x, w.y, w.z, w.w};
+    half8v h;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = __uint_as_float(word[j] << 16), hi = __uint_as_float(word[j] & 0xFFFF0000u);
+      bad |= f16_out_of_range(lo) | f16_out_of_range(hi);
+      h[2 * j] = (_Float16)lo;
+      h[2 * j + 1] = (_Float16)hi;
+    }
+    ((half8v*)y)[i] = h;
+  }
+  for (size_t i = 8 * n8 + blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += stride) {
     const float v = __uint_as_float((uint32_t)x[i] << 16);
     bad |= f16_out_of_range(v);
     y[i] = (_Float16)v;
@@ -646,30 +663,30 @@ __global__ __launch_bounds__(256) void k_bf16_to_f16(const uint16_t* __restrict_
 __global__ __launch_bounds__(256) void k_prefill_combine(const _Float16* __restrict__ y_rows,
                                                           const int32_t* __restrict__ inv, int T, int k,
                                                           int n_shared, int H, float* __restrict__ y) {
-  typedef _Float16 half4v __attribute__((ext_vector_type(4)));
-  const int H4 = H / 4;
-  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)T * H4;
+  typedef _Float16 half8v __attribute__((ext_vector_type(8)));
+  const int H8 = H / 8;  // 8 outputs per thread and step (16-byte row loads)
+  for (size_t idx = blockIdx.x * (size_t)blockDim.x + threadIdx.x; idx < (size_t)T * H8;
        idx += (size_t)gridDim.x * blockDim.x) {
-    const int t = (int)(idx / H4), o4 = (int)(idx - (size_t)t * H4);
+    const int t = (int)(idx / H8), o8 = (int)(idx - (size_t)t * H8);
     int pos[kMaxK + 1];
 #pragma unroll
     for (int j = 0; j < kMaxK; ++j) pos[j] = j < k ? inv[t * k + (j < k ? j : 0)] : -1;
     pos[kMaxK] = n_shared ? inv[T * k + t] : -1;
-    half4v v[kMaxK + 1];
+    half8v v[kMaxK + 1];
 #pragma unroll
     for (int j = 0; j <= kMaxK; ++j)
-      v[j] = ((const half4v*)(y_rows + (size_t)(pos[j] < 0 ? 0 : pos[j]) * H))[o4];
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      v[j] = ((const half8v*)(y_rows + (size_t)(pos[j] < 0 ? 0 : pos[j]) * H))[o8];
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j <= kMaxK; ++j) {
       if (pos[j] >= 0) {
-        acc.x += (float)v[j].x;
-        acc.y += (float)v[j].y;
-        acc.z += (float)v[j].z;
-        acc.w += (float)v[j].w;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] += (float)v[j][c];
       }
     }
-    ((float4*)(y + (size_t)t * H))[o4] = acc;
+    float4* out = (float4*)(y + (size_t)t * H) + 2 * o8;
+    out[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    out[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
   }
 }
 
@@ -748,7 +765,7 @@ hipError_t launch_prefill_ffn(int H, int F, int k, int E, int n_shared, int T, c
   a.y16_out = b.y_rows;
   if ((err = run(std::integral_constant<int, kDown>{}, plan.down)) != hipSuccess) return err;
 
-  const size_t nc = (size_t)T * (H / 4);
+  const size_t nc = (size_t)T * (H / 8);
   grid = (int)((nc + 255) / 256);
   if (grid > 8192) grid = 8192;
   k_prefill_combine<<<grid, 256, 0, st>>>(b.y_rows, g.inv, T, k, n_shared, H, y);

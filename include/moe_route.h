@@ -23,7 +23,10 @@
  *
  * Conventions for every entry point
  *   - Tensor pointers are device pointers owned by the caller (allocated by any means);
- *     the library never allocates or frees device memory.  Its only process-wide state is
+ *     the library never allocates or frees device memory.  The activations x, the outputs y
+ *     and the router matrix are moved with 16-byte vector accesses and must be 16-byte
+ *     aligned (a hipMalloc'd buffer, and a whole-token slice of one, is); a misaligned one is
+ *     MOE_EINVAL.  Its only process-wide state is
  *     the profiling selection of moe_debug_kernel_events (off unless a caller sets it).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Work is
  *     enqueued asynchronously on it; the call returns once it is enqueued.

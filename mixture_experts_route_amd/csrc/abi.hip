@@ -175,6 +175,9 @@ static int check_weights(const moe_dims* d, const moe_layer_weights* w, const in
 
 static int check_dtype(int dt) { return (dt == MOE_F32 || dt == MOE_BF16) ? MOE_OK : MOE_EUNSUPPORTED; }
 
+// Activations, outputs and the router matrix are moved with 16-byte vector accesses.
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
 static int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
 static int32_t* ctrl_of(void* ws) { return (int32_t*)ws; }
@@ -310,9 +313,11 @@ static int check_layer_args(const moe_dims* dims, const moe_layer_weights* w, co
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!x || !y || n_tokens < 1) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y)) return MOE_EINVAL;
   if ((rc = check_dtype(x_dtype))) return rc;
   if ((rc = check_weights(dims, w, table))) return rc;
   if (!w->router || (rc = check_dtype(w->router_dtype))) return rc ? rc : MOE_EINVAL;
+  if (!aligned16(w->router)) return MOE_EINVAL;
   if ((rc = check_bell(bell))) return rc;
   if (bell && !table) return MOE_EINVAL;
   // a doorbell goes with a decode-sized call, whose plan publishes the step's selections
@@ -427,6 +432,7 @@ MOE_API int moe_route(const moe_dims* dims, const void* x, int32_t x_dtype, int3
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!x || !router || !topk_ids || !topk_w || n_tokens < 1) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(router)) return MOE_EINVAL;
   if ((rc = check_dtype(x_dtype)) || (rc = check_dtype(router_dtype))) return rc;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
   return do_route(dims, x, x_dtype, n_tokens, router, router_dtype, bias, topk_ids, topk_w, logits_or_null, ws,
@@ -471,6 +477,7 @@ MOE_API int moe_expert_ffn_decode(const moe_dims* dims, const moe_layer_weights*
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!x || !topk_ids || !topk_w || !y) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y)) return MOE_EINVAL;
   if ((rc = check_dtype(x_dtype))) return rc;
   if (n_tokens < 1 || n_tokens > decode_limit(dims, x_dtype)) return MOE_EINVAL;
   if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
@@ -486,6 +493,7 @@ MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights
   int rc = check_dims(dims);
   if (rc) return rc;
   if (!x || !topk_ids || !topk_w || !y || n_tokens < 1) return MOE_EINVAL;
+  if (!aligned16(x) || !aligned16(y)) return MOE_EINVAL;
   if (x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
   if ((rc = prefill_shape_ok(dims))) return rc;

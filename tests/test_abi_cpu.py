@@ -106,6 +106,29 @@ def test_invalid_arguments_rejected_on_host(N):
                None) == -2
 
 
+def test_misaligned_activations_rejected_on_host(N):
+    """x, y and the router matrix must be 16-byte aligned (the kernels move them with 16-byte vector
+    accesses): an offset of one bf16 element is refused with MOE_EINVAL on the host, before any
+    pointer is used."""
+    d = N.dims(2048, 768, 512, 10, 1)
+    fake, odd = 1 << 20, (1 << 20) + 2
+    w = N.moe_layer_weights(fake, 1, None, fake, 2_654_208, 512, 1 << 24)
+    w_odd_router = N.moe_layer_weights(odd, 1, None, fake, 2_654_208, 512, 1 << 24)
+    route = N.raw("moe_route")
+    assert route(ctypes.byref(d), odd, 1, 1, fake, 1, None, fake, fake, None, fake, 1 << 30, None) == N.MOE_EINVAL
+    assert route(ctypes.byref(d), fake, 1, 1, odd, 1, None, fake, fake, None, fake, 1 << 30, None) == N.MOE_EINVAL
+    dec = N.raw("moe_expert_ffn_decode")
+    pre = N.raw("moe_expert_ffn_prefill")
+    lay = N.raw("moe_layer_forward")
+    for x, y in ((odd, fake), (fake, odd)):
+        assert dec(ctypes.byref(d), ctypes.byref(w), None, x, 1, 1, fake, fake, y, fake, 1 << 30, None) == N.MOE_EINVAL
+        assert pre(ctypes.byref(d), ctypes.byref(w), None, x, 1, 64, fake, fake, y, fake, 1 << 30, None) == N.MOE_EINVAL
+        assert lay(ctypes.byref(d), ctypes.byref(w), None, None, x, 1, 1, y, None, None, fake, 1 << 30,
+                   None) == N.MOE_EINVAL
+    assert lay(ctypes.byref(d), ctypes.byref(w_odd_router), None, None, fake, 1, 1, fake, None, None, fake, 1 << 30,
+               None) == N.MOE_EINVAL
+
+
 @pytest.mark.parametrize("n_tokens", [0, -1])
 def test_empty_batch_rejected_on_host(N, n_tokens):
     """An empty (or negative) token count is refused with MOE_EINVAL by every entry point that takes

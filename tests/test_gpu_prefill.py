@@ -181,6 +181,36 @@ def test_prefill_deterministic_and_batch_invariant_rows(N, dev, model_layer):
     assert torch.equal(y1, y2)
 
 
+def test_prefill_route_model_shape(N, dev, model_layer):
+    """The prefill router GEMM and top-k at the model shape (the pipelined router kernel: 32-row
+    token works below ~3K tokens, 64-row works above, ragged last works at 300 and 5,000 tokens)
+    against the oracle: logits within fp32 accumulation of the fp64 ones, ids exact away from near
+    ties, weights within 1e-5; and a token's logits bitwise the same whatever batch it is routed in
+    (each logit takes the same MFMA steps in every work shape)."""
+    layer = model_layer
+    d = layer.dims()
+    T = 5000
+    x, x64 = layer.x(T, 31, dev)
+    got = {}
+    for n in (T, 300, 40):
+        ws = _ws(N, d, n, dev)
+        ids = torch.full((n, layer.k), -7, dtype=torch.int32, device=dev)
+        w = torch.zeros((n, layer.k), dtype=torch.float32, device=dev)
+        logits = torch.zeros((n, layer.E), dtype=torch.float32, device=dev)
+        N.moe_route(d, x[:n], n, layer.router, layer.bias, ids, w, logits, ws)
+        torch.cuda.synchronize()
+        assert N.moe_check_device_error(ws) == 0
+        got[n] = (logits.cpu().numpy(), ids.cpu().numpy(), w.cpu().numpy())
+    lg = got[T][0]
+    assert np.array_equal(got[300][0], lg[:300]) and np.array_equal(got[40][0], lg[:40])
+    rows = np.r_[0:40, 260:340, 4900:5000]  # the small batches, a work boundary, the ragged tail
+    l64, _, ids_ref, w_ref = O.route(x64[rows], layer.router_np.astype(np.float64), layer.bias_np, layer.k)
+    assert np.max(np.abs(lg[rows].astype(np.float64) - l64)) <= 1e-5 * max(1.0, np.max(np.abs(l64)))
+    ok = ~near_tie_tokens(l64, layer.k)
+    assert np.array_equal(got[T][1][rows][ok], ids_ref[ok])
+    assert np.max(np.abs(got[T][2][rows][ok] - w_ref[ok])) <= 1e-5
+
+
 def test_prefill_not_resident_is_an_error(N, dev, model_layer):
     layer = model_layer
     d = layer.dims()

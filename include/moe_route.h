@@ -116,8 +116,9 @@ enum moe_device_error {
  * supported quantization block; anything else is MOE_EUNSUPPORTED).
  * Supported: H and F multiples of 128 (whole groups of the code layout; else MOE_EINVAL)
  * and at most 4096; 1 <= k <= 16; k <= E <= 1024 (beyond: MOE_EUNSUPPORTED).  The prefill
- * path (more than MOE_DECODE_MAX_TOKENS tokens) further needs H % 256 == 0 and bf16
- * activations and router. */
+ * path (more than MOE_DECODE_MAX_TOKENS tokens) further needs H % 256 == 0, bf16
+ * activations and router, and n_tokens * H < 2^31 (1,048,575 tokens at H = 2048; beyond:
+ * MOE_EUNSUPPORTED). */
 typedef struct moe_dims {
   int32_t hidden;
   int32_t ffn;

@@ -285,7 +285,9 @@ static GroupBuffers group_buffers(const WsLayout& L, void* ws) {
   return g;
 }
 
-static int prefill_shape_ok(const moe_dims* d) {
+// The prefill kernels address activation rows with 32-bit element offsets: T H < 2^31.
+static int prefill_shape_ok(const moe_dims* d, int T) {
+  if ((int64_t)T * d->hidden > INT32_MAX) return MOE_EUNSUPPORTED;
   return (d->hidden % 256 == 0 && d->ffn % 128 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
 }
 
@@ -325,7 +327,7 @@ static int check_layer_args(const moe_dims* dims, const moe_layer_weights* w, co
   if (bell && n_tokens > limit) return MOE_EUNSUPPORTED;
   if (n_tokens > limit) {
     if (x_dtype != MOE_BF16 || w->router_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
-    if ((rc = prefill_shape_ok(dims))) return rc;
+    if ((rc = prefill_shape_ok(dims, n_tokens))) return rc;
   }
   return MOE_OK;
 }
@@ -496,7 +498,7 @@ MOE_API int moe_expert_ffn_prefill(const moe_dims* dims, const moe_layer_weights
   if (!aligned16(x) || !aligned16(y)) return MOE_EINVAL;
   if (x_dtype != MOE_BF16) return MOE_EUNSUPPORTED;
   if ((rc = check_weights(dims, w, layer_table_or_null))) return rc;
-  if ((rc = prefill_shape_ok(dims))) return rc;
+  if ((rc = prefill_shape_ok(dims, n_tokens))) return rc;
   if ((rc = check_ws(dims, n_tokens, ws, ws_bytes))) return rc;
   return do_prefill_ffn(dims, w, layer_table_or_null, x, n_tokens, topk_ids, topk_w, y, ws, (hipStream_t)stream);
 }

@@ -493,7 +493,11 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   // ---- activations: piece j of this thread = row r_j, logical 16-byte chunk lc of the K chunk ----
   const int a_ld = MODE == kDown ? F : H;
   const int lc = threadIdx.x & 15;
-  int a_src[kPAPer];  // element offset of the piece in the activation matrix
+  // element offset of each piece from a_base: gate/up reads token rows of x16 (T H elements, under
+  // 2^31: checked on the host); down reads the item's own rows of h16, counted from the item's
+  // first row, so the offsets stay small however many rows the call has
+  const uint16_t* a_base = MODE == kGateUp ? a.a16 : a.a16 + (size_t)it.row0 * a_ld;
+  int a_src[kPAPer];
   // LDS element offset of piece j: row r_j = r_0 + 32 j has the same r & 15, so only the row moves
   const int a_dst0 = (threadIdx.x >> 4) * kKC + ((lc ^ ((threadIdx.x >> 4) & 15)) * 8);
   constexpr int kRowStep = 64 * kPWaves / 16;
@@ -502,12 +506,12 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   for (int j = 0; j < kPAPer; ++j) {
     const int r = (threadIdx.x >> 4) + kRowStep * j;
     const int rr = r < it.rows ? r : 0;  // padding rows copy row 0 (their outputs are dropped)
-    const int src = MODE == kGateUp ? a.row_tok[it.row0 + rr] : it.row0 + rr;
+    const int src = MODE == kGateUp ? a.row_tok[it.row0 + rr] : rr;
     a_src[j] = src * a_ld + lc * 8;
   }
   auto load_a = [&](u32x4 (&v)[kPAPer], int kc) {
 #pragma unroll
-    for (int j = 0; j < kPAPer; ++j) v[j] = *(const u32x4*)(a.a16 + a_src[j] + kc * kKC);
+    for (int j = 0; j < kPAPer; ++j) v[j] = *(const u32x4*)(a_base + a_src[j] + kc * kKC);
   };
   auto store_a = [&](const u32x4 (&v)[kPAPer], uint16_t* buf) {
 #pragma unroll
@@ -819,15 +823,16 @@ __global__ __launch_bounds__(256, 2) void k_router_gemm_pipe(GemmArgs a) {
   // stored at chunk lc ^ (r & 15) of its LDS row
   const int lc = threadIdx.x & 15;
   const int a_dst0 = (threadIdx.x >> 4) * kKC + ((lc ^ ((threadIdx.x >> 4) & 15)) * 8);
+  const uint16_t* a_base = a.a16 + (size_t)row0 * H;  // offsets from the work's first token row
   int a_src[kAPer];
 #pragma unroll
   for (int j = 0; j < kAPer; ++j) {
     const int r = (threadIdx.x >> 4) + 16 * j;
-    a_src[j] = (row0 + (r < rows ? r : 0)) * H + lc * 8;  // padding rows copy row 0 (outputs dropped)
+    a_src[j] = (r < rows ? r : 0) * H + lc * 8;  // padding rows copy row 0 (outputs dropped)
   }
   auto load_a = [&](u32x4 (&v)[kAPer], int kc) {
 #pragma unroll
-    for (int j = 0; j < kAPer; ++j) v[j] = *(const u32x4*)(a.a16 + a_src[j] + kc * kKC);
+    for (int j = 0; j < kAPer; ++j) v[j] = *(const u32x4*)(a_base + a_src[j] + kc * kKC);
   };
   auto store_a = [&](const u32x4 (&v)[kAPer], uint16_t* buf) {
 #pragma unroll

@@ -104,6 +104,9 @@ def test_invalid_arguments_rejected_on_host(N):
     pre = N.raw("moe_expert_ffn_prefill")
     assert pre(ctypes.byref(d), ctypes.byref(w), None, 1 << 20, 0, 64, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 30,
                None) == -2
+    # and n_tokens * H below 2^31 (32-bit activation offsets)
+    assert pre(ctypes.byref(d), ctypes.byref(w), None, 1 << 20, 1, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20,
+               1 << 62, None) == -2
 
 
 def test_misaligned_activations_rejected_on_host(N):

@@ -477,17 +477,30 @@ __global__ __launch_bounds__(64 * kPWaves, 1) void k_expert_gemm_pipe(GemmArgs a
   u32x4 bc[BD][4];
   u32x2 bs[BD][4];
   u32x2 bm[kAff ? BD : 1][4];  // affine format: the records' mins
+  // a bucket with one item: its weights are read once, with the non-temporal hint (the items of a
+  // larger bucket re-read theirs through the L2)
+  const bool w_once = (it.pad & kItemOnly) != 0;
   auto load_b = [&](auto slot_c, int kc) {
     constexpr int sl = decltype(slot_c)::value;
+    auto go = [&](auto nt_c) {
+      constexpr bool kNT = decltype(nt_c)::value;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int rsub = MODE == kGateUp ? 16 * (s & 1) : 16 * s;  // row offset of the subtile
-      const bool up = MODE == kGateUp && s >= 2;
-      bc[sl][s] = buf_load16(rs, voff_c + rsub * kGroupBytes, cb0 + (up ? cb_up : 0) + kc * wrows * kGroupBytes);
-      bs[sl][s] = buf_load8(rs, voff_s + rsub * kGroupScaleBytes, sb0 + (up ? sb_up : 0) + kc * wrows * kGroupScaleBytes);
-      if constexpr (kAff)
-        bm[sl][s] = buf_load8(rs, voff_s + rsub * kGroupScaleBytes, mb0 + (up ? sb_up : 0) + kc * wrows * kGroupScaleBytes);
-    }
+      for (int s = 0; s < 4; ++s) {
+        const int rsub = MODE == kGateUp ? 16 * (s & 1) : 16 * s;  // row offset of the subtile
+        const bool up = MODE == kGateUp && s >= 2;
+        const int vc = voff_c + rsub * kGroupBytes, vs = voff_s + rsub * kGroupScaleBytes;
+        const int oc = cb0 + (up ? cb_up : 0) + kc * wrows * kGroupBytes;
+        const int os = sb0 + (up ? sb_up : 0) + kc * wrows * kGroupScaleBytes;
+        bc[sl][s] = kNT ? buf_load16_nt(rs, vc, oc) : buf_load16(rs, vc, oc);
+        bs[sl][s] = kNT ? buf_load8_nt(rs, vs, os) : buf_load8(rs, vs, os);
+        if constexpr (kAff) {
+          const int om = mb0 + (up ? sb_up : 0) + kc * wrows * kGroupScaleBytes;
+          bm[sl][s] = kNT ? buf_load8_nt(rs, vs, om) : buf_load8(rs, vs, om);
+        }
+      }
+    };
+    if (w_once) go(std::true_type{});
+    else go(std::false_type{});
   };
 
   // ---- activations: piece j of this thread = row r_j, logical 16-byte chunk lc of the K chunk ----

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(1024) void k_group_offsets(const int32_t* __restric
       it.bucket = e;
       it.row0 = off + i * item_rows;
       it.rows = min(item_rows, c - i * item_rows);
-      it.pad = 0;
+      it.pad = n_it == 1 ? kItemOnly : 0;
       items[ipos + i] = it;
     }
   }
@@ -130,7 +130,7 @@ __global__ __launch_bounds__(1024) void k_group_offsets(const int32_t* __restric
         it.bucket = E;
         it.row0 = total_rows + r0;
         it.rows = min(item_rows, T - r0);
-        it.pad = 0;
+        it.pad = T <= item_rows ? kItemOnly : 0;
         items[n_all++] = it;
       }
     } else {

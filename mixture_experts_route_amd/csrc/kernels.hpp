@@ -96,8 +96,11 @@ struct TileItem {
   int32_t bucket;
   int32_t row0;  // first sorted row
   int32_t rows;  // 1..kTileRows
-  int32_t pad;
+  int32_t pad;   // flags: kItemOnly
 };
+// The item holds all of its bucket's rows: its works are the only readers of the bucket's weights
+// in the call, so they load them with the non-temporal hint.
+constexpr int32_t kItemOnly = 1;
 
 // Upper bound on work items: sum over non-empty buckets of ceil(c / item_rows).
 inline int prefill_max_items(int T, int k, int E, int n_shared, int item_rows = kMinItemRows) {

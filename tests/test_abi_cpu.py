@@ -318,3 +318,38 @@ def test_prefill_plan_get_and_force(N):
     for bad in ((96, 0, 0, 32), (128, 1, 0, 32), (64, 3, 0, 32), (64, 0, 0, 48)):
         with pytest.raises(N.MoeError):
             N.moe_debug_force_prefill_plan(N.moe_prefill_plan(*bad))
+
+
+def _tuned_rows():
+    path = os.path.join(ROOT, "mixture_experts_route_amd", "csrc", "tuned_plans.inc")
+    pat = re.compile(r"^\{(\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), \{(\d+), (\d+), (\d+), (\d+)\}\},")
+    return [tuple(int(v) for v in m.groups()) for m in map(pat.match, open(path)) if m]
+
+
+def test_tuned_plan_table_rows_are_what_the_library_returns(N):
+    """Every row of the measured plan table (a range of token counts for one layer shape and weight
+    format) is the plan the library picks at the range's first, middle and last token count; the rows
+    of one shape and format cover 17 tokens upwards without gap or overlap; below the table, and for a
+    shape with no row, the default plan applies (its router GEMM switches to 64-row works at 3,072
+    tokens with the pipelined router kernel)."""
+    rows = _tuned_rows()
+    assert len(rows) >= 9
+    groups = {}
+    for r in rows:
+        groups.setdefault(r[:5], []).append(r)
+    for key, rs in groups.items():
+        rs.sort(key=lambda r: r[5])
+        assert rs[0][5] == 17 and rs[-1][6] == 2147483647, key
+        for a, b in zip(rs, rs[1:]):
+            assert b[5] == a[6] + 1, (key, a, b)
+    for H, F, E, k, fmt, lo, hi, item_rows, gu, dn, rr in rows:
+        d = N.dims(H, F, E, k, 1, format=fmt)
+        for T in sorted({lo, (lo + min(hi, 1 << 19)) // 2, min(hi, 1 << 19)}):
+            p = N.moe_prefill_plan_get(d, T)
+            assert (p.item_rows, p.gate_up_kernel, p.down_kernel, p.router_rows) == (item_rows, gu, dn, rr), (fmt, T)
+    below = N.moe_prefill_plan_get(N.dims(2048, 768, 512, 10, 1), 16)
+    assert (below.item_rows, below.gate_up_kernel, below.down_kernel, below.router_rows) == (
+        128, N.MOE_GEMM_PIPE128, N.MOE_GEMM_PIPE128, 32)
+    d256 = N.dims(2048, 768, 256, 10, 1)
+    assert N.moe_prefill_plan_get(d256, 3071).router_rows == 32
+    assert N.moe_prefill_plan_get(d256, 3072).router_rows == 64
